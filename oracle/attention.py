@@ -1,0 +1,50 @@
+"""Bidirectional canvas attention (oracle side; test infrastructure only).
+
+What the pages fix: during a denoising step every canvas token attends to the
+committed history held in the KV cache and to all canvas tokens, with no causal
+mask (DiffusionGemma Technical Report, section 6 "Attention" and section 9.1;
+explainer "DiffusionGemma: Google's open diffusion LLM", section
+"Block-autoregressive generation, one canvas after another", quoting report
+section 3.1).  The pages give neither a scale, a soft-cap nor the head grouping;
+the reading taken is standard scaled dot-product attention with scale 1/sqrt(D),
+no soft-cap, rotary embedding already applied to the inputs, and grouped-query
+heads where query head h reads KV head h // (Hq / Hkv).
+
+Definition computed (float64 throughout, inputs widened exactly):
+    K = [K_prefix ; K_canvas],  V = [V_prefix ; V_canvas]     (keys j = 0 .. P+N-1)
+    O[i, h] = sum_j softmax_j(scale * q[i, h] . K[j, h // G]) * V[j, h // G]
+
+Pins (tests/test_oracle_attention.py): explicit-loop brute force on tiny shapes;
+torch's CPU scaled_dot_product_attention with repeated KV heads; closed forms
+(one key gives v; scale 0 gives the mean of V; constant V gives that constant);
+invariance under a permutation applied to canvas (or prefix) keys and values.
+"""
+import numpy as np
+
+
+def canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, scale=None):
+    """q [N,Hq,D]; k/v_prefix [P,Hkv,D] (P may be 0); k/v_canvas [N,Hkv,D] -> O [N,Hq,D] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    kc = np.asarray(k_canvas, dtype=np.float64)
+    vc = np.asarray(v_canvas, dtype=np.float64)
+    n, hq, d = q.shape
+    hkv = kc.shape[1]
+    if k_prefix is None or np.asarray(k_prefix).shape[0] == 0:
+        keys, vals = kc, vc
+    else:
+        keys = np.concatenate([np.asarray(k_prefix, dtype=np.float64), kc], axis=0)
+        vals = np.concatenate([np.asarray(v_prefix, dtype=np.float64), vc], axis=0)
+    if hq % hkv != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    group = hq // hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.empty((n, hq, d), dtype=np.float64)
+    for h in range(hq):
+        kvh = h // group
+        s = scale * (q[:, h, :] @ keys[:, kvh, :].T)          # [N, L]
+        s = s - s.max(axis=1, keepdims=True)
+        w = np.exp(s)
+        w = w / w.sum(axis=1, keepdims=True)
+        out[:, h, :] = w @ vals[:, kvh, :]
+    return out
