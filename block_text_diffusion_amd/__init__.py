@@ -1,0 +1,235 @@
+"""MI355X (gfx950) canvas-denoising kernels for block text diffusion: Python binding.
+
+Thin marshalling layer over the C ABI in libdg.so (include/dg.h).  Functions
+carry the C names and take torch tensors that already live on the GPU; torch is
+used only for device memory and the current stream.  Every computation runs in
+the library's HIP kernels.
+"""
+import ctypes
+
+from . import _lib
+from ._lib import (DG_AUTO_ADVANCE, DG_BF16, DG_COMMIT_ONLY, DG_F32, DG_GUMBEL, DG_T_SCHEDULE,
+                   DgCtrl, DgError, check, load)
+
+__all__ = [
+    "dg_canvas_attention", "dg_sampler_step", "dg_denoise_step", "StepGraph", "dg_canvas_init",
+    "dg_kv_append", "dg_synth_logits", "dg_philox_fill", "dg_attention_workspace_bytes",
+    "dg_sampler_workspace_bytes", "dg_denoise_workspace_bytes", "dg_profile_enable",
+    "dg_profile_read", "make_ctrl", "read_ctrl", "write_ctrl", "DG_GUMBEL", "DG_COMMIT_ONLY",
+    "DG_AUTO_ADVANCE", "DG_T_SCHEDULE", "DG_F32", "DG_BF16", "DgError", "load",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtypes, device=True):
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} dtype {t.dtype} not in {dtypes}")
+    return t
+
+
+def _qkv_dtype(t):
+    torch = _torch()
+    return DG_BF16 if t.dtype == torch.bfloat16 else DG_F32
+
+
+def _workspace(nbytes, device, ws):
+    torch = _torch()
+    if ws is not None:
+        return ws
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ---- workspace queries ----
+def dg_attention_workspace_bytes(n_canvas, n_prefix, hq, hkv, head_dim):
+    return load().dg_attention_workspace_bytes(n_canvas, n_prefix, hq, hkv, head_dim)
+
+
+def dg_sampler_workspace_bytes(n_canvas, vocab, d_model):
+    return load().dg_sampler_workspace_bytes(n_canvas, vocab, d_model)
+
+
+def dg_denoise_workspace_bytes(n_canvas, n_prefix, hq, hkv, head_dim, vocab, d_model):
+    return load().dg_denoise_workspace_bytes(n_canvas, n_prefix, hq, hkv, head_dim, vocab, d_model)
+
+
+# ---- control block ----
+def make_ctrl(seed=0, gstep=0, s_in_block=0, s_max=48, flags=0, tau=0.9, t_start=1.0, t_end=1.0,
+              device="cuda"):
+    """A dg_ctrl in device memory (40-byte uint8 tensor)."""
+    torch = _torch()
+    c = DgCtrl(seed=seed, gstep=gstep, s_in_block=s_in_block, s_max=s_max, flags=flags, tau=tau,
+               t_start=t_start, t_end=t_end, reserved=0)
+    host = torch.frombuffer(bytearray(bytes(c)), dtype=torch.uint8)
+    return host.to(device)
+
+
+def write_ctrl(ctrl_t, **fields):
+    cur = read_ctrl(ctrl_t)
+    cur.update(fields)
+    torch = _torch()
+    c = DgCtrl(**cur)
+    ctrl_t.copy_(torch.frombuffer(bytearray(bytes(c)), dtype=torch.uint8))
+
+
+def read_ctrl(ctrl_t):
+    raw = bytes(ctrl_t.cpu().numpy().tobytes())
+    c = DgCtrl.from_buffer_copy(raw)
+    return {f: getattr(c, f) for f, _ in DgCtrl._fields_}
+
+
+# ---- the three calls of the denoising step ----
+def dg_canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, out=None, scale=0.0,
+                        workspace=None, stream=None):
+    torch = _torch()
+    dt = (torch.bfloat16, torch.float32)
+    _need(q, "q", dt); _need(k_canvas, "k_canvas", dt); _need(v_canvas, "v_canvas", dt)
+    n, hq, d = q.shape
+    hkv = k_canvas.shape[1]
+    n_prefix = 0 if k_prefix is None else k_prefix.shape[0]
+    if n_prefix:
+        _need(k_prefix, "k_prefix", dt); _need(v_prefix, "v_prefix", dt)
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
+    nbytes = dg_attention_workspace_bytes(n, n_prefix, hq, hkv, d)
+    ws = _workspace(nbytes, q.device, workspace)
+    check(load().dg_canvas_attention(_ptr(q), _ptr(k_prefix) if n_prefix else None,
+                                     _ptr(v_prefix) if n_prefix else None, _ptr(k_canvas),
+                                     _ptr(v_canvas), _ptr(out), n, n_prefix, hq, hkv, d,
+                                     _qkv_dtype(q), float(scale), _ptr(ws), ws.numel(),
+                                     _stream(stream)))
+    return out
+
+
+def dg_sampler_step(logits, emb, canvas_ids, committed, selfcond, confidence, n_uncommitted, ctrl,
+                    workspace=None, stream=None):
+    torch = _torch()
+    _need(logits, "logits", (torch.float32,)); _need(emb, "emb", (torch.float32,))
+    _need(canvas_ids, "canvas_ids", (torch.int32,)); _need(committed, "committed", (torch.uint8,))
+    _need(selfcond, "selfcond", (torch.float32,)); _need(n_uncommitted, "n_uncommitted", (torch.int32, torch.uint32))
+    _need(ctrl, "ctrl", (torch.uint8,))
+    if confidence is not None:
+        _need(confidence, "confidence", (torch.float32,))
+    n, vocab = logits.shape
+    d = emb.shape[1]
+    nbytes = dg_sampler_workspace_bytes(n, vocab, d)
+    ws = _workspace(nbytes, logits.device, workspace)
+    check(load().dg_sampler_step(_ptr(logits), _ptr(emb), _ptr(canvas_ids), _ptr(committed),
+                                 _ptr(selfcond), _ptr(confidence), _ptr(n_uncommitted), _ptr(ctrl),
+                                 n, vocab, d, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def _denoise_args(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, scale, logits, emb,
+                  canvas_ids, committed, selfcond, confidence, n_uncommitted, ctrl, ws):
+    n, hq, d = q.shape
+    hkv = k_canvas.shape[1]
+    n_prefix = 0 if k_prefix is None else k_prefix.shape[0]
+    vocab = logits.shape[1]
+    dm = emb.shape[1]
+    return (_ptr(q), _ptr(k_prefix) if n_prefix else None, _ptr(v_prefix) if n_prefix else None,
+            _ptr(k_canvas), _ptr(v_canvas), _ptr(attn_out), n_prefix, hq, hkv, d, _qkv_dtype(q),
+            float(scale), _ptr(logits), _ptr(emb), _ptr(canvas_ids), _ptr(committed), _ptr(selfcond),
+            _ptr(confidence), _ptr(n_uncommitted), _ptr(ctrl), n, vocab, dm, _ptr(ws), ws.numel())
+
+
+def dg_denoise_step(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits, emb, canvas_ids,
+                    committed, selfcond, confidence, n_uncommitted, ctrl, scale=0.0, workspace=None,
+                    stream=None):
+    n, hq, d = q.shape
+    nbytes = dg_denoise_workspace_bytes(n, 0 if k_prefix is None else k_prefix.shape[0], hq,
+                                        k_canvas.shape[1], d, logits.shape[1], emb.shape[1])
+    ws = _workspace(nbytes, q.device, workspace)
+    args = _denoise_args(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, scale, logits, emb,
+                         canvas_ids, committed, selfcond, confidence, n_uncommitted, ctrl, ws)
+    check(load().dg_denoise_step(*args, _stream(stream)))
+
+
+class StepGraph:
+    """dg_step_graph_create / _launch / _destroy: one captured denoising step.
+
+    Keeps references to every tensor the graph reads or writes so they outlive it.
+    """
+
+    def __init__(self, q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits, emb, canvas_ids,
+                 committed, selfcond, confidence, n_uncommitted, ctrl, scale=0.0, workspace=None):
+        n, hq, d = q.shape
+        nbytes = dg_denoise_workspace_bytes(n, 0 if k_prefix is None else k_prefix.shape[0], hq,
+                                            k_canvas.shape[1], d, logits.shape[1], emb.shape[1])
+        self.ws = _workspace(nbytes, q.device, workspace)
+        self._keep = (q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits, emb, canvas_ids,
+                      committed, selfcond, confidence, n_uncommitted, ctrl)
+        args = _denoise_args(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, scale, logits, emb,
+                             canvas_ids, committed, selfcond, confidence, n_uncommitted, ctrl, self.ws)
+        handle = ctypes.c_void_p()
+        check(load().dg_step_graph_create(*args, ctypes.byref(handle)))
+        self.handle = handle
+
+    def launch(self, stream=None):
+        check(load().dg_step_graph_launch(self.handle, _stream(stream)))
+
+    def close(self):
+        if self.handle:
+            load().dg_step_graph_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---- block loop helpers ----
+def dg_canvas_init(canvas_ids, committed, ctrl, vocab, stream=None):
+    check(load().dg_canvas_init(_ptr(canvas_ids), _ptr(committed), _ptr(ctrl), canvas_ids.numel(),
+                                int(vocab), _stream(stream)))
+
+
+def dg_kv_append(k_prefix, v_prefix, k_canvas, v_canvas, n_prefix, stream=None):
+    n, hkv, d = k_canvas.shape
+    check(load().dg_kv_append(_ptr(k_prefix), _ptr(v_prefix), _ptr(k_canvas), _ptr(v_canvas),
+                              int(n_prefix), n, hkv, d, _qkv_dtype(k_canvas), _stream(stream)))
+
+
+def dg_synth_logits(logits, canvas_ids, committed, ctrl, table, stream=None):
+    n, vocab = logits.shape
+    check(load().dg_synth_logits(_ptr(logits), _ptr(canvas_ids), _ptr(committed), _ptr(ctrl),
+                                 _ptr(table), table.numel(), n, vocab, _stream(stream)))
+
+
+def dg_philox_fill(out, seed, c1, c2, c3, stream=None):
+    check(load().dg_philox_fill(_ptr(out), out.numel(), int(seed), int(c1), int(c2), int(c3),
+                                _stream(stream)))
+
+
+# ---- profiling ----
+def dg_profile_enable(on=True):
+    check(load().dg_profile_enable(1 if on else 0))
+
+
+def dg_profile_read(max_kernels=32):
+    names = (ctypes.c_char_p * max_kernels)()
+    ms = (ctypes.c_double * max_kernels)()
+    cnt = (ctypes.c_int * max_kernels)()
+    k = load().dg_profile_read(names, ms, cnt, max_kernels)
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(k)}

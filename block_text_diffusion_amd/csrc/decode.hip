@@ -1,0 +1,111 @@
+// Block-loop helpers on gfx950: canvas initialisation (a canvas starts as
+// uniformly random tokens: explainer "DiffusionGemma: Google's open diffusion
+// LLM", sections quoting report 3.1-3.3), the synthetic logit generator that
+// stands in for the model in the decode-run workload, and a raw Philox dump.
+#include "dg_common.hpp"
+#include "dg_internal.hpp"
+
+namespace dg {
+
+__global__ __launch_bounds__(256) void canvas_init_kernel(int32_t* __restrict__ ids,
+                                                          uint8_t* __restrict__ committed,
+                                                          dg_ctrl* __restrict__ ctrl, int n,
+                                                          int vocab) {
+  const int i = threadIdx.x;
+  const uint64_t seed = ctrl->seed;
+  const uint32_t gstep = ctrl->gstep;
+  if (i < n) {
+    const Philox4 h = philox4x32_10(0u, (uint32_t)i, gstep, kStreamInit, seed_lo(seed), seed_hi(seed));
+    ids[i] = (int32_t)range_draw(h.w0, (uint32_t)vocab);
+    committed[i] = 0;
+  }
+  __syncthreads();
+  if (i == 0) ctrl->s_in_block = 0u;
+}
+
+constexpr int kSynThreads = 256;
+constexpr float kSpike = 30.0f;
+constexpr uint32_t kChoosePerStep = 20u;
+
+// grid (ceil(V / 1024), n); each thread produces ids 4m..4m+3 from one Philox call.
+template <bool kAligned>
+__global__ __launch_bounds__(kSynThreads) void synth_logits_kernel(
+    float* __restrict__ logits, const int32_t* __restrict__ ids,
+    const uint8_t* __restrict__ committed, const dg_ctrl* __restrict__ ctrl,
+    const float* __restrict__ table, int n, int vocab) {
+  const int row = blockIdx.y;
+  const int t = threadIdx.x;
+  const uint64_t seed = ctrl->seed;
+  const uint32_t gstep = ctrl->gstep;
+  const uint32_t k0 = seed_lo(seed), k1 = seed_hi(seed);
+  const int open = (t < n && !committed[t]) ? 1 : 0;
+  const uint32_t n_open = (uint32_t)__syncthreads_count(open);
+
+  int target = -1;
+  if (committed[row]) {
+    target = ids[row];
+  } else {
+    const Philox4 hc = philox4x32_10(0u, (uint32_t)row, gstep, kStreamSynChoose, k0, k1);
+    if (range_draw(hc.w0, n_open) < kChoosePerStep) {
+      const Philox4 ht = philox4x32_10(0u, (uint32_t)row, gstep, kStreamSynTarget, k0, k1);
+      target = (int)range_draw(ht.w0, (uint32_t)vocab);
+    }
+  }
+  const int j = 4 * (blockIdx.x * kSynThreads + t);
+  if (j >= vocab) return;
+  const Philox4 h = philox4x32_10((uint32_t)j >> 2, (uint32_t)row, gstep, kStreamSynNoise, k0, k1);
+  float v[4] = {table[h.w0 >> 16], table[h.w1 >> 16], table[h.w2 >> 16], table[h.w3 >> 16]};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (j + e == target) v[e] = v[e] + kSpike;
+  float* dst = logits + (size_t)row * vocab + j;
+  if (kAligned && j + 3 < vocab) {
+    *reinterpret_cast<f32x4*>(dst) = (f32x4){v[0], v[1], v[2], v[3]};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (j + e < vocab) dst[e] = v[e];
+  }
+}
+
+__global__ __launch_bounds__(256) void philox_fill_kernel(uint32_t* __restrict__ out, size_t n_ctr,
+                                                          uint64_t seed, uint32_t c1, uint32_t c2,
+                                                          uint32_t c3) {
+  const size_t m = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= n_ctr) return;
+  const Philox4 h = philox4x32_10((uint32_t)m, c1, c2, c3, seed_lo(seed), seed_hi(seed));
+  *reinterpret_cast<u32x4*>(out + 4 * m) = (u32x4){h.w0, h.w1, h.w2, h.w3};
+}
+
+hipError_t launch_canvas_init(int32_t* ids, uint8_t* committed, dg_ctrl* ctrl, int n, int vocab,
+                              hipStream_t s) {
+  prof_begin("canvas_init", s);
+  canvas_init_kernel<<<1, 256, 0, s>>>(ids, committed, ctrl, n, vocab);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_synth_logits(float* logits, const int32_t* ids, const uint8_t* committed,
+                               const dg_ctrl* ctrl, const float* table, int table_size, int n,
+                               int vocab, hipStream_t s) {
+  (void)table_size;
+  const dim3 grid((vocab + 4 * kSynThreads - 1) / (4 * kSynThreads), n);
+  prof_begin("synth_logits", s);
+  if (vocab % 4 == 0)
+    synth_logits_kernel<true><<<grid, kSynThreads, 0, s>>>(logits, ids, committed, ctrl, table, n, vocab);
+  else
+    synth_logits_kernel<false><<<grid, kSynThreads, 0, s>>>(logits, ids, committed, ctrl, table, n, vocab);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_philox_fill(uint32_t* out, size_t n_words, uint64_t seed, uint32_t c1,
+                              uint32_t c2, uint32_t c3, hipStream_t s) {
+  const size_t n_ctr = n_words / 4;
+  if (n_ctr == 0) return hipSuccess;
+  const size_t blocks = (n_ctr + 255) / 256;
+  philox_fill_kernel<<<(unsigned)blocks, 256, 0, s>>>(out, n_ctr, seed, c1, c2, c3);
+  return hipGetLastError();
+}
+
+}  // namespace dg

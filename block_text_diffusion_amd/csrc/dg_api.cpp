@@ -1,0 +1,351 @@
+// C ABI of the canvas-denoising library: host validation, workspace carving,
+// launch sequencing, step-graph capture, per-kernel event profiling.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "dg.h"
+#include "dg_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local bool g_capturing = false;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DG_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- profiling ----
+struct ProfRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_event_pool;
+const char* g_prof_pending = nullptr;
+hipEvent_t g_prof_pending_start = nullptr;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// ---- argument checks ----
+int check_attention(const void* q, const void* kp, const void* vp, const void* kc, const void* vc,
+                    const float* out, int n, int np, int hq, int hkv, int d, int dtype) {
+  if (!q || !kc || !vc || !out) return fail(DG_EINVAL, "attention: null q/k_canvas/v_canvas/out");
+  if (np < 0) return fail(DG_EINVAL, "attention: n_prefix < 0");
+  if (np > 0 && (!kp || !vp)) return fail(DG_EINVAL, "attention: null prefix with n_prefix > 0");
+  if (n < 1) return fail(DG_EINVAL, "attention: n_canvas < 1");
+  if (n > 256) return fail(DG_EUNSUPPORTED, "attention: n_canvas > 256");
+  if (hq < 1 || hkv < 1 || hq % hkv != 0) return fail(DG_EINVAL, "attention: hq %% hkv != 0 or < 1");
+  if (d != 64 && d != 128) return fail(DG_EUNSUPPORTED, "attention: head_dim must be 64 or 128");
+  if (dtype != DG_F32 && dtype != DG_BF16) return fail(DG_EUNSUPPORTED, "attention: dtype");
+  if ((long long)np + n > (1ll << 30)) return fail(DG_EINVAL, "attention: sequence too long");
+  if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(out) ||
+      (np > 0 && (!aligned16(kp) || !aligned16(vp))))
+    return fail(DG_EINVAL, "attention: pointers must be 16-byte aligned");
+  return DG_OK;
+}
+
+int check_sampler(const float* logits, const float* emb, const int32_t* ids, const uint8_t* committed,
+                  const float* z, const uint32_t* n_unc, const dg_ctrl* ctrl, int n, int vocab, int d) {
+  if (!logits || !emb || !ids || !committed || !z || !n_unc || !ctrl)
+    return fail(DG_EINVAL, "sampler: null pointer argument");
+  if (n < 1) return fail(DG_EINVAL, "sampler: n_canvas < 1");
+  if (n > 256) return fail(DG_EUNSUPPORTED, "sampler: n_canvas > 256");
+  if (vocab < 2) return fail(DG_EINVAL, "sampler: vocab < 2");
+  if (d < 1) return fail(DG_EINVAL, "sampler: d_model < 1");
+  if ((size_t)vocab * (size_t)d > (1ull << 40)) return fail(DG_EINVAL, "sampler: E too large");
+  // the logits are addressed with 32-bit byte offsets
+  if ((uint64_t)n * (uint64_t)vocab * 4ull >= (1ull << 32))
+    return fail(DG_EUNSUPPORTED, "sampler: n_canvas * vocab * 4 must be below 2^32");
+  if (!aligned16(logits) || !aligned16(emb) || !aligned16(z))
+    return fail(DG_EINVAL, "sampler: logits/emb/selfcond must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(ctrl) & 7u) != 0) return fail(DG_EINVAL, "sampler: ctrl misaligned");
+  return DG_OK;
+}
+
+}  // namespace
+
+namespace dg {
+
+void prof_begin(const char* name, hipStream_t s) {
+  if (!g_prof_on || g_capturing) return;
+  hipEvent_t e = take_event();
+  if (!e) return;
+  hipEventRecord(e, s);
+  g_prof_pending = name;
+  g_prof_pending_start = e;
+}
+
+void prof_end(hipStream_t s) {
+  if (!g_prof_on || g_capturing || !g_prof_pending) return;
+  hipEvent_t e = take_event();
+  if (!e) return;
+  hipEventRecord(e, s);
+  g_prof_recs.push_back(ProfRec{g_prof_pending, g_prof_pending_start, e});
+  g_prof_pending = nullptr;
+  g_prof_pending_start = nullptr;
+}
+
+}  // namespace dg
+
+extern "C" {
+
+const char* dg_status_string(int status) {
+  switch (status) {
+    case DG_OK: return "ok";
+    case DG_EINVAL: return "invalid argument";
+    case DG_EUNSUPPORTED: return "unsupported configuration";
+    case DG_EWORKSPACE: return "workspace too small";
+    case DG_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* dg_last_error(void) { return g_last_error.c_str(); }
+
+size_t dg_attention_workspace_bytes(int n, int np, int hq, int hkv, int d) {
+  if (n < 1 || n > 256 || np < 0 || hq < 1 || hkv < 1 || hq % hkv || (d != 64 && d != 128)) return 0;
+  const size_t t = dg::attn_plan(n, np, hq, hkv, d).total;
+  return t == 0 ? 256 : t;
+}
+
+size_t dg_sampler_workspace_bytes(int n, int vocab, int d) {
+  if (n < 1 || n > 256 || vocab < 2 || d < 1) return 0;
+  return dg::sampler_plan(n, vocab, d).total;
+}
+
+size_t dg_denoise_workspace_bytes(int n, int np, int hq, int hkv, int d, int vocab, int dm) {
+  const size_t a = dg_attention_workspace_bytes(n, np, hq, hkv, d);
+  const size_t b = dg_sampler_workspace_bytes(n, vocab, dm);
+  if (!a || !b) return 0;
+  return a > b ? a : b;  // the two passes run one after the other and share it
+}
+
+int dg_canvas_attention(const void* q, const void* kp, const void* vp, const void* kc,
+                        const void* vc, float* out, int n, int np, int hq, int hkv, int d,
+                        int dtype, float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_attention(q, kp, vp, kc, vc, out, n, np, hq, hkv, d, dtype);
+  if (st != DG_OK) return st;
+  const dg::AttnPlan p = dg::attn_plan(n, np, hq, hkv, d);
+  if (p.total > 0 && (!ws || ws_bytes < p.total))
+    return fail(DG_EWORKSPACE, "attention: workspace %zu < %zu bytes", ws_bytes, p.total);
+  if (p.total > 0 && !aligned16(ws)) return fail(DG_EINVAL, "attention: workspace misaligned");
+  if (!(scale > 0.f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)d);
+  hipError_t e = dg::launch_attention(p, q, kp, vp, kc, vc, out, dtype == DG_BF16, scale, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return DG_OK;
+}
+
+int dg_sampler_step(const float* logits, const float* emb, int32_t* ids, uint8_t* committed,
+                    float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl, int n, int vocab, int d,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, d);
+  if (st != DG_OK) return st;
+  const dg::SamplerPlan p = dg::sampler_plan(n, vocab, d);
+  if (!ws || ws_bytes < p.total)
+    return fail(DG_EWORKSPACE, "sampler: workspace %zu < %zu bytes", ws_bytes, p.total);
+  if (!aligned16(ws)) return fail(DG_EINVAL, "sampler: workspace misaligned");
+  hipError_t e = dg::launch_sampler(p, logits, emb, ids, committed, z, conf, n_unc, ctrl, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "sampler launch");
+  return DG_OK;
+}
+
+int dg_denoise_step(const void* q, const void* kp, const void* vp, const void* kc, const void* vc,
+                    float* attn_out, int np, int hq, int hkv, int d, int dtype, float scale,
+                    const float* logits, const float* emb, int32_t* ids, uint8_t* committed,
+                    float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl, int n, int vocab, int dm,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_attention(q, kp, vp, kc, vc, attn_out, n, np, hq, hkv, d, dtype);
+  if (st != DG_OK) return st;
+  st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, dm);
+  if (st != DG_OK) return st;
+  const size_t need = dg_denoise_workspace_bytes(n, np, hq, hkv, d, vocab, dm);
+  if (!ws || ws_bytes < need) return fail(DG_EWORKSPACE, "denoise: workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned16(ws)) return fail(DG_EINVAL, "denoise: workspace misaligned");
+  if (!(scale > 0.f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)d);
+  const dg::AttnPlan ap = dg::attn_plan(n, np, hq, hkv, d);
+  hipError_t e = dg::launch_attention(ap, q, kp, vp, kc, vc, attn_out, dtype == DG_BF16, scale, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "denoise attention launch");
+  const dg::SamplerPlan sp = dg::sampler_plan(n, vocab, dm);
+  e = dg::launch_sampler(sp, logits, emb, ids, committed, z, conf, n_unc, ctrl, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "denoise sampler launch");
+  return DG_OK;
+}
+
+struct dg_step_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+int dg_step_graph_create(const void* q, const void* kp, const void* vp, const void* kc,
+                         const void* vc, float* attn_out, int np, int hq, int hkv, int d, int dtype,
+                         float scale, const float* logits, const float* emb, int32_t* ids,
+                         uint8_t* committed, float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl,
+                         int n, int vocab, int dm, void* ws, size_t ws_bytes, dg_step_graph** out) {
+  if (!out) return fail(DG_EINVAL, "graph: null output handle");
+  *out = nullptr;
+  int st = check_attention(q, kp, vp, kc, vc, attn_out, n, np, hq, hkv, d, dtype);
+  if (st != DG_OK) return st;
+  st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, dm);
+  if (st != DG_OK) return st;
+  hipStream_t cs = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e, "graph: stream create");
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    hipStreamDestroy(cs);
+    return hip_fail(e, "graph: begin capture");
+  }
+  g_capturing = true;
+  st = dg_denoise_step(q, kp, vp, kc, vc, attn_out, np, hq, hkv, d, dtype, scale, logits, emb, ids,
+                       committed, z, conf, n_unc, ctrl, n, vocab, dm, ws, ws_bytes, cs);
+  g_capturing = false;
+  hipGraph_t graph = nullptr;
+  hipError_t e2 = hipStreamEndCapture(cs, &graph);
+  hipStreamDestroy(cs);
+  if (st != DG_OK) {
+    if (graph) hipGraphDestroy(graph);
+    return st;
+  }
+  if (e2 != hipSuccess) return hip_fail(e2, "graph: end capture");
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hipGraphDestroy(graph);
+    return hip_fail(e, "graph: instantiate");
+  }
+  *out = new dg_step_graph{graph, exec};
+  return DG_OK;
+}
+
+int dg_step_graph_launch(dg_step_graph* g, hipStream_t stream) {
+  if (!g) return fail(DG_EINVAL, "graph: null handle");
+  hipError_t e = hipGraphLaunch(g->exec, stream);
+  if (e != hipSuccess) return hip_fail(e, "graph launch");
+  return DG_OK;
+}
+
+void dg_step_graph_destroy(dg_step_graph* g) {
+  if (!g) return;
+  hipGraphExecDestroy(g->exec);
+  hipGraphDestroy(g->graph);
+  delete g;
+}
+
+int dg_canvas_init(int32_t* ids, uint8_t* committed, dg_ctrl* ctrl, int n, int vocab,
+                   hipStream_t stream) {
+  if (!ids || !committed || !ctrl) return fail(DG_EINVAL, "canvas_init: null pointer");
+  if (n < 1) return fail(DG_EINVAL, "canvas_init: n_canvas < 1");
+  if (n > 256) return fail(DG_EUNSUPPORTED, "canvas_init: n_canvas > 256");
+  if (vocab < 2) return fail(DG_EINVAL, "canvas_init: vocab < 2");
+  hipError_t e = dg::launch_canvas_init(ids, committed, ctrl, n, vocab, stream);
+  if (e != hipSuccess) return hip_fail(e, "canvas_init launch");
+  return DG_OK;
+}
+
+int dg_kv_append(void* kp, void* vp, const void* kc, const void* vc, int np, int n, int hkv, int d,
+                 int dtype, hipStream_t stream) {
+  if (!kp || !vp || !kc || !vc) return fail(DG_EINVAL, "kv_append: null pointer");
+  if (np < 0 || n < 1 || hkv < 1 || d < 1) return fail(DG_EINVAL, "kv_append: bad sizes");
+  if (dtype != DG_F32 && dtype != DG_BF16) return fail(DG_EUNSUPPORTED, "kv_append: dtype");
+  const size_t es = dtype == DG_BF16 ? 2 : 4;
+  const size_t row = (size_t)hkv * d * es;
+  const size_t off = (size_t)np * row;
+  const size_t bytes = (size_t)n * row;
+  hipError_t e = hipMemcpyAsync(static_cast<uint8_t*>(kp) + off, kc, bytes, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(static_cast<uint8_t*>(vp) + off, vc, bytes, hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_append copy");
+  return DG_OK;
+}
+
+int dg_synth_logits(float* logits, const int32_t* ids, const uint8_t* committed, const dg_ctrl* ctrl,
+                    const float* table, int table_size, int n, int vocab, hipStream_t stream) {
+  if (!logits || !ids || !committed || !ctrl || !table) return fail(DG_EINVAL, "synth: null pointer");
+  if (table_size != 65536) return fail(DG_EINVAL, "synth: table_size must be 65536");
+  if (n < 1) return fail(DG_EINVAL, "synth: n_canvas < 1");
+  if (n > 256) return fail(DG_EUNSUPPORTED, "synth: n_canvas > 256");
+  if (vocab < 2) return fail(DG_EINVAL, "synth: vocab < 2");
+  if (!aligned16(logits)) return fail(DG_EINVAL, "synth: logits misaligned");
+  hipError_t e = dg::launch_synth_logits(logits, ids, committed, ctrl, table, table_size, n, vocab, stream);
+  if (e != hipSuccess) return hip_fail(e, "synth launch");
+  return DG_OK;
+}
+
+int dg_philox_fill(uint32_t* out, size_t n_words, uint64_t seed, uint32_t c1, uint32_t c2,
+                   uint32_t c3, hipStream_t stream) {
+  if (!out) return fail(DG_EINVAL, "philox_fill: null pointer");
+  if (n_words % 4 != 0) return fail(DG_EINVAL, "philox_fill: n_words must be a multiple of 4");
+  if (n_words / 4 > 0xFFFFFFFFull) return fail(DG_EINVAL, "philox_fill: too many counters");
+  if (!aligned16(out)) return fail(DG_EINVAL, "philox_fill: output misaligned");
+  hipError_t e = dg::launch_philox_fill(out, n_words, seed, c1, c2, c3, stream);
+  if (e != hipSuccess) return hip_fail(e, "philox_fill launch");
+  return DG_OK;
+}
+
+int dg_profile_enable(int on) {
+  g_prof_on = on != 0;
+  return DG_OK;
+}
+
+int dg_profile_read(const char** names, double* total_ms, int* counts, int max) {
+  std::vector<const char*> keys;
+  std::vector<double> sums;
+  std::vector<int> cnt;
+  for (const ProfRec& r : g_prof_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess) continue;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) continue;
+    size_t k = 0;
+    while (k < keys.size() && std::strcmp(keys[k], r.name) != 0) ++k;
+    if (k == keys.size()) {
+      keys.push_back(r.name);
+      sums.push_back(0.0);
+      cnt.push_back(0);
+    }
+    sums[k] += ms;
+    cnt[k] += 1;
+  }
+  for (const ProfRec& r : g_prof_recs) {
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_prof_recs.clear();
+  int w = 0;
+  for (size_t k = 0; k < keys.size() && w < max; ++k, ++w) {
+    if (names) names[w] = keys[k];
+    if (total_ms) total_ms[w] = sums[k];
+    if (counts) counts[w] = cnt[k];
+  }
+  return w;
+}
+
+}  // extern "C"

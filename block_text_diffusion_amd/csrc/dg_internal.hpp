@@ -1,0 +1,56 @@
+// Host-side plans and launchers shared between the kernel files and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dg.h"
+
+namespace dg {
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Per-kernel event bracketing for benchmarks (no-op unless enabled and not capturing).
+void prof_begin(const char* name, hipStream_t s);
+void prof_end(hipStream_t s);
+
+// ---- sampler ----
+struct SamplerPlan {
+  int n, vocab, d;
+  int n_chunks;      // stats chunks per row
+  int chunk_len;     // logits per stats chunk (multiple of 4)
+  int n_tiles;       // d-tiles of the contraction (256 columns each)
+  int n_splits;      // vocabulary splits of the contraction
+  int ks_per_split;  // 32-wide k steps per split
+  size_t off_stats, off_zp, total;
+};
+SamplerPlan sampler_plan(int n, int vocab, int d);
+hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const float* emb,
+                          int32_t* ids, uint8_t* committed, float* z, float* conf,
+                          uint32_t* n_unc, dg_ctrl* ctrl, void* ws, hipStream_t s);
+
+// ---- attention ----
+struct AttnPlan {
+  int n, n_prefix, hq, hkv, d, group;
+  int rows;          // n * group packed query rows per KV head
+  int n_qtiles;      // 128-row query tiles per KV head
+  int n_chunks;      // key chunks
+  int chunk_len;     // keys per chunk (multiple of 64)
+  size_t off_opart, off_ml, total;
+};
+AttnPlan attn_plan(int n, int n_prefix, int hq, int hkv, int d);
+hipError_t launch_attention(const AttnPlan& p, const void* q, const void* kp, const void* vp,
+                            const void* kc, const void* vc, float* out, bool bf16_in,
+                            float scale, void* ws, hipStream_t s);
+
+// ---- block loop helpers ----
+hipError_t launch_canvas_init(int32_t* ids, uint8_t* committed, dg_ctrl* ctrl, int n, int vocab,
+                              hipStream_t s);
+hipError_t launch_synth_logits(float* logits, const int32_t* ids, const uint8_t* committed,
+                               const dg_ctrl* ctrl, const float* table, int table_size, int n,
+                               int vocab, hipStream_t s);
+hipError_t launch_philox_fill(uint32_t* out, size_t n_words, uint64_t seed, uint32_t c1,
+                              uint32_t c2, uint32_t c3, hipStream_t s);
+
+}  // namespace dg

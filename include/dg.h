@@ -1,0 +1,250 @@
+/*
+ * dg.h - C ABI of the MI355X (gfx950) canvas-denoising kernels for block text
+ * diffusion.
+ *
+ * One denoising step makes two passes over a canvas of up to 256 token slots:
+ *   1. bidirectional canvas attention over the committed KV prefix plus every
+ *      canvas position (DiffusionGemma Technical Report part 4/6, section 6,
+ *      "Attention"; section 9.1);
+ *   2. the diffusion sampler: a full-vocabulary softmax per canvas position, the
+ *      self-conditioning product softmax(logits)·E, and confidence commit with
+ *      uniform re-noise of the other positions (Technical Report section 6,
+ *      "Sampling"; explainer "DiffusionGemma: Google's open diffusion LLM",
+ *      sections quoting report 3.1-3.3; AlphaSignal page "How text diffusion
+ *      actually works").
+ * The whole step can be captured into one HIP graph so the host never
+ * synchronises between the passes (Technical Report section 6, "Eliminating
+ * CPU-GPU synchronization").
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless stated otherwise.  Tensors are dense,
+ *     row-major, and 16-byte aligned.  The caller owns every buffer, including
+ *     the workspace; the library never allocates, frees or synchronises inside
+ *     dg_canvas_attention / dg_sampler_step / dg_denoise_step.
+ *   - Work is enqueued asynchronously on `stream`; results are ready when the
+ *     stream reaches that point.  Calls are capture-safe and deterministic
+ *     (fixed reduction order, no floating-point atomics).
+ *   - Arguments are validated on the host before any HIP call; on a validation
+ *     error nothing is launched and a negative dg_status is returned.
+ *     dg_last_error() gives a thread-local detail string.  A HIP launch error
+ *     maps to DG_EHIP.
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef DG_H_
+#define DG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dg_status {
+  DG_OK = 0,
+  DG_EINVAL = -1,        /* null / misaligned pointer, bad size */
+  DG_EUNSUPPORTED = -2,  /* valid but not supported (head_dim, dtype, n_canvas > 256) */
+  DG_EWORKSPACE = -3,    /* workspace smaller than the *_workspace_bytes query */
+  DG_EHIP = -4           /* a HIP runtime call or launch failed */
+} dg_status;
+
+typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
+
+/* dg_ctrl.flags */
+enum {
+  DG_GUMBEL = 1u,       /* candidate = argmax(l/T + Gumbel noise); else greedy argmax */
+  DG_COMMIT_ONLY = 2u,  /* commit confident positions, do not re-noise the others */
+  DG_AUTO_ADVANCE = 4u, /* the step ends with gstep += 1, s_in_block += 1 on the device */
+  DG_T_SCHEDULE = 8u    /* T = t_start + (t_end - t_start) * s_in_block / (s_max - 1) */
+};
+
+/*
+ * Sampler control block.  It lives in DEVICE memory so a captured step graph can
+ * be replayed: every kernel reads it, and (with DG_AUTO_ADVANCE) the last kernel
+ * of a sampler step advances the step counters.  Table 2 of the explainer
+ * ("Sampler settings that decide DiffusionGemma latency") gives the recommended
+ * 48-step budget and the 0.8 -> 0.4 linear temperature schedule.
+ *   seed        key of the counter-based generator (Philox4x32-10)
+ *   gstep       global step index, part of every random draw's counter
+ *   s_in_block  step index within the current canvas (temperature schedule, cap)
+ *   s_max       step budget of a canvas; on step s_in_block + 1 >= s_max every
+ *               remaining defined position commits its candidate
+ *   tau         commit threshold on the candidate's probability at temperature T
+ */
+typedef struct dg_ctrl {
+  uint64_t seed;
+  uint32_t gstep;
+  uint32_t s_in_block;
+  uint32_t s_max;
+  uint32_t flags;
+  float tau;
+  float t_start;
+  float t_end;
+  uint32_t reserved;
+} dg_ctrl;
+
+/* ------------------------------------------------------------------------ */
+/* Canvas attention                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes dg_canvas_attention needs for these sizes (0 if invalid). */
+size_t dg_attention_workspace_bytes(int n_canvas, int n_prefix, int hq, int hkv, int head_dim);
+
+/*
+ * Bidirectional canvas attention (Technical Report section 6 "Attention"):
+ *   O[i,h] = sum_j softmax_j(scale * q[i,h] . k_j) v_j
+ * over keys j = prefix rows 0..n_prefix-1 then canvas rows 0..n_canvas-1 of KV
+ * head h / (hq / hkv); no mask.
+ *   q          [n_canvas, hq, head_dim]     dtype
+ *   k_prefix   [n_prefix, hkv, head_dim]    dtype (NULL allowed iff n_prefix == 0)
+ *   v_prefix   [n_prefix, hkv, head_dim]    dtype (NULL allowed iff n_prefix == 0)
+ *   k_canvas   [n_canvas, hkv, head_dim]    dtype
+ *   v_canvas   [n_canvas, hkv, head_dim]    dtype
+ *   out        [n_canvas, hq, head_dim]     float32 (written)
+ *   n_canvas in [1, 256]; n_prefix >= 0; hq % hkv == 0; head_dim in {64, 128}.
+ *   dtype DG_BF16 or DG_F32 (float32 inputs are rounded to bf16 when staged;
+ *   products and the softmax accumulate in float32).
+ *   scale <= 0 selects 1/sqrt(head_dim).
+ */
+int dg_canvas_attention(const void* q, const void* k_prefix, const void* v_prefix,
+                        const void* k_canvas, const void* v_canvas, float* out,
+                        int n_canvas, int n_prefix, int hq, int hkv, int head_dim,
+                        int dtype, float scale,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Diffusion sampler                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes dg_sampler_step needs for these sizes (0 if invalid). */
+size_t dg_sampler_workspace_bytes(int n_canvas, int vocab, int d_model);
+
+/*
+ * One sampler step over the canvas (Technical Report section 6 "Sampling").
+ *   logits          [n_canvas, vocab]   float32
+ *   emb             [vocab, d_model]    float32, the embedding table E
+ *   canvas_ids      [n_canvas]          int32, in/out
+ *   committed       [n_canvas]          uint8 0/1, in/out (a committed position is
+ *                                       never changed again)
+ *   selfcond        [n_canvas, d_model] float32 out: z = softmax(logits) · E for
+ *                                       every row (temperature 1)
+ *   confidence      [n_canvas]          float32 out, may be NULL: probability at
+ *                                       temperature T of the row's candidate
+ *   n_uncommitted   [1]                 uint32 out: positions still open after the step
+ *   ctrl            device dg_ctrl, in (and advanced with DG_AUTO_ADVANCE)
+ * For each open position: commit the candidate if confidence >= tau (or on the
+ * last step of the budget), else, unless DG_COMMIT_ONLY, replace its id with a
+ * uniform draw over [0, vocab).  A row holding a NaN or +inf, or no finite
+ * logit, gets confidence NaN and z NaN and is never committed.
+ *   n_canvas in [1, 256]; vocab >= 2 with n_canvas * vocab * 4 < 2^32; d_model >= 1.
+ */
+int dg_sampler_step(const float* logits, const float* emb, int32_t* canvas_ids,
+                    uint8_t* committed, float* selfcond, float* confidence,
+                    uint32_t* n_uncommitted, dg_ctrl* ctrl,
+                    int n_canvas, int vocab, int d_model,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Whole denoising step and its graph                                        */
+/* ------------------------------------------------------------------------ */
+
+size_t dg_denoise_workspace_bytes(int n_canvas, int n_prefix, int hq, int hkv, int head_dim,
+                                  int vocab, int d_model);
+
+/*
+ * Attention then sampler, serialised on one stream, one shared workspace
+ * (arguments as in the two calls above).
+ */
+int dg_denoise_step(const void* q, const void* k_prefix, const void* v_prefix,
+                    const void* k_canvas, const void* v_canvas, float* attn_out,
+                    int n_prefix, int hq, int hkv, int head_dim, int dtype, float scale,
+                    const float* logits, const float* emb, int32_t* canvas_ids,
+                    uint8_t* committed, float* selfcond, float* confidence,
+                    uint32_t* n_uncommitted, dg_ctrl* ctrl,
+                    int n_canvas, int vocab, int d_model,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+typedef struct dg_step_graph dg_step_graph;
+
+/*
+ * Capture dg_denoise_step (same arguments) into an instantiated HIP graph.  The
+ * handle is written to *graph.  Replays re-read ctrl from device memory, so one
+ * graph serves every step of a canvas whose n_prefix is fixed.  Creation
+ * allocates host-side graph objects and is not for the hot path.
+ */
+int dg_step_graph_create(const void* q, const void* k_prefix, const void* v_prefix,
+                         const void* k_canvas, const void* v_canvas, float* attn_out,
+                         int n_prefix, int hq, int hkv, int head_dim, int dtype, float scale,
+                         const float* logits, const float* emb, int32_t* canvas_ids,
+                         uint8_t* committed, float* selfcond, float* confidence,
+                         uint32_t* n_uncommitted, dg_ctrl* ctrl,
+                         int n_canvas, int vocab, int d_model,
+                         void* workspace, size_t workspace_bytes, dg_step_graph** graph);
+int dg_step_graph_launch(dg_step_graph* graph, hipStream_t stream);
+void dg_step_graph_destroy(dg_step_graph* graph);
+
+/* ------------------------------------------------------------------------ */
+/* Block loop helpers                                                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Start a canvas: canvas_ids[i] = uniform draw from the INIT stream at
+ * (seed, gstep, i), committed[i] = 0, ctrl->s_in_block = 0 (explainer section
+ * quoting report 3.1-3.3: a canvas starts from uniformly random tokens).
+ */
+int dg_canvas_init(int32_t* canvas_ids, uint8_t* committed, dg_ctrl* ctrl,
+                   int n_canvas, int vocab, hipStream_t stream);
+
+/*
+ * Append a finished canvas's K/V rows to the prefix cache (explainer section
+ * "Block-autoregressive generation, one canvas after another"): copies
+ * k_canvas/v_canvas [n_canvas, hkv, head_dim] to rows n_prefix.. of
+ * k_prefix/v_prefix, which the caller sized for at least n_prefix + n_canvas rows.
+ */
+int dg_kv_append(void* k_prefix, void* v_prefix, const void* k_canvas, const void* v_canvas,
+                 int n_prefix, int n_canvas, int hkv, int head_dim, int dtype,
+                 hipStream_t stream);
+
+/*
+ * Synthetic logits for the decode-run workload (a stand-in for the model, used
+ * by tests and benchmarks): noise l[i,j] = table[h >> 16] with h the Philox
+ * word (j & 3) of counter (j >> 2, i, gstep, 6); an open row i is "chosen" when
+ * (h_choose * n_open) >> 32 < 20 (counter (0, i, gstep, 4)) and gets +30 at id
+ * (h_target * vocab) >> 32 (counter (0, i, gstep, 5)); a committed row gets +30
+ * at its own id.  table has table_size = 65536 float32 entries.
+ */
+int dg_synth_logits(float* logits, const int32_t* canvas_ids, const uint8_t* committed,
+                    const dg_ctrl* ctrl, const float* table, int table_size,
+                    int n_canvas, int vocab, hipStream_t stream);
+
+/*
+ * Diagnostic: out[4m + w] = output word w of Philox4x32-10 at counter
+ * (m, c1, c2, c3) with key (seed mod 2^32, seed >> 32), m in [0, n_words / 4).
+ * n_words must be a multiple of 4.
+ */
+int dg_philox_fill(uint32_t* out, size_t n_words, uint64_t seed, uint32_t c1, uint32_t c2,
+                   uint32_t c3, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Profiling and errors                                                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * With profiling on, eager (non-captured) calls record a HIP event pair around
+ * each kernel they launch.  dg_profile_read waits for the recorded events and
+ * returns, per kernel name, the summed milliseconds and launch count, then
+ * clears the records.  Returns the number of kernel names written (<= max).
+ * Host pointers.  Not thread-safe; for benchmarks.
+ */
+int dg_profile_enable(int on);
+int dg_profile_read(const char** names, double* total_ms, int* counts, int max);
+
+const char* dg_status_string(int status);
+const char* dg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H_ */

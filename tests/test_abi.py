@@ -1,0 +1,122 @@
+"""The C ABI without a GPU: the library loads, exports what include/dg.h declares,
+answers workspace queries, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_text_diffusion_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libdg.so is not built (run python -m block_text_diffusion_amd.build)")
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("dg_canvas_attention", "dg_sampler_step", "dg_denoise_step",
+                     "dg_step_graph_create", "dg_step_graph_launch", "dg_step_graph_destroy"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from block_text_diffusion_amd import _lib
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"binding lacks {name}"
+
+
+def test_workspace_queries(lib):
+    a = lib.dg_attention_workspace_bytes(256, 4096, 16, 8, 128)
+    assert a > 0 and a % 256 == 0
+    s = lib.dg_sampler_workspace_bytes(256, 262144, 3072)
+    # statistics partials plus the split-K partial sums of z
+    assert s >= 256 * 3072 * 4 and s % 256 == 0
+    d = lib.dg_denoise_workspace_bytes(256, 4096, 16, 8, 128, 262144, 3072)
+    assert d == max(a, s)
+    assert lib.dg_attention_workspace_bytes(257, 0, 8, 8, 64) == 0
+    assert lib.dg_attention_workspace_bytes(16, 0, 6, 4, 64) == 0
+    assert lib.dg_attention_workspace_bytes(16, 0, 8, 8, 96) == 0
+    assert lib.dg_sampler_workspace_bytes(16, 1, 64) == 0
+    assert lib.dg_sampler_workspace_bytes(0, 100, 64) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: validation fails first
+MIS = ctypes.c_void_p(0x10004)
+
+
+def attn(lib, **kw):
+    a = dict(q=FAKE, kp=FAKE, vp=FAKE, kc=FAKE, vc=FAKE, out=FAKE, n=16, np=8, hq=8, hkv=4, d=64,
+             dtype=1, scale=0.0, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return lib.dg_canvas_attention(a["q"], a["kp"], a["vp"], a["kc"], a["vc"], a["out"], a["n"],
+                                   a["np"], a["hq"], a["hkv"], a["d"], a["dtype"], a["scale"],
+                                   a["ws"], a["wsb"], a["stream"])
+
+
+def test_attention_argument_errors(lib):
+    from block_text_diffusion_amd._lib import DG_EINVAL, DG_EUNSUPPORTED, DG_EWORKSPACE
+    assert attn(lib, q=None) == DG_EINVAL
+    assert attn(lib, kp=None) == DG_EINVAL
+    assert attn(lib, n=0) == DG_EINVAL
+    assert attn(lib, n=257) == DG_EUNSUPPORTED
+    assert attn(lib, hq=6) == DG_EINVAL
+    assert attn(lib, d=96) == DG_EUNSUPPORTED
+    assert attn(lib, dtype=7) == DG_EUNSUPPORTED
+    assert attn(lib, q=MIS) == DG_EINVAL
+    assert attn(lib, np=-1) == DG_EINVAL
+    assert attn(lib, n=256, np=4096, hq=16, hkv=8, d=128, wsb=1024) == DG_EWORKSPACE
+    assert b"workspace" in lib.dg_last_error()
+
+
+def samp(lib, **kw):
+    a = dict(l=FAKE, e=FAKE, ids=FAKE, c=FAKE, z=FAKE, conf=None, nu=FAKE, ctrl=FAKE, n=16,
+             v=1000, d=64, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return lib.dg_sampler_step(a["l"], a["e"], a["ids"], a["c"], a["z"], a["conf"], a["nu"],
+                               a["ctrl"], a["n"], a["v"], a["d"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_sampler_argument_errors(lib):
+    from block_text_diffusion_amd._lib import DG_EINVAL, DG_EUNSUPPORTED, DG_EWORKSPACE
+    assert samp(lib, l=None) == DG_EINVAL
+    assert samp(lib, ctrl=None) == DG_EINVAL
+    assert samp(lib, v=1) == DG_EINVAL
+    assert samp(lib, d=0) == DG_EINVAL
+    assert samp(lib, n=300) == DG_EUNSUPPORTED
+    assert samp(lib, e=MIS) == DG_EINVAL
+    assert samp(lib, wsb=16) == DG_EWORKSPACE
+
+
+def test_helper_argument_errors(lib):
+    from block_text_diffusion_amd._lib import DG_EINVAL, DG_EUNSUPPORTED
+    assert lib.dg_canvas_init(None, FAKE, FAKE, 16, 100, None) == DG_EINVAL
+    assert lib.dg_canvas_init(FAKE, FAKE, FAKE, 300, 100, None) == DG_EUNSUPPORTED
+    assert lib.dg_synth_logits(FAKE, FAKE, FAKE, FAKE, FAKE, 1000, 16, 100, None) == DG_EINVAL
+    assert lib.dg_philox_fill(FAKE, 6, 1, 0, 0, 0, None) == DG_EINVAL
+    assert lib.dg_kv_append(FAKE, FAKE, FAKE, FAKE, 0, 16, 8, 64, 9, None) == DG_EUNSUPPORTED
+    h = ctypes.c_void_p()
+    assert lib.dg_step_graph_create(None, None, None, None, None, None, 0, 8, 8, 64, 1, 0.0,
+                                    None, None, None, None, None, None, None, None, 16, 100, 64,
+                                    None, 0, ctypes.byref(h)) == DG_EINVAL
+    assert h.value is None
+    assert lib.dg_status_string(-3) == b"workspace too small"
+
+
+def test_ctrl_layout_matches_header():
+    from block_text_diffusion_amd._lib import DgCtrl
+    assert ctypes.sizeof(DgCtrl) == 40
+    assert DgCtrl.tau.offset == 24 and DgCtrl.seed.offset == 0

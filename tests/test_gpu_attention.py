@@ -1,0 +1,80 @@
+"""Canvas attention on the GPU against the fp64 oracle (max-abs 2e-2, bf16 in, fp32 accumulate)."""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import ATTN_MAX_ABS, log, require_gpu, to_dev
+from oracle.attention import canvas_attention
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(torch, dg, q, kp, vp, kc, vc, qkv, scale=0.0):
+    dt = torch.bfloat16 if qkv == "bf16" else torch.float32
+    tq, tkc, tvc = to_dev(q, dt), to_dev(kc, dt), to_dev(vc, dt)
+    tkp = to_dev(kp, dt) if kp.shape[0] else None
+    tvp = to_dev(vp, dt) if kp.shape[0] else None
+    out = dg.dg_canvas_attention(tq, tkp, tvp, tkc, tvc, scale=scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check(got, ref, label):
+    err = np.abs(got.astype(np.float64) - ref).max()
+    log(f"{label}: max abs err {err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= ATTN_MAX_ABS, f"{label}: max abs err {err}"
+
+
+@pytest.mark.parametrize("workload", [1, 2, 4])
+def test_workloads(workload):
+    torch, dg = require_gpu()
+    c = workloads.CONFIGS[workload]
+    log(f"attention workload {workload}")
+    q, kp, vp, kc, vc = workloads.attention_inputs(workload)
+    got = run_gpu(torch, dg, q, kp, vp, kc, vc, c["qkv"])
+    check(got, canvas_attention(q, kp, vp, kc, vc), f"workload {workload}")
+
+
+@pytest.mark.parametrize("n,p,hq,hkv,d,qkv", [
+    (256, 0, 16, 8, 128, "bf16"),      # no prefix: canvas only
+    (100, 37, 16, 8, 128, "bf16"),     # ragged query tile and ragged key block
+    (1, 5, 8, 8, 64, "bf16"),          # a single canvas position
+    (64, 200, 16, 4, 128, "bf16"),     # group of 4 query heads per KV head
+    (130, 300, 8, 2, 64, "f32"),       # fp32 inputs staged as bf16, D=64, ragged
+    (256, 5120, 16, 8, 128, "bf16"),   # largest prefix of the decode run
+])
+def test_shapes(n, p, hq, hkv, d, qkv):
+    torch, dg = require_gpu()
+    log(f"attention n={n} p={p} hq={hq} hkv={hkv} d={d} {qkv}")
+    q, kp, vp, kc, vc = workloads.attention_inputs(2, n=n, n_prefix=p, hq=hq, hkv=hkv, head_dim=d, qkv=qkv)
+    got = run_gpu(torch, dg, q, kp, vp, kc, vc, qkv)
+    check(got, canvas_attention(q, kp, vp, kc, vc), f"n={n} p={p}")
+
+
+def test_explicit_scale():
+    torch, dg = require_gpu()
+    q, kp, vp, kc, vc = workloads.attention_inputs(2, n=64, n_prefix=64)
+    got = run_gpu(torch, dg, q, kp, vp, kc, vc, "bf16", scale=0.05)
+    check(got, canvas_attention(q, kp, vp, kc, vc, scale=0.05), "scale 0.05")
+
+
+def test_permutation_invariance_and_equivariance():
+    torch, dg = require_gpu()
+    q, kp, vp, kc, vc = workloads.attention_inputs(4)
+    base = run_gpu(torch, dg, q, kp, vp, kc, vc, "bf16")
+    rng = np.random.default_rng(3)
+    pc = rng.permutation(kc.shape[0])
+    permuted = run_gpu(torch, dg, q, kp, vp, kc[pc], vc[pc], "bf16")
+    assert np.abs(permuted - base).max() <= ATTN_MAX_ABS
+    pq = rng.permutation(q.shape[0])
+    # query rows are independent: permuting queries permutes the output exactly
+    np.testing.assert_array_equal(run_gpu(torch, dg, q[pq], kp, vp, kc, vc, "bf16"), base[pq])
+
+
+def test_deterministic():
+    torch, dg = require_gpu()
+    q, kp, vp, kc, vc = workloads.attention_inputs(4)
+    a = run_gpu(torch, dg, q, kp, vp, kc, vc, "bf16")
+    b = run_gpu(torch, dg, q, kp, vp, kc, vc, "bf16")
+    np.testing.assert_array_equal(a, b)

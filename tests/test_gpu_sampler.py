@@ -1,0 +1,226 @@
+"""The diffusion sampler on the GPU against the oracle: decisions bit for bit outside the
+1e-4 bands, confidences, and z = softmax(l)·E within relative L2 1e-4."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import check_step, check_z, log, require_gpu, to_dev
+from oracle import sampler as S
+
+pytestmark = pytest.mark.gpu
+
+
+class GpuSampler:
+    def __init__(self, torch, dg, emb, ids, mask, ctrl):
+        self.torch, self.dg = torch, dg
+        self.emb = to_dev(emb)
+        n = len(ids)
+        self.ids = to_dev(np.asarray(ids, np.int32))
+        self.mask = to_dev(np.asarray(mask, np.uint8))
+        self.z = torch.empty((n, emb.shape[1]), dtype=torch.float32, device="cuda")
+        self.kappa = torch.empty(n, dtype=torch.float32, device="cuda")
+        self.nu = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.ctrl = dg.make_ctrl(seed=ctrl.seed, gstep=ctrl.gstep, s_in_block=ctrl.s_in_block,
+                                 s_max=ctrl.s_max, flags=ctrl.flags, tau=ctrl.tau,
+                                 t_start=ctrl.t_start, t_end=ctrl.t_end)
+
+    def step(self, logits):
+        tl = logits if hasattr(logits, "data_ptr") else to_dev(logits)
+        self.dg.dg_sampler_step(tl, self.emb, self.ids, self.mask, self.z, self.kappa, self.nu, self.ctrl)
+        self.torch.cuda.synchronize()
+        return (self.ids.cpu().numpy(), self.mask.cpu().numpy(), self.kappa.cpu().numpy(),
+                self.z.cpu().numpy(), int(self.nu.item()))
+
+    def set_state(self, ids, mask):
+        self.ids.copy_(self.torch.from_numpy(np.asarray(ids, np.int32)))
+        self.mask.copy_(self.torch.from_numpy(np.asarray(mask, np.uint8)))
+
+
+def run_steps(workload, n_steps, z_every=True):
+    torch, dg = require_gpu()
+    c = workloads.CONFIGS[workload]
+    emb = workloads.embedding(workload)
+    ids, mask = workloads.initial_canvas(workload)
+    ctrl = S.Ctrl(seed=workload, tau=c["tau"], s_max=48, flags=S.AUTO_ADVANCE)
+    g = GpuSampler(torch, dg, emb, ids, mask, ctrl)
+    e64 = emb.astype(np.float64)
+    exempt = 0
+    for step in range(n_steps):
+        log(f"sampler workload {workload} step {step}")
+        logits = workloads.step_logits(workload, step)
+        ref = S.sampler_step(logits, e64, ids, mask, ctrl, z_rows="all" if z_every else None)
+        gids, gmask, gk, gz, gnu = g.step(logits)
+        exempt += check_step(ids, mask, gids, gmask, gk, ref, c["tau"])
+        if z_every:
+            check_z(gz, ref["z"])
+        assert gnu == ref["n_uncommitted"] or exempt
+        ctrl = ref["ctrl"]
+        assert dg.read_ctrl(g.ctrl)["gstep"] == ctrl.gstep
+        ids, mask = ref["ids"], ref["committed"]
+        if exempt:
+            g.set_state(ids, mask)
+    return exempt
+
+
+def test_workload1_eight_steps():
+    assert run_steps(1, 8) == 0
+
+
+def test_workload2_eight_steps():
+    assert run_steps(2, 8) == 0
+
+
+def test_workload3_full_vocab():
+    """262144 x 3072 at full size: every decision, z on sampled rows."""
+    torch, dg = require_gpu()
+    log("sampler workload 3: generating inputs")
+    emb = workloads.embedding(3)
+    logits = workloads.step_logits(3, 0)
+    ids, mask = workloads.initial_canvas(3)
+    ctrl = S.Ctrl(seed=3, tau=0.9, flags=S.AUTO_ADVANCE)
+    g = GpuSampler(torch, dg, emb, ids, mask, ctrl)
+    rows = np.array([0, 1, 37, 100, 128, 200, 254, 255])
+    log("sampler workload 3: gpu step")
+    gids, gmask, gk, gz, gnu = g.step(logits)
+    log("sampler workload 3: oracle")
+    ref = S.sampler_step(logits, emb, ids, mask, ctrl, z_rows=rows)
+    assert check_step(ids, mask, gids, gmask, gk, ref, 0.9) == 0
+    check_z(gz[rows], ref["z"])
+    assert gnu == ref["n_uncommitted"]
+    log(f"workload 3: {int(gmask.sum())} committed of 256")
+
+
+@pytest.mark.parametrize("n,vocab,d", [(256, 4097, 260), (100, 1001, 64), (1, 2, 4), (256, 33, 3),
+                                       (17, 12345, 513)])
+def test_ragged_shapes(n, vocab, d):
+    torch, dg = require_gpu()
+    log(f"sampler ragged n={n} V={vocab} d={d}")
+    rng = np.random.default_rng(n * 7 + vocab)
+    logits = (rng.standard_normal((n, vocab)) * 3).astype(np.float32)
+    logits[::3, 0] += 12.0
+    emb = (rng.standard_normal((vocab, d)) * 0.02).astype(np.float32)
+    ids = rng.integers(0, vocab, n).astype(np.int32)
+    mask = (rng.random(n) < 0.2).astype(np.uint8)
+    ctrl = S.Ctrl(seed=11, gstep=4, tau=0.9, flags=S.AUTO_ADVANCE)
+    g = GpuSampler(torch, dg, emb, ids, mask, ctrl)
+    gids, gmask, gk, gz, gnu = g.step(logits)
+    ref = S.sampler_step(logits, emb, ids, mask, ctrl)
+    assert check_step(ids, mask, gids, gmask, gk, ref, 0.9) == 0
+    check_z(gz, ref["z"])
+
+
+def test_identity_embedding_and_probability_sum():
+    """E = I gives z = p; an all-ones column of E gives sum(p) = 1 (through the ABI)."""
+    torch, dg = require_gpu()
+    from scipy import special
+    rng = np.random.default_rng(2)
+    vocab = 64
+    logits = (rng.standard_normal((32, vocab)) * 4).astype(np.float32)
+    emb = np.eye(vocab, dtype=np.float32)
+    g = GpuSampler(torch, dg, emb, np.zeros(32), np.zeros(32), S.Ctrl(tau=2.0))
+    _, _, _, z, _ = g.step(logits)
+    p = special.softmax(logits.astype(np.float64), axis=1)
+    check_z(z, p)
+    emb2 = (rng.standard_normal((vocab, 8)) * 0.02).astype(np.float32)
+    emb2[:, 5] = 1.0
+    g = GpuSampler(torch, dg, emb2, np.zeros(32), np.zeros(32), S.Ctrl(tau=2.0))
+    _, _, _, z, _ = g.step(logits)
+    np.testing.assert_allclose(z[:, 5], 1.0, atol=2e-5)
+
+
+def test_ties_nan_and_inf_rows():
+    torch, dg = require_gpu()
+    vocab, n = 5000, 8
+    rng = np.random.default_rng(4)
+    logits = rng.standard_normal((n, vocab)).astype(np.float32)
+    logits[0, [40, 4000]] = 50.0            # tie: smallest id wins
+    logits[1, 7] = np.nan
+    logits[2, :] = -np.inf
+    logits[3, 99] = np.inf
+    logits[4, :] = 0.0                       # uniform: never commits
+    logits[5, 4999] = 60.0                   # spike at the last id
+    emb = (rng.standard_normal((vocab, 16)) * 0.02).astype(np.float32)
+    ctrl = S.Ctrl(seed=1, tau=0.4, flags=S.AUTO_ADVANCE)
+    g = GpuSampler(torch, dg, emb, np.zeros(n), np.zeros(n), ctrl)
+    gids, gmask, gk, gz, gnu = g.step(logits)
+    ref = S.sampler_step(logits, emb, np.zeros(n), np.zeros(n), ctrl)
+    assert check_step(np.zeros(n), np.zeros(n), gids, gmask, gk, ref, 0.4) == 0
+    assert gids[0] == 40 and gmask[0] == 1
+    assert gids[5] == 4999 and gmask[5] == 1
+    assert np.all(np.isnan(gk[1:4])) and np.all(np.isnan(gz[1:4]))
+    assert gmask[4] == 0
+    ok = [0, 4, 5, 6, 7]
+    check_z(gz[ok], ref["z"][ok])
+
+
+def test_commit_only_and_last_step():
+    torch, dg = require_gpu()
+    rng = np.random.default_rng(5)
+    n, vocab = 64, 3000
+    logits = rng.standard_normal((n, vocab)).astype(np.float32)
+    logits[:10, 3] += 40
+    ids = rng.integers(0, vocab, n).astype(np.int32)
+    mask = np.zeros(n, np.uint8); mask[5:15] = 1
+    emb = (rng.standard_normal((vocab, 8)) * 0.02).astype(np.float32)
+    ctrl = S.Ctrl(seed=2, gstep=3, tau=0.9, flags=S.COMMIT_ONLY | S.AUTO_ADVANCE)
+    g = GpuSampler(torch, dg, emb, ids, mask, ctrl)
+    gids, gmask, gk, gz, _ = g.step(logits)
+    ref = S.sampler_step(logits, emb, ids, mask, ctrl)
+    assert check_step(ids, mask, gids, gmask, gk, ref, 0.9, commit_only=True) == 0
+    assert set(np.nonzero(gids != ids)[0]) == set(range(5))
+    # the last step of the budget commits every open defined row
+    ctrl2 = S.Ctrl(seed=2, gstep=9, s_in_block=47, s_max=48, tau=0.99, flags=S.AUTO_ADVANCE)
+    g = GpuSampler(torch, dg, emb, ids, mask, ctrl2)
+    gids, gmask, gk, gz, gnu = g.step(logits)
+    ref = S.sampler_step(logits, emb, ids, mask, ctrl2)
+    assert gnu == 0 and gmask.sum() == n
+    assert check_step(ids, mask, gids, gmask, gk, ref, 0.99) == 0
+
+
+@pytest.mark.parametrize("sched", [False, True])
+def test_gumbel_and_temperature(sched):
+    torch, dg = require_gpu()
+    rng = np.random.default_rng(6)
+    n, vocab = 256, 8192
+    logits = (rng.standard_normal((n, vocab)) * 2).astype(np.float32)
+    logits[::2, 100] += 16.0
+    emb = (rng.standard_normal((vocab, 64)) * 0.02).astype(np.float32)
+    flags = S.GUMBEL | S.AUTO_ADVANCE | (S.T_SCHEDULE if sched else 0)
+    ctrl = S.Ctrl(seed=99, gstep=12, s_in_block=20, s_max=48, tau=0.5, flags=flags,
+                  t_start=0.8 if sched else 0.7, t_end=0.4)
+    ids = rng.integers(0, vocab, n).astype(np.int32)
+    mask = np.zeros(n, np.uint8)
+    g = GpuSampler(torch, dg, emb, ids, mask, ctrl)
+    gids, gmask, gk, gz, _ = g.step(logits)
+    ref = S.sampler_step(logits, emb, ids, mask, ctrl)
+    assert check_step(ids, mask, gids, gmask, gk, ref, 0.5) == 0
+    check_z(gz, ref["z"])
+    assert 10 < gmask.sum() < n
+
+
+def test_deterministic_and_resume():
+    """Same inputs give bit-identical outputs; a step replayed from saved state matches."""
+    torch, dg = require_gpu()
+    emb = workloads.embedding(2)
+    ids, mask = workloads.initial_canvas(2)
+    ctrl = S.Ctrl(seed=2, tau=0.9, flags=S.AUTO_ADVANCE)
+    outs = []
+    for _ in range(2):
+        g = GpuSampler(torch, dg, emb, ids, mask, ctrl)
+        r0 = g.step(workloads.step_logits(2, 0))
+        saved = (r0[0].copy(), r0[1].copy(), dg.read_ctrl(g.ctrl))
+        r1 = g.step(workloads.step_logits(2, 1))
+        outs.append((r0, r1))
+    for a, b in zip(outs[0], outs[1]):
+        for x, y in zip(a[:4], b[:4]):
+            np.testing.assert_array_equal(x, y)
+    # resume: a fresh sampler started from the state saved after step 0
+    c = saved[2]
+    g = GpuSampler(torch, dg, emb, saved[0], saved[1],
+                   S.Ctrl(seed=c["seed"], gstep=c["gstep"], s_in_block=c["s_in_block"], s_max=c["s_max"],
+                          flags=c["flags"], tau=c["tau"], t_start=c["t_start"], t_end=c["t_end"]))
+    r1b = g.step(workloads.step_logits(2, 1))
+    for x, y in zip(outs[0][1][:4], r1b[:4]):
+        np.testing.assert_array_equal(x, y)

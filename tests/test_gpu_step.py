@@ -1,0 +1,93 @@
+"""The whole denoising step (attention then sampler) eagerly and as a replayed HIP graph,
+at the long-context, full-vocabulary shape, against the oracle."""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import ATTN_MAX_ABS, check_step, check_z, log, require_gpu, to_dev
+from oracle import sampler as S
+from oracle.attention import canvas_attention
+
+pytestmark = pytest.mark.gpu
+
+ROWS = np.array([0, 3, 64, 127, 128, 190, 255])
+
+
+@pytest.fixture(scope="module")
+def inputs():
+    log("step: generating workload-4 inputs")
+    q, kp, vp, kc, vc = workloads.attention_inputs(4)
+    emb = workloads.embedding(3)
+    logits = workloads.step_logits(4, 0)
+    ids, mask = workloads.initial_canvas(4)
+    return dict(q=q, kp=kp, vp=vp, kc=kc, vc=vc, emb=emb, logits=logits, ids=ids, mask=mask)
+
+
+def device_state(torch, dg, x, ctrl):
+    bf = torch.bfloat16
+    st = dict(q=to_dev(x["q"], bf), kp=to_dev(x["kp"], bf), vp=to_dev(x["vp"], bf),
+              kc=to_dev(x["kc"], bf), vc=to_dev(x["vc"], bf), emb=to_dev(x["emb"]),
+              logits=to_dev(x["logits"]), ids=to_dev(x["ids"].astype(np.int32)),
+              mask=to_dev(x["mask"].astype(np.uint8)))
+    n, hq, d = x["q"].shape
+    st["attn"] = torch.empty((n, hq, d), dtype=torch.float32, device="cuda")
+    st["z"] = torch.empty((n, x["emb"].shape[1]), dtype=torch.float32, device="cuda")
+    st["kappa"] = torch.empty(n, dtype=torch.float32, device="cuda")
+    st["nu"] = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st["ctrl"] = dg.make_ctrl(seed=ctrl.seed, gstep=ctrl.gstep, s_max=ctrl.s_max, flags=ctrl.flags,
+                              tau=ctrl.tau)
+    return st
+
+
+def args(st):
+    return (st["q"], st["kp"], st["vp"], st["kc"], st["vc"], st["attn"], st["logits"], st["emb"],
+            st["ids"], st["mask"], st["z"], st["kappa"], st["nu"], st["ctrl"])
+
+
+def snapshot(torch, st):
+    torch.cuda.synchronize()
+    return {k: st[k].cpu().numpy().copy() for k in ("attn", "ids", "mask", "kappa", "z", "nu", "ctrl")}
+
+
+def test_eager_and_graph_steps(inputs):
+    torch, dg = require_gpu()
+    ctrl = S.Ctrl(seed=4, tau=0.9, flags=S.AUTO_ADVANCE)
+    ref_attn = canvas_attention(inputs["q"], inputs["kp"], inputs["vp"], inputs["kc"], inputs["vc"])
+    e64 = inputs["emb"].astype(np.float64)
+
+    # eager: three steps on the same logits
+    log("step: eager")
+    st = device_state(torch, dg, inputs, ctrl)
+    eager = []
+    for _ in range(3):
+        dg.dg_denoise_step(*args(st))
+        eager.append(snapshot(torch, st))
+
+    # the oracle, step by step
+    ids, mask, c = inputs["ids"], inputs["mask"], ctrl
+    for k in range(3):
+        log(f"step: oracle step {k}")
+        ref = S.sampler_step(inputs["logits"], e64, ids, mask, c, z_rows=ROWS)
+        got = eager[k]
+        err = np.abs(got["attn"] - ref_attn).max()
+        assert err <= ATTN_MAX_ABS, err
+        assert check_step(ids, mask, got["ids"], got["mask"], got["kappa"], ref, 0.9) == 0
+        check_z(got["z"][ROWS], ref["z"])
+        assert int(got["nu"][0]) == ref["n_uncommitted"]
+        ids, mask, c = ref["ids"], ref["committed"], ref["ctrl"]
+
+    # graph: same three steps by replay, eager work and syncs in between
+    log("step: graph")
+    st = device_state(torch, dg, inputs, ctrl)
+    graph = dg.StepGraph(*args(st))
+    try:
+        for k in range(3):
+            graph.launch()
+            got = snapshot(torch, st)
+            scratch = torch.ones(1 << 20, device="cuda").sum().item()   # unrelated eager work
+            assert scratch == float(1 << 20)
+            for key in got:
+                np.testing.assert_array_equal(got[key], eager[k][key], err_msg=f"replay {k} {key}")
+            assert dg.read_ctrl(st["ctrl"])["gstep"] == k + 1
+    finally:
+        graph.close()

@@ -16,7 +16,7 @@ vocabulary, a 4096-token committed history, a 1024-token answer):
                 pre-committed with their initial ids; 8 steps.
   3 full vocab  sampler only: V=262144, d=3072; logits N(0,2) plus 12 at one
                 uniformly drawn id per row; E ~ N(0,0.02); 1 step.
-  4 long ctx    attention as 2 with P=4096, then the sampler of 3, one step.
+  4 long ctx    attention as 2 with P=4096, then the sampler of 3 (same E), one step.
   5 decode run  P=4096 prefix, 4 canvases of 256; per canvas fresh Q/K/V;
                 E is workload 3's E; logits come from the threshold-tuned
                 synthetic generator fed by a 65536-entry N(0,1) table drawn here.
@@ -92,8 +92,8 @@ def attention_inputs(workload, n_prefix=None, block=None, n=None, hq=None, hkv=N
 
 
 def embedding(workload, vocab=None, d_model=None):
-    """E [V, d] float32 ~ N(0, 0.02).  The decode run reuses workload 3's table."""
-    if workload == 5:
+    """E [V, d] float32 ~ N(0, 0.02).  Workloads 4 and 5 reuse workload 3's table."""
+    if workload in (4, 5):
         workload = 3
     c = CONFIGS[workload]
     vocab = c["vocab"] if vocab is None else vocab
