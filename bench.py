@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--profile-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
     return ap.parse_args()
 
 
@@ -68,7 +70,15 @@ def main():
     bf = torch.bfloat16
     dev = lambda x, dt=None: (torch.from_numpy(x).to(dt) if dt else torch.from_numpy(x)).cuda()
     T = dict(q=dev(q, bf), kp=dev(kp, bf), vp=dev(vp, bf), kc=dev(kc, bf), vc=dev(vc, bf),
-             logits=dev(logits), emb=dev(emb), ids=dev(ids.astype(np.int32)), mask=dev(mask))
+             logits=dev(logits), ids=dev(ids.astype(np.int32)), mask=dev(mask))
+    # E is converted once to the split-bf16 layout the sampler streams (load time, not per step)
+    emb_f32 = dev(emb)
+    torch.cuda.synchronize()
+    tp = time.perf_counter()
+    T["emb"] = dg.dg_embedding_pack(emb_f32)
+    torch.cuda.synchronize()
+    pack_ms = (time.perf_counter() - tp) * 1e3
+    del emb_f32
     T["attn"] = torch.empty((n, hq, hd), dtype=torch.float32, device="cuda")
     T["z"] = torch.empty((n, dm), dtype=torch.float32, device="cuda")
     T["kappa"] = torch.empty(n, dtype=torch.float32, device="cuda")
@@ -130,6 +140,16 @@ def main():
     attn = {"us": round(attn_us, 2), "tflops": round(attn_flops / (attn_us * 1e-6) / 1e12, 1),
             "frac_bf16_peak": round(attn_flops / (attn_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
+    if a.copy_probe_mib:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters calibrate
+        # the HBM byte counts read for the kernels above
+        src = torch.ones(a.copy_probe_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {a.copy_probe_mib} MiB read + {a.copy_probe_mib} MiB written per launch, 3 launches")
+
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(q, kp, vp, kc, vc, emb, logits, ids, mask)
@@ -151,6 +171,7 @@ def main():
                                "bf16; vocab 262144, d_model 3072 fp32; one captured graph per step",
                    "canvas_tokens_per_s": round(256 * steps_per_s, 1),
                    "per_kernel_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
+                   "embedding_pack_ms_once": round(pack_ms, 2),
                    "attention": attn},
         "roofline": roofline,
         "cpu_baseline": cpu,

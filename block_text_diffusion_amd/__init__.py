@@ -12,7 +12,7 @@ from ._lib import (DG_AUTO_ADVANCE, DG_BF16, DG_COMMIT_ONLY, DG_F32, DG_GUMBEL, 
                    DgCtrl, DgError, check, load)
 
 __all__ = [
-    "dg_canvas_attention", "dg_sampler_step", "dg_denoise_step", "StepGraph", "dg_canvas_init",
+    "dg_canvas_attention", "dg_sampler_step", "dg_embedding_pack", "dg_embedding_packed_bytes", "dg_denoise_step", "StepGraph", "dg_canvas_init",
     "dg_kv_append", "dg_synth_logits", "dg_philox_fill", "dg_attention_workspace_bytes",
     "dg_sampler_workspace_bytes", "dg_denoise_workspace_bytes", "dg_profile_enable",
     "dg_profile_read", "make_ctrl", "read_ctrl", "write_ctrl", "DG_GUMBEL", "DG_COMMIT_ONLY",
@@ -69,6 +69,21 @@ def dg_sampler_workspace_bytes(n_canvas, vocab, d_model):
     return load().dg_sampler_workspace_bytes(n_canvas, vocab, d_model)
 
 
+def dg_embedding_packed_bytes(vocab, d_model):
+    return load().dg_embedding_packed_bytes(vocab, d_model)
+
+
+def dg_embedding_pack(emb, packed=None, stream=None):
+    """E [V, d] float32 on the GPU -> the split-bf16 layout dg_sampler_step streams (uint8 tensor)."""
+    torch = _torch()
+    _need(emb, "emb", (torch.float32,))
+    vocab, d = emb.shape
+    if packed is None:
+        packed = torch.empty(dg_embedding_packed_bytes(vocab, d), dtype=torch.uint8, device=emb.device)
+    check(load().dg_embedding_pack(_ptr(emb), _ptr(packed), vocab, d, _stream(stream)))
+    return packed
+
+
 def dg_denoise_workspace_bytes(n_canvas, n_prefix, hq, hkv, head_dim, vocab, d_model):
     return load().dg_denoise_workspace_bytes(n_canvas, n_prefix, hq, hkv, head_dim, vocab, d_model)
 
@@ -121,20 +136,22 @@ def dg_canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, out=None, sca
     return out
 
 
-def dg_sampler_step(logits, emb, canvas_ids, committed, selfcond, confidence, n_uncommitted, ctrl,
-                    workspace=None, stream=None):
+def dg_sampler_step(logits, emb_packed, canvas_ids, committed, selfcond, confidence, n_uncommitted,
+                    ctrl, workspace=None, stream=None):
     torch = _torch()
-    _need(logits, "logits", (torch.float32,)); _need(emb, "emb", (torch.float32,))
+    _need(logits, "logits", (torch.float32,)); _need(emb_packed, "emb_packed", (torch.uint8,))
     _need(canvas_ids, "canvas_ids", (torch.int32,)); _need(committed, "committed", (torch.uint8,))
     _need(selfcond, "selfcond", (torch.float32,)); _need(n_uncommitted, "n_uncommitted", (torch.int32, torch.uint32))
     _need(ctrl, "ctrl", (torch.uint8,))
     if confidence is not None:
         _need(confidence, "confidence", (torch.float32,))
     n, vocab = logits.shape
-    d = emb.shape[1]
+    d = selfcond.shape[1]
+    if emb_packed.numel() < dg_embedding_packed_bytes(vocab, d):
+        raise ValueError("emb_packed is smaller than dg_embedding_packed_bytes(vocab, d_model)")
     nbytes = dg_sampler_workspace_bytes(n, vocab, d)
     ws = _workspace(nbytes, logits.device, workspace)
-    check(load().dg_sampler_step(_ptr(logits), _ptr(emb), _ptr(canvas_ids), _ptr(committed),
+    check(load().dg_sampler_step(_ptr(logits), _ptr(emb_packed), _ptr(canvas_ids), _ptr(committed),
                                  _ptr(selfcond), _ptr(confidence), _ptr(n_uncommitted), _ptr(ctrl),
                                  n, vocab, d, _ptr(ws), ws.numel(), _stream(stream)))
 
@@ -145,19 +162,22 @@ def _denoise_args(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, scale, lo
     hkv = k_canvas.shape[1]
     n_prefix = 0 if k_prefix is None else k_prefix.shape[0]
     vocab = logits.shape[1]
-    dm = emb.shape[1]
+    dm = selfcond.shape[1]
+    if emb.numel() < dg_embedding_packed_bytes(vocab, dm):
+        raise ValueError("emb_packed is smaller than dg_embedding_packed_bytes(vocab, d_model)")
     return (_ptr(q), _ptr(k_prefix) if n_prefix else None, _ptr(v_prefix) if n_prefix else None,
             _ptr(k_canvas), _ptr(v_canvas), _ptr(attn_out), n_prefix, hq, hkv, d, _qkv_dtype(q),
             float(scale), _ptr(logits), _ptr(emb), _ptr(canvas_ids), _ptr(committed), _ptr(selfcond),
             _ptr(confidence), _ptr(n_uncommitted), _ptr(ctrl), n, vocab, dm, _ptr(ws), ws.numel())
 
 
-def dg_denoise_step(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits, emb, canvas_ids,
-                    committed, selfcond, confidence, n_uncommitted, ctrl, scale=0.0, workspace=None,
-                    stream=None):
+def dg_denoise_step(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits, emb_packed,
+                    canvas_ids, committed, selfcond, confidence, n_uncommitted, ctrl, scale=0.0,
+                    workspace=None, stream=None):
+    emb = emb_packed
     n, hq, d = q.shape
     nbytes = dg_denoise_workspace_bytes(n, 0 if k_prefix is None else k_prefix.shape[0], hq,
-                                        k_canvas.shape[1], d, logits.shape[1], emb.shape[1])
+                                        k_canvas.shape[1], d, logits.shape[1], selfcond.shape[1])
     ws = _workspace(nbytes, q.device, workspace)
     args = _denoise_args(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, scale, logits, emb,
                          canvas_ids, committed, selfcond, confidence, n_uncommitted, ctrl, ws)
@@ -170,11 +190,13 @@ class StepGraph:
     Keeps references to every tensor the graph reads or writes so they outlive it.
     """
 
-    def __init__(self, q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits, emb, canvas_ids,
-                 committed, selfcond, confidence, n_uncommitted, ctrl, scale=0.0, workspace=None):
+    def __init__(self, q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits, emb_packed,
+                 canvas_ids, committed, selfcond, confidence, n_uncommitted, ctrl, scale=0.0,
+                 workspace=None):
+        emb = emb_packed
         n, hq, d = q.shape
         nbytes = dg_denoise_workspace_bytes(n, 0 if k_prefix is None else k_prefix.shape[0], hq,
-                                            k_canvas.shape[1], d, logits.shape[1], emb.shape[1])
+                                            k_canvas.shape[1], d, logits.shape[1], selfcond.shape[1])
         self.ws = _workspace(nbytes, q.device, workspace)
         self._keep = (q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits, emb, canvas_ids,
                       committed, selfcond, confidence, n_uncommitted, ctrl)

@@ -50,6 +50,8 @@ SIGNATURES = {
     "dg_attention_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "dg_canvas_attention": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "dg_sampler_workspace_bytes": (_sz, [_i, _i, _i]),
+    "dg_embedding_packed_bytes": (_sz, [_i, _i]),
+    "dg_embedding_pack": (_i, [_vp, _vp, _i, _i, _vp]),
     "dg_sampler_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]),
     "dg_denoise_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "dg_denoise_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,

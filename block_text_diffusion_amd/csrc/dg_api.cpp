@@ -73,7 +73,7 @@ int check_attention(const void* q, const void* kp, const void* vp, const void* k
   return DG_OK;
 }
 
-int check_sampler(const float* logits, const float* emb, const int32_t* ids, const uint8_t* committed,
+int check_sampler(const float* logits, const void* emb, const int32_t* ids, const uint8_t* committed,
                   const float* z, const uint32_t* n_unc, const dg_ctrl* ctrl, int n, int vocab, int d) {
   if (!logits || !emb || !ids || !committed || !z || !n_unc || !ctrl)
     return fail(DG_EINVAL, "sampler: null pointer argument");
@@ -81,12 +81,12 @@ int check_sampler(const float* logits, const float* emb, const int32_t* ids, con
   if (n > 256) return fail(DG_EUNSUPPORTED, "sampler: n_canvas > 256");
   if (vocab < 2) return fail(DG_EINVAL, "sampler: vocab < 2");
   if (d < 1) return fail(DG_EINVAL, "sampler: d_model < 1");
-  if ((size_t)vocab * (size_t)d > (1ull << 40)) return fail(DG_EINVAL, "sampler: E too large");
+  if (dg::embedding_packed_bytes(vocab, d) >= (1ull << 40)) return fail(DG_EINVAL, "sampler: E too large");
   // the logits are addressed with 32-bit byte offsets
   if ((uint64_t)n * (uint64_t)vocab * 4ull >= (1ull << 32))
     return fail(DG_EUNSUPPORTED, "sampler: n_canvas * vocab * 4 must be below 2^32");
   if (!aligned16(logits) || !aligned16(emb) || !aligned16(z))
-    return fail(DG_EINVAL, "sampler: logits/emb/selfcond must be 16-byte aligned");
+    return fail(DG_EINVAL, "sampler: logits/emb_packed/selfcond must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(ctrl) & 7u) != 0) return fail(DG_EINVAL, "sampler: ctrl misaligned");
   return DG_OK;
 }
@@ -164,7 +164,7 @@ int dg_canvas_attention(const void* q, const void* kp, const void* vp, const voi
   return DG_OK;
 }
 
-int dg_sampler_step(const float* logits, const float* emb, int32_t* ids, uint8_t* committed,
+int dg_sampler_step(const float* logits, const void* emb, int32_t* ids, uint8_t* committed,
                     float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl, int n, int vocab, int d,
                     void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, d);
@@ -180,7 +180,7 @@ int dg_sampler_step(const float* logits, const float* emb, int32_t* ids, uint8_t
 
 int dg_denoise_step(const void* q, const void* kp, const void* vp, const void* kc, const void* vc,
                     float* attn_out, int np, int hq, int hkv, int d, int dtype, float scale,
-                    const float* logits, const float* emb, int32_t* ids, uint8_t* committed,
+                    const float* logits, const void* emb, int32_t* ids, uint8_t* committed,
                     float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl, int n, int vocab, int dm,
                     void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_attention(q, kp, vp, kc, vc, attn_out, n, np, hq, hkv, d, dtype);
@@ -207,7 +207,7 @@ struct dg_step_graph {
 
 int dg_step_graph_create(const void* q, const void* kp, const void* vp, const void* kc,
                          const void* vc, float* attn_out, int np, int hq, int hkv, int d, int dtype,
-                         float scale, const float* logits, const float* emb, int32_t* ids,
+                         float scale, const float* logits, const void* emb, int32_t* ids,
                          uint8_t* committed, float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl,
                          int n, int vocab, int dm, void* ws, size_t ws_bytes, dg_step_graph** out) {
   if (!out) return fail(DG_EINVAL, "graph: null output handle");
@@ -258,6 +258,21 @@ void dg_step_graph_destroy(dg_step_graph* g) {
   hipGraphExecDestroy(g->exec);
   hipGraphDestroy(g->graph);
   delete g;
+}
+
+size_t dg_embedding_packed_bytes(int vocab, int d) {
+  if (vocab < 2 || d < 1) return 0;
+  return dg::embedding_packed_bytes(vocab, d);
+}
+
+int dg_embedding_pack(const float* emb, void* packed, int vocab, int d, hipStream_t stream) {
+  if (!emb || !packed) return fail(DG_EINVAL, "embedding_pack: null pointer");
+  if (vocab < 2 || d < 1) return fail(DG_EINVAL, "embedding_pack: bad sizes");
+  if (dg::embedding_packed_bytes(vocab, d) >= (1ull << 40)) return fail(DG_EINVAL, "embedding_pack: E too large");
+  if (!aligned16(packed)) return fail(DG_EINVAL, "embedding_pack: output misaligned");
+  hipError_t e = dg::launch_embedding_pack(emb, packed, vocab, d, stream);
+  if (e != hipSuccess) return hip_fail(e, "embedding_pack launch");
+  return DG_OK;
 }
 
 int dg_canvas_init(int32_t* ids, uint8_t* committed, dg_ctrl* ctrl, int n, int vocab,

@@ -18,15 +18,17 @@ void prof_end(hipStream_t s);
 // ---- sampler ----
 struct SamplerPlan {
   int n, vocab, d;
-  int n_chunks;      // stats chunks per row
-  int chunk_len;     // logits per stats chunk (multiple of 4)
-  int n_tiles;       // d-tiles of the contraction (256 columns each)
-  int n_splits;      // vocabulary splits of the contraction
-  int ks_per_split;  // 32-wide k steps per split
-  size_t off_stats, off_zp, total;
+  int n_kb;          // 16-id k-blocks of the vocabulary
+  int n_tiles;       // 256-column tiles of d
+  int col_pad;       // d rounded up to whole tiles
+  int kb_per_split;  // k-blocks per vocabulary split
+  int n_splits;      // vocabulary splits (own maxima, own partial z)
+  size_t off_stats, off_pimg, off_zp, total;
 };
 SamplerPlan sampler_plan(int n, int vocab, int d);
-hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const float* emb,
+size_t embedding_packed_bytes(int vocab, int d);
+hipError_t launch_embedding_pack(const float* emb, void* packed, int vocab, int d, hipStream_t s);
+hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void* emb_packed,
                           int32_t* ids, uint8_t* committed, float* z, float* conf,
                           uint32_t* n_unc, dg_ctrl* ctrl, void* ws, hipStream_t s);
 

@@ -5,17 +5,24 @@
 // quoting report 3.1-3.3, and AlphaSignal "How text diffusion actually works":
 // confident positions are locked in, the others re-noised uniformly).
 //
-// Four kernels, serialised on one stream:
-//   samp_stats     one pass over the logits: per (row, vocab chunk) the max, the
-//                  sums of exp(l - m) at T = 1 and at T, the greedy argmax and the
-//                  Gumbel-perturbed argmax.  HBM-bound.
-//   samp_gemm      z_partial[split] = sum_j exp(l_j - m) E_j over a vocab split:
-//                  a 256 x 256 tile per workgroup, bf16x3 split precision on
-//                  v_mfma_f32_32x32x16_bf16 (p = p_hi + p_lo, E = E_hi + E_lo,
-//                  p_hi E_hi + p_hi E_lo + p_lo E_hi accumulated in fp32), the
-//                  exponentials computed while staging the tile into LDS.
-//   samp_combine   per row: merge the chunk statistics, pick the candidate,
-//                  confidence, commit / re-noise, and z = sum(z_partial) / S.
+// The vocabulary is cut into splits (a few hundred k-blocks of 16 ids each);
+// every (row, split) pair keeps its own maximum m_s, so no pass needs the
+// global row maximum before the contraction.
+//
+//   samp_stats     per (split, row): pass 1 over the split's logits gives the
+//                  max, the greedy argmax and the Gumbel-perturbed argmax; pass 2
+//                  (re-read from L2) gives the sums of exp(l - m_s) at T = 1 and
+//                  at T and writes p = exp(l - m_s) as bf16 hi/lo "images": per
+//                  k-block of 16 ids, 256 row slots of 64 bytes (16 hi, 16 lo).
+//   samp_gemm      z_s = sum_j p_j E_j over one split for a 256 x 256 tile: p
+//                  and E (packed once by dg_embedding_pack into the same image
+//                  form) stream through LDS; bf16x3 split precision on
+//                  v_mfma_f32_32x32x16_bf16: p_hi E_hi + p_hi E_lo + p_lo E_hi
+//                  accumulated in fp32.  No exponentials or conversions in the
+//                  loop: 16-byte loads, LDS stores, fragment reads and MFMAs.
+//   samp_combine   per row: merge the split statistics (log-sum-exp), the
+//                  candidate, its confidence, commit / re-noise, and
+//                  z = sum_s 2^((m_s - m) log2 e) z_s / S.
 //   samp_finalize  count open positions; advance the step counters.
 #include "dg_common.hpp"
 #include "dg_internal.hpp"
@@ -23,7 +30,7 @@
 namespace dg {
 
 struct StatsPartial {
-  float m;           // max logit of the chunk (-inf if none)
+  float m;           // max logit of the (row, split) range (-inf if none)
   float s1;          // sum exp(l - m)
   float st;          // sum exp((l - m) / T)
   uint32_t best_id;  // smallest id attaining m
@@ -33,8 +40,15 @@ struct StatsPartial {
   uint32_t pad;
 };
 
+constexpr int kKB = 16;            // vocabulary ids per k-block
+constexpr int kImgRow = 64;        // bytes per row slot of a k-block image: 16 bf16 hi, 16 bf16 lo
+constexpr int kGM = 256;           // canvas row slots per image / rows per contraction tile
+constexpr int kGN = 256;           // embedding columns per contraction tile
+constexpr int kPImg = kGM * kImgRow;   // 16 KB: the p image of one k-block
+constexpr int kGThreads = 256;     // 4 waves (one per SIMD): 2 x 2, 128 x 128 each
+constexpr int kArr = kGM * kImgRow;    // 16 KB: one operand of one LDS stage
+constexpr int kStage = 2 * kArr;       // p tile + E tile
 constexpr int kStatsThreads = 256;
-constexpr int kStatsChunk = 16384;
 
 __device__ __forceinline__ float rescale_factor(float m_old, float m_new, float c) {
   return (m_old == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_old - m_new) * c);
@@ -50,13 +64,38 @@ __device__ __forceinline__ void merge_sums(float& m, float& s1, float& st, float
   m = mn;
 }
 
+__device__ __forceinline__ void merge_partial(StatsPartial& r, const StatsPartial& o, float c_t) {
+  const float mm = r.m;
+  merge_sums(r.m, r.s1, r.st, o.m, o.s1, o.st, c_t);
+  if (better(o.m, o.best_id, mm, r.best_id)) r.best_id = o.best_id;
+  if (better(o.gscore, o.gid, r.gscore, r.gid)) { r.gscore = o.gscore; r.gid = o.gid; }
+  r.bad |= o.bad;
+}
+
+// 16 logits of one k-block (ids >= vocab read as -inf).
+template <bool kAligned>
+__device__ __forceinline__ void load16(const float* __restrict__ x, int j, int vocab, float (&v)[16]) {
+  if (kAligned && j + 15 < vocab) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(x + j + 4 * q);
+      v[4 * q] = w[0]; v[4 * q + 1] = w[1]; v[4 * q + 2] = w[2]; v[4 * q + 3] = w[3];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = (j + e < vocab) ? x[j + e] : -INFINITY;
+  }
+}
+
+// grid (n_splits, n_rows); each thread takes whole k-blocks of the split.
 template <bool kAligned>
 __global__ __launch_bounds__(kStatsThreads) void samp_stats(const float* __restrict__ logits,
                                                             const dg_ctrl* __restrict__ ctrl,
                                                             StatsPartial* __restrict__ part,
-                                                            int vocab, int chunk_len) {
+                                                            uint8_t* __restrict__ pimg, int vocab,
+                                                            int kb_per_split, int n_kb) {
   const int row = blockIdx.y;
-  const int chunk = blockIdx.x;
+  const int split = blockIdx.x;
   const dg_ctrl cb = *ctrl;
   const float temp = temperature(cb);
   const float inv_t = 1.0f / temp;
@@ -65,261 +104,212 @@ __global__ __launch_bounds__(kStatsThreads) void samp_stats(const float* __restr
   const float c_t = kLog2e * inv_t;
   const uint32_t k0 = seed_lo(cb.seed), k1 = seed_hi(cb.seed);
   const float* x = logits + (size_t)row * (size_t)vocab;
-  const int j0 = chunk * chunk_len;
-  const int j1 = min(vocab, j0 + chunk_len);
+  const int kb0 = split * kb_per_split;
+  const int kb1 = min(n_kb, kb0 + kb_per_split);
+  const int w = threadIdx.x / kWave;
+  __shared__ StatsPartial red[kStatsThreads / kWave];
+  __shared__ float s_m;
 
-  float m = -INFINITY, s1 = 0.f, st = 0.f;
+  // pass 1: max, argmax, Gumbel argmax, undefined values
+  float m = -INFINITY;
   uint32_t bid = 0xFFFFFFFFu;
   float gbest = -INFINITY;
   uint32_t gid = 0xFFFFFFFFu;
   uint32_t bad = 0;
-
-  for (int j = j0 + 4 * (int)threadIdx.x; j < j1; j += 4 * kStatsThreads) {
-    float v[4];
-    if (kAligned && j + 3 < j1) {
-      const f32x4 q = *reinterpret_cast<const f32x4*>(x + j);
-      v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
-    } else {
+  for (int kb = kb0 + (int)threadIdx.x; kb < kb1; kb += kStatsThreads) {
+    const int j = kb * kKB;
+    float v[16];
+    load16<kAligned>(x, j, vocab, v);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (j + e < j1) ? x[j + e] : -INFINITY;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) bad |= (v[e] != v[e]) | (v[e] == INFINITY);
-    const float lmax = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-    if (lmax > m) {
-      const uint32_t li = (v[0] == lmax) ? j : (v[1] == lmax) ? j + 1 : (v[2] == lmax) ? j + 2 : j + 3;
-      s1 *= rescale_factor(m, lmax, kLog2e);
-      st *= rescale_factor(m, lmax, c_t);
-      m = lmax;
-      bid = li;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float dlt = v[e] - m;
-      s1 += __builtin_amdgcn_exp2f(fmaxf(dlt * kLog2e, -200.f));
-      if (tempered) st += __builtin_amdgcn_exp2f(fmaxf(dlt * c_t, -200.f));
+    for (int e = 0; e < 16; ++e) {
+      bad |= (v[e] != v[e]) | (v[e] == INFINITY);
+      if (v[e] > m) { m = v[e]; bid = (uint32_t)(j + e); }
     }
     if (gumbel) {
-      const Philox4 h = philox4x32_10((uint32_t)j >> 2, (uint32_t)row, cb.gstep, kStreamGumbel, k0, k1);
-      const uint32_t hw[4] = {h.w0, h.w1, h.w2, h.w3};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float sc = v[e] * inv_t + gumbel_from_bits(hw[e]);
-        if (sc > gbest) { gbest = sc; gid = (uint32_t)(j + e); }
+      for (int q = 0; q < 4; ++q) {
+        const Philox4 h = philox4x32_10((uint32_t)(j >> 2) + q, (uint32_t)row, cb.gstep, kStreamGumbel, k0, k1);
+        const uint32_t hw[4] = {h.w0, h.w1, h.w2, h.w3};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sc = v[4 * q + e] * inv_t + gumbel_from_bits(hw[e]);
+          if (sc > gbest) { gbest = sc; gid = (uint32_t)(j + 4 * q + e); }
+        }
       }
     }
   }
-  if (!tempered) st = s1;
-
-  // wavefront reduction
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    const float om = __shfl_xor(m, o), os1 = __shfl_xor(s1, o), ost = __shfl_xor(st, o);
+    const float om = __shfl_xor(m, o);
     const uint32_t obid = __shfl_xor(bid, o);
-    const float mm = m;
-    merge_sums(m, s1, st, om, os1, ost, c_t);
-    if (better(om, obid, mm, bid)) bid = obid;
+    if (better(om, obid, m, bid)) { m = om; bid = obid; }
     const float og = __shfl_xor(gbest, o);
     const uint32_t ogid = __shfl_xor(gid, o);
     if (better(og, ogid, gbest, gid)) { gbest = og; gid = ogid; }
     bad |= __shfl_xor(bad, o);
   }
-  __shared__ StatsPartial red[kStatsThreads / kWave];
-  const int w = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = StatsPartial{m, s1, st, bid, gbest, gid, bad, 0};
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = StatsPartial{m, 0.f, 0.f, bid, gbest, gid, bad, 0};
   __syncthreads();
   if (threadIdx.x == 0) {
     StatsPartial r = red[0];
     for (int i = 1; i < kStatsThreads / kWave; ++i) {
-      const StatsPartial o = red[i];
-      const float mm = r.m;
-      merge_sums(r.m, r.s1, r.st, o.m, o.s1, o.st, c_t);
-      if (better(o.m, o.best_id, mm, r.best_id)) r.best_id = o.best_id;
+      const StatsPartial& o = red[i];
+      if (better(o.m, o.best_id, r.m, r.best_id)) { r.m = o.m; r.best_id = o.best_id; }
       if (better(o.gscore, o.gid, r.gscore, r.gid)) { r.gscore = o.gscore; r.gid = o.gid; }
       r.bad |= o.bad;
     }
-    part[(size_t)row * gridDim.x + chunk] = r;
+    red[0] = r;
+    s_m = r.m;
+  }
+  __syncthreads();
+  const float mr = s_m;
+
+  // pass 2: exp(l - m_s), its sums, and the bf16 hi/lo image rows
+  const float mc = (mr == -INFINITY) ? 0.0f : -mr * kLog2e;
+  float s1 = 0.f, st = 0.f;
+  for (int kb = kb0 + (int)threadIdx.x; kb < kb1; kb += kStatsThreads) {
+    const int j = kb * kKB;
+    float v[16];
+    load16<kAligned>(x, j, vocab, v);
+    float p[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[e], kLog2e, mc));
+      s1 += p[e];
+      if (tempered) st += __builtin_amdgcn_exp2f(fmaxf((v[e] - mr) * c_t, -200.f));
+    }
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split2(p[2 * e], p[2 * e + 1], hi[e], lo[e]);
+    uint8_t* dst = pimg + (size_t)kb * kPImg + (size_t)row * kImgRow;
+    *reinterpret_cast<u32x4*>(dst) = (u32x4){hi[0], hi[1], hi[2], hi[3]};
+    *reinterpret_cast<u32x4*>(dst + 16) = (u32x4){hi[4], hi[5], hi[6], hi[7]};
+    *reinterpret_cast<u32x4*>(dst + 32) = (u32x4){lo[0], lo[1], lo[2], lo[3]};
+    *reinterpret_cast<u32x4*>(dst + 48) = (u32x4){lo[4], lo[5], lo[6], lo[7]};
+  }
+  if (!tempered) st = s1;
+  s1 = wave_sum(s1);
+  st = wave_sum(st);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) { red[w].s1 = s1; red[w].st = st; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    StatsPartial r = red[0];
+    for (int i = 1; i < kStatsThreads / kWave; ++i) { r.s1 += red[i].s1; r.st += red[i].st; }
+    r.m = mr;
+    part[(size_t)row * gridDim.x + split] = r;
   }
 }
 
 // ---------------------------------------------------------------------------
-// z_partial = exp(l - m) · E over one vocabulary split, bf16x3 on MFMA.
+// E packing: the embedding table as bf16 hi/lo k-block images, columns padded
+// to a multiple of 256 (zeros), ids padded to a multiple of 16 (zeros).
 // ---------------------------------------------------------------------------
-constexpr int kGM = 256;        // canvas rows per tile
-constexpr int kGN = 256;        // embedding columns per tile
-constexpr int kGK = 32;         // vocabulary entries per k step
-constexpr int kGThreads = 256;  // 4 waves (one per SIMD): 2 (rows) x 2 (columns), 128 x 128 each
-constexpr int kArrBytes = kGM * kGK * 2;        // 16 KB per bf16 array
-constexpr int kStageBytes = 4 * kArrBytes;      // A_hi, A_lo, B_hi, B_lo
+__global__ __launch_bounds__(256) void emb_pack_kernel(const float* __restrict__ emb,
+                                                       uint8_t* __restrict__ out, int vocab, int d,
+                                                       int col_pad) {
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  const int kb = blockIdx.y;
+  float v[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int k = kb * kKB + e;
+    v[e] = (k < vocab && col < d) ? emb[(size_t)k * d + col] : 0.0f;
+  }
+  uint32_t hi[8], lo[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) split2(v[2 * e], v[2 * e + 1], hi[e], lo[e]);
+  uint8_t* dst = out + ((size_t)kb * col_pad + col) * kImgRow;
+  *reinterpret_cast<u32x4*>(dst) = (u32x4){hi[0], hi[1], hi[2], hi[3]};
+  *reinterpret_cast<u32x4*>(dst + 16) = (u32x4){hi[4], hi[5], hi[6], hi[7]};
+  *reinterpret_cast<u32x4*>(dst + 32) = (u32x4){lo[0], lo[1], lo[2], lo[3]};
+  *reinterpret_cast<u32x4*>(dst + 48) = (u32x4){lo[4], lo[5], lo[6], lo[7]};
+}
 
-// LDS rows are 64 bytes (32 bf16 = four 16-byte chunks); the chunk index is
-// xor-swizzled with row bits so a wavefront's 16-byte reads of one chunk
-// column spread over all banks.
+// ---------------------------------------------------------------------------
+// z_s = p · E over one split, bf16x3 on MFMA.
+// ---------------------------------------------------------------------------
+
+// LDS rows are 64 bytes (four 16-byte chunks: hi k0-7, hi k8-15, lo k0-7,
+// lo k8-15); the chunk index is xor-swizzled with row bits so a wavefront's
+// 16-byte reads of one chunk column spread over all banks.
 __device__ __forceinline__ int swz_off(int row, int chunk) {
   return row * 64 + ((chunk ^ (((row >> 1) ^ (row >> 2)) & 3)) << 4);
 }
 
-// One k step's global data held by a thread between its load and its LDS store.
-struct GemmRegs {
-  f32x4 a[8];     // logits: rows (t>>3) + 32q, k = 4*(t&7) .. +3
-  float b[32];    // E: column t, all 32 k
+constexpr int kBufFlags = 0x00020000;  // raw 32-bit buffer access (gfx9 family)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufFlags);
+}
+
+// One k step of global data held by a thread between its load and its LDS store:
+// 4 x 16 bytes of the p image (rows 64w+16j .. of this wave) and 4 x 16 bytes of
+// the E image (columns 64w+16j ..).
+struct StepRegs {
+  u32x4 a[4];
+  u32x4 b[4];
 };
 
-// Per-lane addressing fixed for the whole k loop: 32-bit byte offsets from
-// uniform (scalar) bases; rows/columns past the end read a valid address and
-// are masked when the tile is staged.
-struct GemmLanes {
-  uint32_t a_off0;    // byte offset of (row t>>3, k 4*(t&7)) from the logits base
-  uint32_t a_step;    // bytes between rows r and r + 32
-  uint32_t b_off;     // byte offset of column col0 + t from an E row base
-  uint32_t row_ok;    // bit q: row (t>>3) + 32q < n_rows
-  bool col_ok;
-};
-
-__device__ __forceinline__ GemmLanes gemm_lanes(int n_rows, int vocab, int d, int col0) {
-  GemmLanes g;
-  const int t = threadIdx.x;
-  g.row_ok = 0;
+__device__ __forceinline__ void gemm_load(StepRegs& r, const uint8_t* __restrict__ pimg,
+                                          const uint8_t* __restrict__ eimg, int kb, int col_pad,
+                                          int col0, uint32_t lane_off, int wave) {
+  const __amdgpu_buffer_rsrc_t ra = rsrc(pimg + (size_t)kb * kPImg, kPImg);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(eimg + ((size_t)kb * col_pad + col0) * kImgRow, kArr);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) g.row_ok |= ((t >> 3) + 32 * q < n_rows) ? (1u << q) : 0u;
-  g.a_off0 = ((uint32_t)(t >> 3) * (uint32_t)vocab + 4u * (uint32_t)(t & 7)) * 4u;
-  g.a_step = 32u * (uint32_t)vocab * 4u;
-  const int col = col0 + t;
-  g.col_ok = col < d;
-  g.b_off = (uint32_t)(g.col_ok ? col : d - 1) * 4u;
-  return g;
-}
-
-__device__ __forceinline__ uint32_t a_offset(const GemmLanes& g, int q) {
-  return ((g.row_ok >> q) & 1u) ? g.a_off0 + (uint32_t)q * g.a_step : 0u;
-}
-
-// Interior k step: every k index is in range, no per-element checks.
-__device__ __forceinline__ void gemm_load_full(GemmRegs& r, const GemmLanes& g,
-                                               const float* __restrict__ logits,
-                                               const float* __restrict__ emb, int d, int kbase) {
-  const char* abase = reinterpret_cast<const char*>(logits + kbase);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) r.a[q] = *reinterpret_cast<const f32x4*>(abase + a_offset(g, q));
-  const char* bbase = reinterpret_cast<const char*>(emb + (size_t)kbase * (size_t)d);
-  const size_t row_bytes = (size_t)d * 4u;
-#pragma unroll
-  for (int e = 0; e < 32; ++e) r.b[e] = *reinterpret_cast<const float*>(bbase + e * row_bytes + g.b_off);
-}
-
-// Last (ragged) k step, or an unaligned vocabulary: element-wise with k checks.
-template <bool kAligned>
-__device__ __forceinline__ void gemm_load_tail(GemmRegs& r, const GemmLanes& g,
-                                               const float* __restrict__ logits,
-                                               const float* __restrict__ emb, int d, int kbase,
-                                               int kend) {
-  const int t = threadIdx.x;
-  const int kk = kbase + 4 * (t & 7);
-  const char* abase = reinterpret_cast<const char*>(logits + kbase);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const float* src = reinterpret_cast<const float*>(abase + a_offset(g, q));
-    if (kAligned && kk + 3 < kend) {
-      r.a[q] = *reinterpret_cast<const f32x4*>(src);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) r.a[q][e] = (kk + e < kend) ? src[e] : -INFINITY;
-    }
-  }
-  const char* bbase = reinterpret_cast<const char*>(emb);
-#pragma unroll
-  for (int e = 0; e < 32; ++e)
-    r.b[e] = (kbase + e < kend)
-                 ? *reinterpret_cast<const float*>(bbase + (size_t)(kbase + e) * d * 4u + g.b_off)
-                 : 0.0f;
-}
-
-// exp, split and store one k step's tiles into an LDS stage.
-__device__ __forceinline__ void gemm_store(const GemmRegs& r, const GemmLanes& g, uint8_t* stage,
-                                           const float* rm) {
-  const int t = threadIdx.x;
-  uint8_t* a_hi = stage;
-  uint8_t* a_lo = stage + kArrBytes;
-  uint8_t* b_hi = stage + 2 * kArrBytes;
-  uint8_t* b_lo = stage + 3 * kArrBytes;
-  const int kk = 4 * (t & 7);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int row = (t >> 3) + 32 * q;
-    const bool ok = (g.row_ok >> q) & 1u;
-    float p[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = r.a[q][e];
-      p[e] = (!ok || x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x - rm[q]) * kLog2e);
-    }
-    uint32_t h0, l0, h1, l1;
-    split2(p[0], p[1], h0, l0);
-    split2(p[2], p[3], h1, l1);
-    const int off = swz_off(row, kk >> 3) + ((kk & 4) << 1);
-    *reinterpret_cast<u32x2*>(a_hi + off) = (u32x2){h0, h1};
-    *reinterpret_cast<u32x2*>(a_lo + off) = (u32x2){l0, l1};
-  }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x0 = g.col_ok ? r.b[8 * c + 2 * e] : 0.f;
-      const float x1 = g.col_ok ? r.b[8 * c + 2 * e + 1] : 0.f;
-      split2(x0, x1, h[e], l[e]);
-    }
-    const int off = swz_off(t, c);
-    *reinterpret_cast<u32x4*>(b_hi + off) = (u32x4){h[0], h[1], h[2], h[3]};
-    *reinterpret_cast<u32x4*>(b_lo + off) = (u32x4){l[0], l[1], l[2], l[3]};
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t off = (uint32_t)((64 * wave + 16 * j) * kImgRow) + lane_off;
+    r.a[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+    r.b[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
   }
 }
 
-// acc[mb][nb] += A_tile(rows 128*wm + 32*mb ..) x B_tile(cols 128*wn + 32*nb ..), bf16x3.
-__device__ __forceinline__ void gemm_mma(const uint8_t* stage, f32x16 (&acc)[4][4], int wm, int wn) {
-  const int lane = threadIdx.x & 63;
-  const uint8_t* a_hi = stage;
-  const uint8_t* a_lo = stage + kArrBytes;
-  const uint8_t* b_hi = stage + 2 * kArrBytes;
-  const uint8_t* b_lo = stage + 3 * kArrBytes;
+// Lane i of a 16-row group holds global chunk (i & 3) of row (i >> 2); it lands
+// at that row's swizzled chunk position.
+__device__ __forceinline__ void gemm_store(const StepRegs& r, uint8_t* stage, int wave, int lane) {
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int chunk = 2 * ks + (lane >> 5);
-    bf16x8 ah[4], al[4], bh[4], bl[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int oa = swz_off(128 * wm + 32 * i + (lane & 31), chunk);
-      ah[i] = *reinterpret_cast<const bf16x8*>(a_hi + oa);
-      al[i] = *reinterpret_cast<const bf16x8*>(a_lo + oa);
-      const int ob = swz_off(128 * wn + 32 * i + (lane & 31), chunk);
-      bh[i] = *reinterpret_cast<const bf16x8*>(b_hi + ob);
-      bl[i] = *reinterpret_cast<const bf16x8*>(b_lo + ob);
-    }
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bh[nb], acc[mb][nb], 0, 0, 0);
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bl[nb], acc[mb][nb], 0, 0, 0);
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], bh[nb], acc[mb][nb], 0, 0, 0);
-      }
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int row = 64 * wave + 16 * j + (lane >> 2);
+    const int off = swz_off(row, lane & 3);
+    *reinterpret_cast<u32x4*>(stage + off) = r.a[j];
+    *reinterpret_cast<u32x4*>(stage + kArr + off) = r.b[j];
   }
 }
 
-template <bool kAligned>
-__global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const float* __restrict__ logits,
-                                                          const float* __restrict__ emb,
-                                                          const StatsPartial* __restrict__ part,
-                                                          float* __restrict__ zp, int n_rows,
-                                                          int vocab, int d, int n_chunks,
-                                                          int n_tiles, int ks_per_split) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
-  __shared__ float rowmax[kGM];
+// acc[mb][nb] += A(rows 128*wm + 32*mb ..) x B(cols 128*wn + 32*nb ..) for one 16-id k step.
+__device__ __forceinline__ void gemm_mma(const uint8_t* stage, f32x16 (&acc)[4][4], int wm, int wn,
+                                         int lane) {
+  const int h = lane >> 5;
+  bf16x8 ah[4], al[4], bh[4], bl[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra = 128 * wm + 32 * i + (lane & 31);
+    ah[i] = *reinterpret_cast<const bf16x8*>(stage + swz_off(ra, h));
+    al[i] = *reinterpret_cast<const bf16x8*>(stage + swz_off(ra, 2 + h));
+    const int rb = 128 * wn + 32 * i + (lane & 31);
+    bh[i] = *reinterpret_cast<const bf16x8*>(stage + kArr + swz_off(rb, h));
+    bl[i] = *reinterpret_cast<const bf16x8*>(stage + kArr + swz_off(rb, 2 + h));
+  }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bh[nb], acc[mb][nb], 0, 0, 0);
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bl[nb], acc[mb][nb], 0, 0, 0);
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], bh[nb], acc[mb][nb], 0, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restrict__ pimg,
+                                                          const uint8_t* __restrict__ eimg,
+                                                          float* __restrict__ zp, int n_rows, int d,
+                                                          int col_pad, int n_tiles, int kb_per_split,
+                                                          int n_kb) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
 
   // Workgroups are dealt round-robin to the 8 XCDs; renumber them so the
   // d-tiles of one vocabulary split sit on the same XCD and share its L2 copy
-  // of the logits slice.
+  // of the p images.
   const int nwg = gridDim.x;
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
@@ -328,24 +318,15 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const float* __restric
   const int tile = lin % n_tiles;
   const int split = lin / n_tiles;
   const int col0 = tile * kGN;
-  const int kbegin = split * ks_per_split * kGK;
-  const int kend = min(vocab, kbegin + ks_per_split * kGK);
-  const int nsteps = (kend - kbegin + kGK - 1) / kGK;
+  const int kb0 = split * kb_per_split;
+  const int nsteps = min(n_kb, kb0 + kb_per_split) - kb0;
 
   const int t = threadIdx.x;
-  {
-    float m = -INFINITY;
-    if (t < n_rows)
-      for (int c = 0; c < n_chunks; ++c) m = fmaxf(m, part[(size_t)t * n_chunks + c].m);
-    rowmax[t] = m;
-  }
-  __syncthreads();
-  float rm[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) rm[q] = rowmax[(t >> 3) + 32 * q];
-
+  const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lane_off = (uint32_t)((lane >> 2) * kImgRow + (lane & 3) * 16);
+
   f32x16 acc[4][4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -354,51 +335,36 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const float* __restric
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
 
-  const GemmLanes g = gemm_lanes(n_rows, vocab, d, col0);
-  // Interior steps [0, nfull) run software-pipelined with two register sets:
-  // step k is loaded into set k&1 and staged into LDS buffer k&1; iteration s
-  // runs the MFMAs of step s, then stages step s+1 and issues the loads of step
-  // s+3, so every global load has a full iteration of MFMAs to land.
-  const int nfull = kAligned ? (kend - kbegin) / kGK : 0;
-  GemmRegs ra, rb;
-  if (nfull > 0) {
-    gemm_load_full(ra, g, logits, emb, d, kbegin);
-    if (nfull > 1) gemm_load_full(rb, g, logits, emb, d, kbegin + kGK);
-    gemm_store(ra, g, smem, rm);
-    if (nfull > 2) gemm_load_full(ra, g, logits, emb, d, kbegin + 2 * kGK);
+  // Step k is loaded into register set k&1 two iterations ahead and stored
+  // into LDS stage k&1 one iteration ahead; iteration s multiplies stage s&1.
+  StepRegs ra, rb;
+  if (nsteps > 0) {
+    gemm_load(ra, pimg, eimg, kb0, col_pad, col0, lane_off, wave);
+    if (nsteps > 1) gemm_load(rb, pimg, eimg, kb0 + 1, col_pad, col0, lane_off, wave);
+    gemm_store(ra, smem, wave, lane);
+    if (nsteps > 2) gemm_load(ra, pimg, eimg, kb0 + 2, col_pad, col0, lane_off, wave);
   }
   __syncthreads();
   int s = 0;
-  for (; s + 4 < nfull; s += 2) {
-    gemm_mma(smem, acc, wm, wn);
-    gemm_store(rb, g, smem + kStageBytes, rm);
-    gemm_load_full(rb, g, logits, emb, d, kbegin + (s + 3) * kGK);
+  for (; s + 4 <= nsteps; s += 2) {
+    gemm_mma(smem, acc, wm, wn, lane);
+    gemm_store(rb, smem + kStage, wave, lane);
+    if (s + 3 < nsteps) gemm_load(rb, pimg, eimg, kb0 + s + 3, col_pad, col0, lane_off, wave);
     __syncthreads();
-    gemm_mma(smem + kStageBytes, acc, wm, wn);
-    gemm_store(ra, g, smem, rm);
-    gemm_load_full(ra, g, logits, emb, d, kbegin + (s + 4) * kGK);
+    gemm_mma(smem + kStage, acc, wm, wn, lane);
+    gemm_store(ra, smem, wave, lane);
+    if (s + 4 < nsteps) gemm_load(ra, pimg, eimg, kb0 + s + 4, col_pad, col0, lane_off, wave);
     __syncthreads();
   }
-  for (; s < nfull; ++s) {
+  for (; s < nsteps; ++s) {
     const bool odd = s & 1;
-    gemm_mma(smem + (odd ? kStageBytes : 0), acc, wm, wn);
-    if (s + 1 < nfull) gemm_store(odd ? ra : rb, g, smem + (odd ? 0 : kStageBytes), rm);
-    if (s + 3 < nfull) gemm_load_full(odd ? ra : rb, g, logits, emb, d, kbegin + (s + 3) * kGK);
-    __syncthreads();
-  }
-  GemmRegs& regs = ra;
-  // The ragged last step (or every step of an unaligned vocabulary): checked
-  // loads, not pipelined.
-  for (int s = nfull; s < nsteps; ++s) {
-    gemm_load_tail<kAligned>(regs, g, logits, emb, d, kbegin + s * kGK, kend);
-    gemm_store(regs, g, smem, rm);
-    __syncthreads();
-    gemm_mma(smem, acc, wm, wn);
+    gemm_mma(smem + (odd ? kStage : 0), acc, wm, wn, lane);
+    if (s + 1 < nsteps) gemm_store(odd ? ra : rb, smem + (odd ? 0 : kStage), wave, lane);
+    if (s + 3 < nsteps) gemm_load(odd ? ra : rb, pimg, eimg, kb0 + s + 3, col_pad, col0, lane_off, wave);
     __syncthreads();
   }
 
   // epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block, column lane%32
-  const int lane = t & 63;
   float* out = zp + (size_t)split * (size_t)n_rows * (size_t)d;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
@@ -416,67 +382,90 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const float* __restric
 
 // ---------------------------------------------------------------------------
 // Per row: statistics merge, candidate, confidence, commit / re-noise, z.
+// grid (ceil(d / 1024), n_rows); each thread owns 4 columns of z.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void samp_combine(const float* __restrict__ logits,
                                                     const StatsPartial* __restrict__ part,
-                                                    int n_chunks, const float* __restrict__ zp,
-                                                    int n_splits, const dg_ctrl* __restrict__ ctrl,
+                                                    int n_splits, const float* __restrict__ zp,
+                                                    const dg_ctrl* __restrict__ ctrl,
                                                     int32_t* __restrict__ ids,
                                                     uint8_t* __restrict__ committed,
                                                     float* __restrict__ z, float* __restrict__ conf,
                                                     int n_rows, int vocab, int d) {
-  const int row = blockIdx.x;
-  __shared__ float s_inv_s1;
+  const int row = blockIdx.y;
+  __shared__ float s_w[256];
   __shared__ uint32_t s_bad;
-  if (threadIdx.x == 0) {
-    const dg_ctrl cb = *ctrl;
-    const float temp = temperature(cb);
-    const float inv_t = 1.0f / temp;
-    const float c_t = kLog2e * inv_t;
-    StatsPartial r = part[(size_t)row * n_chunks];
-    for (int c = 1; c < n_chunks; ++c) {
-      const StatsPartial o = part[(size_t)row * n_chunks + c];
-      const float mm = r.m;
-      merge_sums(r.m, r.s1, r.st, o.m, o.s1, o.st, c_t);
-      if (better(o.m, o.best_id, mm, r.best_id)) r.best_id = o.best_id;
-      if (better(o.gscore, o.gid, r.gscore, r.gid)) { r.gscore = o.gscore; r.gid = o.gid; }
-      r.bad |= o.bad;
+  const dg_ctrl cb = *ctrl;
+  const float temp = temperature(cb);
+  const float inv_t = 1.0f / temp;
+  const float c_t = kLog2e * inv_t;
+  const StatsPartial* pr = part + (size_t)row * n_splits;
+  if (threadIdx.x < kWave) {
+    // wave 0 merges the split statistics; lane s takes splits s, s+64, ...
+    StatsPartial r{-INFINITY, 0.f, 0.f, 0xFFFFFFFFu, -INFINITY, 0xFFFFFFFFu, 0u, 0u};
+    for (int sp = threadIdx.x; sp < n_splits; sp += kWave) merge_partial(r, pr[sp], c_t);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      StatsPartial q;
+      q.m = __shfl_xor(r.m, o); q.s1 = __shfl_xor(r.s1, o); q.st = __shfl_xor(r.st, o);
+      q.best_id = __shfl_xor(r.best_id, o); q.gscore = __shfl_xor(r.gscore, o);
+      q.gid = __shfl_xor(r.gid, o); q.bad = __shfl_xor(r.bad, o);
+      merge_partial(r, q, c_t);
     }
     const bool bad = r.bad || !(r.m > -INFINITY);
-    const bool gumbel = (cb.flags & DG_GUMBEL) != 0;
-    uint32_t cand = gumbel ? r.gid : r.best_id;
-    if (cand >= (uint32_t)vocab) cand = 0;
-    float kappa;
-    if (bad) {
-      kappa = __builtin_nanf("");
-    } else {
-      const float lc = logits[(size_t)row * vocab + cand];
-      kappa = exp2f((lc - r.m) * c_t) / r.st;
-    }
-    if (conf) conf[row] = kappa;
-    if (!committed[row]) {
-      const bool last = cb.s_in_block + 1u >= cb.s_max;
-      if (!bad && (kappa >= cb.tau || last)) {
-        ids[row] = (int32_t)cand;
-        committed[row] = 1;
-      } else if (!(cb.flags & DG_COMMIT_ONLY)) {
-        const Philox4 h = philox4x32_10(0u, (uint32_t)row, cb.gstep, kStreamRenoise,
-                                        seed_lo(cb.seed), seed_hi(cb.seed));
-        ids[row] = (int32_t)range_draw(h.w0, (uint32_t)vocab);
+    const float inv_s1 = 1.0f / r.s1;
+    for (int sp = threadIdx.x; sp < n_splits; sp += kWave)
+      s_w[sp] = rescale_factor(pr[sp].m, r.m, kLog2e) * inv_s1;
+    if (threadIdx.x == 0) {
+      s_bad = bad;
+      if (blockIdx.x == 0) {
+        const bool gumbel = (cb.flags & DG_GUMBEL) != 0;
+        uint32_t cand = gumbel ? r.gid : r.best_id;
+        if (cand >= (uint32_t)vocab) cand = 0;
+        float kappa;
+        if (bad) {
+          kappa = __builtin_nanf("");
+        } else {
+          const float lc = logits[(size_t)row * vocab + cand];
+          kappa = exp2f((lc - r.m) * c_t) / r.st;
+        }
+        if (conf) conf[row] = kappa;
+        if (!committed[row]) {
+          const bool last = cb.s_in_block + 1u >= cb.s_max;
+          if (!bad && (kappa >= cb.tau || last)) {
+            ids[row] = (int32_t)cand;
+            committed[row] = 1;
+          } else if (!(cb.flags & DG_COMMIT_ONLY)) {
+            const Philox4 h = philox4x32_10(0u, (uint32_t)row, cb.gstep, kStreamRenoise,
+                                            seed_lo(cb.seed), seed_hi(cb.seed));
+            ids[row] = (int32_t)range_draw(h.w0, (uint32_t)vocab);
+          }
+        }
       }
     }
-    s_inv_s1 = 1.0f / r.s1;
-    s_bad = bad;
   }
   __syncthreads();
-  const float inv = s_inv_s1;
   const bool bad = s_bad != 0;
+  const int col = blockIdx.x * 1024 + 4 * threadIdx.x;
+  if (col >= d) return;
   const size_t stride = (size_t)n_rows * (size_t)d;
-  for (int col = threadIdx.x; col < d; col += blockDim.x) {
-    const float* src = zp + (size_t)row * d + col;
-    float acc = 0.f;
-    for (int s = 0; s < n_splits; ++s) acc += src[s * stride];
-    z[(size_t)row * d + col] = bad ? __builtin_nanf("") : acc * inv;
+  const float* src = zp + (size_t)row * d + col;
+  float* dst = z + (size_t)row * d + col;
+  if ((d & 3) == 0) {
+    f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < n_splits; ++sp) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + sp * stride);
+      const float wsp = s_w[sp];
+      acc[0] += wsp * v[0]; acc[1] += wsp * v[1]; acc[2] += wsp * v[2]; acc[3] += wsp * v[3];
+    }
+    if (bad) acc = (f32x4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    *reinterpret_cast<f32x4*>(dst) = acc;
+  } else {
+    for (int e = 0; e < 4 && col + e < d; ++e) {
+      float acc = 0.f;
+      for (int sp = 0; sp < n_splits; ++sp) acc += s_w[sp] * src[sp * stride + e];
+      dst[e] = bad ? __builtin_nanf("") : acc;
+    }
   }
 }
 
@@ -496,57 +485,73 @@ __global__ __launch_bounds__(256) void samp_finalize(const uint8_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+size_t embedding_packed_bytes(int vocab, int d) {
+  const size_t n_kb = (size_t)(vocab + kKB - 1) / kKB;
+  const size_t col_pad = (size_t)(d + kGN - 1) / kGN * kGN;
+  return n_kb * col_pad * kImgRow;
+}
+
+hipError_t launch_embedding_pack(const float* emb, void* packed, int vocab, int d, hipStream_t s) {
+  const int n_kb = (vocab + kKB - 1) / kKB;
+  const int col_pad = (d + kGN - 1) / kGN * kGN;
+  prof_begin("emb_pack", s);
+  emb_pack_kernel<<<dim3(col_pad / 256, n_kb), 256, 0, s>>>(emb, static_cast<uint8_t*>(packed), vocab,
+                                                            d, col_pad);
+  prof_end(s);
+  return hipGetLastError();
+}
+
 SamplerPlan sampler_plan(int n, int vocab, int d) {
   SamplerPlan p{};
   p.n = n; p.vocab = vocab; p.d = d;
-  p.chunk_len = kStatsChunk;
-  p.n_chunks = (vocab + kStatsChunk - 1) / kStatsChunk;
+  p.n_kb = (vocab + kKB - 1) / kKB;
   p.n_tiles = (d + kGN - 1) / kGN;
-  const int ksteps = (vocab + kGK - 1) / kGK;
+  p.col_pad = p.n_tiles * kGN;
   int splits = 256 / p.n_tiles;
   if (splits < 1) splits = 1;
-  const int by_len = (ksteps + 7) / 8;
+  const int by_len = (p.n_kb + 15) / 16;     // at least 16 k-blocks per split
   if (splits > by_len) splits = by_len;
   if (splits < 1) splits = 1;
-  p.ks_per_split = (ksteps + splits - 1) / splits;
-  p.n_splits = (ksteps + p.ks_per_split - 1) / p.ks_per_split;
+  p.kb_per_split = (p.n_kb + splits - 1) / splits;
+  p.n_splits = (p.n_kb + p.kb_per_split - 1) / p.kb_per_split;
   p.off_stats = 0;
-  p.off_zp = align_up((size_t)n * p.n_chunks * sizeof(StatsPartial), 256);
+  p.off_pimg = align_up((size_t)n * p.n_splits * sizeof(StatsPartial), 256);
+  p.off_zp = p.off_pimg + align_up((size_t)p.n_kb * kPImg, 256);
   p.total = p.off_zp + align_up((size_t)p.n_splits * n * d * sizeof(float), 256);
   return p;
 }
 
-hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const float* emb,
+hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void* emb_packed,
                           int32_t* ids, uint8_t* committed, float* z, float* conf,
                           uint32_t* n_unc, dg_ctrl* ctrl, void* ws, hipStream_t s) {
-  StatsPartial* part = reinterpret_cast<StatsPartial*>(static_cast<uint8_t*>(ws) + p.off_stats);
-  float* zp = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p.off_zp);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  StatsPartial* part = reinterpret_cast<StatsPartial*>(base + p.off_stats);
+  uint8_t* pimg = base + p.off_pimg;
+  float* zp = reinterpret_cast<float*>(base + p.off_zp);
   const bool aligned = (p.vocab % 4) == 0;
 
   prof_begin("samp_stats", s);
   if (aligned)
-    samp_stats<true><<<dim3(p.n_chunks, p.n), kStatsThreads, 0, s>>>(logits, ctrl, part, p.vocab, p.chunk_len);
+    samp_stats<true><<<dim3(p.n_splits, p.n), kStatsThreads, 0, s>>>(logits, ctrl, part, pimg, p.vocab,
+                                                                     p.kb_per_split, p.n_kb);
   else
-    samp_stats<false><<<dim3(p.n_chunks, p.n), kStatsThreads, 0, s>>>(logits, ctrl, part, p.vocab, p.chunk_len);
+    samp_stats<false><<<dim3(p.n_splits, p.n), kStatsThreads, 0, s>>>(logits, ctrl, part, pimg, p.vocab,
+                                                                      p.kb_per_split, p.n_kb);
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   prof_begin("samp_gemm", s);
-  const int nwg = p.n_tiles * p.n_splits;
-  if (aligned)
-    samp_gemm<true><<<nwg, kGThreads, 0, s>>>(logits, emb, part, zp, p.n, p.vocab, p.d, p.n_chunks,
-                                              p.n_tiles, p.ks_per_split);
-  else
-    samp_gemm<false><<<nwg, kGThreads, 0, s>>>(logits, emb, part, zp, p.n, p.vocab, p.d, p.n_chunks,
-                                               p.n_tiles, p.ks_per_split);
+  samp_gemm<<<p.n_tiles * p.n_splits, kGThreads, 0, s>>>(pimg, static_cast<const uint8_t*>(emb_packed),
+                                                         zp, p.n, p.d, p.col_pad, p.n_tiles,
+                                                         p.kb_per_split, p.n_kb);
   prof_end(s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   prof_begin("samp_combine", s);
-  samp_combine<<<p.n, 256, 0, s>>>(logits, part, p.n_chunks, zp, p.n_splits, ctrl, ids, committed,
-                                   z, conf, p.n, p.vocab, p.d);
+  samp_combine<<<dim3((p.d + 1023) / 1024, p.n), 256, 0, s>>>(logits, part, p.n_splits, zp, ctrl, ids,
+                                                              committed, z, conf, p.n, p.vocab, p.d);
   prof_end(s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -121,9 +121,25 @@ int dg_canvas_attention(const void* q, const void* k_prefix, const void* v_prefi
 size_t dg_sampler_workspace_bytes(int n_canvas, int vocab, int d_model);
 
 /*
+ * The embedding table E in the layout the sampler streams.  The contraction
+ * z = softmax(logits)·E runs on bf16 matrix cores in split precision
+ * (E = E_hi + E_lo, both bf16, E_hi = round(E), E_lo = round(E - E_hi)), so E is
+ * converted once, when the weights are loaded, rather than on every step:
+ *   emb        [vocab, d_model] float32 (input)
+ *   packed     dg_embedding_packed_bytes(vocab, d_model) bytes (output): for
+ *              each block of 16 ids and each column (d_model rounded up to a
+ *              multiple of 256, zero padded), 16 bf16 E_hi then 16 bf16 E_lo;
+ *              ids past vocab are zero.
+ * The caller owns both buffers.  Asynchronous on `stream`.
+ */
+size_t dg_embedding_packed_bytes(int vocab, int d_model);
+int dg_embedding_pack(const float* emb, void* packed, int vocab, int d_model, hipStream_t stream);
+
+/*
  * One sampler step over the canvas (Technical Report section 6 "Sampling").
  *   logits          [n_canvas, vocab]   float32
- *   emb             [vocab, d_model]    float32, the embedding table E
+ *   emb_packed      the embedding table E [vocab, d_model] as written by
+ *                   dg_embedding_pack
  *   canvas_ids      [n_canvas]          int32, in/out
  *   committed       [n_canvas]          uint8 0/1, in/out (a committed position is
  *                                       never changed again)
@@ -139,7 +155,7 @@ size_t dg_sampler_workspace_bytes(int n_canvas, int vocab, int d_model);
  * logit, gets confidence NaN and z NaN and is never committed.
  *   n_canvas in [1, 256]; vocab >= 2 with n_canvas * vocab * 4 < 2^32; d_model >= 1.
  */
-int dg_sampler_step(const float* logits, const float* emb, int32_t* canvas_ids,
+int dg_sampler_step(const float* logits, const void* emb_packed, int32_t* canvas_ids,
                     uint8_t* committed, float* selfcond, float* confidence,
                     uint32_t* n_uncommitted, dg_ctrl* ctrl,
                     int n_canvas, int vocab, int d_model,
@@ -159,7 +175,7 @@ size_t dg_denoise_workspace_bytes(int n_canvas, int n_prefix, int hq, int hkv, i
 int dg_denoise_step(const void* q, const void* k_prefix, const void* v_prefix,
                     const void* k_canvas, const void* v_canvas, float* attn_out,
                     int n_prefix, int hq, int hkv, int head_dim, int dtype, float scale,
-                    const float* logits, const float* emb, int32_t* canvas_ids,
+                    const float* logits, const void* emb_packed, int32_t* canvas_ids,
                     uint8_t* committed, float* selfcond, float* confidence,
                     uint32_t* n_uncommitted, dg_ctrl* ctrl,
                     int n_canvas, int vocab, int d_model,
@@ -176,7 +192,7 @@ typedef struct dg_step_graph dg_step_graph;
 int dg_step_graph_create(const void* q, const void* k_prefix, const void* v_prefix,
                          const void* k_canvas, const void* v_canvas, float* attn_out,
                          int n_prefix, int hq, int hkv, int head_dim, int dtype, float scale,
-                         const float* logits, const float* emb, int32_t* canvas_ids,
+                         const float* logits, const void* emb_packed, int32_t* canvas_ids,
                          uint8_t* committed, float* selfcond, float* confidence,
                          uint32_t* n_uncommitted, dg_ctrl* ctrl,
                          int n_canvas, int vocab, int d_model,

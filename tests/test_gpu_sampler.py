@@ -15,7 +15,9 @@ pytestmark = pytest.mark.gpu
 class GpuSampler:
     def __init__(self, torch, dg, emb, ids, mask, ctrl):
         self.torch, self.dg = torch, dg
-        self.emb = to_dev(emb)
+        e32 = to_dev(emb)
+        self.emb = dg.dg_embedding_pack(e32)
+        del e32
         n = len(ids)
         self.ids = to_dev(np.asarray(ids, np.int32))
         self.mask = to_dev(np.asarray(mask, np.uint8))
@@ -224,3 +226,23 @@ def test_deterministic_and_resume():
     r1b = g.step(workloads.step_logits(2, 1))
     for x, y in zip(outs[0][1][:4], r1b[:4]):
         np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("vocab,d", [(37, 260), (4096, 512), (16, 1)])
+def test_embedding_pack_layout(vocab, d):
+    """The packed table holds bf16 E_hi, E_lo per 16-id block and column; E_hi + E_lo ~ E."""
+    torch, dg = require_gpu()
+    rng = np.random.default_rng(vocab + d)
+    emb = (rng.standard_normal((vocab, d)) * 0.02).astype(np.float32)
+    packed = dg.dg_embedding_pack(to_dev(emb)).cpu().numpy()
+    n_kb, col_pad = -(-vocab // 16), -(-d // 256) * 256
+    assert packed.size == n_kb * col_pad * 64
+    words = packed.view(np.uint16).reshape(n_kb, col_pad, 2, 16)
+    as_f32 = lambda h: (h.astype(np.uint32) << 16).view(np.float32)
+    hi, lo = as_f32(words[:, :, 0, :]), as_f32(words[:, :, 1, :])
+    full = np.zeros((n_kb * 16, col_pad), np.float64)
+    full[:vocab, :d] = emb
+    ref = full.reshape(n_kb, 16, col_pad).transpose(0, 2, 1)
+    recon = hi.astype(np.float64) + lo.astype(np.float64)
+    assert np.all(np.abs(recon - ref) <= 2.0 ** -16 * np.abs(ref) + 1e-30)
+    np.testing.assert_array_equal(hi.astype(np.float32), (workloads.round_bf16(ref.astype(np.float32))))

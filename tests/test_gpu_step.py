@@ -26,7 +26,7 @@ def inputs():
 def device_state(torch, dg, x, ctrl):
     bf = torch.bfloat16
     st = dict(q=to_dev(x["q"], bf), kp=to_dev(x["kp"], bf), vp=to_dev(x["vp"], bf),
-              kc=to_dev(x["kc"], bf), vc=to_dev(x["vc"], bf), emb=to_dev(x["emb"]),
+              kc=to_dev(x["kc"], bf), vc=to_dev(x["vc"], bf), emb=dg.dg_embedding_pack(to_dev(x["emb"])),
               logits=to_dev(x["logits"]), ids=to_dev(x["ids"].astype(np.int32)),
               mask=to_dev(x["mask"].astype(np.uint8)))
     n, hq, d = x["q"].shape
