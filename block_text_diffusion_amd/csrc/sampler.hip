@@ -45,7 +45,7 @@ constexpr int kImgRow = 64;        // bytes per row slot of a k-block image: 16 
 constexpr int kGM = 256;           // canvas row slots per image / rows per contraction tile
 constexpr int kGN = 256;           // embedding columns per contraction tile
 constexpr int kPImg = kGM * kImgRow;   // 16 KB: the p image of one k-block
-constexpr int kGThreads = 256;     // 4 waves (one per SIMD): 2 x 2, 128 x 128 each
+constexpr int kGThreads = 512;     // 8 waves (two per SIMD): 2 x 4, 128 x 64 each
 constexpr int kArr = kGM * kImgRow;    // 16 KB: one operand of one LDS stage
 constexpr int kStage = 2 * kArr;       // p tile + E tile
 constexpr int kStatsThreads = 256;
@@ -227,7 +227,10 @@ __global__ __launch_bounds__(256) void emb_pack_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// z_s = p · E over one split, bf16x3 on MFMA.
+// z_s = p · E over one split, bf16x3 on MFMA.  A four-stage LDS pipeline fed
+// by direct global-to-LDS loads: no staging registers and no LDS store
+// instructions; the fragments of the next step are read while the MFMAs of
+// the current one run.
 // ---------------------------------------------------------------------------
 
 // LDS rows are 64 bytes (four 16-byte chunks: hi k0-7, hi k8-15, lo k0-7,
@@ -243,61 +246,115 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufFlags);
 }
 
-// One k step of global data held by a thread between its load and its LDS store:
-// 4 x 16 bytes of the p image (rows 64w+16j .. of this wave) and 4 x 16 bytes of
-// the E image (columns 64w+16j ..).
-struct StepRegs {
-  u32x4 a[4];
-  u32x4 b[4];
-};
+constexpr int kStages = 4;            // LDS stages of 32 KB
+constexpr int kDist = kStages - 1;     // DMA runs this many steps ahead
+constexpr int kDmaPerStep = 4;         // LDS DMA instructions per wave per k step
 
-__device__ __forceinline__ void gemm_load(StepRegs& r, const uint8_t* __restrict__ pimg,
-                                          const uint8_t* __restrict__ eimg, int kb, int col_pad,
-                                          int col0, uint32_t lane_off, int wave) {
+// vmcnt(n) with the LDS / export counters left open (gfx9 s_waitcnt encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// vmcnt(n) and lgkmcnt(0) together.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fences of __syncthreads(): those would
+// make every wave drain all outstanding vector loads (including the LDS DMA of
+// later stages) at each barrier.  LDS DMA completion is handled by the explicit
+// vmcnt waits; the asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// DMA one k step into an LDS stage: 16-byte buffer loads that write LDS
+// directly (lane i of an instruction lands at destination + 16 i).  Wave w
+// moves rows 32w..32w+31 of the p image and columns 32w..32w+31 of the E
+// image; lane i fetches the global chunk that belongs at its swizzled slot.
+__device__ __forceinline__ void gemm_dma(uint8_t* stage, const uint8_t* __restrict__ pimg,
+                                         const uint8_t* __restrict__ eimg, int kb, int col_pad,
+                                         int col0, const uint32_t (&voff)[2], int wave) {
   const __amdgpu_buffer_rsrc_t ra = rsrc(pimg + (size_t)kb * kPImg, kPImg);
   const __amdgpu_buffer_rsrc_t rb = rsrc(eimg + ((size_t)kb * col_pad + col0) * kImgRow, kArr);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t off = (uint32_t)((64 * wave + 16 * j) * kImgRow) + lane_off;
-    r.a[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
-    r.b[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+  for (int j = 0; j < 2; ++j) {
+    uint8_t* dst = stage + (32 * wave + 16 * j) * kImgRow;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)dst, 16, voff[j], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[j], 0, 0, 0);
   }
 }
 
-// Lane i of a 16-row group holds global chunk (i & 3) of row (i >> 2); it lands
-// at that row's swizzled chunk position.
-__device__ __forceinline__ void gemm_store(const StepRegs& r, uint8_t* stage, int wave, int lane) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 64 * wave + 16 * j + (lane >> 2);
-    const int off = swz_off(row, lane & 3);
-    *reinterpret_cast<u32x4*>(stage + off) = r.a[j];
-    *reinterpret_cast<u32x4*>(stage + kArr + off) = r.b[j];
-  }
-}
+struct Frags {
+  bf16x8 ah[4], al[4], bh[2], bl[2];
+};
 
-// acc[mb][nb] += A(rows 128*wm + 32*mb ..) x B(cols 128*wn + 32*nb ..) for one 16-id k step.
-__device__ __forceinline__ void gemm_mma(const uint8_t* stage, f32x16 (&acc)[4][4], int wm, int wn,
-                                         int lane) {
+__device__ __forceinline__ void gemm_frags(Frags& f, const uint8_t* stage, int wm, int wn, int lane) {
   const int h = lane >> 5;
-  bf16x8 ah[4], al[4], bh[4], bl[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ra = 128 * wm + 32 * i + (lane & 31);
-    ah[i] = *reinterpret_cast<const bf16x8*>(stage + swz_off(ra, h));
-    al[i] = *reinterpret_cast<const bf16x8*>(stage + swz_off(ra, 2 + h));
-    const int rb = 128 * wn + 32 * i + (lane & 31);
-    bh[i] = *reinterpret_cast<const bf16x8*>(stage + kArr + swz_off(rb, h));
-    bl[i] = *reinterpret_cast<const bf16x8*>(stage + kArr + swz_off(rb, 2 + h));
+    f.ah[i] = *reinterpret_cast<const bf16x8*>(stage + swz_off(ra, h));
+    f.al[i] = *reinterpret_cast<const bf16x8*>(stage + swz_off(ra, 2 + h));
   }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rb = 64 * wn + 32 * i + (lane & 31);
+    f.bh[i] = *reinterpret_cast<const bf16x8*>(stage + kArr + swz_off(rb, h));
+    f.bl[i] = *reinterpret_cast<const bf16x8*>(stage + kArr + swz_off(rb, 2 + h));
+  }
+}
+
+// acc[mb][nb] += A(rows 128*wm + 32*mb ..) x B(cols 64*wn + 32*nb ..) for one 16-id k step.
+__device__ __forceinline__ void gemm_mma(const Frags& f, f32x16 (&acc)[4][2]) {
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bh[nb], acc[mb][nb], 0, 0, 0);
-      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bl[nb], acc[mb][nb], 0, 0, 0);
-      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], bh[nb], acc[mb][nb], 0, 0, 0);
+    for (int nb = 0; nb < 2; ++nb) {
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ah[mb], f.bh[nb], acc[mb][nb], 0, 0, 0);
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ah[mb], f.bl[nb], acc[mb][nb], 0, 0, 0);
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.al[mb], f.bh[nb], acc[mb][nb], 0, 0, 0);
     }
+}
+
+// Iteration s of the pipeline: step s+1 has landed in LDS (waited before the
+// barrier), step s+kDist is sent to the stage step s-1 used (kDma), the MFMAs
+// consume the fragments of step s (read during iteration s-1) while the
+// fragments of step s+1 are read (kFrags).  kAhead = number of DMA steps
+// issued beyond s+1 at the wait.  Every variant is straight-line code, so the
+// compiler's wait-count tracking stays exact across the unrolled iterations.
+template <int kAhead, bool kDma, bool kFrags>
+__device__ __forceinline__ void gemm_iter(int s, uint8_t* smem, Frags& cur, Frags& nxt,
+                                          f32x16 (&acc)[4][2], const uint8_t* __restrict__ pimg,
+                                          const uint8_t* __restrict__ eimg, int kb0, int col_pad,
+                                          int col0, const uint32_t (&voff)[2], int wave, int wm,
+                                          int wn, int lane) {
+  // the fragments of step s were read an iteration ago: drain them here, before
+  // this iteration's reads are queued behind them
+  wait_vmcnt_lgkm0<kDmaPerStep * kAhead>();
+  raw_barrier();
+  if (kDma)
+    gemm_dma(smem + ((s + kDist) % kStages) * kStage, pimg, eimg, kb0 + s + kDist, col_pad, col0, voff, wave);
+  if (kFrags) gemm_frags(nxt, smem + ((s + 1) % kStages) * kStage, wm, wn, lane);
+  gemm_mma(cur, acc);
+  // issue order: the next step's fragment reads first, then the MFMAs with the
+  // LDS DMA instructions spread between them, so a DMA that has to wait for
+  // queue space never holds back more than a few MFMAs
+  if (kFrags) __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    if (kDma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
 }
 
 __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restrict__ pimg,
@@ -305,7 +362,7 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
                                                           float* __restrict__ zp, int n_rows, int d,
                                                           int col_pad, int n_tiles, int kb_per_split,
                                                           int n_kb) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
 
   // Workgroups are dealt round-robin to the 8 XCDs; renumber them so the
   // d-tiles of one vocabulary split sit on the same XCD and share its L2 copy
@@ -324,53 +381,77 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  const uint32_t lane_off = (uint32_t)((lane >> 2) * kImgRow + (lane & 3) * 16);
+  const int wm = wave >> 2, wn = wave & 3;
+  uint32_t voff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 32 * wave + 16 * j + (lane >> 2);
+    const int chunk = (lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
+    voff[j] = (uint32_t)(row * kImgRow + chunk * 16);
+  }
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
 
-  // Step k is loaded into register set k&1 two iterations ahead and stored
-  // into LDS stage k&1 one iteration ahead; iteration s multiplies stage s&1.
-  StepRegs ra, rb;
-  if (nsteps > 0) {
-    gemm_load(ra, pimg, eimg, kb0, col_pad, col0, lane_off, wave);
-    if (nsteps > 1) gemm_load(rb, pimg, eimg, kb0 + 1, col_pad, col0, lane_off, wave);
-    gemm_store(ra, smem, wave, lane);
-    if (nsteps > 2) gemm_load(ra, pimg, eimg, kb0 + 2, col_pad, col0, lane_off, wave);
+  // prologue: steps 0..kDist-1 in flight, step 0 landed, its fragments read
+#pragma unroll
+  for (int k = 0; k < kDist; ++k)
+    if (k < nsteps) gemm_dma(smem + k * kStage, pimg, eimg, kb0 + k, col_pad, col0, voff, wave);
+  Frags fa, fb;
+  switch (min(nsteps, kDist)) {
+    case 3: wait_vmcnt<2 * kDmaPerStep>(); break;
+    case 2: wait_vmcnt<kDmaPerStep>(); break;
+    case 1: wait_vmcnt<0>(); break;
+    default: break;
   }
-  __syncthreads();
+  raw_barrier();
+  if (nsteps > 0) gemm_frags(fa, smem, wm, wn, lane);
+
+#define DG_ITER(K, D, F, S, C, N) \
+  gemm_iter<K, D, F>(S, smem, C, N, acc, pimg, eimg, kb0, col_pad, col0, voff, wave, wm, wn, lane)
+  // steady state: both unrolled iterations send a DMA step and read fragments
   int s = 0;
-  for (; s + 4 <= nsteps; s += 2) {
-    gemm_mma(smem, acc, wm, wn, lane);
-    gemm_store(rb, smem + kStage, wave, lane);
-    if (s + 3 < nsteps) gemm_load(rb, pimg, eimg, kb0 + s + 3, col_pad, col0, lane_off, wave);
-    __syncthreads();
-    gemm_mma(smem + kStage, acc, wm, wn, lane);
-    gemm_store(ra, smem, wave, lane);
-    if (s + 4 < nsteps) gemm_load(ra, pimg, eimg, kb0 + s + 4, col_pad, col0, lane_off, wave);
-    __syncthreads();
+  for (; s + kDist + 1 < nsteps; s += 2) {
+    DG_ITER(1, true, true, s, fa, fb);
+    DG_ITER(1, true, true, s + 1, fb, fa);
   }
-  for (; s < nsteps; ++s) {
-    const bool odd = s & 1;
-    gemm_mma(smem + (odd ? kStage : 0), acc, wm, wn, lane);
-    if (s + 1 < nsteps) gemm_store(odd ? ra : rb, smem + (odd ? 0 : kStage), wave, lane);
-    if (s + 3 < nsteps) gemm_load(odd ? ra : rb, pimg, eimg, kb0 + s + 3, col_pad, col0, lane_off, wave);
-    __syncthreads();
+  // tail: r = nsteps - s in [1, kDist + 1] steps left
+  switch (nsteps - s) {
+    case 4:
+      DG_ITER(1, true, true, s, fa, fb);
+      DG_ITER(1, false, true, s + 1, fb, fa);
+      DG_ITER(0, false, true, s + 2, fa, fb);
+      DG_ITER(0, false, false, s + 3, fb, fa);
+      break;
+    case 3:
+      DG_ITER(1, false, true, s, fa, fb);
+      DG_ITER(0, false, true, s + 1, fb, fa);
+      DG_ITER(0, false, false, s + 2, fa, fb);
+      break;
+    case 2:
+      DG_ITER(0, false, true, s, fa, fb);
+      DG_ITER(0, false, false, s + 1, fb, fa);
+      break;
+    case 1:
+      DG_ITER(0, false, false, s, fa, fb);
+      break;
+    default:
+      break;
   }
+#undef DG_ITER
 
   // epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block, column lane%32
   float* out = zp + (size_t)split * (size_t)n_rows * (size_t)d;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int col = col0 + 128 * wn + 32 * nb + (lane & 31);
+    for (int nb = 0; nb < 2; ++nb) {
+      const int col = col0 + 64 * wn + 32 * nb + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = 128 * wm + 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
