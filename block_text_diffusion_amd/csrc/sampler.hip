@@ -87,15 +87,28 @@ __device__ __forceinline__ void load16(const float* __restrict__ x, int j, int v
   }
 }
 
-// grid (n_splits, n_rows); each thread takes whole k-blocks of the split.
+constexpr int kStatsRows = 16;                 // canvas rows per workgroup (one per wave)
+constexpr int kStatsThreadsWG = 64 * kStatsRows;
+constexpr int kStatsChunk = 64;                // k-blocks staged per pass-2 round
+
+// grid (n_splits, ceil(n_rows / 16)), 16 waves.  Wave r owns canvas row
+// row0 + r; its 64 lanes take 64 consecutive k-blocks (4 KB of logits, one
+// coalesced read).  Pass 2 stages each round's bf16 hi/lo rows in LDS as
+// [k-block][row][64 B] and writes them out k-block by k-block: 16 rows x 64 B =
+// 1 KB contiguous per store instruction (the p images are [k-block][row][64 B]).
 template <bool kAligned>
-__global__ __launch_bounds__(kStatsThreads) void samp_stats(const float* __restrict__ logits,
-                                                            const dg_ctrl* __restrict__ ctrl,
-                                                            StatsPartial* __restrict__ part,
-                                                            uint8_t* __restrict__ pimg, int vocab,
-                                                            int kb_per_split, int n_kb) {
-  const int row = blockIdx.y;
+__global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __restrict__ logits,
+                                                              const dg_ctrl* __restrict__ ctrl,
+                                                              StatsPartial* __restrict__ part,
+                                                              uint8_t* __restrict__ pimg, int n_rows,
+                                                              int vocab, int kb_per_split, int n_kb) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kStatsChunk * kStatsRows * kImgRow];
   const int split = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int row0 = blockIdx.y * kStatsRows;
+  const int row = row0 + wave;
+  const bool row_ok = row < n_rows;
   const dg_ctrl cb = *ctrl;
   const float temp = temperature(cb);
   const float inv_t = 1.0f / temp;
@@ -103,102 +116,89 @@ __global__ __launch_bounds__(kStatsThreads) void samp_stats(const float* __restr
   const bool gumbel = (cb.flags & DG_GUMBEL) != 0;
   const float c_t = kLog2e * inv_t;
   const uint32_t k0 = seed_lo(cb.seed), k1 = seed_hi(cb.seed);
-  const float* x = logits + (size_t)row * (size_t)vocab;
+  const float* x = logits + (size_t)(row_ok ? row : 0) * (size_t)vocab;
   const int kb0 = split * kb_per_split;
   const int kb1 = min(n_kb, kb0 + kb_per_split);
-  const int w = threadIdx.x / kWave;
-  __shared__ StatsPartial red[kStatsThreads / kWave];
-  __shared__ float s_m;
 
-  // pass 1: max, argmax, Gumbel argmax, undefined values
+  // pass 1: max, argmax, Gumbel argmax, undefined values (one wave per row)
   float m = -INFINITY;
   uint32_t bid = 0xFFFFFFFFu;
   float gbest = -INFINITY;
   uint32_t gid = 0xFFFFFFFFu;
   uint32_t bad = 0;
-  for (int kb = kb0 + (int)threadIdx.x; kb < kb1; kb += kStatsThreads) {
-    const int j = kb * kKB;
-    float v[16];
-    load16<kAligned>(x, j, vocab, v);
+  if (row_ok) {
+    for (int kb = kb0 + lane; kb < kb1; kb += 64) {
+      const int j = kb * kKB;
+      float v[16];
+      load16<kAligned>(x, j, vocab, v);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      bad |= (v[e] != v[e]) | (v[e] == INFINITY);
-      if (v[e] > m) { m = v[e]; bid = (uint32_t)(j + e); }
-    }
-    if (gumbel) {
+      for (int e = 0; e < 16; ++e) {
+        bad |= (v[e] != v[e]) | (v[e] == INFINITY);
+        if (v[e] > m) { m = v[e]; bid = (uint32_t)(j + e); }
+      }
+      if (gumbel) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const Philox4 h = philox4x32_10((uint32_t)(j >> 2) + q, (uint32_t)row, cb.gstep, kStreamGumbel, k0, k1);
-        const uint32_t hw[4] = {h.w0, h.w1, h.w2, h.w3};
+        for (int q = 0; q < 4; ++q) {
+          const Philox4 h = philox4x32_10((uint32_t)(j >> 2) + q, (uint32_t)row, cb.gstep, kStreamGumbel, k0, k1);
+          const uint32_t hw[4] = {h.w0, h.w1, h.w2, h.w3};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float sc = v[4 * q + e] * inv_t + gumbel_from_bits(hw[e]);
-          if (sc > gbest) { gbest = sc; gid = (uint32_t)(j + 4 * q + e); }
+          for (int e = 0; e < 4; ++e) {
+            const float sc = v[4 * q + e] * inv_t + gumbel_from_bits(hw[e]);
+            if (sc > gbest) { gbest = sc; gid = (uint32_t)(j + 4 * q + e); }
+          }
         }
       }
     }
   }
+  wave_argmax(m, bid);
+  wave_argmax(gbest, gid);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float om = __shfl_xor(m, o);
-    const uint32_t obid = __shfl_xor(bid, o);
-    if (better(om, obid, m, bid)) { m = om; bid = obid; }
-    const float og = __shfl_xor(gbest, o);
-    const uint32_t ogid = __shfl_xor(gid, o);
-    if (better(og, ogid, gbest, gid)) { gbest = og; gid = ogid; }
-    bad |= __shfl_xor(bad, o);
-  }
-  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = StatsPartial{m, 0.f, 0.f, bid, gbest, gid, bad, 0};
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    StatsPartial r = red[0];
-    for (int i = 1; i < kStatsThreads / kWave; ++i) {
-      const StatsPartial& o = red[i];
-      if (better(o.m, o.best_id, r.m, r.best_id)) { r.m = o.m; r.best_id = o.best_id; }
-      if (better(o.gscore, o.gid, r.gscore, r.gid)) { r.gscore = o.gscore; r.gid = o.gid; }
-      r.bad |= o.bad;
-    }
-    red[0] = r;
-    s_m = r.m;
-  }
-  __syncthreads();
-  const float mr = s_m;
+  for (int o = 32; o > 0; o >>= 1) bad |= __shfl_xor(bad, o);
 
-  // pass 2: exp(l - m_s), its sums, and the bf16 hi/lo image rows
-  const float mc = (mr == -INFINITY) ? 0.0f : -mr * kLog2e;
+  // pass 2 (re-read from L2): exp(l - m_s), its sums, the bf16 hi/lo image rows
+  const float mc = (m == -INFINITY) ? 0.0f : -m * kLog2e;
   float s1 = 0.f, st = 0.f;
-  for (int kb = kb0 + (int)threadIdx.x; kb < kb1; kb += kStatsThreads) {
-    const int j = kb * kKB;
-    float v[16];
-    load16<kAligned>(x, j, vocab, v);
-    float p[16];
+  for (int base = kb0; base < kb1; base += kStatsChunk) {
+    const int kb = base + lane;
+    if (row_ok && kb < kb1) {
+      const int j = kb * kKB;
+      float v[16];
+      load16<kAligned>(x, j, vocab, v);
+      float pp[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[e], kLog2e, mc));
-      s1 += p[e];
-      if (tempered) st += __builtin_amdgcn_exp2f(fmaxf((v[e] - mr) * c_t, -200.f));
+      for (int e = 0; e < 16; ++e) {
+        pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[e], kLog2e, mc));
+        s1 += pp[e];
+        if (tempered) st += __builtin_amdgcn_exp2f(fmaxf((v[e] - m) * c_t, -200.f));
+      }
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split2(pp[2 * e], pp[2 * e + 1], hi[e], lo[e]);
+      uint8_t* dst = stage + (lane * kStatsRows + wave) * kImgRow;
+      *reinterpret_cast<u32x4*>(dst) = (u32x4){hi[0], hi[1], hi[2], hi[3]};
+      *reinterpret_cast<u32x4*>(dst + 16) = (u32x4){hi[4], hi[5], hi[6], hi[7]};
+      *reinterpret_cast<u32x4*>(dst + 32) = (u32x4){lo[0], lo[1], lo[2], lo[3]};
+      *reinterpret_cast<u32x4*>(dst + 48) = (u32x4){lo[4], lo[5], lo[6], lo[7]};
     }
-    uint32_t hi[8], lo[8];
+    __syncthreads();
+    // write-out: wave w stores k-blocks base + 4w .. base + 4w + 3, 1 KB each;
+    // lane i carries bytes 16i .. 16i + 15 of the 16 rows' slots
 #pragma unroll
-    for (int e = 0; e < 8; ++e) split2(p[2 * e], p[2 * e + 1], hi[e], lo[e]);
-    uint8_t* dst = pimg + (size_t)kb * kPImg + (size_t)row * kImgRow;
-    *reinterpret_cast<u32x4*>(dst) = (u32x4){hi[0], hi[1], hi[2], hi[3]};
-    *reinterpret_cast<u32x4*>(dst + 16) = (u32x4){hi[4], hi[5], hi[6], hi[7]};
-    *reinterpret_cast<u32x4*>(dst + 32) = (u32x4){lo[0], lo[1], lo[2], lo[3]};
-    *reinterpret_cast<u32x4*>(dst + 48) = (u32x4){lo[4], lo[5], lo[6], lo[7]};
+    for (int q = 0; q < 4; ++q) {
+      const int kbl = 4 * wave + q;
+      const int kbo = base + kbl;
+      const int r = lane >> 2;
+      if (kbo < kb1 && row0 + r < n_rows) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(stage + kbl * kStatsRows * kImgRow + lane * 16);
+        *reinterpret_cast<u32x4*>(pimg + (size_t)kbo * kPImg + (size_t)row0 * kImgRow + lane * 16) = w;
+      }
+    }
+    __syncthreads();
   }
   if (!tempered) st = s1;
   s1 = wave_sum(s1);
   st = wave_sum(st);
-  __syncthreads();
-  if ((threadIdx.x & (kWave - 1)) == 0) { red[w].s1 = s1; red[w].st = st; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    StatsPartial r = red[0];
-    for (int i = 1; i < kStatsThreads / kWave; ++i) { r.s1 += red[i].s1; r.st += red[i].st; }
-    r.m = mr;
-    part[(size_t)row * gridDim.x + split] = r;
-  }
+  if (lane == 0 && row_ok) part[(size_t)row * gridDim.x + split] = StatsPartial{m, s1, st, bid, gbest, gid, bad, 0};
 }
 
 // ---------------------------------------------------------------------------
@@ -282,14 +282,15 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // moves rows 32w..32w+31 of the p image and columns 32w..32w+31 of the E
 // image; lane i fetches the global chunk that belongs at its swizzled slot.
 __device__ __forceinline__ void gemm_dma(uint8_t* stage, const uint8_t* __restrict__ pimg,
-                                         const uint8_t* __restrict__ eimg, int kb, int col_pad,
-                                         int col0, const uint32_t (&voff)[2], int wave) {
+                                         const uint8_t* __restrict__ eimg, int kb, int n_kb,
+                                         int col_pad, int col0, const uint32_t (&voff)[2],
+                                         const uint32_t (&poff)[2], int wave) {
   const __amdgpu_buffer_rsrc_t ra = rsrc(pimg + (size_t)kb * kPImg, kPImg);
   const __amdgpu_buffer_rsrc_t rb = rsrc(eimg + ((size_t)kb * col_pad + col0) * kImgRow, kArr);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     uint8_t* dst = stage + (32 * wave + 16 * j) * kImgRow;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)dst, 16, voff[j], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)dst, 16, poff[j], 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[j], 0, 0, 0);
   }
 }
@@ -335,15 +336,17 @@ __device__ __forceinline__ void gemm_mma(const Frags& f, f32x16 (&acc)[4][2]) {
 template <int kAhead, bool kDma, bool kFrags>
 __device__ __forceinline__ void gemm_iter(int s, uint8_t* smem, Frags& cur, Frags& nxt,
                                           f32x16 (&acc)[4][2], const uint8_t* __restrict__ pimg,
-                                          const uint8_t* __restrict__ eimg, int kb0, int col_pad,
-                                          int col0, const uint32_t (&voff)[2], int wave, int wm,
-                                          int wn, int lane) {
+                                          const uint8_t* __restrict__ eimg, int kb0, int n_kb,
+                                          int col_pad, int col0, const uint32_t (&voff)[2],
+                                          const uint32_t (&poff)[2], int wave, int wm, int wn,
+                                          int lane) {
   // the fragments of step s were read an iteration ago: drain them here, before
   // this iteration's reads are queued behind them
   wait_vmcnt_lgkm0<kDmaPerStep * kAhead>();
   raw_barrier();
   if (kDma)
-    gemm_dma(smem + ((s + kDist) % kStages) * kStage, pimg, eimg, kb0 + s + kDist, col_pad, col0, voff, wave);
+    gemm_dma(smem + ((s + kDist) % kStages) * kStage, pimg, eimg, kb0 + s + kDist, n_kb, col_pad, col0,
+             voff, poff, wave);
   if (kFrags) gemm_frags(nxt, smem + ((s + 1) % kStages) * kStage, wm, wn, lane);
   gemm_mma(cur, acc);
   // issue order: the next step's fragment reads first, then the MFMAs with the
@@ -382,12 +385,15 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 2, wn = wave & 3;
-  uint32_t voff[2];
+  // lane offsets of the 16-byte chunk that belongs at this lane's swizzled LDS
+  // slot (p images and E tiles are both [row or column][64 B] per k-block)
+  uint32_t voff[2], poff[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int row = 32 * wave + 16 * j + (lane >> 2);
     const int chunk = (lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
     voff[j] = (uint32_t)(row * kImgRow + chunk * 16);
+    poff[j] = voff[j];
   }
 
   f32x16 acc[4][2];
@@ -401,7 +407,7 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
   // prologue: steps 0..kDist-1 in flight, step 0 landed, its fragments read
 #pragma unroll
   for (int k = 0; k < kDist; ++k)
-    if (k < nsteps) gemm_dma(smem + k * kStage, pimg, eimg, kb0 + k, col_pad, col0, voff, wave);
+    if (k < nsteps) gemm_dma(smem + k * kStage, pimg, eimg, kb0 + k, n_kb, col_pad, col0, voff, poff, wave);
   Frags fa, fb;
   switch (min(nsteps, kDist)) {
     case 3: wait_vmcnt<2 * kDmaPerStep>(); break;
@@ -413,7 +419,7 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
   if (nsteps > 0) gemm_frags(fa, smem, wm, wn, lane);
 
 #define DG_ITER(K, D, F, S, C, N) \
-  gemm_iter<K, D, F>(S, smem, C, N, acc, pimg, eimg, kb0, col_pad, col0, voff, wave, wm, wn, lane)
+  gemm_iter<K, D, F>(S, smem, C, N, acc, pimg, eimg, kb0, n_kb, col_pad, col0, voff, poff, wave, wm, wn, lane)
   // steady state: both unrolled iterations send a DMA step and read fragments
   int s = 0;
   for (; s + kDist + 1 < nsteps; s += 2) {
@@ -612,12 +618,13 @@ hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void*
   const bool aligned = (p.vocab % 4) == 0;
 
   prof_begin("samp_stats", s);
+  const dim3 sgrid(p.n_splits, (p.n + kStatsRows - 1) / kStatsRows);
   if (aligned)
-    samp_stats<true><<<dim3(p.n_splits, p.n), kStatsThreads, 0, s>>>(logits, ctrl, part, pimg, p.vocab,
-                                                                     p.kb_per_split, p.n_kb);
+    samp_stats<true><<<sgrid, kStatsThreadsWG, 0, s>>>(logits, ctrl, part, pimg, p.n, p.vocab,
+                                                       p.kb_per_split, p.n_kb);
   else
-    samp_stats<false><<<dim3(p.n_splits, p.n), kStatsThreads, 0, s>>>(logits, ctrl, part, pimg, p.vocab,
-                                                                      p.kb_per_split, p.n_kb);
+    samp_stats<false><<<sgrid, kStatsThreadsWG, 0, s>>>(logits, ctrl, part, pimg, p.n, p.vocab,
+                                                        p.kb_per_split, p.n_kb);
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
