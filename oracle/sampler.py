@@ -50,7 +50,7 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-from . import philox
+from . import native, philox
 
 GUMBEL = 1
 COMMIT_ONLY = 2
@@ -108,12 +108,18 @@ def candidates(logits, ctrl, temp, rows=None):
     cand = np.zeros(len(rows), dtype=np.int64)
     gap = np.zeros(len(rows), dtype=np.float64)
     inv_t = np.float32(np.float32(1.0) / np.float32(temp))
+    # Gumbel scores for all requested rows at once from the C helper (same draws,
+    # evaluated natively); None when no C compiler is available
+    fast = native.gumbel_scores(l32[rows], inv_t, ctrl.seed, ctrl.gstep, rows) \
+        if (ctrl.flags & GUMBEL) else None
     for out_i, i in enumerate(rows):
         row = l32[i]
         if ctrl.flags & GUMBEL:
-            g = philox.gumbel_row(ctrl.seed, ctrl.gstep, int(i), vocab)
-            score = (row * inv_t).astype(np.float32) + g
-            score = score.astype(np.float32)
+            if fast is not None:
+                score = fast[out_i]
+            else:
+                g = philox.gumbel_row(ctrl.seed, ctrl.gstep, int(i), vocab)
+                score = ((row * inv_t).astype(np.float32) + g).astype(np.float32)
             c = int(np.argmax(score))
             top2 = np.partition(score.astype(np.float64), -2)[-2:]
             gap[out_i] = top2[1] - top2[0]

@@ -23,7 +23,7 @@ stay far below the commit threshold at every temperature in [0.4, 1].
 """
 import numpy as np
 
-from . import philox
+from . import native, philox
 
 SPIKE = np.float32(30.0)
 CHOOSE_PER_STEP = 20
@@ -38,11 +38,15 @@ def synth_logits(ids, committed, gstep, seed, table, vocab, rows=None):
     table = np.asarray(table, dtype=np.float32)
     n_unc = int(n - committed.sum())
     jj = np.arange(vocab, dtype=np.uint64)
-    out = np.empty((len(rows), vocab), dtype=np.float32)
+    # the noise part from the C helper when it is available (same draws)
+    out = native.synth_noise(table, len(rows), vocab, seed, gstep, rows)
+    if out is None:
+        out = np.empty((len(rows), vocab), dtype=np.float32)
+        for r, i in enumerate(rows):
+            h = philox.word(seed, philox.STREAM_SYN_NOISE, gstep, int(i), c0=jj >> np.uint64(2),
+                            w=(jj & np.uint64(3)).astype(np.int64))
+            out[r] = table[(h >> np.uint32(16)).astype(np.int64)]
     for r, i in enumerate(rows):
-        h = philox.word(seed, philox.STREAM_SYN_NOISE, gstep, int(i), c0=jj >> np.uint64(2),
-                        w=(jj & np.uint64(3)).astype(np.int64))
-        out[r] = table[(h >> np.uint32(16)).astype(np.int64)]
         if committed[i]:
             out[r, ids[i]] = np.float32(out[r, ids[i]] + SPIKE)
         else:

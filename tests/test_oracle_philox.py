@@ -102,3 +102,56 @@ def test_gumbel_word_addressing():
     words = philox.philox4x32_10(5, 7, 2, philox.STREAM_GUMBEL, k0, k1)
     g = philox.gumbel_row(11, 2, 7, 24)
     np.testing.assert_array_equal(g[20:24], philox.gumbel_f32(np.array([int(w) for w in words], dtype=np.uint32)))
+
+
+# ---- the C helper (oracle/philox_c.c) must draw exactly what the numpy oracle draws ----
+
+def _native_or_skip():
+    from oracle import native
+    if native.lib() is None:
+        pytest.skip("no C compiler for the oracle's C helper")
+    return native
+
+
+def test_native_philox_bit_exact():
+    native = _native_or_skip()
+    rng = np.random.default_rng(11)
+    ctr = rng.integers(0, 2 ** 32, size=(4096, 4), dtype=np.uint64).astype(np.uint32)
+    ctr[:4] = [[0, 0, 0, 0], [2 ** 32 - 1] * 4, [1, 2, 3, 4], [0, 7, 0, 6]]
+    k0, k1 = 0xDEADBEEF, 0x01234567
+    got = native.philox(ctr, k0, k1)
+    ref = np.stack(philox.philox4x32_10(ctr[:, 0], ctr[:, 1], ctr[:, 2], ctr[:, 3], k0, k1), axis=1)
+    assert np.array_equal(got, ref)
+
+
+def test_native_gumbel_scores_match_numpy():
+    """Same Philox words; float32 logs may differ by an ulp between libm and numpy."""
+    native = _native_or_skip()
+    vocab = 262144
+    rng = np.random.default_rng(12)
+    logits = (rng.standard_normal((3, vocab)) * 3).astype(np.float32)
+    rows = np.array([0, 5, 255])
+    seed, gstep, inv_t = (1 << 40) + 77, 9, np.float32(1.25)
+    got = native.gumbel_scores(logits, inv_t, seed, gstep, rows)
+    for r, pos in enumerate(rows):
+        g = philox.gumbel_row(seed, gstep, int(pos), vocab)
+        ref = (logits[r] * inv_t).astype(np.float32) + g
+        # g = -log(t): an ulp of t (relative 2^-23) moves g by up to 2^-23 in
+        # absolute terms, plus an ulp of g and one from rounding the sum
+        tol = 2 * np.spacing(np.abs(g)) + 2.0 ** -22 + np.spacing(np.abs(ref))
+        assert np.all(np.abs(got[r] - ref) <= tol)
+        assert int(np.argmax(got[r])) == int(np.argmax(ref))
+
+
+def test_native_synth_noise_bit_exact():
+    native = _native_or_skip()
+    from oracle import synth
+    import workloads
+    table = workloads.synth_table()
+    vocab, rows = 5003, np.array([0, 3, 200])
+    got = native.synth_noise(table, len(rows), vocab, 5, 17, rows)
+    jj = np.arange(vocab, dtype=np.uint64)
+    for r, pos in enumerate(rows):
+        h = philox.word(5, philox.STREAM_SYN_NOISE, 17, int(pos), c0=jj >> np.uint64(2),
+                        w=(jj & np.uint64(3)).astype(np.int64))
+        assert np.array_equal(got[r], table[(h >> np.uint32(16)).astype(np.int64)])
