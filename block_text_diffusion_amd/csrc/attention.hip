@@ -2,37 +2,59 @@
 // part 4/6, section 6 "Attention" and section 9.1: every canvas position attends
 // to the committed KV-cache history and to all canvas positions, no mask).
 //
-// Layout per workgroup: one KV head, 128 packed query rows (canvas position x
-// query head of the group, so the heads sharing a KV head share each K/V tile),
-// one chunk of the key sequence [prefix ; canvas].  Four wavefronts each own 32
-// query rows.  Scores are formed transposed, S^T = K Q^T, on
-// v_mfma_f32_32x32x16_bf16, so a lane holds 16 keys of one query and the
-// row-wise softmax needs a single cross-lane exchange; the probabilities then
-// feed O^T = V^T P^T straight from the score registers.  K is staged in LDS as
-// [key][d], V transposed as [d][key]; both xor-swizzled.  Online softmax in
-// fp32 (base 2).  Key chunks are merged by a log-sum-exp combine kernel.
+// Work split.  The key sequence [prefix ; canvas] is cut into 64-key blocks
+// that never straddle the prefix/canvas boundary; a workgroup takes one KV
+// head, 128 packed query rows (canvas position x query head of the group, so
+// the heads sharing a KV head share every K/V block) and a run of consecutive
+// blocks (a chunk).  Chunks are merged by a log-sum-exp combine kernel; the
+// partial outputs travel as fp16 scaled by the row's largest magnitude.
+//
+// Inside a workgroup.  Eight wavefronts: wave w owns query rows 32(w%4)..+31
+// and keys 32(w/4)..+31 of every block, with its own running max and sum; the
+// two key halves are merged through LDS at the end.  K and V blocks go to a
+// double-buffered LDS stage through registers (the next block's loads are in
+// flight while the current one is multiplied), both kept as [key][d] rows with
+// xor-swizzled 16-byte chunks.  Scores are formed
+// transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16 (a lane holds 16 keys
+// of one query, so the row softmax needs one cross-lane exchange) and feed
+// O^T = V^T P^T straight from the score registers; the V^T operand comes from
+// ds_read_b64_tr_b16, which transposes 16-bit elements across 16 lanes, so V
+// needs no transposition pass.  Online softmax in fp32, base 2.
 #include "dg_common.hpp"
 #include "dg_internal.hpp"
 
 namespace dg {
 
-constexpr int kAThreads = 256;
+constexpr int kAWaves = 8;
+constexpr int kAThreads = 64 * kAWaves;
 constexpr int kARows = 128;   // packed query rows per workgroup
-constexpr int kAKeys = 64;    // keys per LDS block
+constexpr int kAKeys = 64;    // keys per block
 
 template <int D>
-__device__ __forceinline__ int k_swz(int key, int chunk) {
-  // rows of D*2 bytes, 16-byte chunks
-  if constexpr (D == 128) return key * (D * 2) + ((chunk ^ (key & 15)) << 4);
-  else return key * (D * 2) + ((chunk ^ ((key ^ (key >> 3)) & 7)) << 4);
+struct AGeom {
+  static constexpr int kRowBytes = D * 2;                       // one bf16 key row
+  static constexpr int kCpr = D / 8;                            // 16-byte chunks per row
+  static constexpr int kBlockBytes = kAKeys * kRowBytes;
+  static constexpr int kStageBytes = 2 * kBlockBytes;           // K then V
+  static_assert(kCpr * kAKeys % kAThreads == 0, "block does not split evenly over the threads");
+};
+
+// K rows: chunk c of key k sits at slot c ^ f(k); a wave's 16-byte reads of one
+// chunk column over 32 consecutive keys spread over all banks.
+template <int D>
+__device__ __forceinline__ int k_slot(int key, int c) {
+  if constexpr (D == 128) return c ^ (key & 15);
+  else return c ^ ((key ^ (key >> 3)) & 7);
+}
+// V rows: the transposing reads take two adjacent chunks of four consecutive
+// keys; this map sends those eight 16-byte pieces to eight different slots.
+template <int D>
+__device__ __forceinline__ int v_slot(int key, int c) {
+  if constexpr (D == 128) return c ^ (((key & 7) << 1) | ((key >> 3) & 1));
+  else return c ^ (((key & 3) << 1) | ((key >> 2) & 1));
 }
 
-// V^T rows are 64 keys = 128 bytes = sixteen 8-byte units of 4 keys.
-__device__ __forceinline__ int v_swz(int d, int unit) {
-  return d * 128 + ((unit ^ ((d ^ (d >> 4)) & 15)) << 3);
-}
-
-// Load 8 consecutive elements as 8 bf16 (packed in 4 u32).
+// Eight consecutive elements as eight bf16 (packed in 4 u32).
 __device__ __forceinline__ u32x4 load8(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x4 load8(const float* p) {
   const f32x4 a = *reinterpret_cast<const f32x4*>(p);
@@ -41,16 +63,61 @@ __device__ __forceinline__ u32x4 load8(const float* p) {
                  pack_bf16x2(b[2], b[3])};
 }
 
-template <int D, typename T>
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p));
+}
+
+// One block of K and V (one KV head, keys kb0.. of one segment) in flight in
+// registers: each thread carries kPer 16-byte chunks of K and of V.  Keys past
+// the segment end are clamped to its last key (finite data, masked later).
+template <int D>
+struct KvRegs {
+  static constexpr int kPer = AGeom<D>::kCpr * kAKeys / kAThreads;
+  u32x4 k[kPer], v[kPer];
+};
+
+template <int D>
+__device__ __forceinline__ void kv_fetch(KvRegs<D>& r, __amdgpu_buffer_rsrc_t rk,
+                                         __amdgpu_buffer_rsrc_t rv, int kb0, int seg_len,
+                                         int hkv, int kvh, int t) {
+  using G = AGeom<D>;
+#pragma unroll
+  for (int i = 0; i < KvRegs<D>::kPer; ++i) {
+    const int idx = t + kAThreads * i;
+    const int key = min(kb0 + idx / G::kCpr, seg_len - 1);
+    const uint32_t off = (uint32_t)(key * hkv + kvh) * G::kRowBytes + (uint32_t)(idx % G::kCpr) * 16u;
+    r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+    r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void kv_store(const KvRegs<D>& r, uint8_t* stage, int t) {
+  using G = AGeom<D>;
+#pragma unroll
+  for (int i = 0; i < KvRegs<D>::kPer; ++i) {
+    const int idx = t + kAThreads * i;
+    const int key = idx / G::kCpr, c = idx % G::kCpr;
+    *reinterpret_cast<u32x4*>(stage + key * G::kRowBytes + (k_slot<D>(key, c) << 4)) = r.k[i];
+    *reinterpret_cast<u32x4*>(stage + G::kBlockBytes + key * G::kRowBytes + (v_slot<D>(key, c) << 4)) = r.v[i];
+  }
+}
+
+template <int D, typename TQ>
 __global__ __launch_bounds__(kAThreads) void attn_partial(
-    const T* __restrict__ q, const T* __restrict__ kp, const T* __restrict__ vp,
-    const T* __restrict__ kc, const T* __restrict__ vc, float* __restrict__ out,
-    float* __restrict__ opart, float* __restrict__ ml, int n, int n_prefix, int hq, int hkv,
-    int chunk_len, int n_chunks, float scale_log2e) {
+    const TQ* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, float* __restrict__ out,
+    _Float16* __restrict__ opart, float* __restrict__ ml, int n, int n_prefix, int hq, int hkv,
+    int blocks_prefix, int blocks_total, int blocks_per_chunk, int n_chunks, float scale_log2e) {
+  using G = AGeom<D>;
   constexpr int KS = D / 16;   // 16-wide k steps over the head dimension
   constexpr int DB = D / 32;   // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint8_t ks_lds[kAKeys * D * 2];
-  __shared__ __attribute__((aligned(16))) uint8_t vt_lds[D * kAKeys * 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * G::kStageBytes];
+  __shared__ float lds_ml[4][64][2];
 
   const int chunk = blockIdx.x;
   const int qtile = blockIdx.y;
@@ -60,14 +127,33 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
+  const int wr = wave & 3;      // query row group
+  const int wh = wave >> 2;     // key half of every block
   const int half = lane >> 5;
 
+  const int gb0 = chunk * blocks_per_chunk;
+  const int nb = min(blocks_total, gb0 + blocks_per_chunk) - gb0;
+
+  const uint32_t pre_bytes = (uint32_t)n_prefix * hkv * G::kRowBytes;
+  const uint32_t can_bytes = (uint32_t)n * hkv * G::kRowBytes;
+  const __amdgpu_buffer_rsrc_t rkp = rsrc(kp, pre_bytes), rvp = rsrc(vp, pre_bytes);
+  const __amdgpu_buffer_rsrc_t rkc = rsrc(kc, can_bytes), rvc = rsrc(vc, can_bytes);
+
+  KvRegs<D> ra;
+  auto fetch = [&](KvRegs<D>& r, int b) {
+    const int gb = gb0 + b;
+    if (gb < blocks_prefix)
+      kv_fetch<D>(r, rkp, rvp, gb * kAKeys, n_prefix, hkv, kvh, t);
+    else
+      kv_fetch<D>(r, rkc, rvc, (gb - blocks_prefix) * kAKeys, n, hkv, kvh, t);
+  };
+  fetch(ra, 0);
+
   // this lane's query row (a column of S^T)
-  const int r = qtile * kARows + wave * 32 + (lane & 31);
+  const int r = qtile * kARows + wr * 32 + (lane & 31);
   const bool r_ok = r < rows;
   const int qn = r_ok ? r / group : 0;
   const int qh = kvh * group + (r_ok ? r % group : 0);
-
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -76,10 +162,6 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
     qf[ks] = __builtin_bit_cast(bf16x8, w);
   }
 
-  const int total = n_prefix + n;
-  const int k0 = chunk * chunk_len;
-  const int k1 = min(total, k0 + chunk_len);
-
   f32x16 acc_o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -87,171 +169,241 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
     for (int v = 0; v < 16; ++v) acc_o[db][v] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int kb0 = k0; kb0 < k1; kb0 += kAKeys) {
-    // ---- stage K [key][d] ----
-#pragma unroll
-    for (int i = 0; i < (kAKeys * D / 8) / kAThreads; ++i) {
-      const int idx = t + kAThreads * i;
-      const int key = idx / (D / 8);
-      const int ch = idx % (D / 8);
-      const int j = kb0 + key;
-      u32x4 w = (u32x4){0u, 0u, 0u, 0u};
-      if (j < k1) {
-        const T* src = (j < n_prefix) ? kp + ((size_t)j * hkv + kvh) * D
-                                      : kc + ((size_t)(j - n_prefix) * hkv + kvh) * D;
-        w = load8(src + ch * 8);
-      }
-      *reinterpret_cast<u32x4*>(ks_lds + k_swz<D>(key, ch)) = w;
-    }
-    // ---- stage V^T [d][key]: each task moves 4 keys x 8 dims ----
-    constexpr int VTASKS = (kAKeys / 4) * (D / 8);
-    if (t < VTASKS) {
-      const int kq = t / (D / 8);   // key quad
-      const int dg = t % (D / 8);   // 8-dim group
-      u32x4 rw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = kb0 + 4 * kq + i;
-        rw[i] = (u32x4){0u, 0u, 0u, 0u};
-        if (j < k1) {
-          const T* src = (j < n_prefix) ? vp + ((size_t)j * hkv + kvh) * D
-                                        : vc + ((size_t)(j - n_prefix) * hkv + kvh) * D;
-          rw[i] = load8(src + dg * 8);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        // dims 2k (low halves) and 2k+1 (high halves) of word k
-        const uint32_t e0a = (rw[0][k] & 0xFFFFu) | (rw[1][k] << 16);
-        const uint32_t e0b = (rw[2][k] & 0xFFFFu) | (rw[3][k] << 16);
-        const uint32_t e1a = (rw[0][k] >> 16) | (rw[1][k] & 0xFFFF0000u);
-        const uint32_t e1b = (rw[2][k] >> 16) | (rw[3][k] & 0xFFFF0000u);
-        const int d0 = dg * 8 + 2 * k;
-        *reinterpret_cast<u32x2*>(vt_lds + v_swz(d0, kq)) = (u32x2){e0a, e0b};
-        *reinterpret_cast<u32x2*>(vt_lds + v_swz(d0 + 1, kq)) = (u32x2){e1a, e1b};
-      }
-    }
-    __syncthreads();
+  // per-lane LDS offsets that do not change from block to block
+  const int kkey = 32 * wh + (lane & 31);             // K fragment row
+  const int g16 = lane >> 4, r16 = lane & 15;          // transposing-read group / lane in group
+  const int vkey0 = 32 * wh + 4 * (g16 >> 1) + (r16 >> 2);
+  const int vbyte = 8 * (r16 & 1);
 
-    // ---- S^T = K Q^T for two 32-key blocks ----
-    f32x16 s[2];
+  kv_store<D>(ra, lds, t);
+  __syncthreads();
+
+  // one block: scores, online softmax, O^T update (reads one LDS stage)
+  auto step = [&](int b, const uint8_t* ks_lds) {
+    const uint8_t* vs_lds = ks_lds + G::kBlockBytes;
+    const int gb = gb0 + b;
+    const int seg_left = (gb < blocks_prefix) ? n_prefix - gb * kAKeys
+                                              : n - (gb - blocks_prefix) * kAKeys;
+
+    // ---- S^T = K Q^T over this wave's 32 keys: two accumulators, even / odd k steps ----
+    f32x16 sa, sb;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int v = 0; v < 16; ++v) { sa[v] = 0.f; sb[v] = 0.f; }
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-      const int key = 32 * kb + (lane & 31);
+    for (int ks = 0; ks < KS; ks += 2) {
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(
+          ks_lds + kkey * G::kRowBytes + (k_slot<D>(kkey, 2 * ks + half) << 4));
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(
+          ks_lds + kkey * G::kRowBytes + (k_slot<D>(kkey, 2 * ks + 2 + half) << 4));
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks + 1], sb, 0, 0, 0);
+    }
+    float s[16];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks_lds + k_swz<D>(key, 2 * ks + half));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+    for (int v = 0; v < 16; ++v) s[v] = sa[v] + sb[v];
+    // lane holds keys 32wh + 8(v/4) + 4half + v%4 of query r
+    if (seg_left < kAKeys) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = 32 * wh + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (key >= seg_left) s[v] = -INFINITY;
       }
     }
-    // ---- online softmax over this block's 64 keys (base 2) ----
-    float mloc = -INFINITY;
+
+    // ---- online softmax (raw score units; exp2 folds in the scale) ----
+    float mloc = s[0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = kb0 + 32 * kb + 8 * (v >> 2) + 4 * half + (v & 3);
-        const float x = (key < k1) ? s[kb][v] * scale_log2e : -INFINITY;
-        s[kb][v] = x;
-        mloc = fmaxf(mloc, x);
-      }
+    for (int v = 1; v < 16; ++v) mloc = fmaxf(mloc, s[v]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    // The exponent reference m_run moves only when a lane's block max exceeds
+    // it by more than 8 (base 2): p then stays below 2^8, and the rescale of O
+    // and l (exact, the shift cancels in O / l) runs a few times per chunk
+    // instead of at almost every block.
+    if (__builtin_amdgcn_ballot_w64((mloc - m_run) * scale_log2e > 8.0f)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2e);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.f : -m_run * scale_log2e;
     float lsum = 0.f;
-    bf16x8 pf[4];
+    bf16x8 pf[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float p[16];
+    for (int tt = 0; tt < 2; ++tt) {
+      float p[8];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        p[v] = __builtin_amdgcn_exp2f(s[kb][v] - m_new);
+      for (int v = 0; v < 8; ++v) {
+        p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * tt + v], scale_log2e, mc));
         lsum += p[v];
       }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const u32x4 w = (u32x4){pack_bf16x2(p[8 * hh + 0], p[8 * hh + 1]),
-                                pack_bf16x2(p[8 * hh + 2], p[8 * hh + 3]),
-                                pack_bf16x2(p[8 * hh + 4], p[8 * hh + 5]),
-                                pack_bf16x2(p[8 * hh + 6], p[8 * hh + 7])};
-        pf[2 * kb + hh] = __builtin_bit_cast(bf16x8, w);
-      }
+      const u32x4 w = (u32x4){pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                              pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+      pf[tt] = __builtin_bit_cast(bf16x8, w);
     }
     lsum += __shfl_xor(lsum, 32);
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
+    l_run += lsum;
 
-    // ---- O^T += V^T P^T: 16-key steps; lane half h supplies keys 16t+4h+{0..3}, 16t+8+4h+{0..3} ----
+    // ---- O^T += V^T P^T: 16-key steps; lane half h supplies keys 16tt+4h+{0..3}, 16tt+8+4h+{0..3} ----
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int dd = 32 * db + (lane & 31);
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vt_lds + v_swz(dd, 4 * tt + half));
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vt_lds + v_swz(dd, 4 * tt + 2 + half));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[tt], acc_o[db], 0, 0, 0);
+        const int d0 = 32 * db + 16 * (g16 & 1) + 4 * (r16 & 3);
+        const int ka = vkey0 + 16 * tt, kb = ka + 8;
+        const s16x4 lo = lds_read_tr16(vs_lds + ka * G::kRowBytes + (v_slot<D>(ka, d0 >> 3) << 4) + vbyte);
+        const s16x4 hi = lds_read_tr16(vs_lds + kb * G::kRowBytes + (v_slot<D>(kb, d0 >> 3) << 4) + vbyte);
+        const u32x2 lw = __builtin_bit_cast(u32x2, lo);
+        const u32x2 hw = __builtin_bit_cast(u32x2, hi);
+        const bf16x8 vfr = __builtin_bit_cast(bf16x8, (u32x4){lw[0], lw[1], hw[0], hw[1]});
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, pf[tt], acc_o[db], 0, 0, 0);
       }
     }
+
+  };
+
+  // The next block's loads are in flight in registers while this one is
+  // multiplied; two LDS stages.
+  for (int b = 0; b < nb; ++b) {
+    if (b + 1 < nb) fetch(ra, b + 1);
+    step(b, lds + (b & 1) * G::kStageBytes);
+    if (b + 1 < nb) kv_store<D>(ra, lds + ((b + 1) & 1) * G::kStageBytes, t);
     __syncthreads();
   }
 
-  if (!r_ok) return;
-  // lane holds O^T rows d = 32*db + 8*(v/4) + 4*half + v%4 for query r
-  const size_t orow = (size_t)qn * hq + qh;
-  if (n_chunks == 1) {
-    const float inv = 1.0f / l_run;
+  // ---- merge the two key halves: waves 4-7 hand (m, l, O) to waves 0-3 ----
+  f32x4* xo = reinterpret_cast<f32x4*>(lds);   // [row group][16 DB-chunks][64 lanes]
+  if (wh == 1) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dd = 32 * db + 8 * g + 4 * half;
-        *reinterpret_cast<f32x4*>(out + orow * D + dd) =
-            (f32x4){acc_o[db][4 * g] * inv, acc_o[db][4 * g + 1] * inv, acc_o[db][4 * g + 2] * inv,
-                    acc_o[db][4 * g + 3] * inv};
-      }
-  } else {
-    float* dst = opart + ((size_t)chunk * n * hq + orow) * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dd = 32 * db + 8 * g + 4 * half;
-        *reinterpret_cast<f32x4*>(dst + dd) =
+      for (int g = 0; g < 4; ++g)
+        xo[(wr * 4 * DB + 4 * db + g) * 64 + lane] =
             (f32x4){acc_o[db][4 * g], acc_o[db][4 * g + 1], acc_o[db][4 * g + 2], acc_o[db][4 * g + 3]};
+    lds_ml[wr][lane][0] = m_run;
+    lds_ml[wr][lane][1] = l_run;
+  }
+  __syncthreads();
+  const size_t orow = (size_t)qn * hq + qh;
+  float rmax = 0.f;
+  if (wh == 0) {
+    const float m2 = lds_ml[wr][lane][0];
+    const float l2 = lds_ml[wr][lane][1];
+    const float m = fmaxf(m_run, m2);
+    const float a1 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m) * scale_log2e);
+    const float a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m2 - m) * scale_log2e);
+    l_run = l_run * a1 + l2 * a2;
+    m_run = m;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 o2 = xo[(wr * 4 * DB + 4 * db + g) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc_o[db][4 * g + e] * a1 + o2[e] * a2;
+          acc_o[db][4 * g + e] = v;
+          rmax = fmaxf(rmax, fabsf(v));
+        }
       }
-    if (half == 0) {
-      float* mp = ml + ((size_t)chunk * n * hq + orow) * 2;
-      mp[0] = m_run;
-      mp[1] = l_run;
+    if (n_chunks == 1) {
+      // one chunk: the normalized output, straight from the registers
+      if (r_ok) {
+        const float inv = 1.0f / l_run;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int dd = 32 * db + 8 * g + 4 * half;
+            *reinterpret_cast<f32x4*>(out + orow * D + dd) =
+                (f32x4){acc_o[db][4 * g] * inv, acc_o[db][4 * g + 1] * inv,
+                        acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv};
+          }
+      }
+      return;
     }
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));   // the row's other half of d
+  }
+  if (n_chunks == 1) return;
+  __syncthreads();   // every xo slot has been read
+
+  // ---- partial output: fp16 values O / s with s = max_d |O| of the row, plus
+  // (m, l, s) per row.  The tile is staged row-major in LDS and written out as
+  // contiguous rows. ----
+  constexpr int kTileRow = D * 2 + 16;   // padded fp16 row
+  uint8_t* tile = lds;
+  if (wh == 0) {
+    const float inv_s = (rmax > 0.f) ? 1.0f / rmax : 0.f;
+    const int i = wr * 32 + (lane & 31);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * db + 8 * g + 4 * half;
+        const f16x4 hv = (f16x4){(_Float16)(acc_o[db][4 * g] * inv_s), (_Float16)(acc_o[db][4 * g + 1] * inv_s),
+                                 (_Float16)(acc_o[db][4 * g + 2] * inv_s), (_Float16)(acc_o[db][4 * g + 3] * inv_s)};
+        *reinterpret_cast<f16x4*>(tile + i * kTileRow + dd * 2) = hv;
+      }
+    if (half == 0 && r_ok)
+      *reinterpret_cast<f32x4*>(ml + ((size_t)chunk * n * hq + orow) * 4) =
+          (f32x4){m_run * scale_log2e, l_run, rmax, 0.f};
+  }
+  __syncthreads();
+  constexpr int kCpr16 = D * 2 / 16;                 // 16-byte pieces per fp16 row
+  _Float16* base = reinterpret_cast<_Float16*>(opart) + (size_t)chunk * n * hq * D;
+#pragma unroll
+  for (int k = 0; k < (kARows * kCpr16 + kAThreads - 1) / kAThreads; ++k) {
+    const int idx = t + kAThreads * k;
+    const int i = idx / kCpr16, c = idx % kCpr16;
+    const int rr = qtile * kARows + i;
+    if (i >= kARows || rr >= rows) continue;
+    const size_t row_o = (size_t)(rr / group) * hq + kvh * group + rr % group;
+    *reinterpret_cast<u32x4*>(base + row_o * D + 8 * c) =
+        *reinterpret_cast<const u32x4*>(tile + i * kTileRow + 16 * c);
   }
 }
 
-// Merge key chunks: O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
+// Merge key chunks: O = sum_c 2^(m_c - M) s_c h_c / sum_c 2^(m_c - M) l_c, with
+// m in base-2 units and h_c the fp16 partial scaled by 1 / s_c.  D/4 lanes per
+// output row, four dims each; a running merge, so no separate max pass, and
+// the loads of different chunks do not depend on each other.
+constexpr int kCThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(D) void attn_combine(const float* __restrict__ opart,
-                                                  const float* __restrict__ ml,
-                                                  float* __restrict__ out, int n_rows_total,
-                                                  int n_chunks) {
-  const int row = blockIdx.x;
-  const int d = threadIdx.x;
-  float mx = -INFINITY;
-  for (int c = 0; c < n_chunks; ++c) mx = fmaxf(mx, ml[((size_t)c * n_rows_total + row) * 2]);
-  float lsum = 0.f, acc = 0.f;
+__global__ __launch_bounds__(kCThreads) void attn_combine(const _Float16* __restrict__ opart,
+                                                          const float* __restrict__ ml,
+                                                          float* __restrict__ out,
+                                                          int n_rows_total, int n_chunks) {
+  constexpr int kLanesPerRow = D / 4;
+  const int row = blockIdx.x * (kCThreads / kLanesPerRow) + threadIdx.x / kLanesPerRow;
+  const int d4 = (threadIdx.x % kLanesPerRow) * 4;
+  if (row >= n_rows_total) return;
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int c = 0; c < n_chunks; ++c) {
     const size_t idx = (size_t)c * n_rows_total + row;
-    const float w = __builtin_amdgcn_exp2f(ml[idx * 2] - mx);
-    lsum += w * ml[idx * 2 + 1];
-    acc += w * opart[idx * D + d];
+    const f32x4 rec = *reinterpret_cast<const f32x4*>(ml + idx * 4);
+    const f16x4 h = *reinterpret_cast<const f16x4*>(opart + idx * D + d4);
+    const float mn = fmaxf(m, rec[0]);
+    const float a = __builtin_amdgcn_exp2f(m - mn);
+    const float bw = __builtin_amdgcn_exp2f(rec[0] - mn);
+    const float sw = bw * rec[2];
+    acc = acc * a + (f32x4){(float)h[0] * sw, (float)h[1] * sw, (float)h[2] * sw, (float)h[3] * sw};
+    l = l * a + rec[1] * bw;
+    m = mn;
   }
-  out[(size_t)row * D + d] = acc / lsum;
+  *reinterpret_cast<f32x4*>(out + (size_t)row * D + d4) = acc * (1.0f / l);
+}
+
+// fp32 K/V are rounded to bf16 once per call (the MFMA operand type).
+__global__ __launch_bounds__(256) void attn_to_bf16(const float* __restrict__ src,
+                                                    uint16_t* __restrict__ dst, size_t n8) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n8) *reinterpret_cast<u32x4*>(dst + 8 * i) = load8(src + 8 * i);
 }
 
 AttnPlan attn_plan(int n, int n_prefix, int hq, int hkv, int d) {
@@ -260,43 +412,49 @@ AttnPlan attn_plan(int n, int n_prefix, int hq, int hkv, int d) {
   p.group = hq / hkv;
   p.rows = n * p.group;
   p.n_qtiles = (p.rows + kARows - 1) / kARows;
-  const int total = n_prefix + n;
-  const int blocks = (total + kAKeys - 1) / kAKeys;
+  p.blocks_prefix = (n_prefix + kAKeys - 1) / kAKeys;
+  p.blocks_total = p.blocks_prefix + (n + kAKeys - 1) / kAKeys;
+  // about one workgroup per CU: enough chunks to fill 256 CUs, no more (every
+  // extra chunk adds a partial output to write and merge)
   const int base = hkv * p.n_qtiles;
-  int want = (512 + base - 1) / base;
-  if (want > blocks) want = blocks;
+  int want = 256 / base;
+  if (want > p.blocks_total) want = p.blocks_total;
   if (want < 1) want = 1;
-  const int blocks_per_chunk = (blocks + want - 1) / want;
-  p.chunk_len = blocks_per_chunk * kAKeys;
-  p.n_chunks = (total + p.chunk_len - 1) / p.chunk_len;
-  p.off_opart = 0;
+  p.blocks_per_chunk = (p.blocks_total + want - 1) / want;
+  p.n_chunks = (p.blocks_total + p.blocks_per_chunk - 1) / p.blocks_per_chunk;
+  // workspace: [bf16 copies of fp32 K/V][fp16 partial O][(m, l, s, -) per row]
+  const size_t kv_elems = (size_t)(n_prefix + n) * hkv * d;
+  p.off_kv16 = 0;
+  p.kv16_bytes = align_up(2 * kv_elems * sizeof(uint16_t), 256);
+  p.off_opart = p.kv16_bytes;
   if (p.n_chunks > 1) {
-    p.off_ml = align_up((size_t)p.n_chunks * n * hq * d * sizeof(float), 256);
-    p.total = p.off_ml + align_up((size_t)p.n_chunks * n * hq * 2 * sizeof(float), 256);
+    p.off_ml = p.off_opart + align_up((size_t)p.n_chunks * n * hq * d * sizeof(uint16_t), 256);
+    p.total = p.off_ml + align_up((size_t)p.n_chunks * n * hq * 4 * sizeof(float), 256);
   } else {
-    p.off_ml = 0;
-    p.total = 0;
+    p.off_ml = p.off_opart;
+    p.total = p.off_opart;
   }
   return p;
 }
 
-template <int D, typename T>
-static hipError_t launch_attn_t(const AttnPlan& p, const void* q, const void* kp, const void* vp,
-                                const void* kc, const void* vc, float* out, float scale,
-                                void* ws, hipStream_t s) {
-  float* opart = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p.off_opart);
+template <int D, typename TQ>
+static hipError_t launch_attn_t(const AttnPlan& p, const void* q, const uint16_t* kp,
+                                const uint16_t* vp, const uint16_t* kc, const uint16_t* vc,
+                                float* out, float scale, void* ws, hipStream_t s) {
+  _Float16* opart = reinterpret_cast<_Float16*>(static_cast<uint8_t*>(ws) + p.off_opart);
   float* ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p.off_ml);
   const float sl2 = scale * kLog2e;
   prof_begin("attn_partial", s);
-  attn_partial<D, T><<<dim3(p.n_chunks, p.n_qtiles, p.hkv), kAThreads, 0, s>>>(
-      static_cast<const T*>(q), static_cast<const T*>(kp), static_cast<const T*>(vp),
-      static_cast<const T*>(kc), static_cast<const T*>(vc), out, opart, ml, p.n, p.n_prefix, p.hq,
-      p.hkv, p.chunk_len, p.n_chunks, sl2);
+  attn_partial<D, TQ><<<dim3(p.n_chunks, p.n_qtiles, p.hkv), kAThreads, 0, s>>>(
+      static_cast<const TQ*>(q), kp, vp, kc, vc, out, opart, ml, p.n, p.n_prefix, p.hq, p.hkv,
+      p.blocks_prefix, p.blocks_total, p.blocks_per_chunk, p.n_chunks, sl2);
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_chunks == 1) return e;
+  const int rows_per_wg = kCThreads / (D / 4);
   prof_begin("attn_combine", s);
-  attn_combine<D><<<p.n * p.hq, D, 0, s>>>(opart, ml, out, p.n * p.hq, p.n_chunks);
+  attn_combine<D><<<(p.n * p.hq + rows_per_wg - 1) / rows_per_wg, kCThreads, 0, s>>>(
+      opart, ml, out, p.n * p.hq, p.n_chunks);
   prof_end(s);
   return hipGetLastError();
 }
@@ -304,11 +462,34 @@ static hipError_t launch_attn_t(const AttnPlan& p, const void* q, const void* kp
 hipError_t launch_attention(const AttnPlan& p, const void* q, const void* kp, const void* vp,
                             const void* kc, const void* vc, float* out, bool bf16_in,
                             float scale, void* ws, hipStream_t s) {
+  const uint16_t *kp16, *vp16, *kc16, *vc16;
+  if (bf16_in) {
+    kp16 = static_cast<const uint16_t*>(kp); vp16 = static_cast<const uint16_t*>(vp);
+    kc16 = static_cast<const uint16_t*>(kc); vc16 = static_cast<const uint16_t*>(vc);
+  } else {
+    // fp32 K/V: round to bf16 into the workspace first
+    uint16_t* base = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + p.off_kv16);
+    const size_t pre = (size_t)p.n_prefix * p.hkv * p.d, can = (size_t)p.n * p.hkv * p.d;
+    uint16_t* kp_w = base;
+    uint16_t* vp_w = kp_w + pre;
+    uint16_t* kc_w = vp_w + pre;
+    uint16_t* vc_w = kc_w + can;
+    const struct { const void* src; uint16_t* dst; size_t n; } jobs[4] = {
+        {kp, kp_w, pre}, {vp, vp_w, pre}, {kc, kc_w, can}, {vc, vc_w, can}};
+    for (const auto& j : jobs) {
+      if (j.n == 0) continue;
+      const size_t n8 = j.n / 8;
+      attn_to_bf16<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(static_cast<const float*>(j.src), j.dst, n8);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    kp16 = kp_w; vp16 = vp_w; kc16 = kc_w; vc16 = vc_w;
+  }
   if (p.d == 128)
-    return bf16_in ? launch_attn_t<128, uint16_t>(p, q, kp, vp, kc, vc, out, scale, ws, s)
-                   : launch_attn_t<128, float>(p, q, kp, vp, kc, vc, out, scale, ws, s);
-  return bf16_in ? launch_attn_t<64, uint16_t>(p, q, kp, vp, kc, vc, out, scale, ws, s)
-                 : launch_attn_t<64, float>(p, q, kp, vp, kc, vc, out, scale, ws, s);
+    return bf16_in ? launch_attn_t<128, uint16_t>(p, q, kp16, vp16, kc16, vc16, out, scale, ws, s)
+                   : launch_attn_t<128, float>(p, q, kp16, vp16, kc16, vc16, out, scale, ws, s);
+  return bf16_in ? launch_attn_t<64, uint16_t>(p, q, kp16, vp16, kc16, vc16, out, scale, ws, s)
+                 : launch_attn_t<64, float>(p, q, kp16, vp16, kc16, vc16, out, scale, ws, s);
 }
 
 }  // namespace dg

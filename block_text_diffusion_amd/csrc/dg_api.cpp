@@ -66,7 +66,9 @@ int check_attention(const void* q, const void* kp, const void* vp, const void* k
   if (hq < 1 || hkv < 1 || hq % hkv != 0) return fail(DG_EINVAL, "attention: hq %% hkv != 0 or < 1");
   if (d != 64 && d != 128) return fail(DG_EUNSUPPORTED, "attention: head_dim must be 64 or 128");
   if (dtype != DG_F32 && dtype != DG_BF16) return fail(DG_EUNSUPPORTED, "attention: dtype");
-  if ((long long)np + n > (1ll << 30)) return fail(DG_EINVAL, "attention: sequence too long");
+  // K/V blocks are fetched with 32-bit buffer offsets
+  if ((uint64_t)np * (uint64_t)hkv * (uint64_t)d * 2ull >= (1ull << 31))
+    return fail(DG_EUNSUPPORTED, "attention: prefix K/V must be below 2 GiB per tensor");
   if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(out) ||
       (np > 0 && (!aligned16(kp) || !aligned16(vp))))
     return fail(DG_EINVAL, "attention: pointers must be 16-byte aligned");

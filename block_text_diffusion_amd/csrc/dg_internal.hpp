@@ -37,8 +37,11 @@ struct AttnPlan {
   int n, n_prefix, hq, hkv, d, group;
   int rows;          // n * group packed query rows per KV head
   int n_qtiles;      // 128-row query tiles per KV head
-  int n_chunks;      // key chunks
-  int chunk_len;     // keys per chunk (multiple of 64)
+  int blocks_prefix;     // 64-key blocks of the prefix
+  int blocks_total;      // prefix blocks then canvas blocks
+  int blocks_per_chunk;  // blocks per key chunk
+  int n_chunks;          // key chunks (partial outputs merged by the combine)
+  size_t off_kv16, kv16_bytes;  // bf16 copies of fp32 K/V
   size_t off_opart, off_ml, total;
 };
 AttnPlan attn_plan(int n, int n_prefix, int hq, int hkv, int d);

@@ -240,42 +240,11 @@ __device__ __forceinline__ int swz_off(int row, int chunk) {
   return row * 64 + ((chunk ^ (((row >> 1) ^ (row >> 2)) & 3)) << 4);
 }
 
-constexpr int kBufFlags = 0x00020000;  // raw 32-bit buffer access (gfx9 family)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufFlags);
-}
-
 constexpr int kStages = 4;            // LDS stages of 32 KB
 constexpr int kDist = kStages - 1;     // DMA runs this many steps ahead
 constexpr int kDmaPerStep = 4;         // LDS DMA instructions per wave per k step
 
-// vmcnt(n) with the LDS / export counters left open (gfx9 s_waitcnt encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
-// vmcnt(n) and lgkmcnt(0) together.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier without the memory fences of __syncthreads(): those would
-// make every wave drain all outstanding vector loads (including the LDS DMA of
-// later stages) at each barrier.  LDS DMA completion is handled by the explicit
-// vmcnt waits; the asm statements keep the compiler from moving memory
-// accesses across the barrier.
-__device__ __forceinline__ void raw_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // DMA one k step into an LDS stage: 16-byte buffer loads that write LDS
 // directly (lane i of an instruction lands at destination + 16 i).  Wave w
