@@ -25,6 +25,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# HBM bytes per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, calibrated
+# on a plain copy; valid only for the kernel sources they were taken from
+COUNTERS = os.path.join(ROOT, "profiles", "long_context_step_counters.json")
+KERNEL_SOURCES = ["block_text_diffusion_amd/csrc/sampler.hip", "block_text_diffusion_amd/csrc/dg_common.hpp",
+                  "block_text_diffusion_amd/csrc/attention.hip"]
 BF16_PEAK_TFLOPS = 2516.6
 FP32_MFMA_PEAK_TFLOPS = 157.3
 
@@ -32,9 +37,10 @@ FP32_MFMA_PEAK_TFLOPS = 157.3
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--profile-steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="eager steps timed kernel by kernel (default: as many as --steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
@@ -104,10 +110,12 @@ def main():
     ms_per_step = elapsed * 1e3 / a.steps
     steps_per_s = a.steps / elapsed
 
-    # ---- per-kernel durations (HIP events on the launch stream, eager calls) ----
+    # ---- per-kernel durations (HIP events on the launch stream, eager calls,
+    # as many steps as the timed region, right after it) ----
+    profile_steps = a.profile_steps or a.steps
     dg.dg_profile_enable(True)
     dg.dg_profile_read()
-    for _ in range(a.profile_steps):
+    for _ in range(profile_steps):
         dg.dg_denoise_step(*step_args, workspace=ws, stream=stream)
     torch.cuda.synchronize()
     prof = dg.dg_profile_read()
@@ -129,7 +137,7 @@ def main():
         "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-        "traffic": None,
+        "traffic": measured_traffic("samp_gemm"),
         "avg_us": round(gemm_us, 2),
         "hbm_gbs": round(bytes_gemm / (gemm_us * 1e-6) / 1e9, 1),
         "hbm_frac": round(bytes_gemm / (gemm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -177,6 +185,28 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary, or None if the
+    kernel sources changed since the counters were taken."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_sha256() or kernel not in rec.get("kernels", {}):
+        return None
+    return rec["kernels"][kernel]["hbm_bytes"]
 
 
 def cpu_baseline(q, kp, vp, kc, vc, emb, logits, ids, mask):

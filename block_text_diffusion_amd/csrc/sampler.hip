@@ -305,17 +305,19 @@ __device__ __forceinline__ void gemm_mma(const Frags& f, f32x16 (&acc)[4][2]) {
 template <int kAhead, bool kDma, bool kFrags>
 __device__ __forceinline__ void gemm_iter(int s, uint8_t* smem, Frags& cur, Frags& nxt,
                                           f32x16 (&acc)[4][2], const uint8_t* __restrict__ pimg,
-                                          const uint8_t* __restrict__ eimg, int kb0, int n_kb,
-                                          int col_pad, int col0, const uint32_t (&voff)[2],
-                                          const uint32_t (&poff)[2], int wave, int wm, int wn,
-                                          int lane) {
+                                          const uint8_t* __restrict__ eimg, int kb0, int kb_last,
+                                          int n_kb, int col_pad, int col0,
+                                          const uint32_t (&voff)[2], const uint32_t (&poff)[2],
+                                          int wave, int wm, int wn, int lane) {
   // the fragments of step s were read an iteration ago: drain them here, before
   // this iteration's reads are queued behind them
   wait_vmcnt_lgkm0<kDmaPerStep * kAhead>();
   raw_barrier();
+  // past the split's last k-block the DMA repeats that block into a stage that
+  // is never read again, so every iteration runs the same code
   if (kDma)
-    gemm_dma(smem + ((s + kDist) % kStages) * kStage, pimg, eimg, kb0 + s + kDist, n_kb, col_pad, col0,
-             voff, poff, wave);
+    gemm_dma(smem + ((s + kDist) % kStages) * kStage, pimg, eimg, min(kb0 + s + kDist, kb_last), n_kb,
+             col_pad, col0, voff, poff, wave);
   if (kFrags) gemm_frags(nxt, smem + ((s + 1) % kStages) * kStage, wm, wn, lane);
   gemm_mma(cur, acc);
   // issue order: the next step's fragment reads first, then the MFMAs with the
@@ -373,52 +375,30 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
 
-  // prologue: steps 0..kDist-1 in flight, step 0 landed, its fragments read
+  // prologue: steps 0..kDist-1 in flight (clamped to the last k-block), step 0
+  // landed, its fragments read
+  const int kb_last = kb0 + nsteps - 1;
 #pragma unroll
   for (int k = 0; k < kDist; ++k)
-    if (k < nsteps) gemm_dma(smem + k * kStage, pimg, eimg, kb0 + k, n_kb, col_pad, col0, voff, poff, wave);
+    gemm_dma(smem + k * kStage, pimg, eimg, min(kb0 + k, kb_last), n_kb, col_pad, col0, voff, poff, wave);
   Frags fa, fb;
-  switch (min(nsteps, kDist)) {
-    case 3: wait_vmcnt<2 * kDmaPerStep>(); break;
-    case 2: wait_vmcnt<kDmaPerStep>(); break;
-    case 1: wait_vmcnt<0>(); break;
-    default: break;
-  }
+  wait_vmcnt<(kDist - 1) * kDmaPerStep>();
   raw_barrier();
-  if (nsteps > 0) gemm_frags(fa, smem, wm, wn, lane);
+  gemm_frags(fa, smem, wm, wn, lane);
 
-#define DG_ITER(K, D, F, S, C, N) \
-  gemm_iter<K, D, F>(S, smem, C, N, acc, pimg, eimg, kb0, n_kb, col_pad, col0, voff, poff, wave, wm, wn, lane)
-  // steady state: both unrolled iterations send a DMA step and read fragments
+#define DG_ITER(S, C, N) \
+  gemm_iter<1, true, true>(S, smem, C, N, acc, pimg, eimg, kb0, kb_last, n_kb, col_pad, col0, voff, poff, \
+                           wave, wm, wn, lane)
+  // every iteration sends a DMA step and reads the next step's fragments (the
+  // last ones read data that is never used)
   int s = 0;
-  for (; s + kDist + 1 < nsteps; s += 2) {
-    DG_ITER(1, true, true, s, fa, fb);
-    DG_ITER(1, true, true, s + 1, fb, fa);
+  for (; s + 1 < nsteps; s += 2) {
+    DG_ITER(s, fa, fb);
+    DG_ITER(s + 1, fb, fa);
   }
-  // tail: r = nsteps - s in [1, kDist + 1] steps left
-  switch (nsteps - s) {
-    case 4:
-      DG_ITER(1, true, true, s, fa, fb);
-      DG_ITER(1, false, true, s + 1, fb, fa);
-      DG_ITER(0, false, true, s + 2, fa, fb);
-      DG_ITER(0, false, false, s + 3, fb, fa);
-      break;
-    case 3:
-      DG_ITER(1, false, true, s, fa, fb);
-      DG_ITER(0, false, true, s + 1, fb, fa);
-      DG_ITER(0, false, false, s + 2, fa, fb);
-      break;
-    case 2:
-      DG_ITER(0, false, true, s, fa, fb);
-      DG_ITER(0, false, false, s + 1, fb, fa);
-      break;
-    case 1:
-      DG_ITER(0, false, false, s, fa, fb);
-      break;
-    default:
-      break;
-  }
+  if (s < nsteps) DG_ITER(s, fa, fb);
 #undef DG_ITER
+  wait_vmcnt<0>();
 
   // epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block, column lane%32
   float* out = zp + (size_t)split * (size_t)n_rows * (size_t)d;
