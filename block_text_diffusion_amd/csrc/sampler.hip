@@ -9,11 +9,11 @@
 // every (row, split) pair keeps its own maximum m_s, so no pass needs the
 // global row maximum before the contraction.
 //
-//   samp_stats     per (split, row): pass 1 over the split's logits gives the
-//                  max, the greedy argmax and the Gumbel-perturbed argmax; pass 2
-//                  (re-read from L2) gives the sums of exp(l - m_s) at T = 1 and
-//                  at T and writes p = exp(l - m_s) as bf16 hi/lo "images": per
-//                  k-block of 16 ids, 256 row slots of 64 bytes (16 hi, 16 lo).
+//   samp_stats     per (split, row), from one read of the logits held in
+//                  registers: the max, the greedy argmax and the Gumbel-perturbed
+//                  argmax, then the sums of exp(l - m_s) at T = 1 and at T, and
+//                  p = exp(l - m_s) written as bf16 hi/lo "images": per k-block of
+//                  16 ids, 256 row slots of 64 bytes (16 hi, 16 lo).
 //   samp_gemm      z_s = sum_j p_j E_j over one split for a 256 x 256 tile: p
 //                  and E (packed once by dg_embedding_pack into the same image
 //                  form) stream through LDS; bf16x3 split precision on
@@ -87,27 +87,38 @@ __device__ __forceinline__ void load16(const float* __restrict__ x, int j, int v
   }
 }
 
-constexpr int kStatsRows = 16;                 // canvas rows per workgroup (one per wave)
-constexpr int kStatsThreadsWG = 64 * kStatsRows;
-constexpr int kStatsChunk = 64;                // k-blocks staged per pass-2 round
+constexpr int kStatsRows = 1;                            // canvas rows per workgroup
+constexpr int kStatsWavesPerRow = 4;
+constexpr int kStatsLanes = 64 * kStatsWavesPerRow;      // lanes sharing one row
+constexpr int kStatsIters = 4;                           // k-blocks held per lane
+constexpr int kMaxKbPerSplit = kStatsLanes * kStatsIters;
+constexpr int kStatsThreadsWG = 64 * kStatsRows * kStatsWavesPerRow;
 
-// grid (n_splits, ceil(n_rows / 16)), 16 waves.  Wave r owns canvas row
-// row0 + r; its 64 lanes take 64 consecutive k-blocks (4 KB of logits, one
-// coalesced read).  Pass 2 stages each round's bf16 hi/lo rows in LDS as
-// [k-block][row][64 B] and writes them out k-block by k-block: 16 rows x 64 B =
-// 1 KB contiguous per store instruction (the p images are [k-block][row][64 B]).
+// grid (n_splits, n_rows), 4 waves per row (four workgroups share a CU, so
+// some load while others store).
+// Lane L of a row holds k-blocks kb0 + L + 256 i (i < 4) of the split in
+// registers, so the logits are read from HBM once: the split maximum is
+// reduced first, then the same registers give exp(l - m_s), the sums and the
+// bf16 hi/lo p images.  Each round's image rows are staged in LDS as
+// [k-block][64 B] and leave as 1 KB per store instruction (16 k-blocks' slots
+// of the row; staging through LDS measured faster than storing straight
+// from the registers).
 template <bool kAligned>
 __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __restrict__ logits,
                                                               const dg_ctrl* __restrict__ ctrl,
                                                               StatsPartial* __restrict__ part,
                                                               uint8_t* __restrict__ pimg, int n_rows,
                                                               int vocab, int kb_per_split, int n_kb) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kStatsChunk * kStatsRows * kImgRow];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kStatsLanes * kStatsRows * kImgRow];
+  __shared__ StatsPartial red[kStatsRows][kStatsWavesPerRow];
   const int split = blockIdx.x;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  const int r = wave / kStatsWavesPerRow;                  // row within the workgroup
+  const int L = (wave % kStatsWavesPerRow) * 64 + lane;    // lane within the row
   const int row0 = blockIdx.y * kStatsRows;
-  const int row = row0 + wave;
+  const int row = row0 + r;
   const bool row_ok = row < n_rows;
   const dg_ctrl cb = *ctrl;
   const float temp = temperature(cb);
@@ -120,32 +131,43 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
   const int kb0 = split * kb_per_split;
   const int kb1 = min(n_kb, kb0 + kb_per_split);
 
-  // pass 1: max, argmax, Gumbel argmax, undefined values (one wave per row)
+  float v[kStatsIters][16];
+#pragma unroll
+  for (int i = 0; i < kStatsIters; ++i) {
+    const int kb = kb0 + L + kStatsLanes * i;
+    if (row_ok && kb < kb1) {
+      load16<kAligned>(x, kb * kKB, vocab, v[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[i][e] = -INFINITY;
+    }
+  }
+
+  // max, argmax, Gumbel argmax, undefined values
   float m = -INFINITY;
   uint32_t bid = 0xFFFFFFFFu;
   float gbest = -INFINITY;
   uint32_t gid = 0xFFFFFFFFu;
   uint32_t bad = 0;
-  if (row_ok) {
-    for (int kb = kb0 + lane; kb < kb1; kb += 64) {
-      const int j = kb * kKB;
-      float v[16];
-      load16<kAligned>(x, j, vocab, v);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        bad |= (v[e] != v[e]) | (v[e] == INFINITY);
-        if (v[e] > m) { m = v[e]; bid = (uint32_t)(j + e); }
-      }
-      if (gumbel) {
+  for (int i = 0; i < kStatsIters; ++i) {
+    const int kb = kb0 + L + kStatsLanes * i;
+    if (!(row_ok && kb < kb1)) continue;
+    const int j = kb * kKB;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const Philox4 h = philox4x32_10((uint32_t)(j >> 2) + q, (uint32_t)row, cb.gstep, kStreamGumbel, k0, k1);
-          const uint32_t hw[4] = {h.w0, h.w1, h.w2, h.w3};
+    for (int e = 0; e < 16; ++e) {
+      bad |= (v[i][e] != v[i][e]) | (v[i][e] == INFINITY);
+      if (v[i][e] > m) { m = v[i][e]; bid = (uint32_t)(j + e); }
+    }
+    if (gumbel) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float sc = v[4 * q + e] * inv_t + gumbel_from_bits(hw[e]);
-            if (sc > gbest) { gbest = sc; gid = (uint32_t)(j + 4 * q + e); }
-          }
+      for (int q = 0; q < 4; ++q) {
+        const Philox4 h = philox4x32_10((uint32_t)(j >> 2) + q, (uint32_t)row, cb.gstep, kStreamGumbel, k0, k1);
+        const uint32_t hw[4] = {h.w0, h.w1, h.w2, h.w3};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sc = v[i][4 * q + e] * inv_t + gumbel_from_bits(hw[e]);
+          if (sc > gbest) { gbest = sc; gid = (uint32_t)(j + 4 * q + e); }
         }
       }
     }
@@ -154,43 +176,58 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
   wave_argmax(gbest, gid);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) bad |= __shfl_xor(bad, o);
+  const int qw = wave % kStatsWavesPerRow;
+  if (lane == 0) red[r][qw] = StatsPartial{m, 0.f, 0.f, bid, gbest, gid, bad, 0};
+  __syncthreads();
+  {
+    StatsPartial acc = red[r][0];
+#pragma unroll
+    for (int w = 1; w < kStatsWavesPerRow; ++w) {
+      const StatsPartial o = red[r][w];
+      if (better(o.m, o.best_id, acc.m, acc.best_id)) { acc.m = o.m; acc.best_id = o.best_id; }
+      if (better(o.gscore, o.gid, acc.gscore, acc.gid)) { acc.gscore = o.gscore; acc.gid = o.gid; }
+      acc.bad |= o.bad;
+    }
+    m = acc.m; bid = acc.best_id; gbest = acc.gscore; gid = acc.gid; bad = acc.bad;
+  }
 
-  // pass 2 (re-read from L2): exp(l - m_s), its sums, the bf16 hi/lo image rows
+  // exp(l - m_s), its sums, the bf16 hi/lo image rows, round by round
   const float mc = (m == -INFINITY) ? 0.0f : -m * kLog2e;
   float s1 = 0.f, st = 0.f;
-  for (int base = kb0; base < kb1; base += kStatsChunk) {
-    const int kb = base + lane;
-    if (row_ok && kb < kb1) {
-      const int j = kb * kKB;
-      float v[16];
-      load16<kAligned>(x, j, vocab, v);
+#pragma unroll
+  for (int i = 0; i < kStatsIters; ++i) {
+    const int base = kb0 + kStatsLanes * i;
+    if (base >= kb1) break;   // uniform over the workgroup
+    {
       float pp[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[e], kLog2e, mc));
+        pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i][e], kLog2e, mc));
         s1 += pp[e];
-        if (tempered) st += __builtin_amdgcn_exp2f(fmaxf((v[e] - m) * c_t, -200.f));
+        if (tempered) st += __builtin_amdgcn_exp2f(fmaxf((v[i][e] - m) * c_t, -200.f));
       }
       uint32_t hi[8], lo[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) split2(pp[2 * e], pp[2 * e + 1], hi[e], lo[e]);
-      uint8_t* dst = stage + (lane * kStatsRows + wave) * kImgRow;
+      uint8_t* dst = stage + (L * kStatsRows + r) * kImgRow;
       *reinterpret_cast<u32x4*>(dst) = (u32x4){hi[0], hi[1], hi[2], hi[3]};
       *reinterpret_cast<u32x4*>(dst + 16) = (u32x4){hi[4], hi[5], hi[6], hi[7]};
       *reinterpret_cast<u32x4*>(dst + 32) = (u32x4){lo[0], lo[1], lo[2], lo[3]};
       *reinterpret_cast<u32x4*>(dst + 48) = (u32x4){lo[4], lo[5], lo[6], lo[7]};
     }
     __syncthreads();
-    // write-out: wave w stores k-blocks base + 4w .. base + 4w + 3, 1 KB each;
-    // lane i carries bytes 16i .. 16i + 15 of the 16 rows' slots
+    // write-out: the row slots of k-block kbl are contiguous; thread T moves
+    // 16-byte pieces T, T + kStatsThreadsWG, ... of the round's staging
+    constexpr int kPieces = kStatsLanes * kStatsRows * kImgRow / 16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int kbl = 4 * wave + q;
-      const int kbo = base + kbl;
-      const int r = lane >> 2;
-      if (kbo < kb1 && row0 + r < n_rows) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(stage + kbl * kStatsRows * kImgRow + lane * 16);
-        *reinterpret_cast<u32x4*>(pimg + (size_t)kbo * kPImg + (size_t)row0 * kImgRow + lane * 16) = w;
+    for (int k = 0; k < kPieces / kStatsThreadsWG; ++k) {
+      const int c = t + kStatsThreadsWG * k;
+      const int kbl = c / (kStatsRows * kImgRow / 16);
+      const int off = c % (kStatsRows * kImgRow / 16);          // 16-byte piece of the k-block's slots
+      const int kb = base + kbl;
+      if (kb < kb1 && row0 + off / (kImgRow / 16) < n_rows) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(stage + c * 16);
+        *reinterpret_cast<u32x4*>(pimg + (size_t)kb * kPImg + (size_t)row0 * kImgRow + off * 16) = w;
       }
     }
     __syncthreads();
@@ -198,7 +235,14 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
   if (!tempered) st = s1;
   s1 = wave_sum(s1);
   st = wave_sum(st);
-  if (lane == 0 && row_ok) part[(size_t)row * gridDim.x + split] = StatsPartial{m, s1, st, bid, gbest, gid, bad, 0};
+  if (lane == 0) { red[r][qw].s1 = s1; red[r][qw].st = st; }
+  __syncthreads();
+  if (qw == 0 && lane == 0 && row_ok) {
+    float a1 = 0.f, at = 0.f;
+#pragma unroll
+    for (int w = 0; w < kStatsWavesPerRow; ++w) { a1 += red[r][w].s1; at += red[r][w].st; }
+    part[(size_t)row * gridDim.x + split] = StatsPartial{m, a1, at, bid, gbest, gid, bad, 0};
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -547,6 +591,9 @@ SamplerPlan sampler_plan(int n, int vocab, int d) {
   if (splits < 1) splits = 1;
   const int by_len = (p.n_kb + 15) / 16;     // at least 16 k-blocks per split
   if (splits > by_len) splits = by_len;
+  // the statistics pass holds a split's logits of one row in 256 lanes x 4 k-blocks
+  const int by_regs = (p.n_kb + kMaxKbPerSplit - 1) / kMaxKbPerSplit;
+  if (splits < by_regs) splits = by_regs;
   if (splits < 1) splits = 1;
   p.kb_per_split = (p.n_kb + splits - 1) / splits;
   p.n_splits = (p.n_kb + p.kb_per_split - 1) / p.kb_per_split;
