@@ -148,6 +148,10 @@ def main():
     attn = {"us": round(attn_us, 2), "tflops": round(attn_flops / (attn_us * 1e-6) / 1e12, 1),
             "frac_bf16_peak": round(attn_flops / (attn_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
+    # ---- the entropy-bounded sampler (the pages' default) on the same inputs ----
+    eb = eb_sampler_timing(torch, dg, T, n, vocab, dm, a.steps)
+    log(f"entropy-bounded sampler: {eb['ms_per_step']:.3f} ms per step")
+
     if a.copy_probe_mib:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters calibrate
         # the HBM byte counts read for the kernels above
@@ -180,11 +184,46 @@ def main():
                    "canvas_tokens_per_s": round(256 * steps_per_s, 1),
                    "per_kernel_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
                    "embedding_pack_ms_once": round(pack_ms, 2),
-                   "attention": attn},
+                   "attention": attn,
+                   "eb_sampler": eb},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def eb_sampler_timing(torch, dg, T, n, vocab, dm, steps):
+    """Time the entropy-bounded sampler step (sampler only, no attention) on the
+    step's logits: eager steps between two events, then per-kernel averages."""
+    acc = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    ent = torch.empty(n, dtype=torch.float32, device="cuda")
+    amax = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    status = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    ids = T["ids"].clone()
+    ctrl = dg.make_ctrl(seed=4, s_max=1 << 30, flags=dg.DG_AUTO_ADVANCE | dg.DG_GUMBEL | dg.DG_T_SCHEDULE,
+                        t_start=0.8, t_end=0.4)
+    ws = torch.empty(dg.dg_sampler_workspace_bytes(n, vocab, dm), dtype=torch.uint8, device="cuda")
+    run = lambda: dg.dg_sampler_step_eb(T["logits"], T["emb"], ids, acc, T["z"], ent, amax, status, ctrl,
+                                        workspace=ws)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    dg.dg_profile_enable(True)
+    dg.dg_profile_read()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    prof = dg.dg_profile_read()
+    dg.dg_profile_enable(False)
+    return {"ms_per_step": round(ms, 4), "flags": "gumbel, T 0.8->0.4, budget 0.1",
+            "per_kernel_us": {k: round(1e3 * t / c, 2) for k, (t, c) in prof.items()}}
 
 
 def sources_sha256():

@@ -156,6 +156,37 @@ def dg_sampler_step(logits, emb_packed, canvas_ids, committed, selfcond, confide
                                  n, vocab, d, _ptr(ws), ws.numel(), _stream(stream)))
 
 
+def dg_sampler_step_eb(logits, emb_packed, canvas_ids, accepted, selfcond, entropy, argmax, status,
+                       ctrl, budget=0.1, stop_entropy=0.005, workspace=None, stream=None):
+    """Entropy-bounded sampler step.  status is a 16-byte uint8 device tensor
+    (read it with read_eb_status); argmax is in/out (previous step's greedy ids)."""
+    torch = _torch()
+    _need(logits, "logits", (torch.float32,)); _need(emb_packed, "emb_packed", (torch.uint8,))
+    _need(canvas_ids, "canvas_ids", (torch.int32,)); _need(accepted, "accepted", (torch.uint8,))
+    _need(selfcond, "selfcond", (torch.float32,)); _need(argmax, "argmax", (torch.int32,))
+    _need(status, "status", (torch.uint8,)); _need(ctrl, "ctrl", (torch.uint8,))
+    if entropy is not None:
+        _need(entropy, "entropy", (torch.float32,))
+    if status.numel() < 16:
+        raise ValueError("status needs 16 bytes")
+    n, vocab = logits.shape
+    d = selfcond.shape[1]
+    if emb_packed.numel() < dg_embedding_packed_bytes(vocab, d):
+        raise ValueError("emb_packed is smaller than dg_embedding_packed_bytes(vocab, d_model)")
+    ws = _workspace(dg_sampler_workspace_bytes(n, vocab, d), logits.device, workspace)
+    check(load().dg_sampler_step_eb(_ptr(logits), _ptr(emb_packed), _ptr(canvas_ids), _ptr(accepted),
+                                    _ptr(selfcond), _ptr(entropy), _ptr(argmax), _ptr(status), _ptr(ctrl),
+                                    float(budget), float(stop_entropy), n, vocab, d, _ptr(ws), ws.numel(),
+                                    _stream(stream)))
+
+
+def read_eb_status(status_t):
+    from ._lib import DgEbStatus
+    raw = bytes(status_t.cpu().numpy().tobytes()[:16])
+    st = DgEbStatus.from_buffer_copy(raw)
+    return {f: getattr(st, f) for f, _ in DgEbStatus._fields_}
+
+
 def _denoise_args(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, scale, logits, emb,
                   canvas_ids, committed, selfcond, confidence, n_uncommitted, ctrl, ws):
     n, hq, d = q.shape

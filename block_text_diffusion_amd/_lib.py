@@ -40,6 +40,19 @@ class DgCtrl(ctypes.Structure):
 
 assert ctypes.sizeof(DgCtrl) == 40
 
+
+class DgEbStatus(ctypes.Structure):
+    """Mirror of dg_eb_status (16 bytes)."""
+    _fields_ = [
+        ("n_accepted", ctypes.c_uint32),
+        ("stop", ctypes.c_uint32),
+        ("mean_entropy", ctypes.c_float),
+        ("n_defined", ctypes.c_uint32),
+    ]
+
+
+assert ctypes.sizeof(DgEbStatus) == 16
+
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _sz = ctypes.c_size_t
@@ -53,6 +66,8 @@ SIGNATURES = {
     "dg_embedding_packed_bytes": (_sz, [_i, _i]),
     "dg_embedding_pack": (_i, [_vp, _vp, _i, _i, _vp]),
     "dg_sampler_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]),
+    "dg_sampler_step_eb": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _i, _i, _i,
+                                _vp, _sz, _vp]),
     "dg_denoise_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "dg_denoise_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]),

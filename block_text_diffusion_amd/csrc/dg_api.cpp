@@ -180,6 +180,28 @@ int dg_sampler_step(const float* logits, const void* emb, int32_t* ids, uint8_t*
   return DG_OK;
 }
 
+int dg_sampler_step_eb(const float* logits, const void* emb, int32_t* ids, uint8_t* accepted,
+                       float* z, float* entropy, int32_t* argmax, dg_eb_status* status,
+                       dg_ctrl* ctrl, float budget, float stop_entropy, int n, int vocab, int d,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  // n_uncommitted is not used in this mode; pass a non-null stand-in to the shared check
+  int st = check_sampler(logits, emb, ids, accepted, z, reinterpret_cast<const uint32_t*>(status),
+                         ctrl, n, vocab, d);
+  if (st != DG_OK) return st;
+  if (!argmax || !status) return fail(DG_EINVAL, "sampler_eb: null argmax or status");
+  if (!(budget >= 0.f) || !std::isfinite(budget)) return fail(DG_EINVAL, "sampler_eb: budget must be finite and >= 0");
+  if (!(stop_entropy >= 0.f) || !std::isfinite(stop_entropy))
+    return fail(DG_EINVAL, "sampler_eb: stop_entropy must be finite and >= 0");
+  const dg::SamplerPlan p = dg::sampler_plan(n, vocab, d);
+  if (!ws || ws_bytes < p.total)
+    return fail(DG_EWORKSPACE, "sampler_eb: workspace %zu < %zu bytes", ws_bytes, p.total);
+  if (!aligned16(ws)) return fail(DG_EINVAL, "sampler_eb: workspace misaligned");
+  const dg::EbCall eb{true, budget, stop_entropy, entropy, argmax, status};
+  hipError_t e = dg::launch_sampler(p, logits, emb, ids, accepted, z, nullptr, nullptr, ctrl, ws, stream, eb);
+  if (e != hipSuccess) return hip_fail(e, "sampler_eb launch");
+  return DG_OK;
+}
+
 int dg_denoise_step(const void* q, const void* kp, const void* vp, const void* kc, const void* vc,
                     float* attn_out, int np, int hq, int hkv, int d, int dtype, float scale,
                     const float* logits, const void* emb, int32_t* ids, uint8_t* committed,

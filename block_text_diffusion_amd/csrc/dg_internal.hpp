@@ -23,14 +23,23 @@ struct SamplerPlan {
   int col_pad;       // d rounded up to whole tiles
   int kb_per_split;  // k-blocks per vocabulary split
   int n_splits;      // vocabulary splits (own maxima, own partial z)
-  size_t off_stats, off_pimg, off_zp, total;
+  size_t off_stats, off_pimg, off_zp, off_eb, total;
+};
+// Extra arguments of the entropy-bounded mode (on == false: threshold sampler).
+struct EbCall {
+  bool on;
+  float budget, stop_entropy;
+  float* entropy_out;       // [n] or null
+  int32_t* argmax;          // [n] in/out
+  dg_eb_status* status;
 };
 SamplerPlan sampler_plan(int n, int vocab, int d);
 size_t embedding_packed_bytes(int vocab, int d);
 hipError_t launch_embedding_pack(const float* emb, void* packed, int vocab, int d, hipStream_t s);
 hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void* emb_packed,
                           int32_t* ids, uint8_t* committed, float* z, float* conf,
-                          uint32_t* n_unc, dg_ctrl* ctrl, void* ws, hipStream_t s);
+                          uint32_t* n_unc, dg_ctrl* ctrl, void* ws, hipStream_t s,
+                          const EbCall& eb = EbCall{false, 0.f, 0.f, nullptr, nullptr, nullptr});
 
 // ---- attention ----
 struct AttnPlan {

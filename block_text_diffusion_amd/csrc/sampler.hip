@@ -37,7 +37,17 @@ struct StatsPartial {
   float gscore;      // best Gumbel-perturbed score
   uint32_t gid;      // its id
   uint32_t bad;      // NaN or +inf seen
-  uint32_t pad;
+  float sy;          // sum 2^y * y with y = (l - m) log2(e) / T (entropy of p_T)
+};
+
+// Per-row results the entropy-bounded mode hands from the combine to the
+// selection kernel (workspace arrays), plus the caller's entropy output.
+struct EbRows {
+  bool on;
+  float* ent;        // [n] entropy of p_T (nats), NaN for undefined rows
+  int32_t* cand;     // [n] candidate id
+  int32_t* argmax;   // [n] greedy argmax id
+  float* ent_out;    // caller's [n] entropy output or null
 };
 
 constexpr int kKB = 16;            // vocabulary ids per k-block
@@ -64,8 +74,16 @@ __device__ __forceinline__ void merge_sums(float& m, float& s1, float& st, float
   m = mn;
 }
 
+// sy moves with the reference: y' = y + (m_a - m) c_t, so sy' = f (sy + st (m_a - m) c_t).
+__device__ __forceinline__ float shift_sy(float sy, float st, float m_a, float m, float c_t) {
+  if (m_a == -INFINITY) return 0.0f;
+  return rescale_factor(m_a, m, c_t) * (sy + st * ((m_a - m) * c_t));
+}
+
 __device__ __forceinline__ void merge_partial(StatsPartial& r, const StatsPartial& o, float c_t) {
   const float mm = r.m;
+  const float mn = fmaxf(r.m, o.m);
+  if (mn != -INFINITY) r.sy = shift_sy(r.sy, r.st, r.m, mn, c_t) + shift_sy(o.sy, o.st, o.m, mn, c_t);
   merge_sums(r.m, r.s1, r.st, o.m, o.s1, o.st, c_t);
   if (better(o.m, o.best_id, mm, r.best_id)) r.best_id = o.best_id;
   if (better(o.gscore, o.gid, r.gscore, r.gid)) { r.gscore = o.gscore; r.gid = o.gid; }
@@ -108,7 +126,8 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
                                                               const dg_ctrl* __restrict__ ctrl,
                                                               StatsPartial* __restrict__ part,
                                                               uint8_t* __restrict__ pimg, int n_rows,
-                                                              int vocab, int kb_per_split, int n_kb) {
+                                                              int vocab, int kb_per_split, int n_kb,
+                                                              bool want_h) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[kStatsLanes * kStatsRows * kImgRow];
   __shared__ StatsPartial red[kStatsRows][kStatsWavesPerRow];
   const int split = blockIdx.x;
@@ -177,7 +196,7 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) bad |= __shfl_xor(bad, o);
   const int qw = wave % kStatsWavesPerRow;
-  if (lane == 0) red[r][qw] = StatsPartial{m, 0.f, 0.f, bid, gbest, gid, bad, 0};
+  if (lane == 0) red[r][qw] = StatsPartial{m, 0.f, 0.f, bid, gbest, gid, bad, 0.f};
   __syncthreads();
   {
     StatsPartial acc = red[r][0];
@@ -193,7 +212,7 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
 
   // exp(l - m_s), its sums, the bf16 hi/lo image rows, round by round
   const float mc = (m == -INFINITY) ? 0.0f : -m * kLog2e;
-  float s1 = 0.f, st = 0.f;
+  float s1 = 0.f, st = 0.f, sy = 0.f;
 #pragma unroll
   for (int i = 0; i < kStatsIters; ++i) {
     const int base = kb0 + kStatsLanes * i;
@@ -204,7 +223,12 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
       for (int e = 0; e < 16; ++e) {
         pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i][e], kLog2e, mc));
         s1 += pp[e];
-        if (tempered) st += __builtin_amdgcn_exp2f(fmaxf((v[i][e] - m) * c_t, -200.f));
+        if (tempered || want_h) {
+          const float y = fmaxf((v[i][e] - m) * c_t, -200.f);   // log2 of the tempered weight
+          const float et = tempered ? __builtin_amdgcn_exp2f(y) : pp[e];
+          st += et;
+          if (want_h) sy += et * y;
+        }
       }
       uint32_t hi[8], lo[8];
 #pragma unroll
@@ -232,16 +256,17 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
     }
     __syncthreads();
   }
-  if (!tempered) st = s1;
+  if (!tempered && !want_h) st = s1;
   s1 = wave_sum(s1);
   st = wave_sum(st);
-  if (lane == 0) { red[r][qw].s1 = s1; red[r][qw].st = st; }
+  sy = wave_sum(sy);
+  if (lane == 0) { red[r][qw].s1 = s1; red[r][qw].st = st; red[r][qw].sy = sy; }
   __syncthreads();
   if (qw == 0 && lane == 0 && row_ok) {
-    float a1 = 0.f, at = 0.f;
+    float a1 = 0.f, at = 0.f, ay = 0.f;
 #pragma unroll
-    for (int w = 0; w < kStatsWavesPerRow; ++w) { a1 += red[r][w].s1; at += red[r][w].st; }
-    part[(size_t)row * gridDim.x + split] = StatsPartial{m, a1, at, bid, gbest, gid, bad, 0};
+    for (int w = 0; w < kStatsWavesPerRow; ++w) { a1 += red[r][w].s1; at += red[r][w].st; ay += red[r][w].sy; }
+    part[(size_t)row * gridDim.x + split] = StatsPartial{m, a1, at, bid, gbest, gid, bad, ay};
   }
 }
 
@@ -471,7 +496,7 @@ __global__ __launch_bounds__(256) void samp_combine(const float* __restrict__ lo
                                                     int32_t* __restrict__ ids,
                                                     uint8_t* __restrict__ committed,
                                                     float* __restrict__ z, float* __restrict__ conf,
-                                                    int n_rows, int vocab, int d) {
+                                                    int n_rows, int vocab, int d, EbRows eb) {
   const int row = blockIdx.y;
   __shared__ float s_w[256];
   __shared__ uint32_t s_bad;
@@ -482,14 +507,14 @@ __global__ __launch_bounds__(256) void samp_combine(const float* __restrict__ lo
   const StatsPartial* pr = part + (size_t)row * n_splits;
   if (threadIdx.x < kWave) {
     // wave 0 merges the split statistics; lane s takes splits s, s+64, ...
-    StatsPartial r{-INFINITY, 0.f, 0.f, 0xFFFFFFFFu, -INFINITY, 0xFFFFFFFFu, 0u, 0u};
+    StatsPartial r{-INFINITY, 0.f, 0.f, 0xFFFFFFFFu, -INFINITY, 0xFFFFFFFFu, 0u, 0.f};
     for (int sp = threadIdx.x; sp < n_splits; sp += kWave) merge_partial(r, pr[sp], c_t);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       StatsPartial q;
       q.m = __shfl_xor(r.m, o); q.s1 = __shfl_xor(r.s1, o); q.st = __shfl_xor(r.st, o);
       q.best_id = __shfl_xor(r.best_id, o); q.gscore = __shfl_xor(r.gscore, o);
-      q.gid = __shfl_xor(r.gid, o); q.bad = __shfl_xor(r.bad, o);
+      q.gid = __shfl_xor(r.gid, o); q.bad = __shfl_xor(r.bad, o); q.sy = __shfl_xor(r.sy, o);
       merge_partial(r, q, c_t);
     }
     const bool bad = r.bad || !(r.m > -INFINITY);
@@ -510,7 +535,14 @@ __global__ __launch_bounds__(256) void samp_combine(const float* __restrict__ lo
           kappa = exp2f((lc - r.m) * c_t) / r.st;
         }
         if (conf) conf[row] = kappa;
-        if (!committed[row]) {
+        if (eb.on) {
+          // entropy of p_T in nats: ln S_T - (sum e^x x) / S_T, x = (l - m) / T
+          const float h = bad ? __builtin_nanf("") : logf(r.st) - r.sy * kLn2 / r.st;
+          eb.ent[row] = h;
+          if (eb.ent_out) eb.ent_out[row] = h;
+          eb.cand[row] = (int32_t)cand;
+          eb.argmax[row] = (bad || r.best_id >= (uint32_t)vocab) ? 0 : (int32_t)r.best_id;
+        } else if (!committed[row]) {
           const bool last = cb.s_in_block + 1u >= cb.s_max;
           if (!bad && (kappa >= cb.tau || last)) {
             ids[row] = (int32_t)cand;
@@ -565,6 +597,96 @@ __global__ __launch_bounds__(256) void samp_finalize(const uint8_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Entropy-bounded acceptance over the canvas (explainer "DiffusionGemma:
+// Google's open diffusion LLM", section "A diffusion language model refines
+// 256 tokens in 12 steps"; Table 2): sort the rows by (entropy, position),
+// accept while the running sum of entropies stays within the budget (the
+// first always), re-noise every other position, and test adaptive stopping
+// (mean entropy below the threshold and the greedy ids unchanged since the
+// previous step).  One workgroup of 256 threads, bitonic sort in LDS, fp64
+// prefix sums.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void samp_eb_select(EbRows eb, int32_t* __restrict__ ids,
+                                                      uint8_t* __restrict__ accepted,
+                                                      int32_t* __restrict__ prev_argmax,
+                                                      dg_eb_status* __restrict__ status,
+                                                      dg_ctrl* __restrict__ ctrl, float budget,
+                                                      float stop_entropy, int n_rows, int vocab) {
+  __shared__ float key[256];
+  __shared__ int idx[256];
+  __shared__ double csum[256];
+  __shared__ uint8_t acc[256];
+  const int t = threadIdx.x;
+  const dg_ctrl cb = *ctrl;
+  const float h = (t < n_rows) ? eb.ent[t] : __builtin_nanf("");
+  const bool defined = t < n_rows && !(h != h);
+  key[t] = defined ? h : INFINITY;
+  idx[t] = t;
+  acc[t] = 0;
+  __syncthreads();
+  // bitonic sort of (key, idx) ascending; undefined rows (+inf) sort last, by index
+  for (int k = 2; k <= 256; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int p = t ^ j;
+      if (p > t) {
+        const float ka = key[t], kb = key[p];
+        const int ia = idx[t], ib = idx[p];
+        const bool a_after_b = (ka > kb) || (ka == kb && ia > ib);
+        const bool up = (t & k) == 0;
+        if (a_after_b == up) { key[t] = kb; key[p] = ka; idx[t] = ib; idx[p] = ia; }
+      }
+      __syncthreads();
+    }
+  }
+  // inclusive prefix sums of the sorted entropies (fp64, Hillis-Steele)
+  const int n_def = __syncthreads_count(defined);
+  double c = (t < n_def) ? (double)key[t] : 0.0;
+  csum[t] = c;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const double add = (t >= o) ? csum[t - o] : 0.0;
+    __syncthreads();
+    c += add;
+    csum[t] = c;
+    __syncthreads();
+  }
+  const bool last = cb.s_in_block + 1u >= cb.s_max;
+  if (t < n_def && (t == 0 || last || c <= (double)budget)) acc[idx[t]] = 1;
+  // mean entropy over the defined rows (fixed-order reduction: the last prefix sum)
+  const double total = csum[255];
+  __syncthreads();
+  const bool stable = __syncthreads_and(t >= n_rows || eb.argmax[t] == prev_argmax[t]) != 0;
+  const float mean_h = (n_def > 0) ? (float)(total / (double)n_def) : __builtin_nanf("");
+  const bool stop = n_def > 0 && mean_h < stop_entropy && stable;
+  const int n_acc = __syncthreads_count(t < n_rows && acc[t]);
+  if (t < n_rows) {
+    int32_t id;
+    if (stop) {
+      id = eb.argmax[t];
+    } else if (acc[t]) {
+      id = eb.cand[t];
+    } else {
+      const Philox4 hh = philox4x32_10(0u, (uint32_t)t, cb.gstep, kStreamRenoise, seed_lo(cb.seed),
+                                       seed_hi(cb.seed));
+      id = (int32_t)range_draw(hh.w0, (uint32_t)vocab);
+    }
+    ids[t] = id;
+    accepted[t] = acc[t];
+    prev_argmax[t] = eb.argmax[t];
+  }
+  if (t == 0) {
+    status->n_accepted = (uint32_t)n_acc;
+    status->stop = stop ? 1u : 0u;
+    status->mean_entropy = mean_h;
+    status->n_defined = (uint32_t)n_def;
+    if (cb.flags & DG_AUTO_ADVANCE) {
+      ctrl->gstep += 1u;
+      ctrl->s_in_block += 1u;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 size_t embedding_packed_bytes(int vocab, int d) {
   const size_t n_kb = (size_t)(vocab + kKB - 1) / kKB;
   const size_t col_pad = (size_t)(d + kGN - 1) / kGN * kGN;
@@ -600,14 +722,20 @@ SamplerPlan sampler_plan(int n, int vocab, int d) {
   p.off_stats = 0;
   p.off_pimg = align_up((size_t)n * p.n_splits * sizeof(StatsPartial), 256);
   p.off_zp = p.off_pimg + align_up((size_t)p.n_kb * kPImg, 256);
-  p.total = p.off_zp + align_up((size_t)p.n_splits * n * d * sizeof(float), 256);
+  p.off_eb = p.off_zp + align_up((size_t)p.n_splits * n * d * sizeof(float), 256);
+  p.total = p.off_eb + 3 * align_up((size_t)n * 4, 256);
   return p;
 }
 
 hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void* emb_packed,
                           int32_t* ids, uint8_t* committed, float* z, float* conf,
-                          uint32_t* n_unc, dg_ctrl* ctrl, void* ws, hipStream_t s) {
+                          uint32_t* n_unc, dg_ctrl* ctrl, void* ws, hipStream_t s,
+                          const EbCall& eb) {
   uint8_t* base = static_cast<uint8_t*>(ws);
+  const size_t eb_arr = align_up((size_t)p.n * 4, 256);
+  EbRows rows{eb.on, reinterpret_cast<float*>(base + p.off_eb),
+              reinterpret_cast<int32_t*>(base + p.off_eb + eb_arr),
+              reinterpret_cast<int32_t*>(base + p.off_eb + 2 * eb_arr), eb.entropy_out};
   StatsPartial* part = reinterpret_cast<StatsPartial*>(base + p.off_stats);
   uint8_t* pimg = base + p.off_pimg;
   float* zp = reinterpret_cast<float*>(base + p.off_zp);
@@ -617,10 +745,10 @@ hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void*
   const dim3 sgrid(p.n_splits, (p.n + kStatsRows - 1) / kStatsRows);
   if (aligned)
     samp_stats<true><<<sgrid, kStatsThreadsWG, 0, s>>>(logits, ctrl, part, pimg, p.n, p.vocab,
-                                                       p.kb_per_split, p.n_kb);
+                                                       p.kb_per_split, p.n_kb, eb.on);
   else
     samp_stats<false><<<sgrid, kStatsThreadsWG, 0, s>>>(logits, ctrl, part, pimg, p.n, p.vocab,
-                                                        p.kb_per_split, p.n_kb);
+                                                        p.kb_per_split, p.n_kb, eb.on);
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -635,11 +763,19 @@ hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void*
 
   prof_begin("samp_combine", s);
   samp_combine<<<dim3((p.d + 1023) / 1024, p.n), 256, 0, s>>>(logits, part, p.n_splits, zp, ctrl, ids,
-                                                              committed, z, conf, p.n, p.vocab, p.d);
+                                                              committed, z, conf, p.n, p.vocab, p.d,
+                                                              rows);
   prof_end(s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
+  if (eb.on) {
+    prof_begin("samp_eb_select", s);
+    samp_eb_select<<<1, 256, 0, s>>>(rows, ids, committed, eb.argmax, eb.status, ctrl, eb.budget,
+                                     eb.stop_entropy, p.n, p.vocab);
+    prof_end(s);
+    return hipGetLastError();
+  }
   prof_begin("samp_finalize", s);
   samp_finalize<<<1, 256, 0, s>>>(committed, n_unc, ctrl, p.n);
   prof_end(s);

@@ -161,6 +161,43 @@ int dg_sampler_step(const float* logits, const void* emb_packed, int32_t* canvas
                     int n_canvas, int vocab, int d_model,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Entropy-bounded sampler step: the pages' default sampler (explainer
+ * "DiffusionGemma: Google's open diffusion LLM", section "A diffusion language
+ * model refines 256 tokens in 12 steps" and Table 2 "Sampler settings that
+ * decide DiffusionGemma latency").
+ *   logits, emb_packed, canvas_ids, selfcond, ctrl, sizes: as dg_sampler_step
+ *   accepted        [n_canvas] uint8 out: 1 where this step accepted the candidate
+ *   entropy         [n_canvas] float32 out, may be NULL: entropy (nats) of the
+ *                   temperature-T distribution, NaN for undefined rows
+ *   argmax          [n_canvas] int32 in/out: in, the previous step's greedy argmax
+ *                   ids (any value that cannot match, e.g. -1, before the first
+ *                   step of a canvas); out, this step's
+ *   status          device dg_eb_status out
+ *   budget          entropy budget (0.1 in Table 2), stop_entropy the adaptive
+ *                   stopping threshold on the mean entropy (0.005)
+ * The defined rows are ranked by (entropy, position); rank k is accepted when
+ * the running sum of the first k + 1 entropies is <= budget, and rank 0 always.
+ * Accepted positions take their candidate (greedy, or Gumbel with DG_GUMBEL);
+ * every other position gets a uniform re-noise draw, whatever it held before
+ * (tokens of the open canvas stay editable).  On the last step of the budget
+ * every defined row is accepted.  When the mean entropy of the defined rows is
+ * below stop_entropy and the greedy ids equal the incoming argmax, status.stop
+ * is set and canvas_ids become the greedy ids.  DG_COMMIT_ONLY is ignored.
+ */
+typedef struct dg_eb_status {
+  uint32_t n_accepted;   /* positions accepted this step */
+  uint32_t stop;         /* 1: adaptive stopping fired, the canvas is final */
+  float mean_entropy;    /* mean entropy of the defined rows (NaN if none) */
+  uint32_t n_defined;    /* rows with a defined distribution */
+} dg_eb_status;
+
+int dg_sampler_step_eb(const float* logits, const void* emb_packed, int32_t* canvas_ids,
+                       uint8_t* accepted, float* selfcond, float* entropy, int32_t* argmax,
+                       dg_eb_status* status, dg_ctrl* ctrl, float budget, float stop_entropy,
+                       int n_canvas, int vocab, int d_model,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Whole denoising step and its graph                                        */
 /* ------------------------------------------------------------------------ */
