@@ -152,6 +152,10 @@ def main():
     eb = eb_sampler_timing(torch, dg, T, n, vocab, dm, a.steps)
     log(f"entropy-bounded sampler: {eb['ms_per_step']:.3f} ms per step")
 
+    # ---- the decode run: 4096-token prefix, four 256-token canvases ----
+    dec = decode_run_timing(torch, dg, T["emb"], vocab, dm)
+    log(f"decode run: {dec['tokens']} tokens in {dec['steps']} steps, {dec['tokens_per_s']:.0f} tokens/s")
+
     if a.copy_probe_mib:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters calibrate
         # the HBM byte counts read for the kernels above
@@ -185,11 +189,66 @@ def main():
                    "per_kernel_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
                    "embedding_pack_ms_once": round(pack_ms, 2),
                    "attention": attn,
-                   "eb_sampler": eb},
+                   "eb_sampler": eb,
+                   "decode_run": dec},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def decode_run_timing(torch, dg, emb_packed, vocab, dm):
+    """The decode-run workload end to end on the device: per canvas, attention
+    over the growing prefix, canvas init, then steps of synthetic logits +
+    Gumbel sampler (T 0.8 -> 0.4) until no position is open (one host read of
+    the open count per step), then the KV append.  Tokens/s over the whole run."""
+    import workloads
+    c = workloads.CONFIGS[5]
+    n, p0, hq, hkv, hd = c["n"], c["n_prefix"], c["hq"], c["hkv"], c["head_dim"]
+    bf = torch.bfloat16
+    dev = lambda x, dt=None: (torch.from_numpy(x).to(dt) if dt else torch.from_numpy(x)).cuda()
+    _, kp, vp, _, _ = workloads.attention_inputs(5, block=0)
+    total = p0 + c["blocks"] * n
+    kbuf = torch.empty((total, hkv, hd), dtype=bf, device="cuda")
+    vbuf = torch.empty((total, hkv, hd), dtype=bf, device="cuda")
+    kbuf[:p0] = dev(kp, bf)
+    vbuf[:p0] = dev(vp, bf)
+    blocks = []
+    for b in range(c["blocks"]):
+        q, _, _, kc, vc = workloads.attention_inputs(5, block=b)
+        blocks.append((dev(q, bf), dev(kc, bf), dev(vc, bf)))
+    table = dev(workloads.synth_table())
+    logits = torch.empty((n, vocab), dtype=torch.float32, device="cuda")
+    ids = torch.zeros(n, dtype=torch.int32, device="cuda")
+    mask = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    z = torch.empty((n, dm), dtype=torch.float32, device="cuda")
+    nu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    attn = torch.empty((n, hq, hd), dtype=torch.float32, device="cuda")
+    ctrl = dg.make_ctrl(seed=c["seed"], s_max=c["s_max"], tau=c["tau"], t_start=c["t_start"],
+                        t_end=c["t_end"], flags=dg.DG_AUTO_ADVANCE | dg.DG_GUMBEL | dg.DG_T_SCHEDULE)
+    ws = torch.empty(max(dg.dg_sampler_workspace_bytes(n, vocab, dm),
+                         dg.dg_attention_workspace_bytes(n, total, hq, hkv, hd)), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    steps, p = 0, p0
+    for q, kc, vc in blocks:
+        dg.dg_canvas_attention(q, kbuf[:p], vbuf[:p], kc, vc, out=attn, workspace=ws)
+        dg.dg_canvas_init(ids, mask, ctrl, vocab)
+        while True:
+            dg.dg_synth_logits(logits, ids, mask, ctrl, table)
+            dg.dg_sampler_step(logits, emb_packed, ids, mask, z, None, nu, ctrl, workspace=ws)
+            steps += 1
+            if int(nu.item()) == 0:
+                break
+        dg.dg_kv_append(kbuf, vbuf, kc, vc, p)
+        p += n
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    tokens = c["blocks"] * n
+    return {"tokens": tokens, "steps": steps, "seconds": round(dt, 5),
+            "tokens_per_s": round(tokens / dt, 1), "ms_per_step": round(dt * 1e3 / steps, 4),
+            "note": "synthetic logits generated on the device inside the loop; one host read per step"}
 
 
 def eb_sampler_timing(torch, dg, T, n, vocab, dm, steps):
