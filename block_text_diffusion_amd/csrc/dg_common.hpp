@@ -56,10 +56,14 @@ __device__ __forceinline__ uint32_t range_draw(uint32_t h, uint32_t n) {
 }
 
 // u = (2*(h >> 9) + 1) * 2^-24, exact in float32 and strictly inside (0, 1);
-// Gumbel noise g = -log(-log u) with the accurate (not the fast) logarithm.
+// Gumbel noise g = -ln(-ln u), evaluated with the hardware base-2 logarithm
+// (v_log_f32) and ln x = ln2 * log2 x.  u is never denormal or 1, so both
+// logarithm arguments are normal; the result is within a few ulp of the
+// correctly rounded value, far inside the score gap that decides a candidate.
 __device__ __forceinline__ float gumbel_from_bits(uint32_t h) {
   const float u = (float)(((h >> 9) << 1) | 1u) * 5.9604644775390625e-08f;
-  return -logf(-logf(u));
+  const float t = -kLn2 * __builtin_amdgcn_logf(u);
+  return -kLn2 * __builtin_amdgcn_logf(t);
 }
 
 // Temperature rule, evaluated in float32 with no contraction:
