@@ -120,3 +120,30 @@ def test_ctrl_layout_matches_header():
     from block_text_diffusion_amd._lib import DgCtrl
     assert ctypes.sizeof(DgCtrl) == 40
     assert DgCtrl.tau.offset == 24 and DgCtrl.seed.offset == 0
+
+
+def samp_eb(lib, **kw):
+    a = dict(l=FAKE, e=FAKE, ids=FAKE, acc=FAKE, z=FAKE, ent=None, amax=FAKE, st=FAKE, ctrl=FAKE,
+             budget=0.1, stop=0.005, n=16, v=1000, d=64, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return lib.dg_sampler_step_eb(a["l"], a["e"], a["ids"], a["acc"], a["z"], a["ent"], a["amax"], a["st"],
+                                  a["ctrl"], a["budget"], a["stop"], a["n"], a["v"], a["d"], a["ws"],
+                                  a["wsb"], a["stream"])
+
+
+def test_entropy_bounded_sampler_argument_errors(lib):
+    from block_text_diffusion_amd._lib import DG_EINVAL, DG_EUNSUPPORTED, DG_EWORKSPACE
+    assert samp_eb(lib, l=None) == DG_EINVAL
+    assert samp_eb(lib, amax=None) == DG_EINVAL
+    assert samp_eb(lib, st=None) == DG_EINVAL
+    assert samp_eb(lib, budget=-1.0) == DG_EINVAL
+    assert samp_eb(lib, budget=float("nan")) == DG_EINVAL
+    assert samp_eb(lib, stop=float("inf")) == DG_EINVAL
+    assert samp_eb(lib, n=300) == DG_EUNSUPPORTED
+    assert samp_eb(lib, wsb=16) == DG_EWORKSPACE
+
+
+def test_eb_status_layout_matches_header():
+    from block_text_diffusion_amd._lib import DgEbStatus
+    assert ctypes.sizeof(DgEbStatus) == 16
+    assert DgEbStatus.mean_entropy.offset == 8 and DgEbStatus.n_defined.offset == 12
