@@ -603,7 +603,7 @@ __global__ __launch_bounds__(256) void samp_finalize(const uint8_t* __restrict__
 // accept while the running sum of entropies stays within the budget (the
 // first always), re-noise every other position, and test adaptive stopping
 // (mean entropy below the threshold and the greedy ids unchanged since the
-// previous step).  One workgroup of 256 threads, bitonic sort in LDS, fp64
+// previous step).  One workgroup of 256 threads: ranks by counting, fp64
 // prefix sums.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void samp_eb_select(EbRows eb, int32_t* __restrict__ ids,
@@ -613,7 +613,7 @@ __global__ __launch_bounds__(256) void samp_eb_select(EbRows eb, int32_t* __rest
                                                       dg_ctrl* __restrict__ ctrl, float budget,
                                                       float stop_entropy, int n_rows, int vocab) {
   __shared__ float key[256];
-  __shared__ int idx[256];
+  __shared__ int idx[256];   // position at each rank
   __shared__ double csum[256];
   __shared__ uint8_t acc[256];
   const int t = threadIdx.x;
@@ -621,23 +621,22 @@ __global__ __launch_bounds__(256) void samp_eb_select(EbRows eb, int32_t* __rest
   const float h = (t < n_rows) ? eb.ent[t] : __builtin_nanf("");
   const bool defined = t < n_rows && !(h != h);
   key[t] = defined ? h : INFINITY;
-  idx[t] = t;
   acc[t] = 0;
   __syncthreads();
-  // bitonic sort of (key, idx) ascending; undefined rows (+inf) sort last, by index
-  for (int k = 2; k <= 256; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const int p = t ^ j;
-      if (p > t) {
-        const float ka = key[t], kb = key[p];
-        const int ia = idx[t], ib = idx[p];
-        const bool a_after_b = (ka > kb) || (ka == kb && ia > ib);
-        const bool up = (t & k) == 0;
-        if (a_after_b == up) { key[t] = kb; key[p] = ka; idx[t] = ib; idx[p] = ia; }
-      }
-      __syncthreads();
-    }
+  // rank of (key, position) among all 256 entries: the number of entries that
+  // sort before it (undefined rows, key +inf, sort last by position); the
+  // sorted order is then written by scattering each entry to its rank
+  const float mine = key[t];
+  int rank = 0;
+#pragma unroll 8
+  for (int j = 0; j < 256; ++j) {
+    const float kj = key[j];
+    rank += (kj < mine) || (kj == mine && j < t);
   }
+  __syncthreads();
+  key[rank] = mine;
+  idx[rank] = t;
+  __syncthreads();
   // inclusive prefix sums of the sorted entropies (fp64, Hillis-Steele)
   const int n_def = __syncthreads_count(defined);
   double c = (t < n_def) ? (double)key[t] : 0.0;
