@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="eager steps timed kernel by kernel (default: as many as --steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="also time one plain bf16 GEMM of the contraction's shape through torch")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -166,6 +168,23 @@ def main():
         torch.cuda.synchronize()
         log(f"copy probe: {a.copy_probe_mib} MiB read + {a.copy_probe_mib} MiB written per launch, 3 launches")
 
+    blas = None
+    if a.blas_reference:
+        # calibration only: one bf16 GEMM [N, V] x [V, d] (a third of the contraction's work)
+        A = torch.randn(n, vocab, device="cuda").to(torch.bfloat16)
+        B = (torch.randn(vocab, dm, device="cuda") * 0.02).to(torch.bfloat16)
+        for _ in range(3):
+            A @ B
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10):
+            A @ B
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) / 10 * 1e6
+        blas = {"us": round(us, 1), "tflops": round(2.0 * n * vocab * dm / (us * 1e-6) / 1e12, 1)}
+        log(f"torch bf16 GEMM of the same shape: {us:.1f} us")
+        del A, B
+
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(q, kp, vp, kc, vc, emb, logits, ids, mask)
@@ -190,7 +209,8 @@ def main():
                    "embedding_pack_ms_once": round(pack_ms, 2),
                    "attention": attn,
                    "eb_sampler": eb,
-                   "decode_run": dec},
+                   "decode_run": dec,
+                   "blas_reference_bf16_gemm": blas},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
