@@ -14,6 +14,12 @@ Definition computed (float64 throughout, inputs widened exactly):
     K = [K_prefix ; K_canvas],  V = [V_prefix ; V_canvas]     (keys j = 0 .. P+N-1)
     O[i, h] = sum_j softmax_j(scale * q[i, h] . K[j, h // G]) * V[j, h // G]
 
+The KV-update pass (the committed canvas written into the cache) is causal
+over the canvas instead (explainer, "Block-autoregressive generation, one canvas
+after another": a causal encoder reads the history).  Reading taken for the
+causal flag: canvas row i attends to every prefix key and to canvas keys
+0 .. i.
+
 Pins (tests/test_oracle_attention.py): explicit-loop brute force on tiny shapes;
 torch's CPU scaled_dot_product_attention with repeated KV heads; closed forms
 (one key gives v; scale 0 gives the mean of V; constant V gives that constant);
@@ -22,8 +28,10 @@ invariance under a permutation applied to canvas (or prefix) keys and values.
 import numpy as np
 
 
-def canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, scale=None):
-    """q [N,Hq,D]; k/v_prefix [P,Hkv,D] (P may be 0); k/v_canvas [N,Hkv,D] -> O [N,Hq,D] float64."""
+def canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, scale=None, causal=False):
+    """q [N,Hq,D]; k/v_prefix [P,Hkv,D] (P may be 0); k/v_canvas [N,Hkv,D] -> O [N,Hq,D] float64.
+
+    causal: canvas row i sees the prefix and canvas keys 0..i only."""
     q = np.asarray(q, dtype=np.float64)
     kc = np.asarray(k_canvas, dtype=np.float64)
     vc = np.asarray(v_canvas, dtype=np.float64)
@@ -40,9 +48,16 @@ def canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, scale=None):
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     out = np.empty((n, hq, d), dtype=np.float64)
+    p = keys.shape[0] - n
+    masked = None
+    if causal:
+        j = np.arange(n)
+        masked = j[None, :] > j[:, None]                       # canvas key j after row i
     for h in range(hq):
         kvh = h // group
         s = scale * (q[:, h, :] @ keys[:, kvh, :].T)          # [N, L]
+        if masked is not None:
+            s[:, p:][masked] = -np.inf
         s = s - s.max(axis=1, keepdims=True)
         w = np.exp(s)
         w = w / w.sum(axis=1, keepdims=True)

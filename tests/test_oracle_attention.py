@@ -96,3 +96,43 @@ def test_gqa_mapping_is_blocked():
     vc = rng.standard_normal((n, hkv, d)); vc[:, 1] = 0
     o = canvas_attention(q, np.zeros((0, hkv, d)), np.zeros((0, hkv, d)), kc, vc)
     assert np.all(o[:, 2:] == 0) and np.all(np.abs(o[:, :2]) > 0)
+
+
+@pytest.mark.parametrize("p", [0, 40])
+def test_causal_matches_torch_sdpa_with_mask(p):
+    """Causal flag: canvas row i sees the prefix and canvas keys 0..i (torch's SDPA
+    with an explicit boolean mask is the independent routine)."""
+    rng = np.random.default_rng(70 + p)
+    n, hq, hkv, d = 48, 8, 4, 64
+    q = rng.standard_normal((n, hq, d)); kp = rng.standard_normal((p, hkv, d))
+    vp = rng.standard_normal((p, hkv, d)); kc = rng.standard_normal((n, hkv, d))
+    vc = rng.standard_normal((n, hkv, d))
+    got = canvas_attention(q, kp, vp, kc, vc, causal=True)
+    K = torch.from_numpy(np.concatenate([kp, kc])).permute(1, 0, 2)[None].repeat_interleave(hq // hkv, dim=1)
+    V = torch.from_numpy(np.concatenate([vp, vc])).permute(1, 0, 2)[None].repeat_interleave(hq // hkv, dim=1)
+    Q = torch.from_numpy(q).permute(1, 0, 2)[None]
+    allowed = np.ones((n, p + n), dtype=bool)
+    allowed[:, p:] = np.tril(np.ones((n, n), dtype=bool))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        Q, K, V, attn_mask=torch.from_numpy(allowed))[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-10)
+
+
+def test_causal_special_cases():
+    rng = np.random.default_rng(71)
+    n, p, hq, hkv, d = 20, 9, 4, 4, 16
+    q = rng.standard_normal((n, hq, d)); kp = rng.standard_normal((p, hkv, d))
+    vp = rng.standard_normal((p, hkv, d)); kc = rng.standard_normal((n, hkv, d))
+    vc = rng.standard_normal((n, hkv, d))
+    full = canvas_attention(q, kp, vp, kc, vc)
+    causal = canvas_attention(q, kp, vp, kc, vc, causal=True)
+    # the last canvas row sees every key either way
+    np.testing.assert_allclose(causal[-1], full[-1], rtol=1e-13, atol=1e-13)
+    # with no prefix, canvas row 0 sees only its own key: O = v_0
+    c0 = canvas_attention(q, None, None, kc, vc, causal=True)
+    np.testing.assert_allclose(c0[0], vc[0], rtol=1e-13, atol=1e-13)
+    # row i does not depend on canvas keys after i
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[10:] = rng.standard_normal((n - 10, hkv, d)); vc2[10:] = 5.0
+    c2 = canvas_attention(q, kp, vp, kc2, vc2, causal=True)
+    np.testing.assert_allclose(c2[:10], causal[:10], rtol=1e-13, atol=1e-13)
