@@ -8,15 +8,15 @@ the library's HIP kernels.
 import ctypes
 
 from . import _lib
-from ._lib import (DG_AUTO_ADVANCE, DG_BF16, DG_COMMIT_ONLY, DG_F32, DG_GUMBEL, DG_T_SCHEDULE,
-                   DgCtrl, DgError, check, load)
+from ._lib import (DG_ATTN_CAUSAL, DG_AUTO_ADVANCE, DG_BF16, DG_COMMIT_ONLY, DG_F32, DG_GUMBEL,
+                   DG_T_SCHEDULE, DgCtrl, DgError, check, load)
 
 __all__ = [
-    "dg_canvas_attention", "dg_sampler_step", "dg_embedding_pack", "dg_embedding_packed_bytes", "dg_denoise_step", "StepGraph", "dg_canvas_init",
+    "dg_canvas_attention", "dg_sampler_step", "dg_sampler_step_eb", "read_eb_status", "dg_embedding_pack", "dg_embedding_packed_bytes", "dg_denoise_step", "StepGraph", "dg_canvas_init",
     "dg_kv_append", "dg_synth_logits", "dg_philox_fill", "dg_attention_workspace_bytes",
     "dg_sampler_workspace_bytes", "dg_denoise_workspace_bytes", "dg_profile_enable",
     "dg_profile_read", "make_ctrl", "read_ctrl", "write_ctrl", "DG_GUMBEL", "DG_COMMIT_ONLY",
-    "DG_AUTO_ADVANCE", "DG_T_SCHEDULE", "DG_F32", "DG_BF16", "DgError", "load",
+    "DG_AUTO_ADVANCE", "DG_T_SCHEDULE", "DG_ATTN_CAUSAL", "DG_F32", "DG_BF16", "DgError", "load",
 ]
 
 
@@ -115,7 +115,7 @@ def read_ctrl(ctrl_t):
 
 # ---- the three calls of the denoising step ----
 def dg_canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, out=None, scale=0.0,
-                        workspace=None, stream=None):
+                        workspace=None, stream=None, causal=False):
     torch = _torch()
     dt = (torch.bfloat16, torch.float32)
     _need(q, "q", dt); _need(k_canvas, "k_canvas", dt); _need(v_canvas, "v_canvas", dt)
@@ -128,11 +128,11 @@ def dg_canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, out=None, sca
         out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
     nbytes = dg_attention_workspace_bytes(n, n_prefix, hq, hkv, d)
     ws = _workspace(nbytes, q.device, workspace)
-    check(load().dg_canvas_attention(_ptr(q), _ptr(k_prefix) if n_prefix else None,
-                                     _ptr(v_prefix) if n_prefix else None, _ptr(k_canvas),
-                                     _ptr(v_canvas), _ptr(out), n, n_prefix, hq, hkv, d,
-                                     _qkv_dtype(q), float(scale), _ptr(ws), ws.numel(),
-                                     _stream(stream)))
+    check(load().dg_canvas_attention_ex(_ptr(q), _ptr(k_prefix) if n_prefix else None,
+                                        _ptr(v_prefix) if n_prefix else None, _ptr(k_canvas),
+                                        _ptr(v_canvas), _ptr(out), n, n_prefix, hq, hkv, d,
+                                        _qkv_dtype(q), float(scale), DG_ATTN_CAUSAL if causal else 0,
+                                        _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 

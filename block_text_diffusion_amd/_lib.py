@@ -21,6 +21,7 @@ DG_GUMBEL = 1
 DG_COMMIT_ONLY = 2
 DG_AUTO_ADVANCE = 4
 DG_T_SCHEDULE = 8
+DG_ATTN_CAUSAL = 1
 
 
 class DgCtrl(ctypes.Structure):
@@ -62,6 +63,8 @@ _f = ctypes.c_float
 SIGNATURES = {
     "dg_attention_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "dg_canvas_attention": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "dg_canvas_attention_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
+                                    ctypes.c_uint32, _vp, _sz, _vp]),
     "dg_sampler_workspace_bytes": (_sz, [_i, _i, _i]),
     "dg_embedding_packed_bytes": (_sz, [_i, _i]),
     "dg_embedding_pack": (_i, [_vp, _vp, _i, _i, _vp]),

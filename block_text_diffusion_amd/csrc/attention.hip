@@ -112,7 +112,8 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
     const TQ* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, float* __restrict__ out,
     _Float16* __restrict__ opart, float* __restrict__ ml, int n, int n_prefix, int hq, int hkv,
-    int blocks_prefix, int blocks_total, int blocks_per_chunk, int n_chunks, float scale_log2e) {
+    int blocks_prefix, int blocks_total, int blocks_per_chunk, int n_chunks, float scale_log2e,
+    bool causal) {
   using G = AGeom<D>;
   constexpr int KS = D / 16;   // 16-wide k steps over the head dimension
   constexpr int DB = D / 32;   // 32-row blocks of O^T
@@ -201,12 +202,16 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
     float s[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = sa[v] + sb[v];
-    // lane holds keys 32wh + 8(v/4) + 4half + v%4 of query r
-    if (seg_left < kAKeys) {
+    // lane holds keys 32wh + 8(v/4) + 4half + v%4 of query r; with the causal
+    // flag canvas key c is visible to canvas row qn only when c <= qn
+    const bool canvas_blk = gb >= blocks_prefix;
+    if (seg_left < kAKeys || (causal && canvas_blk)) {
+      const int lim = (causal && canvas_blk) ? min(seg_left, qn - (gb - blocks_prefix) * kAKeys + 1)
+                                             : seg_left;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = 32 * wh + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (key >= seg_left) s[v] = -INFINITY;
+        if (key >= lim) s[v] = -INFINITY;
       }
     }
 
@@ -388,9 +393,11 @@ __global__ __launch_bounds__(kCThreads) void attn_combine(const _Float16* __rest
     const size_t idx = (size_t)c * n_rows_total + row;
     const f32x4 rec = *reinterpret_cast<const f32x4*>(ml + idx * 4);
     const f16x4 h = *reinterpret_cast<const f16x4*>(opart + idx * D + d4);
+    // a chunk whose keys were all masked for this row (causal) has m = -inf, l = 0
+    // and weight 0
     const float mn = fmaxf(m, rec[0]);
-    const float a = __builtin_amdgcn_exp2f(m - mn);
-    const float bw = __builtin_amdgcn_exp2f(rec[0] - mn);
+    const float a = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    const float bw = (rec[0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(rec[0] - mn);
     const float sw = bw * rec[2];
     acc = acc * a + (f32x4){(float)h[0] * sw, (float)h[1] * sw, (float)h[2] * sw, (float)h[3] * sw};
     l = l * a + rec[1] * bw;
@@ -440,14 +447,14 @@ AttnPlan attn_plan(int n, int n_prefix, int hq, int hkv, int d) {
 template <int D, typename TQ>
 static hipError_t launch_attn_t(const AttnPlan& p, const void* q, const uint16_t* kp,
                                 const uint16_t* vp, const uint16_t* kc, const uint16_t* vc,
-                                float* out, float scale, void* ws, hipStream_t s) {
+                                float* out, float scale, bool causal, void* ws, hipStream_t s) {
   _Float16* opart = reinterpret_cast<_Float16*>(static_cast<uint8_t*>(ws) + p.off_opart);
   float* ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p.off_ml);
   const float sl2 = scale * kLog2e;
   prof_begin("attn_partial", s);
   attn_partial<D, TQ><<<dim3(p.n_chunks, p.n_qtiles, p.hkv), kAThreads, 0, s>>>(
       static_cast<const TQ*>(q), kp, vp, kc, vc, out, opart, ml, p.n, p.n_prefix, p.hq, p.hkv,
-      p.blocks_prefix, p.blocks_total, p.blocks_per_chunk, p.n_chunks, sl2);
+      p.blocks_prefix, p.blocks_total, p.blocks_per_chunk, p.n_chunks, sl2, causal);
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_chunks == 1) return e;
@@ -461,7 +468,7 @@ static hipError_t launch_attn_t(const AttnPlan& p, const void* q, const uint16_t
 
 hipError_t launch_attention(const AttnPlan& p, const void* q, const void* kp, const void* vp,
                             const void* kc, const void* vc, float* out, bool bf16_in,
-                            float scale, void* ws, hipStream_t s) {
+                            float scale, void* ws, hipStream_t s, bool causal) {
   const uint16_t *kp16, *vp16, *kc16, *vc16;
   if (bf16_in) {
     kp16 = static_cast<const uint16_t*>(kp); vp16 = static_cast<const uint16_t*>(vp);
@@ -486,10 +493,10 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* kp, co
     kp16 = kp_w; vp16 = vp_w; kc16 = kc_w; vc16 = vc_w;
   }
   if (p.d == 128)
-    return bf16_in ? launch_attn_t<128, uint16_t>(p, q, kp16, vp16, kc16, vc16, out, scale, ws, s)
-                   : launch_attn_t<128, float>(p, q, kp16, vp16, kc16, vc16, out, scale, ws, s);
-  return bf16_in ? launch_attn_t<64, uint16_t>(p, q, kp16, vp16, kc16, vc16, out, scale, ws, s)
-                 : launch_attn_t<64, float>(p, q, kp16, vp16, kc16, vc16, out, scale, ws, s);
+    return bf16_in ? launch_attn_t<128, uint16_t>(p, q, kp16, vp16, kc16, vc16, out, scale, causal, ws, s)
+                   : launch_attn_t<128, float>(p, q, kp16, vp16, kc16, vc16, out, scale, causal, ws, s);
+  return bf16_in ? launch_attn_t<64, uint16_t>(p, q, kp16, vp16, kc16, vc16, out, scale, causal, ws, s)
+                 : launch_attn_t<64, float>(p, q, kp16, vp16, kc16, vc16, out, scale, causal, ws, s);
 }
 
 }  // namespace dg

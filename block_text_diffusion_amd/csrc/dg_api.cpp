@@ -154,6 +154,15 @@ size_t dg_denoise_workspace_bytes(int n, int np, int hq, int hkv, int d, int voc
 int dg_canvas_attention(const void* q, const void* kp, const void* vp, const void* kc,
                         const void* vc, float* out, int n, int np, int hq, int hkv, int d,
                         int dtype, float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return dg_canvas_attention_ex(q, kp, vp, kc, vc, out, n, np, hq, hkv, d, dtype, scale, 0u, ws,
+                                ws_bytes, stream);
+}
+
+int dg_canvas_attention_ex(const void* q, const void* kp, const void* vp, const void* kc,
+                           const void* vc, float* out, int n, int np, int hq, int hkv, int d,
+                           int dtype, float scale, uint32_t attn_flags, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  if (attn_flags & ~(uint32_t)DG_ATTN_CAUSAL) return fail(DG_EINVAL, "attention: unknown flag bits");
   int st = check_attention(q, kp, vp, kc, vc, out, n, np, hq, hkv, d, dtype);
   if (st != DG_OK) return st;
   const dg::AttnPlan p = dg::attn_plan(n, np, hq, hkv, d);
@@ -161,7 +170,8 @@ int dg_canvas_attention(const void* q, const void* kp, const void* vp, const voi
     return fail(DG_EWORKSPACE, "attention: workspace %zu < %zu bytes", ws_bytes, p.total);
   if (p.total > 0 && !aligned16(ws)) return fail(DG_EINVAL, "attention: workspace misaligned");
   if (!(scale > 0.f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)d);
-  hipError_t e = dg::launch_attention(p, q, kp, vp, kc, vc, out, dtype == DG_BF16, scale, ws, stream);
+  hipError_t e = dg::launch_attention(p, q, kp, vp, kc, vc, out, dtype == DG_BF16, scale, ws, stream,
+                                      (attn_flags & DG_ATTN_CAUSAL) != 0);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return DG_OK;
 }

@@ -56,7 +56,7 @@ struct AttnPlan {
 AttnPlan attn_plan(int n, int n_prefix, int hq, int hkv, int d);
 hipError_t launch_attention(const AttnPlan& p, const void* q, const void* kp, const void* vp,
                             const void* kc, const void* vc, float* out, bool bf16_in,
-                            float scale, void* ws, hipStream_t s);
+                            float scale, void* ws, hipStream_t s, bool causal = false);
 
 // ---- block loop helpers ----
 hipError_t launch_canvas_init(int32_t* ids, uint8_t* committed, dg_ctrl* ctrl, int n, int vocab,

@@ -113,6 +113,24 @@ int dg_canvas_attention(const void* q, const void* k_prefix, const void* v_prefi
                         int dtype, float scale,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Canvas attention with options (attn_flags, 0 = dg_canvas_attention).
+ *   DG_ATTN_CAUSAL   canvas row i attends to every prefix key and to canvas
+ *                    keys 0..i only: the KV-update pass, in which a finished
+ *                    canvas is written into the cache as causal history
+ *                    (explainer "DiffusionGemma: Google's open diffusion LLM",
+ *                    section "Block-autoregressive generation, one canvas
+ *                    after another": a causal encoder reads the history).
+ * Other arguments, workspace and errors as dg_canvas_attention; unknown flag
+ * bits return DG_EINVAL.
+ */
+enum { DG_ATTN_CAUSAL = 1u };
+int dg_canvas_attention_ex(const void* q, const void* k_prefix, const void* v_prefix,
+                           const void* k_canvas, const void* v_canvas, float* out,
+                           int n_canvas, int n_prefix, int hq, int hkv, int head_dim,
+                           int dtype, float scale, uint32_t attn_flags,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Diffusion sampler                                                         */
 /* ------------------------------------------------------------------------ */

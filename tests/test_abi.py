@@ -147,3 +147,11 @@ def test_eb_status_layout_matches_header():
     from block_text_diffusion_amd._lib import DgEbStatus
     assert ctypes.sizeof(DgEbStatus) == 16
     assert DgEbStatus.mean_entropy.offset == 8 and DgEbStatus.n_defined.offset == 12
+
+
+def test_attention_ex_flags(lib):
+    from block_text_diffusion_amd._lib import DG_EINVAL
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 8, 8, 4, 64, 1, 0.0]
+    assert lib.dg_canvas_attention_ex(*a, 2, FAKE, 0, None) == DG_EINVAL     # unknown flag bit
+    assert b"flag" in lib.dg_last_error()
+    assert lib.dg_canvas_attention_ex(*a[:6], 0, 8, 8, 4, 64, 1, 0.0, 1, FAKE, 0, None) == DG_EINVAL

@@ -78,3 +78,21 @@ def test_deterministic():
     a = run_gpu(torch, dg, q, kp, vp, kc, vc, "bf16")
     b = run_gpu(torch, dg, q, kp, vp, kc, vc, "bf16")
     np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("n,p,hq,hkv,d,qkv", [
+    (256, 4096, 16, 8, 128, "bf16"),   # the KV-update pass at the long-context shape
+    (256, 0, 16, 8, 128, "bf16"),      # no prefix: row 0 sees only its own key
+    (100, 37, 16, 8, 128, "bf16"),     # ragged tiles and blocks
+    (130, 300, 8, 2, 64, "f32"),       # fp32 inputs, D=64
+    (1, 5, 8, 8, 64, "bf16"),          # a single canvas position
+])
+def test_causal(n, p, hq, hkv, d, qkv):
+    torch, dg = require_gpu()
+    log(f"causal attention n={n} p={p} hq={hq} hkv={hkv} d={d} {qkv}")
+    q, kp, vp, kc, vc = workloads.attention_inputs(2, n=n, n_prefix=p, hq=hq, hkv=hkv, head_dim=d, qkv=qkv)
+    dt = torch.bfloat16 if qkv == "bf16" else torch.float32
+    t = lambda x: to_dev(x, dt)
+    got = dg.dg_canvas_attention(t(q), t(kp) if p else None, t(vp) if p else None, t(kc), t(vc),
+                                 causal=True).cpu().numpy()
+    check(got, canvas_attention(q, kp, vp, kc, vc, causal=True), f"causal n={n} p={p}")
