@@ -154,6 +154,11 @@ def main():
     eb = eb_sampler_timing(torch, dg, T, n, vocab, dm, a.steps)
     log(f"entropy-bounded sampler: {eb['ms_per_step']:.3f} ms per step")
 
+    # ---- batches of canvases sharing one pass over E ----
+    batched = batched_sampler_timing(torch, dg, T, n, vocab, dm, a.steps)
+    log("batched sampler: " + ", ".join(f"B={r['batch']}: {r['ms_per_step']:.3f} ms ({r['canvas_steps_per_s']:.0f} canvas-steps/s)"
+                                        for r in batched))
+
     # ---- the decode run: 4096-token prefix, four 256-token canvases ----
     dec = decode_run_timing(torch, dg, T["emb"], vocab, dm)
     log(f"decode run: {dec['tokens']} tokens in {dec['steps']} steps, {dec['tokens_per_s']:.0f} tokens/s")
@@ -210,6 +215,7 @@ def main():
                    "attention": attn,
                    "eb_sampler": eb,
                    "decode_run": dec,
+                   "batched_sampler": batched,
                    "blas_reference_bf16_gemm": blas},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -269,6 +275,37 @@ def decode_run_timing(torch, dg, emb_packed, vocab, dm):
     return {"tokens": tokens, "steps": steps, "seconds": round(dt, 5),
             "tokens_per_s": round(tokens / dt, 1), "ms_per_step": round(dt * 1e3 / steps, 4),
             "note": "synthetic logits generated on the device inside the loop; one host read per step"}
+
+
+def batched_sampler_timing(torch, dg, T, n, vocab, dm, steps, batches=(2, 4, 8)):
+    """The threshold sampler over B canvases in one pass (each canvas its own
+    control block): ms per batched step and canvas-steps/s.  The step's logits
+    are replicated B times; greedy candidates, T = 1."""
+    out = []
+    for B in batches:
+        logits = T["logits"].repeat(B, 1)
+        ids = T["ids"].repeat(B)
+        mask = torch.zeros(B * n, dtype=torch.uint8, device="cuda")
+        z = torch.empty((B * n, dm), dtype=torch.float32, device="cuda")
+        nu = torch.zeros(B, dtype=torch.int32, device="cuda")
+        ctrl = dg.stack_ctrl([dg.make_ctrl(seed=10 + b, tau=0.9, flags=dg.DG_AUTO_ADVANCE) for b in range(B)])
+        ws = torch.empty(dg.dg_sampler_workspace_bytes_batched(n, B, vocab, dm), dtype=torch.uint8, device="cuda")
+        run = lambda: dg.dg_sampler_step_batched(logits, T["emb"], ids, mask, z, None, nu, ctrl, B, workspace=ws)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        k = max(5, steps // B)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(k):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / k
+        out.append({"batch": B, "ms_per_step": round(ms, 4), "canvas_steps_per_s": round(B * 1e3 / ms, 1)})
+        del logits, ids, mask, z, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def eb_sampler_timing(torch, dg, T, n, vocab, dm, steps):

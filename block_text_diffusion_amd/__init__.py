@@ -12,7 +12,9 @@ from ._lib import (DG_ATTN_CAUSAL, DG_AUTO_ADVANCE, DG_BF16, DG_COMMIT_ONLY, DG_
                    DG_T_SCHEDULE, DgCtrl, DgError, check, load)
 
 __all__ = [
-    "dg_canvas_attention", "dg_sampler_step", "dg_sampler_step_eb", "read_eb_status", "dg_embedding_pack", "dg_embedding_packed_bytes", "dg_denoise_step", "StepGraph", "dg_canvas_init",
+    "dg_canvas_attention", "dg_sampler_step", "dg_sampler_step_eb", "read_eb_status",
+    "dg_sampler_step_batched", "dg_sampler_step_eb_batched", "dg_sampler_workspace_bytes_batched",
+    "stack_ctrl", "dg_embedding_pack", "dg_embedding_packed_bytes", "dg_denoise_step", "StepGraph", "dg_canvas_init",
     "dg_kv_append", "dg_synth_logits", "dg_philox_fill", "dg_attention_workspace_bytes",
     "dg_sampler_workspace_bytes", "dg_denoise_workspace_bytes", "dg_profile_enable",
     "dg_profile_read", "make_ctrl", "read_ctrl", "write_ctrl", "DG_GUMBEL", "DG_COMMIT_ONLY",
@@ -107,8 +109,8 @@ def write_ctrl(ctrl_t, **fields):
     ctrl_t.copy_(torch.frombuffer(bytearray(bytes(c)), dtype=torch.uint8))
 
 
-def read_ctrl(ctrl_t):
-    raw = bytes(ctrl_t.cpu().numpy().tobytes())
+def read_ctrl(ctrl_t, index=0):
+    raw = bytes(ctrl_t.cpu().numpy().tobytes()[40 * index:40 * index + 40])
     c = DgCtrl.from_buffer_copy(raw)
     return {f: getattr(c, f) for f, _ in DgCtrl._fields_}
 
@@ -180,9 +182,57 @@ def dg_sampler_step_eb(logits, emb_packed, canvas_ids, accepted, selfcond, entro
                                     _stream(stream)))
 
 
-def read_eb_status(status_t):
+def dg_sampler_workspace_bytes_batched(n_canvas, batch, vocab, d_model):
+    return load().dg_sampler_workspace_bytes_batched(n_canvas, batch, vocab, d_model)
+
+
+def stack_ctrl(ctrls):
+    """Concatenate device control blocks (make_ctrl outputs) into one [batch * 40] tensor."""
+    return _torch().cat(list(ctrls))
+
+
+def dg_sampler_step_batched(logits, emb_packed, canvas_ids, committed, selfcond, confidence,
+                            n_uncommitted, ctrl, batch, workspace=None, stream=None):
+    """A batch of canvases stacked along the rows (logits [batch * n, V]); ctrl
+    holds `batch` control blocks (stack_ctrl), n_uncommitted `batch` counts."""
+    torch = _torch()
+    _need(logits, "logits", (torch.float32,)); _need(emb_packed, "emb_packed", (torch.uint8,))
+    _need(canvas_ids, "canvas_ids", (torch.int32,)); _need(committed, "committed", (torch.uint8,))
+    _need(selfcond, "selfcond", (torch.float32,)); _need(n_uncommitted, "n_uncommitted", (torch.int32, torch.uint32))
+    _need(ctrl, "ctrl", (torch.uint8,))
+    rows, vocab = logits.shape
+    if rows % batch or ctrl.numel() < 40 * batch or n_uncommitted.numel() < batch:
+        raise ValueError("rows must split into `batch` canvases with a control block and a count each")
+    n = rows // batch
+    d = selfcond.shape[1]
+    if emb_packed.numel() < dg_embedding_packed_bytes(vocab, d):
+        raise ValueError("emb_packed is smaller than dg_embedding_packed_bytes(vocab, d_model)")
+    ws = _workspace(dg_sampler_workspace_bytes_batched(n, batch, vocab, d), logits.device, workspace)
+    check(load().dg_sampler_step_batched(_ptr(logits), _ptr(emb_packed), _ptr(canvas_ids), _ptr(committed),
+                                         _ptr(selfcond), _ptr(confidence), _ptr(n_uncommitted), _ptr(ctrl),
+                                         n, batch, vocab, d, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def dg_sampler_step_eb_batched(logits, emb_packed, canvas_ids, accepted, selfcond, entropy, argmax,
+                               status, ctrl, batch, budget=0.1, stop_entropy=0.005, workspace=None,
+                               stream=None):
+    """Entropy-bounded step over a batch; status holds `batch` 16-byte records."""
+    torch = _torch()
+    rows, vocab = logits.shape
+    if rows % batch or ctrl.numel() < 40 * batch or status.numel() < 16 * batch:
+        raise ValueError("rows must split into `batch` canvases with a control block and a status each")
+    n = rows // batch
+    d = selfcond.shape[1]
+    ws = _workspace(dg_sampler_workspace_bytes_batched(n, batch, vocab, d), logits.device, workspace)
+    check(load().dg_sampler_step_eb_batched(_ptr(logits), _ptr(emb_packed), _ptr(canvas_ids), _ptr(accepted),
+                                            _ptr(selfcond), _ptr(entropy), _ptr(argmax), _ptr(status),
+                                            _ptr(ctrl), float(budget), float(stop_entropy), n, batch, vocab,
+                                            d, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def read_eb_status(status_t, index=0):
     from ._lib import DgEbStatus
-    raw = bytes(status_t.cpu().numpy().tobytes()[:16])
+    raw = bytes(status_t.cpu().numpy().tobytes()[16 * index:16 * index + 16])
     st = DgEbStatus.from_buffer_copy(raw)
     return {f: getattr(st, f) for f, _ in DgEbStatus._fields_}
 

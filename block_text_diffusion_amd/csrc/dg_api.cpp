@@ -76,17 +76,20 @@ int check_attention(const void* q, const void* kp, const void* vp, const void* k
 }
 
 int check_sampler(const float* logits, const void* emb, const int32_t* ids, const uint8_t* committed,
-                  const float* z, const uint32_t* n_unc, const dg_ctrl* ctrl, int n, int vocab, int d) {
+                  const float* z, const uint32_t* n_unc, const dg_ctrl* ctrl, int n, int vocab, int d,
+                  int batch = 1) {
   if (!logits || !emb || !ids || !committed || !z || !n_unc || !ctrl)
     return fail(DG_EINVAL, "sampler: null pointer argument");
   if (n < 1) return fail(DG_EINVAL, "sampler: n_canvas < 1");
   if (n > 256) return fail(DG_EUNSUPPORTED, "sampler: n_canvas > 256");
+  if (batch < 1) return fail(DG_EINVAL, "sampler: batch < 1");
+  if (batch > 4096) return fail(DG_EUNSUPPORTED, "sampler: batch > 4096");
   if (vocab < 2) return fail(DG_EINVAL, "sampler: vocab < 2");
   if (d < 1) return fail(DG_EINVAL, "sampler: d_model < 1");
   if (dg::embedding_packed_bytes(vocab, d) >= (1ull << 40)) return fail(DG_EINVAL, "sampler: E too large");
   // the logits are addressed with 32-bit byte offsets
-  if ((uint64_t)n * (uint64_t)vocab * 4ull >= (1ull << 32))
-    return fail(DG_EUNSUPPORTED, "sampler: n_canvas * vocab * 4 must be below 2^32");
+  if ((uint64_t)n * (uint64_t)batch * (uint64_t)vocab * 4ull >= (1ull << 32))
+    return fail(DG_EUNSUPPORTED, "sampler: n_canvas * batch * vocab * 4 must be below 2^32");
   if (!aligned16(logits) || !aligned16(emb) || !aligned16(z))
     return fail(DG_EINVAL, "sampler: logits/emb_packed/selfcond must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(ctrl) & 7u) != 0) return fail(DG_EINVAL, "sampler: ctrl misaligned");
@@ -140,8 +143,12 @@ size_t dg_attention_workspace_bytes(int n, int np, int hq, int hkv, int d) {
 }
 
 size_t dg_sampler_workspace_bytes(int n, int vocab, int d) {
-  if (n < 1 || n > 256 || vocab < 2 || d < 1) return 0;
-  return dg::sampler_plan(n, vocab, d).total;
+  return dg_sampler_workspace_bytes_batched(n, 1, vocab, d);
+}
+
+size_t dg_sampler_workspace_bytes_batched(int n, int batch, int vocab, int d) {
+  if (n < 1 || n > 256 || batch < 1 || batch > 4096 || vocab < 2 || d < 1) return 0;
+  return dg::sampler_plan(n, batch, vocab, d).total;
 }
 
 size_t dg_denoise_workspace_bytes(int n, int np, int hq, int hkv, int d, int vocab, int dm) {
@@ -179,9 +186,16 @@ int dg_canvas_attention_ex(const void* q, const void* kp, const void* vp, const 
 int dg_sampler_step(const float* logits, const void* emb, int32_t* ids, uint8_t* committed,
                     float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl, int n, int vocab, int d,
                     void* ws, size_t ws_bytes, hipStream_t stream) {
-  int st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, d);
+  return dg_sampler_step_batched(logits, emb, ids, committed, z, conf, n_unc, ctrl, n, 1, vocab, d, ws,
+                                 ws_bytes, stream);
+}
+
+int dg_sampler_step_batched(const float* logits, const void* emb, int32_t* ids, uint8_t* committed,
+                            float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl, int n, int batch,
+                            int vocab, int d, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, d, batch);
   if (st != DG_OK) return st;
-  const dg::SamplerPlan p = dg::sampler_plan(n, vocab, d);
+  const dg::SamplerPlan p = dg::sampler_plan(n, batch, vocab, d);
   if (!ws || ws_bytes < p.total)
     return fail(DG_EWORKSPACE, "sampler: workspace %zu < %zu bytes", ws_bytes, p.total);
   if (!aligned16(ws)) return fail(DG_EINVAL, "sampler: workspace misaligned");
@@ -194,15 +208,23 @@ int dg_sampler_step_eb(const float* logits, const void* emb, int32_t* ids, uint8
                        float* z, float* entropy, int32_t* argmax, dg_eb_status* status,
                        dg_ctrl* ctrl, float budget, float stop_entropy, int n, int vocab, int d,
                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  return dg_sampler_step_eb_batched(logits, emb, ids, accepted, z, entropy, argmax, status, ctrl, budget,
+                                    stop_entropy, n, 1, vocab, d, ws, ws_bytes, stream);
+}
+
+int dg_sampler_step_eb_batched(const float* logits, const void* emb, int32_t* ids, uint8_t* accepted,
+                               float* z, float* entropy, int32_t* argmax, dg_eb_status* status,
+                               dg_ctrl* ctrl, float budget, float stop_entropy, int n, int batch,
+                               int vocab, int d, void* ws, size_t ws_bytes, hipStream_t stream) {
   // n_uncommitted is not used in this mode; pass a non-null stand-in to the shared check
   int st = check_sampler(logits, emb, ids, accepted, z, reinterpret_cast<const uint32_t*>(status),
-                         ctrl, n, vocab, d);
+                         ctrl, n, vocab, d, batch);
   if (st != DG_OK) return st;
   if (!argmax || !status) return fail(DG_EINVAL, "sampler_eb: null argmax or status");
   if (!(budget >= 0.f) || !std::isfinite(budget)) return fail(DG_EINVAL, "sampler_eb: budget must be finite and >= 0");
   if (!(stop_entropy >= 0.f) || !std::isfinite(stop_entropy))
     return fail(DG_EINVAL, "sampler_eb: stop_entropy must be finite and >= 0");
-  const dg::SamplerPlan p = dg::sampler_plan(n, vocab, d);
+  const dg::SamplerPlan p = dg::sampler_plan(n, batch, vocab, d);
   if (!ws || ws_bytes < p.total)
     return fail(DG_EWORKSPACE, "sampler_eb: workspace %zu < %zu bytes", ws_bytes, p.total);
   if (!aligned16(ws)) return fail(DG_EINVAL, "sampler_eb: workspace misaligned");
@@ -228,7 +250,7 @@ int dg_denoise_step(const void* q, const void* kp, const void* vp, const void* k
   const dg::AttnPlan ap = dg::attn_plan(n, np, hq, hkv, d);
   hipError_t e = dg::launch_attention(ap, q, kp, vp, kc, vc, attn_out, dtype == DG_BF16, scale, ws, stream);
   if (e != hipSuccess) return hip_fail(e, "denoise attention launch");
-  const dg::SamplerPlan sp = dg::sampler_plan(n, vocab, dm);
+  const dg::SamplerPlan sp = dg::sampler_plan(n, 1, vocab, dm);
   e = dg::launch_sampler(sp, logits, emb, ids, committed, z, conf, n_unc, ctrl, ws, stream);
   if (e != hipSuccess) return hip_fail(e, "denoise sampler launch");
   return DG_OK;

@@ -17,7 +17,11 @@ void prof_end(hipStream_t s);
 
 // ---- sampler ----
 struct SamplerPlan {
-  int n, vocab, d;
+  int n;             // rows over the whole batch (n_canvas * batch)
+  int n_canvas;      // rows per canvas
+  int batch;         // canvases, each with its own control block
+  int n_mt;          // 256-row image / contraction tiles
+  int vocab, d;
   int n_kb;          // 16-id k-blocks of the vocabulary
   int n_tiles;       // 256-column tiles of d
   int col_pad;       // d rounded up to whole tiles
@@ -33,7 +37,7 @@ struct EbCall {
   int32_t* argmax;          // [n] in/out
   dg_eb_status* status;
 };
-SamplerPlan sampler_plan(int n, int vocab, int d);
+SamplerPlan sampler_plan(int n_canvas, int batch, int vocab, int d);
 size_t embedding_packed_bytes(int vocab, int d);
 hipError_t launch_embedding_pack(const float* emb, void* packed, int vocab, int d, hipStream_t s);
 hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void* emb_packed,

@@ -126,8 +126,8 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
                                                               const dg_ctrl* __restrict__ ctrl,
                                                               StatsPartial* __restrict__ part,
                                                               uint8_t* __restrict__ pimg, int n_rows,
-                                                              int vocab, int kb_per_split, int n_kb,
-                                                              bool want_h) {
+                                                              int n_canvas, int vocab, int kb_per_split,
+                                                              int n_kb, bool want_h) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[kStatsLanes * kStatsRows * kImgRow];
   __shared__ StatsPartial red[kStatsRows][kStatsWavesPerRow];
   const int split = blockIdx.x;
@@ -139,7 +139,10 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
   const int row0 = blockIdx.y * kStatsRows;
   const int row = row0 + r;
   const bool row_ok = row < n_rows;
-  const dg_ctrl cb = *ctrl;
+  // rows of canvas c are c * n_canvas .. ; each canvas has its own control block
+  const dg_ctrl cb = ctrl[row_ok ? row / n_canvas : 0];
+  const uint32_t pos = (uint32_t)(row % n_canvas);   // position within the canvas
+  const int mt = row0 / kGM;                         // 256-row image tile of this row
   const float temp = temperature(cb);
   const float inv_t = 1.0f / temp;
   const bool tempered = inv_t != 1.0f;
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
     if (gumbel) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const Philox4 h = philox4x32_10((uint32_t)(j >> 2) + q, (uint32_t)row, cb.gstep, kStreamGumbel, k0, k1);
+        const Philox4 h = philox4x32_10((uint32_t)(j >> 2) + q, pos, cb.gstep, kStreamGumbel, k0, k1);
         const uint32_t hw[4] = {h.w0, h.w1, h.w2, h.w3};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -251,7 +254,8 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
       const int kb = base + kbl;
       if (kb < kb1 && row0 + off / (kImgRow / 16) < n_rows) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(stage + c * 16);
-        *reinterpret_cast<u32x4*>(pimg + (size_t)kb * kPImg + (size_t)row0 * kImgRow + off * 16) = w;
+        *reinterpret_cast<u32x4*>(pimg + ((size_t)mt * n_kb + kb) * kPImg + (size_t)(row0 % kGM) * kImgRow +
+                                  off * 16) = w;
       }
     }
     __syncthreads();
@@ -403,20 +407,24 @@ __device__ __forceinline__ void gemm_iter(int s, uint8_t* smem, Frags& cur, Frag
 __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restrict__ pimg,
                                                           const uint8_t* __restrict__ eimg,
                                                           float* __restrict__ zp, int n_rows, int d,
-                                                          int col_pad, int n_tiles, int kb_per_split,
-                                                          int n_kb) {
+                                                          int col_pad, int n_tiles, int n_mt,
+                                                          int kb_per_split, int n_kb) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
 
   // Workgroups are dealt round-robin to the 8 XCDs; renumber them so the
   // d-tiles of one vocabulary split sit on the same XCD and share its L2 copy
-  // of the p images.
+  // of the p images, and (with several 256-row tiles, i.e. a batch of
+  // canvases) the row tiles of one (split, d-tile) run side by side and share
+  // its E tiles.
   const int nwg = gridDim.x;
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
   const int per = nwg >> 3, rem = nwg & 7;
   const int lin = xcd * per + min(xcd, rem) + slot;
-  const int tile = lin % n_tiles;
-  const int split = lin / n_tiles;
+  const int mt = lin % n_mt;
+  const int tile = (lin / n_mt) % n_tiles;
+  const int split = lin / (n_mt * n_tiles);
+  pimg += (size_t)mt * n_kb * kPImg;
   const int col0 = tile * kGN;
   const int kb0 = split * kb_per_split;
   const int nsteps = min(n_kb, kb0 + kb_per_split) - kb0;
@@ -478,7 +486,7 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
       const int col = col0 + 64 * wn + 32 * nb + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = 128 * wm + 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int row = kGM * mt + 128 * wm + 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (row < n_rows && col < d) out[(size_t)row * d + col] = acc[mb][nb][v];
       }
     }
@@ -496,11 +504,12 @@ __global__ __launch_bounds__(256) void samp_combine(const float* __restrict__ lo
                                                     int32_t* __restrict__ ids,
                                                     uint8_t* __restrict__ committed,
                                                     float* __restrict__ z, float* __restrict__ conf,
-                                                    int n_rows, int vocab, int d, EbRows eb) {
+                                                    int n_rows, int n_canvas, int vocab, int d,
+                                                    EbRows eb) {
   const int row = blockIdx.y;
   __shared__ float s_w[256];
   __shared__ uint32_t s_bad;
-  const dg_ctrl cb = *ctrl;
+  const dg_ctrl cb = ctrl[row / n_canvas];
   const float temp = temperature(cb);
   const float inv_t = 1.0f / temp;
   const float c_t = kLog2e * inv_t;
@@ -548,7 +557,7 @@ __global__ __launch_bounds__(256) void samp_combine(const float* __restrict__ lo
             ids[row] = (int32_t)cand;
             committed[row] = 1;
           } else if (!(cb.flags & DG_COMMIT_ONLY)) {
-            const Philox4 h = philox4x32_10(0u, (uint32_t)row, cb.gstep, kStreamRenoise,
+            const Philox4 h = philox4x32_10(0u, (uint32_t)(row % n_canvas), cb.gstep, kStreamRenoise,
                                             seed_lo(cb.seed), seed_hi(cb.seed));
             ids[row] = (int32_t)range_draw(h.w0, (uint32_t)vocab);
           }
@@ -583,15 +592,17 @@ __global__ __launch_bounds__(256) void samp_combine(const float* __restrict__ lo
 
 __global__ __launch_bounds__(256) void samp_finalize(const uint8_t* __restrict__ committed,
                                                      uint32_t* __restrict__ n_unc,
-                                                     dg_ctrl* __restrict__ ctrl, int n_rows) {
+                                                     dg_ctrl* __restrict__ ctrl, int n_canvas) {
+  // workgroup b handles canvas b
+  const int b = blockIdx.x;
   const int t = threadIdx.x;
-  const int open = (t < n_rows && !committed[t]) ? 1 : 0;
+  const int open = (t < n_canvas && !committed[(size_t)b * n_canvas + t]) ? 1 : 0;
   const int count = __syncthreads_count(open);
   if (t == 0) {
-    n_unc[0] = (uint32_t)count;
-    if (ctrl->flags & DG_AUTO_ADVANCE) {
-      ctrl->gstep += 1u;
-      ctrl->s_in_block += 1u;
+    n_unc[b] = (uint32_t)count;
+    if (ctrl[b].flags & DG_AUTO_ADVANCE) {
+      ctrl[b].gstep += 1u;
+      ctrl[b].s_in_block += 1u;
     }
   }
 }
@@ -617,6 +628,13 @@ __global__ __launch_bounds__(256) void samp_eb_select(EbRows eb, int32_t* __rest
   __shared__ double csum[256];
   __shared__ uint8_t acc[256];
   const int t = threadIdx.x;
+  // workgroup b handles canvas b (rows b * n_rows ..)
+  {
+    const size_t o = (size_t)blockIdx.x * n_rows;
+    eb.ent += o; eb.cand += o; eb.argmax += o;
+    ids += o; accepted += o; prev_argmax += o;
+    status += blockIdx.x; ctrl += blockIdx.x;
+  }
   const dg_ctrl cb = *ctrl;
   const float h = (t < n_rows) ? eb.ent[t] : __builtin_nanf("");
   const bool defined = t < n_rows && !(h != h);
@@ -702,13 +720,15 @@ hipError_t launch_embedding_pack(const float* emb, void* packed, int vocab, int 
   return hipGetLastError();
 }
 
-SamplerPlan sampler_plan(int n, int vocab, int d) {
+SamplerPlan sampler_plan(int n_canvas, int batch, int vocab, int d) {
   SamplerPlan p{};
-  p.n = n; p.vocab = vocab; p.d = d;
+  const int n = n_canvas * batch;
+  p.n = n; p.n_canvas = n_canvas; p.batch = batch; p.vocab = vocab; p.d = d;
+  p.n_mt = (n + kGM - 1) / kGM;
   p.n_kb = (vocab + kKB - 1) / kKB;
   p.n_tiles = (d + kGN - 1) / kGN;
   p.col_pad = p.n_tiles * kGN;
-  int splits = 256 / p.n_tiles;
+  int splits = 256 / (p.n_tiles * p.n_mt);
   if (splits < 1) splits = 1;
   const int by_len = (p.n_kb + 15) / 16;     // at least 16 k-blocks per split
   if (splits > by_len) splits = by_len;
@@ -720,7 +740,7 @@ SamplerPlan sampler_plan(int n, int vocab, int d) {
   p.n_splits = (p.n_kb + p.kb_per_split - 1) / p.kb_per_split;
   p.off_stats = 0;
   p.off_pimg = align_up((size_t)n * p.n_splits * sizeof(StatsPartial), 256);
-  p.off_zp = p.off_pimg + align_up((size_t)p.n_kb * kPImg, 256);
+  p.off_zp = p.off_pimg + align_up((size_t)p.n_mt * p.n_kb * kPImg, 256);
   p.off_eb = p.off_zp + align_up((size_t)p.n_splits * n * d * sizeof(float), 256);
   p.total = p.off_eb + 3 * align_up((size_t)n * 4, 256);
   return p;
@@ -743,40 +763,40 @@ hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void*
   prof_begin("samp_stats", s);
   const dim3 sgrid(p.n_splits, (p.n + kStatsRows - 1) / kStatsRows);
   if (aligned)
-    samp_stats<true><<<sgrid, kStatsThreadsWG, 0, s>>>(logits, ctrl, part, pimg, p.n, p.vocab,
+    samp_stats<true><<<sgrid, kStatsThreadsWG, 0, s>>>(logits, ctrl, part, pimg, p.n, p.n_canvas, p.vocab,
                                                        p.kb_per_split, p.n_kb, eb.on);
   else
-    samp_stats<false><<<sgrid, kStatsThreadsWG, 0, s>>>(logits, ctrl, part, pimg, p.n, p.vocab,
+    samp_stats<false><<<sgrid, kStatsThreadsWG, 0, s>>>(logits, ctrl, part, pimg, p.n, p.n_canvas, p.vocab,
                                                         p.kb_per_split, p.n_kb, eb.on);
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   prof_begin("samp_gemm", s);
-  samp_gemm<<<p.n_tiles * p.n_splits, kGThreads, 0, s>>>(pimg, static_cast<const uint8_t*>(emb_packed),
-                                                         zp, p.n, p.d, p.col_pad, p.n_tiles,
-                                                         p.kb_per_split, p.n_kb);
+  samp_gemm<<<p.n_mt * p.n_tiles * p.n_splits, kGThreads, 0, s>>>(
+      pimg, static_cast<const uint8_t*>(emb_packed), zp, p.n, p.d, p.col_pad, p.n_tiles, p.n_mt,
+      p.kb_per_split, p.n_kb);
   prof_end(s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   prof_begin("samp_combine", s);
   samp_combine<<<dim3((p.d + 1023) / 1024, p.n), 256, 0, s>>>(logits, part, p.n_splits, zp, ctrl, ids,
-                                                              committed, z, conf, p.n, p.vocab, p.d,
-                                                              rows);
+                                                              committed, z, conf, p.n, p.n_canvas,
+                                                              p.vocab, p.d, rows);
   prof_end(s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   if (eb.on) {
     prof_begin("samp_eb_select", s);
-    samp_eb_select<<<1, 256, 0, s>>>(rows, ids, committed, eb.argmax, eb.status, ctrl, eb.budget,
-                                     eb.stop_entropy, p.n, p.vocab);
+    samp_eb_select<<<p.batch, 256, 0, s>>>(rows, ids, committed, eb.argmax, eb.status, ctrl, eb.budget,
+                                           eb.stop_entropy, p.n_canvas, p.vocab);
     prof_end(s);
     return hipGetLastError();
   }
   prof_begin("samp_finalize", s);
-  samp_finalize<<<1, 256, 0, s>>>(committed, n_unc, ctrl, p.n);
+  samp_finalize<<<p.batch, 256, 0, s>>>(committed, n_unc, ctrl, p.n_canvas);
   prof_end(s);
   return hipGetLastError();
 }

@@ -216,6 +216,31 @@ int dg_sampler_step_eb(const float* logits, const void* emb_packed, int32_t* can
                        int n_canvas, int vocab, int d_model,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * A batch of canvases in one sampler pass: `batch` independent canvases of
+ * n_canvas positions each (independent requests), whose logits, ids, masks,
+ * selfcond and confidence rows are stacked canvas after canvas
+ * ([batch * n_canvas, ...]).  Each canvas has its own control block
+ * (ctrl[batch], device) and open-position count (n_uncommitted[batch]); its
+ * random draws use its own seed and step and the position within the canvas,
+ * so canvas b's results are exactly those of dg_sampler_step on canvas b
+ * alone.  The batch shares one pass over the embedding table, which raises
+ * the contraction's arithmetic intensity by `batch`.
+ *   batch in [1, 4096]; n_canvas * batch * vocab * 4 < 2^32.
+ */
+size_t dg_sampler_workspace_bytes_batched(int n_canvas, int batch, int vocab, int d_model);
+int dg_sampler_step_batched(const float* logits, const void* emb_packed, int32_t* canvas_ids,
+                            uint8_t* committed, float* selfcond, float* confidence,
+                            uint32_t* n_uncommitted, dg_ctrl* ctrl,
+                            int n_canvas, int batch, int vocab, int d_model,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+/* Entropy-bounded step over a batch (status[batch], argmax rows stacked). */
+int dg_sampler_step_eb_batched(const float* logits, const void* emb_packed, int32_t* canvas_ids,
+                               uint8_t* accepted, float* selfcond, float* entropy, int32_t* argmax,
+                               dg_eb_status* status, dg_ctrl* ctrl, float budget, float stop_entropy,
+                               int n_canvas, int batch, int vocab, int d_model,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Whole denoising step and its graph                                        */
 /* ------------------------------------------------------------------------ */

@@ -155,3 +155,15 @@ def test_attention_ex_flags(lib):
     assert lib.dg_canvas_attention_ex(*a, 2, FAKE, 0, None) == DG_EINVAL     # unknown flag bit
     assert b"flag" in lib.dg_last_error()
     assert lib.dg_canvas_attention_ex(*a[:6], 0, 8, 8, 4, 64, 1, 0.0, 1, FAKE, 0, None) == DG_EINVAL
+
+
+def test_batched_sampler_arguments(lib):
+    from block_text_diffusion_amd._lib import DG_EINVAL, DG_EUNSUPPORTED, DG_EWORKSPACE
+    one = lib.dg_sampler_workspace_bytes(256, 262144, 3072)
+    four = lib.dg_sampler_workspace_bytes_batched(256, 4, 262144, 3072)
+    assert lib.dg_sampler_workspace_bytes_batched(256, 1, 262144, 3072) == one and four > 3 * one
+    assert lib.dg_sampler_workspace_bytes_batched(256, 0, 1000, 64) == 0
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE]
+    assert lib.dg_sampler_step_batched(*a, 16, 0, 1000, 64, FAKE, 0, None) == DG_EINVAL
+    assert lib.dg_sampler_step_batched(*a, 256, 64, 262144, 64, FAKE, 0, None) == DG_EUNSUPPORTED  # > 2^32 bytes
+    assert lib.dg_sampler_step_batched(*a, 16, 4, 1000, 64, FAKE, 16, None) == DG_EWORKSPACE
