@@ -90,37 +90,41 @@ __device__ __forceinline__ void merge_partial(StatsPartial& r, const StatsPartia
   r.bad |= o.bad;
 }
 
-// 16 logits of one k-block (ids >= vocab read as -inf).
+// 4 logits from id j on (ids >= vocab read as -inf); with 16-byte aligned rows
+// (kAligned: vocab % 4 == 0) a group is wholly inside or outside the row.
 template <bool kAligned>
-__device__ __forceinline__ void load16(const float* __restrict__ x, int j, int vocab, float (&v)[16]) {
-  if (kAligned && j + 15 < vocab) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 w = *reinterpret_cast<const f32x4*>(x + j + 4 * q);
-      v[4 * q] = w[0]; v[4 * q + 1] = w[1]; v[4 * q + 2] = w[2]; v[4 * q + 3] = w[3];
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = (j + e < vocab) ? x[j + e] : -INFINITY;
+__device__ __forceinline__ f32x4 load4(const float* __restrict__ x, int j, int vocab) {
+  if (kAligned) {
+    if (j < vocab) return *reinterpret_cast<const f32x4*>(x + j);
+    return (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   }
+  f32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = (j + e < vocab) ? x[j + e] : -INFINITY;
+  return v;
 }
 
-constexpr int kStatsRows = 1;                            // canvas rows per workgroup
+constexpr int kStatsRows = 2;                            // canvas rows per workgroup
 constexpr int kStatsWavesPerRow = 4;
 constexpr int kStatsLanes = 64 * kStatsWavesPerRow;      // lanes sharing one row
-constexpr int kStatsIters = 4;                           // k-blocks held per lane
+constexpr int kStatsIters = 4;                           // rounds of kStatsLanes k-blocks
+constexpr int kStatsChunks = 4 * kStatsIters;            // 4-id groups held per lane
 constexpr int kMaxKbPerSplit = kStatsLanes * kStatsIters;
 constexpr int kStatsThreadsWG = 64 * kStatsRows * kStatsWavesPerRow;
 
-// grid (n_splits, n_rows), 4 waves per row (four workgroups share a CU, so
+// grid (n_splits, ceil(n_rows / 2)), two rows per workgroup, 4 waves per row (two rows
+// fill whole 128-byte lines of the p image; two workgroups share a CU, so
 // some load while others store).
-// Lane L of a row holds k-blocks kb0 + L + 256 i (i < 4) of the split in
-// registers, so the logits are read from HBM once: the split maximum is
-// reduced first, then the same registers give exp(l - m_s), the sums and the
-// bf16 hi/lo p images.  Each round's image rows are staged in LDS as
-// [k-block][64 B] and leave as 1 KB per store instruction (16 k-blocks' slots
-// of the row; staging through LDS measured faster than storing straight
-// from the registers).
+// Round i covers k-blocks kb0 + 256 i .. kb0 + 256 i + 255 of the split.  In
+// it, lane L holds the 4-id groups c = 4 i .. 4 i + 3, group c starting at id
+// 16 kb0 + 4 (256 c + L): every load instruction of the row reads 1 KB of
+// consecutive logits, and lanes 4k .. 4k + 3 hold one k-block.  The logits
+// are read from HBM once and kept in registers: the split maximum is reduced
+// first, then the same registers give exp(l - m_s), the sums and the bf16
+// hi/lo p images.  Each round's image slots are staged in LDS as
+// [k-block][2 rows][64 B] and leave as 1 KB per store instruction (8 k-blocks'
+// 128-byte lines; staging through LDS measured faster than storing from the
+// registers, and whole lines measured faster than one row's 64-byte halves).
 template <bool kAligned>
 __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __restrict__ logits,
                                                               const dg_ctrl* __restrict__ ctrl,
@@ -152,17 +156,16 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
   const float* x = logits + (size_t)(row_ok ? row : 0) * (size_t)vocab;
   const int kb0 = split * kb_per_split;
   const int kb1 = min(n_kb, kb0 + kb_per_split);
+  const int id_end = min(vocab, kb1 * kKB);          // first id past this split
 
-  float v[kStatsIters][16];
+  // group c: first id, and whether it lies in the split
+  auto gid0 = [&](int c) { return kb0 * kKB + 4 * (kStatsLanes * c + L); };
+  f32x4 v[kStatsChunks];
 #pragma unroll
-  for (int i = 0; i < kStatsIters; ++i) {
-    const int kb = kb0 + L + kStatsLanes * i;
-    if (row_ok && kb < kb1) {
-      load16<kAligned>(x, kb * kKB, vocab, v[i]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) v[i][e] = -INFINITY;
-    }
+  for (int c = 0; c < kStatsChunks; ++c) {
+    const int j = gid0(c);
+    if (row_ok && j < id_end) v[c] = load4<kAligned>(x, j, id_end);
+    else v[c] = (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   }
 
   // max, argmax, Gumbel argmax, undefined values
@@ -172,25 +175,21 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
   uint32_t gid = 0xFFFFFFFFu;
   uint32_t bad = 0;
 #pragma unroll
-  for (int i = 0; i < kStatsIters; ++i) {
-    const int kb = kb0 + L + kStatsLanes * i;
-    if (!(row_ok && kb < kb1)) continue;
-    const int j = kb * kKB;
+  for (int c = 0; c < kStatsChunks; ++c) {
+    const int j = gid0(c);
+    if (!(row_ok && j < id_end)) continue;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      bad |= (v[i][e] != v[i][e]) | (v[i][e] == INFINITY);
-      if (v[i][e] > m) { m = v[i][e]; bid = (uint32_t)(j + e); }
+    for (int e = 0; e < 4; ++e) {
+      bad |= (v[c][e] != v[c][e]) | (v[c][e] == INFINITY);
+      if (v[c][e] > m) { m = v[c][e]; bid = (uint32_t)(j + e); }
     }
     if (gumbel) {
+      const Philox4 h = philox4x32_10((uint32_t)(j >> 2), pos, cb.gstep, kStreamGumbel, k0, k1);
+      const uint32_t hw[4] = {h.w0, h.w1, h.w2, h.w3};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const Philox4 h = philox4x32_10((uint32_t)(j >> 2) + q, pos, cb.gstep, kStreamGumbel, k0, k1);
-        const uint32_t hw[4] = {h.w0, h.w1, h.w2, h.w3};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float sc = v[i][4 * q + e] * inv_t + gumbel_from_bits(hw[e]);
-          if (sc > gbest) { gbest = sc; gid = (uint32_t)(j + 4 * q + e); }
-        }
+      for (int e = 0; e < 4; ++e) {
+        const float sc = v[c][e] * inv_t + gumbel_from_bits(hw[e]);
+        if (sc > gbest) { gbest = sc; gid = (uint32_t)(j + e); }
       }
     }
   }
@@ -220,27 +219,28 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
   for (int i = 0; i < kStatsIters; ++i) {
     const int base = kb0 + kStatsLanes * i;
     if (base >= kb1) break;   // uniform over the workgroup
-    {
-      float pp[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i][e], kLog2e, mc));
+    for (int q = 0; q < 4; ++q) {
+      const int c = 4 * i + q;
+      float pp[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[c][e], kLog2e, mc));
         s1 += pp[e];
         if (tempered || want_h) {
-          const float y = fmaxf((v[i][e] - m) * c_t, -200.f);   // log2 of the tempered weight
+          const float y = fmaxf((v[c][e] - m) * c_t, -200.f);   // log2 of the tempered weight
           const float et = tempered ? __builtin_amdgcn_exp2f(y) : pp[e];
           st += et;
           if (want_h) sy += et * y;
         }
       }
-      uint32_t hi[8], lo[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) split2(pp[2 * e], pp[2 * e + 1], hi[e], lo[e]);
-      uint8_t* dst = stage + (L * kStatsRows + r) * kImgRow;
-      *reinterpret_cast<u32x4*>(dst) = (u32x4){hi[0], hi[1], hi[2], hi[3]};
-      *reinterpret_cast<u32x4*>(dst + 16) = (u32x4){hi[4], hi[5], hi[6], hi[7]};
-      *reinterpret_cast<u32x4*>(dst + 32) = (u32x4){lo[0], lo[1], lo[2], lo[3]};
-      *reinterpret_cast<u32x4*>(dst + 48) = (u32x4){lo[4], lo[5], lo[6], lo[7]};
+      uint32_t hi[2], lo[2];
+      split2(pp[0], pp[1], hi[0], lo[0]);
+      split2(pp[2], pp[3], hi[1], lo[1]);
+      // k-block 64 q + L / 4 of the round, ids 4 (L % 4) .. 4 (L % 4) + 3 of it
+      uint8_t* dst = stage + ((kStatsLanes / 4 * q + L / 4) * kStatsRows + r) * kImgRow + (L % 4) * 8;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(hi[0], hi[1]);
+      *reinterpret_cast<uint2*>(dst + 32) = make_uint2(lo[0], lo[1]);
     }
     __syncthreads();
     // write-out: the row slots of k-block kbl are contiguous; thread T moves
