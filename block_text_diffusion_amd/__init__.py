@@ -14,6 +14,7 @@ from ._lib import (DG_ATTN_CAUSAL, DG_AUTO_ADVANCE, DG_BF16, DG_COMMIT_ONLY, DG_
 __all__ = [
     "dg_canvas_attention", "dg_sampler_step", "dg_sampler_step_eb", "read_eb_status",
     "dg_sampler_step_batched", "dg_sampler_step_eb_batched", "dg_sampler_workspace_bytes_batched",
+    "dg_sampler_step_topk", "dg_sampler_step_eb_topk", "dg_sampler_workspace_bytes_topk",
     "stack_ctrl", "dg_embedding_pack", "dg_embedding_packed_bytes", "dg_denoise_step", "StepGraph", "dg_canvas_init",
     "dg_kv_append", "dg_synth_logits", "dg_philox_fill", "dg_attention_workspace_bytes",
     "dg_sampler_workspace_bytes", "dg_denoise_workspace_bytes", "dg_profile_enable",
@@ -228,6 +229,51 @@ def dg_sampler_step_eb_batched(logits, emb_packed, canvas_ids, accepted, selfcon
                                             _ptr(selfcond), _ptr(entropy), _ptr(argmax), _ptr(status),
                                             _ptr(ctrl), float(budget), float(stop_entropy), n, batch, vocab,
                                             d, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def dg_sampler_workspace_bytes_topk(n, batch, vocab, d_model, top_k):
+    return load().dg_sampler_workspace_bytes_topk(n, batch, vocab, d_model, top_k)
+
+
+def dg_sampler_step_topk(logits, emb, canvas_ids, committed, selfcond, confidence, n_uncommitted, ctrl,
+                         top_k, batch=1, workspace=None, stream=None):
+    """Top-k truncated threshold step over `batch` stacked canvases; emb is the
+    plain fp32 table [V, d] (not the packed image)."""
+    torch = _torch()
+    _need(logits, "logits", (torch.float32,)); _need(emb, "emb", (torch.float32,))
+    _need(canvas_ids, "canvas_ids", (torch.int32,)); _need(committed, "committed", (torch.uint8,))
+    _need(selfcond, "selfcond", (torch.float32,)); _need(n_uncommitted, "n_uncommitted", (torch.int32, torch.uint32))
+    _need(ctrl, "ctrl", (torch.uint8,))
+    rows, vocab = logits.shape
+    if rows % batch or ctrl.numel() < 40 * batch or n_uncommitted.numel() < batch:
+        raise ValueError("rows must split into `batch` canvases with a control block and a count each")
+    n = rows // batch
+    d = selfcond.shape[1]
+    if tuple(emb.shape) != (vocab, d):
+        raise ValueError("emb must be [vocab, d_model]")
+    ws = _workspace(dg_sampler_workspace_bytes_topk(n, batch, vocab, d, top_k), logits.device, workspace)
+    check(load().dg_sampler_step_topk(_ptr(logits), _ptr(emb), _ptr(canvas_ids), _ptr(committed),
+                                      _ptr(selfcond), _ptr(confidence), _ptr(n_uncommitted), _ptr(ctrl),
+                                      n, batch, vocab, d, top_k, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def dg_sampler_step_eb_topk(logits, emb, canvas_ids, accepted, selfcond, entropy, argmax, status, ctrl,
+                            top_k, batch=1, budget=0.1, stop_entropy=0.005, workspace=None, stream=None):
+    """Top-k truncated entropy-bounded step; emb is the plain fp32 table [V, d]."""
+    torch = _torch()
+    _need(logits, "logits", (torch.float32,)); _need(emb, "emb", (torch.float32,))
+    rows, vocab = logits.shape
+    if rows % batch or ctrl.numel() < 40 * batch or status.numel() < 16 * batch:
+        raise ValueError("rows must split into `batch` canvases with a control block and a status each")
+    n = rows // batch
+    d = selfcond.shape[1]
+    if tuple(emb.shape) != (vocab, d):
+        raise ValueError("emb must be [vocab, d_model]")
+    ws = _workspace(dg_sampler_workspace_bytes_topk(n, batch, vocab, d, top_k), logits.device, workspace)
+    check(load().dg_sampler_step_eb_topk(_ptr(logits), _ptr(emb), _ptr(canvas_ids), _ptr(accepted),
+                                         _ptr(selfcond), _ptr(entropy), _ptr(argmax), _ptr(status), _ptr(ctrl),
+                                         float(budget), float(stop_entropy), n, batch, vocab, d, top_k,
+                                         _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def read_eb_status(status_t, index=0):

@@ -75,6 +75,10 @@ SIGNATURES = {
     "dg_sampler_step_batched": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
     "dg_sampler_step_eb_batched": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _i, _i, _i, _i,
                                         _vp, _sz, _vp]),
+    "dg_sampler_workspace_bytes_topk": (_sz, [_i, _i, _i, _i, _i]),
+    "dg_sampler_step_topk": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "dg_sampler_step_eb_topk": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _i, _i, _i, _i, _i,
+                                     _vp, _sz, _vp]),
     "dg_denoise_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "dg_denoise_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]),

@@ -96,6 +96,17 @@ int check_sampler(const float* logits, const void* emb, const int32_t* ids, cons
   return DG_OK;
 }
 
+int check_topk(int k, const dg::TopkPlan& p, void* ws, size_t ws_bytes, const char* who) {
+  if (k < 1) return fail(DG_EINVAL, "%s: top_k < 1", who);
+  if (k > 256) return fail(DG_EUNSUPPORTED, "%s: top_k > 256", who);
+  if ((int64_t)p.n_slices * k > p.max_candidates)
+    return fail(DG_EUNSUPPORTED, "%s: ceil(vocab / 16384) * top_k = %lld exceeds %d", who,
+                (long long)p.n_slices * k, p.max_candidates);
+  if (!ws || ws_bytes < p.total) return fail(DG_EWORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, p.total);
+  if (!aligned16(ws)) return fail(DG_EINVAL, "%s: workspace misaligned", who);
+  return DG_OK;
+}
+
 }  // namespace
 
 namespace dg {
@@ -231,6 +242,49 @@ int dg_sampler_step_eb_batched(const float* logits, const void* emb, int32_t* id
   const dg::EbCall eb{true, budget, stop_entropy, entropy, argmax, status};
   hipError_t e = dg::launch_sampler(p, logits, emb, ids, accepted, z, nullptr, nullptr, ctrl, ws, stream, eb);
   if (e != hipSuccess) return hip_fail(e, "sampler_eb launch");
+  return DG_OK;
+}
+
+size_t dg_sampler_workspace_bytes_topk(int n, int batch, int vocab, int d, int k) {
+  if (n < 1 || n > 256 || batch < 1 || batch > 4096 || vocab < 2 || d < 1 || k < 1 || k > 256) return 0;
+  return dg::topk_plan(n, batch, vocab, d, k).total;
+}
+
+int dg_sampler_step_topk(const float* logits, const float* emb, int32_t* ids, uint8_t* committed, float* z,
+                         float* conf, uint32_t* n_unc, dg_ctrl* ctrl, int n, int batch, int vocab, int d,
+                         int k, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, d, batch);
+  if (st != DG_OK) return st;
+  if (k < 1 || k > 256) return fail(k < 1 ? DG_EINVAL : DG_EUNSUPPORTED, "sampler_topk: top_k must be in [1, 256]");
+  const dg::TopkPlan p = dg::topk_plan(n, batch, vocab, d, k);
+  st = check_topk(k, p, ws, ws_bytes, "sampler_topk");
+  if (st != DG_OK) return st;
+  hipError_t e = dg::launch_sampler_topk(p, logits, emb, ids, committed, z, conf, n_unc, ctrl, ws, stream,
+                                         dg::EbCall{false, 0.f, 0.f, nullptr, nullptr, nullptr});
+  if (e != hipSuccess) return hip_fail(e, "sampler_topk launch");
+  return DG_OK;
+}
+
+int dg_sampler_step_eb_topk(const float* logits, const float* emb, int32_t* ids, uint8_t* accepted, float* z,
+                            float* entropy, int32_t* argmax, dg_eb_status* status, dg_ctrl* ctrl, float budget,
+                            float stop_entropy, int n, int batch, int vocab, int d, int k, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  int st = check_sampler(logits, emb, ids, accepted, z, reinterpret_cast<const uint32_t*>(status), ctrl, n,
+                         vocab, d, batch);
+  if (st != DG_OK) return st;
+  if (!argmax || !status) return fail(DG_EINVAL, "sampler_eb_topk: null argmax or status");
+  if (!(budget >= 0.f) || !std::isfinite(budget))
+    return fail(DG_EINVAL, "sampler_eb_topk: budget must be finite and >= 0");
+  if (!(stop_entropy >= 0.f) || !std::isfinite(stop_entropy))
+    return fail(DG_EINVAL, "sampler_eb_topk: stop_entropy must be finite and >= 0");
+  if (k < 1 || k > 256)
+    return fail(k < 1 ? DG_EINVAL : DG_EUNSUPPORTED, "sampler_eb_topk: top_k must be in [1, 256]");
+  const dg::TopkPlan p = dg::topk_plan(n, batch, vocab, d, k);
+  st = check_topk(k, p, ws, ws_bytes, "sampler_eb_topk");
+  if (st != DG_OK) return st;
+  const dg::EbCall eb{true, budget, stop_entropy, entropy, argmax, status};
+  hipError_t e = dg::launch_sampler_topk(p, logits, emb, ids, accepted, z, nullptr, nullptr, ctrl, ws, stream, eb);
+  if (e != hipSuccess) return hip_fail(e, "sampler_eb_topk launch");
   return DG_OK;
 }
 

@@ -45,6 +45,19 @@ hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void*
                           uint32_t* n_unc, dg_ctrl* ctrl, void* ws, hipStream_t s,
                           const EbCall& eb = EbCall{false, 0.f, 0.f, nullptr, nullptr, nullptr});
 
+// ---- top-k truncated sampler ----
+struct TopkPlan {
+  int n, n_canvas, batch, vocab, d;
+  int k;               // kept logits per row
+  int n_slices;        // 16384-id slices of the vocabulary
+  int max_candidates;  // slice candidates one row pass can hold (n_slices * k must not exceed it)
+  size_t off_part, off_cand, off_bad, off_list, off_zp, off_eb, total;
+};
+TopkPlan topk_plan(int n_canvas, int batch, int vocab, int d, int k);
+hipError_t launch_sampler_topk(const TopkPlan& p, const float* logits, const float* emb, int32_t* ids,
+                               uint8_t* committed, float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl,
+                               void* ws, hipStream_t s, const EbCall& eb);
+
 // ---- attention ----
 struct AttnPlan {
   int n, n_prefix, hq, hkv, d, group;

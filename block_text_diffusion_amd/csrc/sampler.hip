@@ -704,6 +704,302 @@ __global__ __launch_bounds__(256) void samp_eb_select(EbRows eb, int32_t* __rest
 }
 
 // ---------------------------------------------------------------------------
+// Top-k truncated sampler.  The pages expect truncating the sampling step to
+// the top k tokens to raise throughput at larger batches (explainer
+// "DiffusionGemma: Google's open diffusion LLM", section "Throughput flips at
+// about 32 concurrent users").  Per row the kept set S is the k largest
+// logits, ties to the smaller id; the step is then the full one on logits
+// with everything outside S at -inf, so the contraction shrinks to k rows of
+// E per canvas row.
+//   topk_slice   per (16384-id slice, row): the slice's own top k by a radix
+//                select over order-preserving keys held in registers (then by
+//                id among equal keys); NaN / +inf flags.
+//   topk_row     per row: the top k of the slices' candidates (same select),
+//                then one split's statistics record (max, argmax, Gumbel
+//                argmax within S, sums at T = 1 and T, entropy term) and the
+//                weights exp(l - m) of S.
+//   topk_z       z_0 = sum over S of exp(l - m) E[id] from the fp32 table.
+//   samp_combine, samp_finalize / samp_eb_select as in the full sampler, with
+//                one split.
+// ---------------------------------------------------------------------------
+constexpr int kTkThreads = 256;
+constexpr int kTkChunks = 16;                          // 4-id groups per thread in a slice
+constexpr int kTkSliceIds = kTkThreads * kTkChunks * 4;  // 16384
+constexpr int kTkRowPer = 32;                          // candidates per thread in the row pass
+
+struct TopkItem {
+  float v;       // logit (slice candidates) or weight exp(l - m) (row list)
+  int32_t id;
+};
+
+// Larger float, larger key (NaN above +inf).
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+struct TkShared {
+  uint32_t hist[256];
+  uint32_t wsum[kTkThreads / kWave];
+  uint32_t res[3];
+};
+
+// Inclusive prefix sum over the workgroup (one value per thread).
+__device__ __forceinline__ uint32_t wg_scan(uint32_t x, TkShared& sh) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh.wsum[w] = x;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) x += sh.wsum[i];
+  __syncthreads();
+  return x;
+}
+
+// The kk-th largest key (1-based) among the workgroup's active elements, by
+// four 8-bit histogram passes from the top byte.  Returns tau, the number of
+// active keys above it (gt) and equal to it (eq).  Needs kk <= number active.
+template <int E, typename KeyF, typename ActF>
+__device__ void wg_select(KeyF keyf, ActF act, uint32_t kk, TkShared& sh, uint32_t& tau, uint32_t& gt,
+                          uint32_t& eq) {
+  const int t = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  gt = 0;
+  eq = 0;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    sh.hist[t] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t k = keyf(e);
+      if (act(e) && (k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // thread t takes bin 255 - t, so its inclusive scan counts the keys in bins >= 255 - t
+    const uint32_t h = sh.hist[255 - t];
+    const uint32_t incl = wg_scan(h, sh);
+    if (incl - h < kk && incl >= kk) {   // exactly one thread
+      sh.res[0] = 255u - (uint32_t)t;
+      sh.res[1] = incl - h;
+      sh.res[2] = h;
+    }
+    __syncthreads();
+    prefix |= sh.res[0] << shift;
+    pmask |= 0xFFu << shift;
+    kk -= sh.res[1];
+    gt += sh.res[1];
+    eq = sh.res[2];
+    __syncthreads();
+  }
+  tau = prefix;
+}
+
+// Cut of the k largest active elements, ties to the smaller id: element e is
+// kept iff key > tau, or key == tau and ~id >= tau2.
+struct TopkCut {
+  uint32_t tau, tau2;
+};
+
+template <int E, typename KeyF, typename IdF, typename ActF>
+__device__ TopkCut wg_topk_cut(KeyF keyf, IdF idf, ActF act, uint32_t k, TkShared& sh) {
+  TopkCut c{0u, 0u};
+  uint32_t gt, eq;
+  wg_select<E>(keyf, act, k, sh, c.tau, gt, eq);
+  const uint32_t need = k - gt;   // equal keys to keep, 1 .. eq (uniform)
+  if (need < eq) {
+    uint32_t g2, e2;
+    const uint32_t tau = c.tau;
+    wg_select<E>([&](int e) { return ~idf(e); }, [&](int e) { return act(e) && keyf(e) == tau; }, need, sh,
+                 c.tau2, g2, e2);
+  }
+  return c;
+}
+
+template <bool kAligned>
+__global__ __launch_bounds__(kTkThreads) void topk_slice(const float* __restrict__ logits,
+                                                         TopkItem* __restrict__ cand,
+                                                         uint8_t* __restrict__ badf, int vocab,
+                                                         int n_slices, int k) {
+  __shared__ TkShared sh;
+  const int slice = blockIdx.x, row = blockIdx.y, t = threadIdx.x;
+  const float* x = logits + (size_t)row * (size_t)vocab;
+  const int base = slice * kTkSliceIds;
+  // group c of thread t: ids base + 4 (256 c + t) .. + 3 (1 KB per load instruction)
+  uint32_t key[4 * kTkChunks];
+  int bad = 0;
+#pragma unroll
+  for (int c = 0; c < kTkChunks; ++c) {
+    const f32x4 v = load4<kAligned>(x, base + 4 * (kTkThreads * c + t), vocab);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bad |= (v[e] != v[e]) | (v[e] == INFINITY);
+      key[4 * c + e] = order_key(v[e]);
+    }
+  }
+  auto idf = [&](int e) { return (uint32_t)(base + 4 * (kTkThreads * (e >> 2) + t) + (e & 3)); };
+  auto all = [](int) { return true; };
+  const TopkCut cut = wg_topk_cut<4 * kTkChunks>([&](int e) { return key[e]; }, idf, all, (uint32_t)k, sh);
+  auto kept = [&](int e) { return key[e] > cut.tau || (key[e] == cut.tau && ~idf(e) >= cut.tau2); };
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int e = 0; e < 4 * kTkChunks; ++e) cnt += kept(e) ? 1u : 0u;
+  uint32_t off = wg_scan(cnt, sh) - cnt;
+  TopkItem* out = cand + ((size_t)row * n_slices + slice) * k;
+#pragma unroll
+  for (int e = 0; e < 4 * kTkChunks; ++e)
+    if (kept(e) && off < (uint32_t)k) out[off++] = TopkItem{key_value(key[e]), (int32_t)idf(e)};
+  bad = __syncthreads_or(bad);
+  if (t == 0) badf[(size_t)row * n_slices + slice] = bad ? 1 : 0;
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_row(const TopkItem* __restrict__ cand,
+                                                       const uint8_t* __restrict__ badf,
+                                                       const dg_ctrl* __restrict__ ctrl,
+                                                       StatsPartial* __restrict__ part,
+                                                       TopkItem* __restrict__ list, int n_slices, int k,
+                                                       int n_canvas, bool want_h) {
+  __shared__ TkShared sh;
+  __shared__ StatsPartial red[kTkThreads / kWave];
+  const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int count = n_slices * k;
+  const TopkItem* src = cand + (size_t)row * count;
+  uint32_t key[kTkRowPer], idv[kTkRowPer];
+#pragma unroll
+  for (int e = 0; e < kTkRowPer; ++e) {
+    const int i = t + kTkThreads * e;
+    if (i < count) {
+      const TopkItem it = src[i];
+      key[e] = order_key(it.v);
+      idv[e] = (uint32_t)it.id;
+    } else {
+      key[e] = 0u;
+      idv[e] = 0xFFFFFFFFu;
+    }
+  }
+  auto act = [&](int e) { return t + kTkThreads * e < count; };
+  const TopkCut cut = wg_topk_cut<kTkRowPer>([&](int e) { return key[e]; }, [&](int e) { return idv[e]; }, act,
+                                             (uint32_t)k, sh);
+  auto kept = [&](int e) {
+    return act(e) && (key[e] > cut.tau || (key[e] == cut.tau && ~idv[e] >= cut.tau2));
+  };
+
+  const dg_ctrl cb = ctrl[row / n_canvas];
+  const uint32_t pos = (uint32_t)(row % n_canvas);
+  const float temp = temperature(cb);
+  const float inv_t = 1.0f / temp;
+  const bool tempered = inv_t != 1.0f;
+  const bool gumbel = (cb.flags & DG_GUMBEL) != 0;
+  const float c_t = kLog2e * inv_t;
+  const uint32_t k0 = seed_lo(cb.seed), k1 = seed_hi(cb.seed);
+
+  // max, argmax, Gumbel argmax over S
+  float m = -INFINITY, gbest = -INFINITY;
+  uint32_t bid = 0xFFFFFFFFu, gid = 0xFFFFFFFFu;
+#pragma unroll
+  for (int e = 0; e < kTkRowPer; ++e) {
+    if (!kept(e)) continue;
+    const float v = key_value(key[e]);
+    if (better(v, idv[e], m, bid)) { m = v; bid = idv[e]; }
+    if (gumbel) {
+      const Philox4 h = philox4x32_10(idv[e] >> 2, pos, cb.gstep, kStreamGumbel, k0, k1);
+      const uint32_t word = (idv[e] & 3u) == 0 ? h.w0 : (idv[e] & 3u) == 1 ? h.w1 : (idv[e] & 3u) == 2 ? h.w2 : h.w3;
+      const float sc = v * inv_t + gumbel_from_bits(word);
+      if (better(sc, idv[e], gbest, gid)) { gbest = sc; gid = idv[e]; }
+    }
+  }
+  wave_argmax(m, bid);
+  wave_argmax(gbest, gid);
+  if (lane == 0) red[w] = StatsPartial{m, 0.f, 0.f, bid, gbest, gid, 0u, 0.f};
+  uint32_t bad = 0;
+  for (int i = t; i < n_slices; i += kTkThreads) bad |= badf[(size_t)row * n_slices + i];
+  bad = __syncthreads_or((int)bad) ? 1u : 0u;
+  {
+    StatsPartial acc = red[0];
+#pragma unroll
+    for (int o = 1; o < kTkThreads / kWave; ++o) {
+      const StatsPartial q = red[o];
+      if (better(q.m, q.best_id, acc.m, acc.best_id)) { acc.m = q.m; acc.best_id = q.best_id; }
+      if (better(q.gscore, q.gid, acc.gscore, acc.gid)) { acc.gscore = q.gscore; acc.gid = q.gid; }
+    }
+    m = acc.m; bid = acc.best_id; gbest = acc.gscore; gid = acc.gid;
+  }
+
+  // weights exp(l - m) over S, their sums, and the row's list
+  const float mc = (m == -INFINITY) ? 0.0f : -m * kLog2e;
+  float s1 = 0.f, st = 0.f, sy = 0.f;
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int e = 0; e < kTkRowPer; ++e) cnt += kept(e) ? 1u : 0u;
+  uint32_t off = wg_scan(cnt, sh) - cnt;
+  TopkItem* out = list + (size_t)row * k;
+#pragma unroll
+  for (int e = 0; e < kTkRowPer; ++e) {
+    if (!kept(e)) continue;
+    const float v = key_value(key[e]);
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(v, kLog2e, mc));
+    s1 += p;
+    if (tempered || want_h) {
+      const float y = fmaxf((v - m) * c_t, -200.f);
+      const float et = tempered ? __builtin_amdgcn_exp2f(y) : p;
+      st += et;
+      if (want_h) sy += et * y;
+    }
+    if (off < (uint32_t)k) out[off++] = TopkItem{p, (int32_t)idv[e]};
+  }
+  if (!tempered && !want_h) st = s1;
+  s1 = wave_sum(s1);
+  st = wave_sum(st);
+  sy = wave_sum(sy);
+  __syncthreads();   // red is reused
+  if (lane == 0) { red[w].s1 = s1; red[w].st = st; red[w].sy = sy; }
+  __syncthreads();
+  if (t == 0) {
+    float a1 = 0.f, at = 0.f, ay = 0.f;
+#pragma unroll
+    for (int o = 0; o < kTkThreads / kWave; ++o) { a1 += red[o].s1; at += red[o].st; ay += red[o].sy; }
+    part[row] = StatsPartial{m, a1, at, bid, gbest, gid, bad, ay};
+  }
+}
+
+// z_0[row] = sum over the row's list of weight * E[id]; grid (ceil(d / 1024), n_rows),
+// each thread 4 columns.  Weight 0 (underflow, or the -inf fill of short rows) and
+// ids past the vocabulary are skipped.
+__global__ __launch_bounds__(256) void topk_z(const TopkItem* __restrict__ list, const float* __restrict__ emb,
+                                              float* __restrict__ zp, int k, int vocab, int d) {
+  const int row = blockIdx.y;
+  const int col = blockIdx.x * 1024 + 4 * threadIdx.x;
+  if (col >= d) return;
+  const TopkItem* L = list + (size_t)row * k;
+  float* dst = zp + (size_t)row * d + col;
+  if ((d & 3) == 0) {
+    f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < k; ++i) {
+      const TopkItem it = L[i];
+      if (!(it.v > 0.f) || it.id >= vocab) continue;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(emb + (size_t)it.id * d + col);
+      acc[0] += it.v * v[0]; acc[1] += it.v * v[1]; acc[2] += it.v * v[2]; acc[3] += it.v * v[3];
+    }
+    *reinterpret_cast<f32x4*>(dst) = acc;
+  } else {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < k; ++i) {
+      const TopkItem it = L[i];
+      if (!(it.v > 0.f) || it.id >= vocab) continue;
+      const float* e = emb + (size_t)it.id * d + col;
+      for (int q = 0; q < 4 && col + q < d; ++q) acc[q] += it.v * e[q];
+    }
+    for (int q = 0; q < 4 && col + q < d; ++q) dst[q] = acc[q];
+  }
+}
+
+// ---------------------------------------------------------------------------
 size_t embedding_packed_bytes(int vocab, int d) {
   const size_t n_kb = (size_t)(vocab + kKB - 1) / kKB;
   const size_t col_pad = (size_t)(d + kGN - 1) / kGN * kGN;
@@ -788,6 +1084,72 @@ hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void*
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
+  if (eb.on) {
+    prof_begin("samp_eb_select", s);
+    samp_eb_select<<<p.batch, 256, 0, s>>>(rows, ids, committed, eb.argmax, eb.status, ctrl, eb.budget,
+                                           eb.stop_entropy, p.n_canvas, p.vocab);
+    prof_end(s);
+    return hipGetLastError();
+  }
+  prof_begin("samp_finalize", s);
+  samp_finalize<<<p.batch, 256, 0, s>>>(committed, n_unc, ctrl, p.n_canvas);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+TopkPlan topk_plan(int n_canvas, int batch, int vocab, int d, int k) {
+  TopkPlan p{};
+  p.n = n_canvas * batch; p.n_canvas = n_canvas; p.batch = batch; p.vocab = vocab; p.d = d; p.k = k;
+  p.n_slices = (vocab + kTkSliceIds - 1) / kTkSliceIds;
+  p.max_candidates = kTkThreads * kTkRowPer;
+  p.off_part = 0;
+  p.off_cand = align_up((size_t)p.n * sizeof(StatsPartial), 256);
+  p.off_bad = p.off_cand + align_up((size_t)p.n * p.n_slices * k * sizeof(TopkItem), 256);
+  p.off_list = p.off_bad + align_up((size_t)p.n * p.n_slices, 256);
+  p.off_zp = p.off_list + align_up((size_t)p.n * k * sizeof(TopkItem), 256);
+  p.off_eb = p.off_zp + align_up((size_t)p.n * d * sizeof(float), 256);
+  p.total = p.off_eb + 3 * align_up((size_t)p.n * 4, 256);
+  return p;
+}
+
+hipError_t launch_sampler_topk(const TopkPlan& p, const float* logits, const float* emb, int32_t* ids,
+                               uint8_t* committed, float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl,
+                               void* ws, hipStream_t s, const EbCall& eb) {
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const size_t eb_arr = align_up((size_t)p.n * 4, 256);
+  EbRows rows{eb.on, reinterpret_cast<float*>(base + p.off_eb),
+              reinterpret_cast<int32_t*>(base + p.off_eb + eb_arr),
+              reinterpret_cast<int32_t*>(base + p.off_eb + 2 * eb_arr), eb.entropy_out};
+  StatsPartial* part = reinterpret_cast<StatsPartial*>(base + p.off_part);
+  TopkItem* cand = reinterpret_cast<TopkItem*>(base + p.off_cand);
+  uint8_t* badf = base + p.off_bad;
+  TopkItem* list = reinterpret_cast<TopkItem*>(base + p.off_list);
+  float* zp = reinterpret_cast<float*>(base + p.off_zp);
+
+  prof_begin("topk_slice", s);
+  if (p.vocab % 4 == 0)
+    topk_slice<true><<<dim3(p.n_slices, p.n), kTkThreads, 0, s>>>(logits, cand, badf, p.vocab, p.n_slices, p.k);
+  else
+    topk_slice<false><<<dim3(p.n_slices, p.n), kTkThreads, 0, s>>>(logits, cand, badf, p.vocab, p.n_slices, p.k);
+  prof_end(s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  prof_begin("topk_row", s);
+  topk_row<<<p.n, kTkThreads, 0, s>>>(cand, badf, ctrl, part, list, p.n_slices, p.k, p.n_canvas, eb.on);
+  prof_end(s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  prof_begin("topk_z", s);
+  topk_z<<<dim3((p.d + 1023) / 1024, p.n), 256, 0, s>>>(list, emb, zp, p.k, p.vocab, p.d);
+  prof_end(s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  prof_begin("samp_combine", s);
+  samp_combine<<<dim3((p.d + 1023) / 1024, p.n), 256, 0, s>>>(logits, part, 1, zp, ctrl, ids, committed, z, conf,
+                                                              p.n, p.n_canvas, p.vocab, p.d, rows);
+  prof_end(s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (eb.on) {
     prof_begin("samp_eb_select", s);
     samp_eb_select<<<p.batch, 256, 0, s>>>(rows, ids, committed, eb.argmax, eb.status, ctrl, eb.budget,

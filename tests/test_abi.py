@@ -167,3 +167,24 @@ def test_batched_sampler_arguments(lib):
     assert lib.dg_sampler_step_batched(*a, 16, 0, 1000, 64, FAKE, 0, None) == DG_EINVAL
     assert lib.dg_sampler_step_batched(*a, 256, 64, 262144, 64, FAKE, 0, None) == DG_EUNSUPPORTED  # > 2^32 bytes
     assert lib.dg_sampler_step_batched(*a, 16, 4, 1000, 64, FAKE, 16, None) == DG_EWORKSPACE
+
+
+def test_topk_sampler_arguments(lib):
+    from block_text_diffusion_amd._lib import DG_EINVAL, DG_EUNSUPPORTED, DG_EWORKSPACE
+    w = lib.dg_sampler_workspace_bytes_topk(256, 1, 262144, 3072, 64)
+    # the top-k workspace holds candidates, lists and one partial z, far below the full sampler's
+    assert 0 < w < lib.dg_sampler_workspace_bytes(256, 262144, 3072) // 10 and w % 256 == 0
+    assert lib.dg_sampler_workspace_bytes_topk(256, 1, 262144, 3072, 0) == 0
+    assert lib.dg_sampler_workspace_bytes_topk(256, 1, 262144, 3072, 257) == 0
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE]
+    assert lib.dg_sampler_step_topk(*a, 16, 1, 1000, 64, 0, FAKE, 1 << 30, None) == DG_EINVAL
+    assert lib.dg_sampler_step_topk(*a, 16, 1, 1000, 64, 257, FAKE, 1 << 30, None) == DG_EUNSUPPORTED
+    # 32 slices of 16384 ids times 256 candidates exceed what one row pass holds
+    assert lib.dg_sampler_step_topk(*a, 1, 1, 16384 * 33, 64, 256, FAKE, 1 << 30, None) == DG_EUNSUPPORTED
+    assert b"top_k" in lib.dg_last_error()
+    assert lib.dg_sampler_step_topk(*a, 16, 1, 1000, 64, 8, FAKE, 16, None) == DG_EWORKSPACE
+    assert lib.dg_sampler_step_topk(None, *a[1:], 16, 1, 1000, 64, 8, FAKE, 1 << 30, None) == DG_EINVAL
+    e = [FAKE] * 9
+    assert lib.dg_sampler_step_eb_topk(*e, 0.1, 0.005, 16, 1, 1000, 64, 8, FAKE, 16, None) == DG_EWORKSPACE
+    assert lib.dg_sampler_step_eb_topk(*e, -0.1, 0.005, 16, 1, 1000, 64, 8, FAKE, 1 << 30, None) == DG_EINVAL
+    assert lib.dg_sampler_step_eb_topk(*e, 0.1, 0.005, 16, 1, 1000, 64, 300, FAKE, 1 << 30, None) == DG_EUNSUPPORTED
