@@ -86,7 +86,7 @@ def main():
     T["emb"] = dg.dg_embedding_pack(emb_f32)
     torch.cuda.synchronize()
     pack_ms = (time.perf_counter() - tp) * 1e3
-    del emb_f32
+    T["emb_f32"] = emb_f32          # the top-k sampler gathers rows of the plain fp32 table
     T["attn"] = torch.empty((n, hq, hd), dtype=torch.float32, device="cuda")
     T["z"] = torch.empty((n, dm), dtype=torch.float32, device="cuda")
     T["kappa"] = torch.empty(n, dtype=torch.float32, device="cuda")
@@ -159,6 +159,11 @@ def main():
     log("batched sampler: " + ", ".join(f"B={r['batch']}: {r['ms_per_step']:.3f} ms ({r['canvas_steps_per_s']:.0f} canvas-steps/s)"
                                         for r in batched))
 
+    # ---- the top-k truncated sampler (approximate), alone and after attention ----
+    topk = topk_sampler_timing(torch, dg, T, n, p, hq, hkv, hd, vocab, dm, a.steps)
+    log("top-k sampler: " + ", ".join(f"k={r['k']} B={r['batch']}: {r['sampler_ms']:.3f} ms"
+                                      for r in topk["runs"]))
+
     # ---- the decode run: 4096-token prefix, four 256-token canvases ----
     dec = decode_run_timing(torch, dg, T["emb"], vocab, dm)
     log(f"decode run: {dec['tokens']} tokens in {dec['steps']} steps, {dec['tokens_per_s']:.0f} tokens/s")
@@ -216,6 +221,7 @@ def main():
                    "eb_sampler": eb,
                    "decode_run": dec,
                    "batched_sampler": batched,
+                   "topk_sampler": topk,
                    "blas_reference_bf16_gemm": blas},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -306,6 +312,71 @@ def batched_sampler_timing(torch, dg, T, n, vocab, dm, steps, batches=(2, 4, 8))
         del logits, ids, mask, z, ws
         torch.cuda.empty_cache()
     return out
+
+
+def topk_sampler_timing(torch, dg, T, n, p, hq, hkv, hd, vocab, dm, steps, ks=(64, 256), batches=(1, 8)):
+    """The top-k truncated threshold sampler on the step's logits (replicated
+    over B canvases): ms per sampler step, per-kernel averages at B = 1, the HBM
+    rate of its algorithmic bytes (logits once, the gathered E rows, z), and
+    at B = 1 a whole step (attention over the 4352 keys, then this sampler)
+    timed eagerly between two events."""
+    runs = []
+    attn_ws = torch.empty(dg.dg_attention_workspace_bytes(n, p, hq, hkv, hd), dtype=torch.uint8, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for k in ks:
+        for B in batches:
+            logits = T["logits"] if B == 1 else T["logits"].repeat(B, 1)
+            ids = T["ids"].repeat(B)
+            mask = torch.zeros(B * n, dtype=torch.uint8, device="cuda")
+            z = torch.empty((B * n, dm), dtype=torch.float32, device="cuda")
+            kappa = torch.empty(B * n, dtype=torch.float32, device="cuda")
+            nu = torch.zeros(B, dtype=torch.int32, device="cuda")
+            ctrl = dg.stack_ctrl([dg.make_ctrl(seed=20 + b, tau=0.9, flags=dg.DG_AUTO_ADVANCE) for b in range(B)])
+            ws = torch.empty(dg.dg_sampler_workspace_bytes_topk(n, B, vocab, dm, k), dtype=torch.uint8,
+                             device="cuda")
+            run = lambda: dg.dg_sampler_step_topk(logits, T["emb_f32"], ids, mask, z, kappa, nu, ctrl, k, batch=B,
+                                                  workspace=ws)
+            for _ in range(3):
+                run()
+            torch.cuda.synchronize()
+            reps = max(10, steps // B)
+            e0.record()
+            for _ in range(reps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            nbytes = 4.0 * B * (n * vocab + n * k * dm + n * dm)
+            rec = {"k": k, "batch": B, "sampler_ms": round(ms, 4), "canvas_steps_per_s": round(B * 1e3 / ms, 1),
+                   "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                   "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            if B == 1:
+                dg.dg_profile_enable(True)
+                dg.dg_profile_read()
+                for _ in range(reps):
+                    run()
+                torch.cuda.synchronize()
+                prof = dg.dg_profile_read()
+                dg.dg_profile_enable(False)
+                rec["per_kernel_us"] = {kk: round(1e3 * t / c, 2) for kk, (t, c) in prof.items()}
+                step = lambda: (dg.dg_canvas_attention(T["q"], T["kp"], T["vp"], T["kc"], T["vc"], T["attn"],
+                                                       workspace=attn_ws), run())
+                for _ in range(3):
+                    step()
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(reps):
+                    step()
+                e1.record()
+                torch.cuda.synchronize()
+                sms = e0.elapsed_time(e1) / reps
+                rec["step_ms_with_attention"] = round(sms, 4)
+                rec["steps_per_s_with_attention"] = round(1e3 / sms, 1)
+            runs.append(rec)
+            del ws, z, kappa
+    torch.cuda.empty_cache()
+    return {"note": "approximate sampler: per row only the k largest logits are kept (ties to the smaller id); "
+                    "z gathers k rows of the fp32 table; greedy, T = 1", "runs": runs}
 
 
 def eb_sampler_timing(torch, dg, T, n, vocab, dm, steps):

@@ -100,7 +100,7 @@ int check_topk(int k, const dg::TopkPlan& p, void* ws, size_t ws_bytes, const ch
   if (k < 1) return fail(DG_EINVAL, "%s: top_k < 1", who);
   if (k > 256) return fail(DG_EUNSUPPORTED, "%s: top_k > 256", who);
   if ((int64_t)p.n_slices * k > p.max_candidates)
-    return fail(DG_EUNSUPPORTED, "%s: ceil(vocab / 16384) * top_k = %lld exceeds %d", who,
+    return fail(DG_EUNSUPPORTED, "%s: slices * top_k = %lld candidates exceed %d (top_k too large for vocab)", who,
                 (long long)p.n_slices * k, p.max_candidates);
   if (!ws || ws_bytes < p.total) return fail(DG_EWORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, p.total);
   if (!aligned16(ws)) return fail(DG_EINVAL, "%s: workspace misaligned", who);

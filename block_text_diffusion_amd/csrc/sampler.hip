@@ -711,7 +711,7 @@ __global__ __launch_bounds__(256) void samp_eb_select(EbRows eb, int32_t* __rest
 // logits, ties to the smaller id; the step is then the full one on logits
 // with everything outside S at -inf, so the contraction shrinks to k rows of
 // E per canvas row.
-//   topk_slice   per (16384-id slice, row): the slice's own top k by a radix
+//   topk_slice   per (8192-id slice, row): the slice's own top k by a radix
 //                select over order-preserving keys held in registers (then by
 //                id among equal keys); NaN / +inf flags.
 //   topk_row     per row: the top k of the slices' candidates (same select),
@@ -723,9 +723,9 @@ __global__ __launch_bounds__(256) void samp_eb_select(EbRows eb, int32_t* __rest
 //                one split.
 // ---------------------------------------------------------------------------
 constexpr int kTkThreads = 256;
-constexpr int kTkChunks = 16;                          // 4-id groups per thread in a slice
-constexpr int kTkSliceIds = kTkThreads * kTkChunks * 4;  // 16384
-constexpr int kTkRowPer = 32;                          // candidates per thread in the row pass
+constexpr int kTkChunks = 8;                           // 4-id groups per thread in a slice
+constexpr int kTkSliceIds = kTkThreads * kTkChunks * 4;  // 8192
+constexpr int kTkRowPer = 64;                          // candidates per thread in the row pass
 
 struct TopkItem {
   float v;       // logit (slice candidates) or weight exp(l - m) (row list)
@@ -772,6 +772,8 @@ __device__ void wg_select(KeyF keyf, ActF act, uint32_t kk, TkShared& sh, uint32
   uint32_t prefix = 0, pmask = 0;
   gt = 0;
   eq = 0;
+  // passes stay a loop: unrolled, the element loops inside would multiply the code size
+#pragma unroll 1
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     sh.hist[t] = 0;
@@ -822,6 +824,29 @@ __device__ TopkCut wg_topk_cut(KeyF keyf, IdF idf, ActF act, uint32_t k, TkShare
   return c;
 }
 
+// A lower bound for the k largest keys (k <= the workgroup size): the k-th
+// largest of the per-thread maxima.  At least k elements reach it, so the
+// k-th largest key overall does too, and every element of the top k (ties
+// included) has key >= the bound; only those need to enter the select.
+template <int E, typename KeyF, typename ActF>
+__device__ uint32_t wg_topk_floor(KeyF keyf, ActF act, uint32_t k, TkShared& sh) {
+  uint32_t tmax = 0u;
+  bool any = false;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (act(e)) { tmax = max(tmax, keyf(e)); any = true; }
+  uint32_t n_any = wg_scan(any ? 1u : 0u, sh);
+  // the last thread's inclusive count is the number of threads holding an element
+  if (threadIdx.x == kTkThreads - 1) sh.res[0] = n_any;
+  __syncthreads();
+  n_any = sh.res[0];
+  __syncthreads();
+  if (n_any < k) return 0u;   // fewer holders than k: no cut
+  uint32_t f, g, e;
+  wg_select<1>([&](int) { return tmax; }, [&](int) { return any; }, k, sh, f, g, e);
+  return f;
+}
+
 template <bool kAligned>
 __global__ __launch_bounds__(kTkThreads) void topk_slice(const float* __restrict__ logits,
                                                          TopkItem* __restrict__ cand,
@@ -844,8 +869,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_slice(const float* __restrict
     }
   }
   auto idf = [&](int e) { return (uint32_t)(base + 4 * (kTkThreads * (e >> 2) + t) + (e & 3)); };
-  auto all = [](int) { return true; };
-  const TopkCut cut = wg_topk_cut<4 * kTkChunks>([&](int e) { return key[e]; }, idf, all, (uint32_t)k, sh);
+  auto keyf = [&](int e) { return key[e]; };
+  const uint32_t floor_key = wg_topk_floor<4 * kTkChunks>(keyf, [](int) { return true; }, (uint32_t)k, sh);
+  auto act = [&](int e) { return key[e] >= floor_key; };
+  const TopkCut cut = wg_topk_cut<4 * kTkChunks>(keyf, idf, act, (uint32_t)k, sh);
   auto kept = [&](int e) { return key[e] > cut.tau || (key[e] == cut.tau && ~idf(e) >= cut.tau2); };
   uint32_t cnt = 0;
 #pragma unroll
@@ -883,9 +910,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_row(const TopkItem* __restric
       idv[e] = 0xFFFFFFFFu;
     }
   }
-  auto act = [&](int e) { return t + kTkThreads * e < count; };
-  const TopkCut cut = wg_topk_cut<kTkRowPer>([&](int e) { return key[e]; }, [&](int e) { return idv[e]; }, act,
-                                             (uint32_t)k, sh);
+  auto held = [&](int e) { return t + kTkThreads * e < count; };
+  auto keyf = [&](int e) { return key[e]; };
+  const uint32_t floor_key = wg_topk_floor<kTkRowPer>(keyf, held, (uint32_t)k, sh);
+  auto act = [&](int e) { return held(e) && key[e] >= floor_key; };
+  const TopkCut cut = wg_topk_cut<kTkRowPer>(keyf, [&](int e) { return idv[e]; }, act, (uint32_t)k, sh);
   auto kept = [&](int e) {
     return act(e) && (key[e] > cut.tau || (key[e] == cut.tau && ~idv[e] >= cut.tau2));
   };
@@ -969,8 +998,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row(const TopkItem* __restric
 }
 
 // z_0[row] = sum over the row's list of weight * E[id]; grid (ceil(d / 1024), n_rows),
-// each thread 4 columns.  Weight 0 (underflow, or the -inf fill of short rows) and
-// ids past the vocabulary are skipped.
+// each thread 4 columns.  Ids past the vocabulary count with weight 0.
 __global__ __launch_bounds__(256) void topk_z(const TopkItem* __restrict__ list, const float* __restrict__ emb,
                                               float* __restrict__ zp, int k, int vocab, int d) {
   const int row = blockIdx.y;
@@ -979,19 +1007,23 @@ __global__ __launch_bounds__(256) void topk_z(const TopkItem* __restrict__ list,
   const TopkItem* L = list + (size_t)row * k;
   float* dst = zp + (size_t)row * d + col;
   if ((d & 3) == 0) {
+    // branch-free, so the loads of several ids are in flight together; ids past
+    // the vocabulary (the fill of short rows) read row 0 with weight 0
     f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
     for (int i = 0; i < k; ++i) {
       const TopkItem it = L[i];
-      if (!(it.v > 0.f) || it.id >= vocab) continue;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(emb + (size_t)it.id * d + col);
-      acc[0] += it.v * v[0]; acc[1] += it.v * v[1]; acc[2] += it.v * v[2]; acc[3] += it.v * v[3];
+      const bool ok = it.id < vocab;
+      const float wgt = ok ? it.v : 0.f;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(emb + (size_t)(ok ? it.id : 0) * d + col);
+      acc[0] += wgt * v[0]; acc[1] += wgt * v[1]; acc[2] += wgt * v[2]; acc[3] += wgt * v[3];
     }
     *reinterpret_cast<f32x4*>(dst) = acc;
   } else {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < k; ++i) {
       const TopkItem it = L[i];
-      if (!(it.v > 0.f) || it.id >= vocab) continue;
+      if (it.id >= vocab) continue;
       const float* e = emb + (size_t)it.id * d + col;
       for (int q = 0; q < 4 && col + q < d; ++q) acc[q] += it.v * e[q];
     }

@@ -41,7 +41,7 @@ def run_topk(torch, dg, logits, emb, ids, mask, ctrls, k):
     (256, 1, 32768, 512, 64),
     (100, 3, 5003, 130, 17),       # unaligned vocabulary, ragged d, canvases sharing a pass
     (1, 5, 1000, 8, 256),
-    (64, 2, 40000, 96, 1),         # three slices, the last one partial; k = 1
+    (64, 2, 40000, 96, 1),         # five slices, the last one partial; k = 1
     (32, 1, 200, 64, 256),         # k >= vocab: the untruncated step
 ])
 def test_topk_threshold_step(n, batch, vocab, d, k):
