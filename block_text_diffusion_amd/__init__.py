@@ -8,18 +8,18 @@ the library's HIP kernels.
 import ctypes
 
 from . import _lib
-from ._lib import (DG_ATTN_CAUSAL, DG_AUTO_ADVANCE, DG_BF16, DG_COMMIT_ONLY, DG_F32, DG_GUMBEL,
+from ._lib import (DG_ATTN_CAUSAL, DG_AUTO_ADVANCE, DG_BF16, DG_COMMIT_ONLY, DG_F32, DG_FP8_E4M3, DG_GUMBEL,
                    DG_T_SCHEDULE, DgCtrl, DgError, check, load)
 
 __all__ = [
-    "dg_canvas_attention", "dg_sampler_step", "dg_sampler_step_eb", "read_eb_status",
+    "dg_canvas_attention", "dg_canvas_attention_fp8", "dg_sampler_step", "dg_sampler_step_eb", "read_eb_status",
     "dg_sampler_step_batched", "dg_sampler_step_eb_batched", "dg_sampler_workspace_bytes_batched",
     "dg_sampler_step_topk", "dg_sampler_step_eb_topk", "dg_sampler_workspace_bytes_topk",
     "stack_ctrl", "dg_embedding_pack", "dg_embedding_packed_bytes", "dg_denoise_step", "StepGraph", "dg_canvas_init",
     "dg_kv_append", "dg_synth_logits", "dg_philox_fill", "dg_attention_workspace_bytes",
     "dg_sampler_workspace_bytes", "dg_denoise_workspace_bytes", "dg_profile_enable",
     "dg_profile_read", "make_ctrl", "read_ctrl", "write_ctrl", "DG_GUMBEL", "DG_COMMIT_ONLY",
-    "DG_AUTO_ADVANCE", "DG_T_SCHEDULE", "DG_ATTN_CAUSAL", "DG_F32", "DG_BF16", "DgError", "load",
+    "DG_AUTO_ADVANCE", "DG_T_SCHEDULE", "DG_ATTN_CAUSAL", "DG_F32", "DG_BF16", "DG_FP8_E4M3", "DgError", "load",
 ]
 
 
@@ -70,6 +70,29 @@ def dg_attention_workspace_bytes(n_canvas, n_prefix, hq, hkv, head_dim):
 
 def dg_sampler_workspace_bytes(n_canvas, vocab, d_model):
     return load().dg_sampler_workspace_bytes(n_canvas, vocab, d_model)
+
+
+def dg_canvas_attention_fp8(q, k_prefix, v_prefix, k_canvas, v_canvas, q_scale=1.0, k_scale=1.0, v_scale=1.0,
+                            out=None, scale=0.0, workspace=None, stream=None, causal=False):
+    """Q/K/V as OCP FP8 E4M3 bytes (uint8 tensors, or torch.float8_e4m3fn) with
+    per-tensor scales; output float32 [N, Hq, D]."""
+    torch = _torch()
+    dt = (torch.uint8, torch.float8_e4m3fn)
+    _need(q, "q", dt); _need(k_canvas, "k_canvas", dt); _need(v_canvas, "v_canvas", dt)
+    n, hq, d = q.shape
+    hkv = k_canvas.shape[1]
+    n_prefix = 0 if k_prefix is None else k_prefix.shape[0]
+    if n_prefix:
+        _need(k_prefix, "k_prefix", dt); _need(v_prefix, "v_prefix", dt)
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
+    ws = _workspace(dg_attention_workspace_bytes(n, n_prefix, hq, hkv, d), q.device, workspace)
+    check(load().dg_canvas_attention_fp8(_ptr(q), _ptr(k_prefix) if n_prefix else None,
+                                         _ptr(v_prefix) if n_prefix else None, _ptr(k_canvas), _ptr(v_canvas),
+                                         _ptr(out), n, n_prefix, hq, hkv, d, float(scale), float(q_scale),
+                                         float(k_scale), float(v_scale), DG_ATTN_CAUSAL if causal else 0,
+                                         _ptr(ws), ws.numel(), _stream(stream)))
+    return out
 
 
 def dg_embedding_packed_bytes(vocab, d_model):

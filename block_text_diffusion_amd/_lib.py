@@ -17,6 +17,7 @@ DG_EWORKSPACE = -3
 DG_EHIP = -4
 DG_F32 = 0
 DG_BF16 = 1
+DG_FP8_E4M3 = 2
 DG_GUMBEL = 1
 DG_COMMIT_ONLY = 2
 DG_AUTO_ADVANCE = 4
@@ -58,6 +59,7 @@ _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _sz = ctypes.c_size_t
 _f = ctypes.c_float
+_u32 = ctypes.c_uint32
 
 # name -> (restype, argtypes)
 SIGNATURES = {
@@ -65,6 +67,8 @@ SIGNATURES = {
     "dg_canvas_attention": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "dg_canvas_attention_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
                                     ctypes.c_uint32, _vp, _sz, _vp]),
+    "dg_canvas_attention_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _f, _f, _u32,
+                                     _vp, _sz, _vp]),
     "dg_sampler_workspace_bytes": (_sz, [_i, _i, _i]),
     "dg_embedding_packed_bytes": (_sz, [_i, _i]),
     "dg_embedding_pack": (_i, [_vp, _vp, _i, _i, _vp]),

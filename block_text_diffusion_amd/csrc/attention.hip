@@ -20,6 +20,8 @@
 // O^T = V^T P^T straight from the score registers; the V^T operand comes from
 // ds_read_b64_tr_b16, which transposes 16-bit elements across 16 lanes, so V
 // needs no transposition pass.  Online softmax in fp32, base 2.
+#include <type_traits>
+
 #include "dg_common.hpp"
 #include "dg_internal.hpp"
 
@@ -63,6 +65,21 @@ __device__ __forceinline__ u32x4 load8(const float* p) {
                  pack_bf16x2(b[2], b[3])};
 }
 
+// Eight OCP FP8 E4M3 values (8 bytes in two u32) as eight bf16: every E4M3
+// value is exactly a bf16 value, so the conversion is exact.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+  return (u32x4){pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]),
+                 pack_bf16x2(d[0], d[1])};
+}
+__device__ __forceinline__ u32x4 load8(const uint8_t* p) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  return fp8x8_to_bf16(w[0], w[1]);
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
@@ -72,48 +89,69 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 }
 
 // One block of K and V (one KV head, keys kb0.. of one segment) in flight in
-// registers: each thread carries kPer 16-byte chunks of K and of V.  Keys past
-// the segment end are clamped to its last key (finite data, masked later).
-template <int D>
+// registers: each thread carries kPer 8-element chunks of K and of V, as bf16
+// (16 bytes) or, with kF8, as the raw FP8 bytes (8 bytes, converted to bf16
+// when stored to LDS, so the loads stay in flight across the block's math).
+// Keys past the segment end are clamped to its last key (finite data, masked
+// later).
+template <int D, bool kF8>
 struct KvRegs {
   static constexpr int kPer = AGeom<D>::kCpr * kAKeys / kAThreads;
-  u32x4 k[kPer], v[kPer];
+  using Raw = std::conditional_t<kF8, u32x2, u32x4>;
+  Raw k[kPer], v[kPer];
 };
 
-template <int D>
-__device__ __forceinline__ void kv_fetch(KvRegs<D>& r, __amdgpu_buffer_rsrc_t rk,
+template <int D, bool kF8>
+__device__ __forceinline__ void kv_fetch(KvRegs<D, kF8>& r, __amdgpu_buffer_rsrc_t rk,
                                          __amdgpu_buffer_rsrc_t rv, int kb0, int seg_len,
                                          int hkv, int kvh, int t) {
   using G = AGeom<D>;
+  constexpr uint32_t kElemBytes = kF8 ? 1u : 2u;
 #pragma unroll
-  for (int i = 0; i < KvRegs<D>::kPer; ++i) {
+  for (int i = 0; i < KvRegs<D, kF8>::kPer; ++i) {
     const int idx = t + kAThreads * i;
     const int key = min(kb0 + idx / G::kCpr, seg_len - 1);
-    const uint32_t off = (uint32_t)(key * hkv + kvh) * G::kRowBytes + (uint32_t)(idx % G::kCpr) * 16u;
-    r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-    r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    const uint32_t off = ((uint32_t)(key * hkv + kvh) * D + (uint32_t)(idx % G::kCpr) * 8u) * kElemBytes;
+    if constexpr (kF8) {
+      r.k[i] = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0);
+      r.v[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0);
+    } else {
+      r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+      r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    }
   }
 }
 
-template <int D>
-__device__ __forceinline__ void kv_store(const KvRegs<D>& r, uint8_t* stage, int t) {
+template <int D, bool kF8>
+__device__ __forceinline__ void kv_store(const KvRegs<D, kF8>& r, uint8_t* stage, int t) {
   using G = AGeom<D>;
 #pragma unroll
-  for (int i = 0; i < KvRegs<D>::kPer; ++i) {
+  for (int i = 0; i < KvRegs<D, kF8>::kPer; ++i) {
     const int idx = t + kAThreads * i;
     const int key = idx / G::kCpr, c = idx % G::kCpr;
-    *reinterpret_cast<u32x4*>(stage + key * G::kRowBytes + (k_slot<D>(key, c) << 4)) = r.k[i];
-    *reinterpret_cast<u32x4*>(stage + G::kBlockBytes + key * G::kRowBytes + (v_slot<D>(key, c) << 4)) = r.v[i];
+    u32x4 kw, vw;
+    if constexpr (kF8) {
+      kw = fp8x8_to_bf16(r.k[i][0], r.k[i][1]);
+      vw = fp8x8_to_bf16(r.v[i][0], r.v[i][1]);
+    } else {
+      kw = r.k[i];
+      vw = r.v[i];
+    }
+    *reinterpret_cast<u32x4*>(stage + key * G::kRowBytes + (k_slot<D>(key, c) << 4)) = kw;
+    *reinterpret_cast<u32x4*>(stage + G::kBlockBytes + key * G::kRowBytes + (v_slot<D>(key, c) << 4)) = vw;
   }
 }
 
-template <int D, typename TQ>
+// TQ: query element type (bf16 bits, float, or FP8 bytes); kF8: K/V are FP8
+// bytes (otherwise bf16).  out_scale multiplies the normalised output (the V
+// scale of FP8 inputs, 1 otherwise).
+template <int D, typename TQ, bool kF8>
 __global__ __launch_bounds__(kAThreads) void attn_partial(
-    const TQ* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
-    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, float* __restrict__ out,
+    const TQ* __restrict__ q, const void* __restrict__ kp, const void* __restrict__ vp,
+    const void* __restrict__ kc, const void* __restrict__ vc, float* __restrict__ out,
     _Float16* __restrict__ opart, float* __restrict__ ml, int n, int n_prefix, int hq, int hkv,
     int blocks_prefix, int blocks_total, int blocks_per_chunk, int n_chunks, float scale_log2e,
-    bool causal) {
+    bool causal, float out_scale) {
   using G = AGeom<D>;
   constexpr int KS = D / 16;   // 16-wide k steps over the head dimension
   constexpr int DB = D / 32;   // 32-row blocks of O^T
@@ -135,18 +173,18 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
   const int gb0 = chunk * blocks_per_chunk;
   const int nb = min(blocks_total, gb0 + blocks_per_chunk) - gb0;
 
-  const uint32_t pre_bytes = (uint32_t)n_prefix * hkv * G::kRowBytes;
-  const uint32_t can_bytes = (uint32_t)n * hkv * G::kRowBytes;
+  const uint32_t pre_bytes = (uint32_t)n_prefix * hkv * D * (kF8 ? 1u : 2u);
+  const uint32_t can_bytes = (uint32_t)n * hkv * D * (kF8 ? 1u : 2u);
   const __amdgpu_buffer_rsrc_t rkp = rsrc(kp, pre_bytes), rvp = rsrc(vp, pre_bytes);
   const __amdgpu_buffer_rsrc_t rkc = rsrc(kc, can_bytes), rvc = rsrc(vc, can_bytes);
 
-  KvRegs<D> ra;
-  auto fetch = [&](KvRegs<D>& r, int b) {
+  KvRegs<D, kF8> ra;
+  auto fetch = [&](KvRegs<D, kF8>& r, int b) {
     const int gb = gb0 + b;
     if (gb < blocks_prefix)
-      kv_fetch<D>(r, rkp, rvp, gb * kAKeys, n_prefix, hkv, kvh, t);
+      kv_fetch<D, kF8>(r, rkp, rvp, gb * kAKeys, n_prefix, hkv, kvh, t);
     else
-      kv_fetch<D>(r, rkc, rvc, (gb - blocks_prefix) * kAKeys, n, hkv, kvh, t);
+      kv_fetch<D, kF8>(r, rkc, rvc, (gb - blocks_prefix) * kAKeys, n, hkv, kvh, t);
   };
   fetch(ra, 0);
 
@@ -176,7 +214,7 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
   const int vkey0 = 32 * wh + 4 * (g16 >> 1) + (r16 >> 2);
   const int vbyte = 8 * (r16 & 1);
 
-  kv_store<D>(ra, lds, t);
+  kv_store<D, kF8>(ra, lds, t);
   __syncthreads();
 
   // one block: scores, online softmax, O^T update (reads one LDS stage)
@@ -275,7 +313,7 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
   for (int b = 0; b < nb; ++b) {
     if (b + 1 < nb) fetch(ra, b + 1);
     step(b, lds + (b & 1) * G::kStageBytes);
-    if (b + 1 < nb) kv_store<D>(ra, lds + ((b + 1) & 1) * G::kStageBytes, t);
+    if (b + 1 < nb) kv_store<D, kF8>(ra, lds + ((b + 1) & 1) * G::kStageBytes, t);
     __syncthreads();
   }
 
@@ -317,7 +355,7 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
     if (n_chunks == 1) {
       // one chunk: the normalized output, straight from the registers
       if (r_ok) {
-        const float inv = 1.0f / l_run;
+        const float inv = out_scale / l_run;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -381,7 +419,7 @@ template <int D>
 __global__ __launch_bounds__(kCThreads) void attn_combine(const _Float16* __restrict__ opart,
                                                           const float* __restrict__ ml,
                                                           float* __restrict__ out,
-                                                          int n_rows_total, int n_chunks) {
+                                                          int n_rows_total, int n_chunks, float out_scale) {
   constexpr int kLanesPerRow = D / 4;
   const int row = blockIdx.x * (kCThreads / kLanesPerRow) + threadIdx.x / kLanesPerRow;
   const int d4 = (threadIdx.x % kLanesPerRow) * 4;
@@ -403,7 +441,7 @@ __global__ __launch_bounds__(kCThreads) void attn_combine(const _Float16* __rest
     l = l * a + rec[1] * bw;
     m = mn;
   }
-  *reinterpret_cast<f32x4*>(out + (size_t)row * D + d4) = acc * (1.0f / l);
+  *reinterpret_cast<f32x4*>(out + (size_t)row * D + d4) = acc * (out_scale / l);
 }
 
 // fp32 K/V are rounded to bf16 once per call (the MFMA operand type).
@@ -444,36 +482,43 @@ AttnPlan attn_plan(int n, int n_prefix, int hq, int hkv, int d) {
   return p;
 }
 
-template <int D, typename TQ>
-static hipError_t launch_attn_t(const AttnPlan& p, const void* q, const uint16_t* kp,
-                                const uint16_t* vp, const uint16_t* kc, const uint16_t* vc,
-                                float* out, float scale, bool causal, void* ws, hipStream_t s) {
+template <int D, typename TQ, bool kF8>
+static hipError_t launch_attn_t(const AttnPlan& p, const void* q, const void* kp, const void* vp,
+                                const void* kc, const void* vc, float* out, float scale, bool causal,
+                                float out_scale, void* ws, hipStream_t s) {
   _Float16* opart = reinterpret_cast<_Float16*>(static_cast<uint8_t*>(ws) + p.off_opart);
   float* ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p.off_ml);
   const float sl2 = scale * kLog2e;
   prof_begin("attn_partial", s);
-  attn_partial<D, TQ><<<dim3(p.n_chunks, p.n_qtiles, p.hkv), kAThreads, 0, s>>>(
+  attn_partial<D, TQ, kF8><<<dim3(p.n_chunks, p.n_qtiles, p.hkv), kAThreads, 0, s>>>(
       static_cast<const TQ*>(q), kp, vp, kc, vc, out, opart, ml, p.n, p.n_prefix, p.hq, p.hkv,
-      p.blocks_prefix, p.blocks_total, p.blocks_per_chunk, p.n_chunks, sl2, causal);
+      p.blocks_prefix, p.blocks_total, p.blocks_per_chunk, p.n_chunks, sl2, causal, out_scale);
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_chunks == 1) return e;
   const int rows_per_wg = kCThreads / (D / 4);
   prof_begin("attn_combine", s);
   attn_combine<D><<<(p.n * p.hq + rows_per_wg - 1) / rows_per_wg, kCThreads, 0, s>>>(
-      opart, ml, out, p.n * p.hq, p.n_chunks);
+      opart, ml, out, p.n * p.hq, p.n_chunks, out_scale);
   prof_end(s);
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_attn_d(const AttnPlan& p, int dtype, const void* q, const void* kp, const void* vp,
+                                const void* kc, const void* vc, float* out, float scale, bool causal,
+                                float out_scale, void* ws, hipStream_t s) {
+  if (dtype == DG_FP8_E4M3)
+    return launch_attn_t<D, uint8_t, true>(p, q, kp, vp, kc, vc, out, scale, causal, out_scale, ws, s);
+  if (dtype == DG_BF16)
+    return launch_attn_t<D, uint16_t, false>(p, q, kp, vp, kc, vc, out, scale, causal, out_scale, ws, s);
+  return launch_attn_t<D, float, false>(p, q, kp, vp, kc, vc, out, scale, causal, out_scale, ws, s);
+}
+
 hipError_t launch_attention(const AttnPlan& p, const void* q, const void* kp, const void* vp,
-                            const void* kc, const void* vc, float* out, bool bf16_in,
-                            float scale, void* ws, hipStream_t s, bool causal) {
-  const uint16_t *kp16, *vp16, *kc16, *vc16;
-  if (bf16_in) {
-    kp16 = static_cast<const uint16_t*>(kp); vp16 = static_cast<const uint16_t*>(vp);
-    kc16 = static_cast<const uint16_t*>(kc); vc16 = static_cast<const uint16_t*>(vc);
-  } else {
+                            const void* kc, const void* vc, float* out, int dtype, float scale,
+                            void* ws, hipStream_t s, bool causal, float out_scale) {
+  if (dtype == DG_F32) {
     // fp32 K/V: round to bf16 into the workspace first
     uint16_t* base = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + p.off_kv16);
     const size_t pre = (size_t)p.n_prefix * p.hkv * p.d, can = (size_t)p.n * p.hkv * p.d;
@@ -490,13 +535,10 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* kp, co
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    kp16 = kp_w; vp16 = vp_w; kc16 = kc_w; vc16 = vc_w;
+    kp = kp_w; vp = vp_w; kc = kc_w; vc = vc_w;
   }
-  if (p.d == 128)
-    return bf16_in ? launch_attn_t<128, uint16_t>(p, q, kp16, vp16, kc16, vc16, out, scale, causal, ws, s)
-                   : launch_attn_t<128, float>(p, q, kp16, vp16, kc16, vc16, out, scale, causal, ws, s);
-  return bf16_in ? launch_attn_t<64, uint16_t>(p, q, kp16, vp16, kc16, vc16, out, scale, causal, ws, s)
-                 : launch_attn_t<64, float>(p, q, kp16, vp16, kc16, vc16, out, scale, causal, ws, s);
+  if (p.d == 128) return launch_attn_d<128>(p, dtype, q, kp, vp, kc, vc, out, scale, causal, out_scale, ws, s);
+  return launch_attn_d<64>(p, dtype, q, kp, vp, kc, vc, out, scale, causal, out_scale, ws, s);
 }
 
 }  // namespace dg

@@ -65,9 +65,10 @@ int check_attention(const void* q, const void* kp, const void* vp, const void* k
   if (n > 256) return fail(DG_EUNSUPPORTED, "attention: n_canvas > 256");
   if (hq < 1 || hkv < 1 || hq % hkv != 0) return fail(DG_EINVAL, "attention: hq %% hkv != 0 or < 1");
   if (d != 64 && d != 128) return fail(DG_EUNSUPPORTED, "attention: head_dim must be 64 or 128");
-  if (dtype != DG_F32 && dtype != DG_BF16) return fail(DG_EUNSUPPORTED, "attention: dtype");
+  if (dtype != DG_F32 && dtype != DG_BF16 && dtype != DG_FP8_E4M3) return fail(DG_EUNSUPPORTED, "attention: dtype");
   // K/V blocks are fetched with 32-bit buffer offsets
-  if ((uint64_t)np * (uint64_t)hkv * (uint64_t)d * 2ull >= (1ull << 31))
+  const uint64_t elem = dtype == DG_FP8_E4M3 ? 1ull : 2ull;
+  if ((uint64_t)np * (uint64_t)hkv * (uint64_t)d * elem >= (1ull << 31))
     return fail(DG_EUNSUPPORTED, "attention: prefix K/V must be below 2 GiB per tensor");
   if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(out) ||
       (np > 0 && (!aligned16(kp) || !aligned16(vp))))
@@ -181,6 +182,7 @@ int dg_canvas_attention_ex(const void* q, const void* kp, const void* vp, const 
                            int dtype, float scale, uint32_t attn_flags, void* ws, size_t ws_bytes,
                            hipStream_t stream) {
   if (attn_flags & ~(uint32_t)DG_ATTN_CAUSAL) return fail(DG_EINVAL, "attention: unknown flag bits");
+  if (dtype == DG_FP8_E4M3) return fail(DG_EINVAL, "attention: FP8 inputs take dg_canvas_attention_fp8 (scales)");
   int st = check_attention(q, kp, vp, kc, vc, out, n, np, hq, hkv, d, dtype);
   if (st != DG_OK) return st;
   const dg::AttnPlan p = dg::attn_plan(n, np, hq, hkv, d);
@@ -188,9 +190,31 @@ int dg_canvas_attention_ex(const void* q, const void* kp, const void* vp, const 
     return fail(DG_EWORKSPACE, "attention: workspace %zu < %zu bytes", ws_bytes, p.total);
   if (p.total > 0 && !aligned16(ws)) return fail(DG_EINVAL, "attention: workspace misaligned");
   if (!(scale > 0.f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)d);
-  hipError_t e = dg::launch_attention(p, q, kp, vp, kc, vc, out, dtype == DG_BF16, scale, ws, stream,
+  hipError_t e = dg::launch_attention(p, q, kp, vp, kc, vc, out, dtype, scale, ws, stream,
                                       (attn_flags & DG_ATTN_CAUSAL) != 0);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return DG_OK;
+}
+
+int dg_canvas_attention_fp8(const void* q, const void* kp, const void* vp, const void* kc, const void* vc,
+                            float* out, int n, int np, int hq, int hkv, int d, float scale, float q_scale,
+                            float k_scale, float v_scale, uint32_t attn_flags, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (attn_flags & ~(uint32_t)DG_ATTN_CAUSAL) return fail(DG_EINVAL, "attention_fp8: unknown flag bits");
+  int st = check_attention(q, kp, vp, kc, vc, out, n, np, hq, hkv, d, DG_FP8_E4M3);
+  if (st != DG_OK) return st;
+  if (!(q_scale > 0.f) || !std::isfinite(q_scale) || !(k_scale > 0.f) || !std::isfinite(k_scale) ||
+      !(v_scale > 0.f) || !std::isfinite(v_scale))
+    return fail(DG_EINVAL, "attention_fp8: q_scale, k_scale and v_scale must be finite and > 0");
+  const dg::AttnPlan p = dg::attn_plan(n, np, hq, hkv, d);
+  if (p.total > 0 && (!ws || ws_bytes < p.total))
+    return fail(DG_EWORKSPACE, "attention_fp8: workspace %zu < %zu bytes", ws_bytes, p.total);
+  if (p.total > 0 && !aligned16(ws)) return fail(DG_EINVAL, "attention_fp8: workspace misaligned");
+  if (!(scale > 0.f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)d);
+  // the tensor scales fold into the score scale and the output
+  hipError_t e = dg::launch_attention(p, q, kp, vp, kc, vc, out, DG_FP8_E4M3, scale * q_scale * k_scale, ws,
+                                      stream, (attn_flags & DG_ATTN_CAUSAL) != 0, v_scale);
+  if (e != hipSuccess) return hip_fail(e, "attention_fp8 launch");
   return DG_OK;
 }
 
@@ -293,6 +317,7 @@ int dg_denoise_step(const void* q, const void* kp, const void* vp, const void* k
                     const float* logits, const void* emb, int32_t* ids, uint8_t* committed,
                     float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl, int n, int vocab, int dm,
                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (dtype == DG_FP8_E4M3) return fail(DG_EUNSUPPORTED, "denoise: FP8 attention inputs take dg_canvas_attention_fp8");
   int st = check_attention(q, kp, vp, kc, vc, attn_out, n, np, hq, hkv, d, dtype);
   if (st != DG_OK) return st;
   st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, dm);
@@ -302,7 +327,7 @@ int dg_denoise_step(const void* q, const void* kp, const void* vp, const void* k
   if (!aligned16(ws)) return fail(DG_EINVAL, "denoise: workspace misaligned");
   if (!(scale > 0.f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)d);
   const dg::AttnPlan ap = dg::attn_plan(n, np, hq, hkv, d);
-  hipError_t e = dg::launch_attention(ap, q, kp, vp, kc, vc, attn_out, dtype == DG_BF16, scale, ws, stream);
+  hipError_t e = dg::launch_attention(ap, q, kp, vp, kc, vc, attn_out, dtype, scale, ws, stream);
   if (e != hipSuccess) return hip_fail(e, "denoise attention launch");
   const dg::SamplerPlan sp = dg::sampler_plan(n, 1, vocab, dm);
   e = dg::launch_sampler(sp, logits, emb, ids, committed, z, conf, n_unc, ctrl, ws, stream);

@@ -71,9 +71,13 @@ struct AttnPlan {
   size_t off_opart, off_ml, total;
 };
 AttnPlan attn_plan(int n, int n_prefix, int hq, int hkv, int d);
+// dtype: DG_F32 (K/V rounded to bf16 into the workspace first), DG_BF16, or
+// DG_FP8_E4M3 (Q/K/V bytes converted exactly to bf16 while staged).
+// out_scale multiplies the normalised output.
 hipError_t launch_attention(const AttnPlan& p, const void* q, const void* kp, const void* vp,
-                            const void* kc, const void* vc, float* out, bool bf16_in,
-                            float scale, void* ws, hipStream_t s, bool causal = false);
+                            const void* kc, const void* vc, float* out, int dtype,
+                            float scale, void* ws, hipStream_t s, bool causal = false,
+                            float out_scale = 1.0f);
 
 // ---- block loop helpers ----
 hipError_t launch_canvas_init(int32_t* ids, uint8_t* committed, dg_ctrl* ctrl, int n, int vocab,

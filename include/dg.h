@@ -49,7 +49,7 @@ typedef enum dg_status {
   DG_EHIP = -4           /* a HIP runtime call or launch failed */
 } dg_status;
 
-typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
+typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1, DG_FP8_E4M3 = 2 } dg_dtype;
 
 /* dg_ctrl.flags */
 enum {
@@ -104,7 +104,8 @@ size_t dg_attention_workspace_bytes(int n_canvas, int n_prefix, int hq, int hkv,
  *   out        [n_canvas, hq, head_dim]     float32 (written)
  *   n_canvas in [1, 256]; n_prefix >= 0; hq % hkv == 0; head_dim in {64, 128}.
  *   dtype DG_BF16 or DG_F32 (float32 inputs are rounded to bf16 when staged;
- *   products and the softmax accumulate in float32).
+ *   products and the softmax accumulate in float32).  FP8 inputs take
+ *   dg_canvas_attention_fp8 (DG_FP8_E4M3 here returns DG_EINVAL).
  *   scale <= 0 selects 1/sqrt(head_dim).
  */
 int dg_canvas_attention(const void* q, const void* k_prefix, const void* v_prefix,
@@ -130,6 +131,26 @@ int dg_canvas_attention_ex(const void* q, const void* k_prefix, const void* v_pr
                            int n_canvas, int n_prefix, int hq, int hkv, int head_dim,
                            int dtype, float scale, uint32_t attn_flags,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * FP8 canvas attention: the pages' timings are taken in FP8 (explainer
+ * "DiffusionGemma: Google's open diffusion LLM", section "Throughput flips at
+ * about 32 concurrent users", Figure 12 caption).  q, k_prefix, v_prefix,
+ * k_canvas and v_canvas are OCP FP8 E4M3 bytes (1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN) in the layouts of
+ * dg_canvas_attention; the real values are q_scale * q, k_scale * k and
+ * v_scale * v.  Every E4M3 value is exactly a bf16 value, so the kernel stages
+ * them as bf16 without rounding and computes as the bf16 path does (bf16
+ * products, float32 softmax and accumulation); the K/V bytes read are half
+ * those of bf16.  The scales must be finite and > 0.  attn_flags, scale,
+ * workspace (dg_attention_workspace_bytes) and errors as dg_canvas_attention_ex.
+ */
+int dg_canvas_attention_fp8(const void* q, const void* k_prefix, const void* v_prefix,
+                            const void* k_canvas, const void* v_canvas, float* out,
+                            int n_canvas, int n_prefix, int hq, int hkv, int head_dim,
+                            float scale, float q_scale, float k_scale, float v_scale,
+                            uint32_t attn_flags, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Diffusion sampler                                                         */

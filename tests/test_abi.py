@@ -188,3 +188,18 @@ def test_topk_sampler_arguments(lib):
     assert lib.dg_sampler_step_eb_topk(*e, 0.1, 0.005, 16, 1, 1000, 64, 8, FAKE, 16, None) == DG_EWORKSPACE
     assert lib.dg_sampler_step_eb_topk(*e, -0.1, 0.005, 16, 1, 1000, 64, 8, FAKE, 1 << 30, None) == DG_EINVAL
     assert lib.dg_sampler_step_eb_topk(*e, 0.1, 0.005, 16, 1, 1000, 64, 300, FAKE, 1 << 30, None) == DG_EUNSUPPORTED
+
+
+def test_fp8_attention_arguments(lib):
+    from block_text_diffusion_amd._lib import DG_EINVAL, DG_EUNSUPPORTED, DG_EWORKSPACE, DG_FP8_E4M3
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 8, 8, 4, 64, 0.0]
+    big = 1 << 30
+    assert lib.dg_canvas_attention_fp8(*a, 1.0, 1.0, 1.0, 0, FAKE, 16, None) == DG_EWORKSPACE
+    assert lib.dg_canvas_attention_fp8(*a, 0.0, 1.0, 1.0, 0, FAKE, big, None) == DG_EINVAL
+    assert lib.dg_canvas_attention_fp8(*a, 1.0, float("inf"), 1.0, 0, FAKE, big, None) == DG_EINVAL
+    assert lib.dg_canvas_attention_fp8(*a, 1.0, 1.0, -2.0, 0, FAKE, big, None) == DG_EINVAL
+    assert lib.dg_canvas_attention_fp8(*a, 1.0, 1.0, 1.0, 4, FAKE, big, None) == DG_EINVAL    # unknown flag
+    assert lib.dg_canvas_attention_fp8(*a[:10], 96, 0.0, 1.0, 1.0, 1.0, 0, FAKE, big, None) == DG_EUNSUPPORTED
+    # the bf16 entry points do not take FP8 (no scales there)
+    assert lib.dg_canvas_attention_ex(*a[:11], DG_FP8_E4M3, 0.0, 0, FAKE, big, None) == DG_EINVAL
+    assert b"fp8" in lib.dg_last_error()

@@ -1,0 +1,70 @@
+"""FP8 (OCP E4M3) canvas attention on the GPU against the oracle: attention of
+the decoded, scaled inputs in fp64 (oracle.fp8).  The kernel stages E4M3 as
+bf16 exactly, so the bf16 path's bound applies: max-abs 2e-2 on outputs of
+unit-scale values, scaled by v_scale."""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import ATTN_MAX_ABS, log, require_gpu, to_dev
+from oracle import fp8 as F
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fp8(torch, dg, q, kp, vp, kc, vc, scales=(1.0, 1.0, 1.0), causal=False):
+    tq, tkc, tvc = to_dev(q), to_dev(kc), to_dev(vc)
+    tkp = to_dev(kp) if kp.shape[0] else None
+    tvp = to_dev(vp) if kp.shape[0] else None
+    out = dg.dg_canvas_attention_fp8(tq, tkp, tvp, tkc, tvc, *scales, causal=causal)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check(got, ref, label, tol):
+    err = np.abs(got.astype(np.float64) - ref).max()
+    log(f"{label}: max abs err {err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= tol, f"{label}: max abs err {err}"
+
+
+def test_long_context_fp8_with_scales():
+    torch, dg = require_gpu()
+    q, kp, vp, kc, vc = workloads.attention_inputs_fp8(4)
+    scales = (0.5, 0.75, 2.0)
+    got = run_fp8(torch, dg, q, kp, vp, kc, vc, scales)
+    ref = F.canvas_attention_fp8(q, kp, vp, kc, vc, *scales)
+    check(got, ref, "long context, fp8", ATTN_MAX_ABS * scales[2])
+
+
+@pytest.mark.parametrize("n,p,hq,hkv,d,causal", [
+    (256, 0, 16, 8, 128, False),
+    (100, 37, 16, 8, 128, False),
+    (130, 300, 8, 2, 64, False),
+    (1, 5, 8, 8, 64, False),
+    (256, 512, 16, 8, 128, True),
+    (77, 130, 16, 4, 64, True),
+])
+def test_fp8_shapes(n, p, hq, hkv, d, causal):
+    torch, dg = require_gpu()
+    log(f"fp8 attention n={n} p={p} hq={hq} hkv={hkv} d={d} causal={causal}")
+    q, kp, vp, kc, vc = workloads.attention_inputs_fp8(2, n=n, n_prefix=p, hq=hq, hkv=hkv, head_dim=d)
+    got = run_fp8(torch, dg, q, kp, vp, kc, vc, causal=causal)
+    check(got, F.canvas_attention_fp8(q, kp, vp, kc, vc, causal=causal), f"n={n} p={p}", ATTN_MAX_ABS)
+
+
+def test_every_code_decodes_exactly():
+    """Zero keys give equal weights (exactly 1 each on the device), so O is the
+    mean of the decoded values; one 64-key block means one chunk and an fp32
+    output straight from the registers.  Every finite code appears in V."""
+    torch, dg = require_gpu()
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    n, d = 64, 64
+    vc = np.stack([np.roll(codes, -4 * j)[:d] for j in range(n)])[:, None, :]    # [64, 1, 64]
+    assert set(np.unique(vc).tolist()) == set(codes.tolist())
+    kc = np.zeros((n, 1, d), np.uint8)
+    empty = np.zeros((0, 1, d), np.uint8)
+    q = workloads.fp8_codes(np.random.default_rng(0).standard_normal((n, 1, d)))
+    got = run_fp8(torch, dg, q, empty, empty, kc, vc)
+    ref = F.canvas_attention_fp8(q, empty, empty, kc, vc)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-3)

@@ -91,6 +91,20 @@ def attention_inputs(workload, n_prefix=None, block=None, n=None, hq=None, hkv=N
     return q, kp, vp, kc, vc
 
 
+def fp8_codes(x):
+    """OCP FP8 E4M3 bytes of float32 values (torch's round-to-nearest-even
+    conversion); input preparation only."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def attention_inputs_fp8(workload, **overrides):
+    """The same Q/K/V draws as attention_inputs (float32 recipe), as E4M3 bytes."""
+    overrides["qkv"] = "f32"
+    return tuple(fp8_codes(t) for t in attention_inputs(workload, **overrides))
+
+
 def embedding(workload, vocab=None, d_model=None):
     """E [V, d] float32 ~ N(0, 0.02).  Workloads 4 and 5 reuse workload 3's table."""
     if workload in (4, 5):
