@@ -159,6 +159,10 @@ def main():
     log("batched sampler: " + ", ".join(f"B={r['batch']}: {r['ms_per_step']:.3f} ms ({r['canvas_steps_per_s']:.0f} canvas-steps/s)"
                                         for r in batched))
 
+    # ---- FP8 (E4M3) attention on the same draws ----
+    attn_fp8 = fp8_attention_timing(torch, dg, workloads, n, p, hq, hkv, hd, a.steps)
+    log(f"fp8 attention: {attn_fp8['us']:.1f} us per call")
+
     # ---- the top-k truncated sampler (approximate), alone and after attention ----
     topk = topk_sampler_timing(torch, dg, T, n, p, hq, hkv, hd, vocab, dm, a.steps)
     log("top-k sampler: " + ", ".join(f"k={r['k']} B={r['batch']}: {r['sampler_ms']:.3f} ms"
@@ -222,6 +226,7 @@ def main():
                    "decode_run": dec,
                    "batched_sampler": batched,
                    "topk_sampler": topk,
+                   "attention_fp8": attn_fp8,
                    "blas_reference_bf16_gemm": blas},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -312,6 +317,39 @@ def batched_sampler_timing(torch, dg, T, n, vocab, dm, steps, batches=(2, 4, 8))
         del logits, ids, mask, z, ws
         torch.cuda.empty_cache()
     return out
+
+
+def fp8_attention_timing(torch, dg, workloads, n, p, hq, hkv, hd, steps):
+    """Canvas attention with OCP E4M3 inputs (the long-context shapes), eager
+    calls between two events, and the per-kernel split."""
+    q, kp, vp, kc, vc = (torch.from_numpy(x).cuda() for x in workloads.attention_inputs_fp8(4))
+    out = torch.empty((n, hq, hd), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dg.dg_attention_workspace_bytes(n, p, hq, hkv, hd), dtype=torch.uint8, device="cuda")
+    run = lambda: dg.dg_canvas_attention_fp8(q, kp, vp, kc, vc, 1.0, 1.0, 1.0, out=out, workspace=ws)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    dg.dg_profile_enable(True)
+    dg.dg_profile_read()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    prof = dg.dg_profile_read()
+    dg.dg_profile_enable(False)
+    flops = 4.0 * n * (p + n) * hd * hq
+    kv_bytes = 2.0 * (p + n) * hkv * hd          # K and V, one byte per element
+    return {"us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "frac_bf16_peak": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "kv_mb": round(kv_bytes / 1e6, 2),
+            "per_kernel_us": {k: round(1e3 * t / c, 2) for k, (t, c) in prof.items()},
+            "note": "E4M3 Q/K/V staged exactly as bf16; bf16 MFMA, fp32 softmax"}
 
 
 def topk_sampler_timing(torch, dg, T, n, p, hq, hkv, hd, vocab, dm, steps, ks=(64, 256), batches=(1, 8)):
