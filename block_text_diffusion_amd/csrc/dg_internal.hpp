@@ -49,7 +49,7 @@ hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void*
 struct TopkPlan {
   int n, n_canvas, batch, vocab, d;
   int k;               // kept logits per row
-  int n_slices;        // 8192-id slices of the vocabulary
+  int n_slices;        // 4096-id sub-slices of the vocabulary (one wavefront each)
   int max_candidates;  // slice candidates one row pass can hold (n_slices * k must not exceed it)
   size_t off_part, off_cand, off_bad, off_list, off_zp, off_eb, total;
 };

@@ -711,9 +711,10 @@ __global__ __launch_bounds__(256) void samp_eb_select(EbRows eb, int32_t* __rest
 // logits, ties to the smaller id; the step is then the full one on logits
 // with everything outside S at -inf, so the contraction shrinks to k rows of
 // E per canvas row.
-//   topk_slice   per (8192-id slice, row): the slice's own top k by a radix
-//                select over order-preserving keys held in registers (then by
-//                id among equal keys); NaN / +inf flags.
+//   topk_slice   per (4096-id sub-slice, row), one wavefront each: the
+//                sub-slice's own top k by a radix select over order-preserving
+//                keys held in registers (then by id among equal keys); NaN /
+//                +inf flags.
 //   topk_row     per row: the top k of the slices' candidates (same select),
 //                then one split's statistics record (max, argmax, Gumbel
 //                argmax within S, sums at T = 1 and T, entropy term) and the
@@ -723,8 +724,6 @@ __global__ __launch_bounds__(256) void samp_eb_select(EbRows eb, int32_t* __rest
 //                one split.
 // ---------------------------------------------------------------------------
 constexpr int kTkThreads = 256;
-constexpr int kTkChunks = 8;                           // 4-id groups per thread in a slice
-constexpr int kTkSliceIds = kTkThreads * kTkChunks * 4;  // 8192
 constexpr int kTkRowPer = 64;                          // candidates per thread in the row pass
 
 struct TopkItem {
@@ -847,44 +846,268 @@ __device__ uint32_t wg_topk_floor(KeyF keyf, ActF act, uint32_t k, TkShared& sh)
   return f;
 }
 
-template <bool kAligned>
-__global__ __launch_bounds__(kTkThreads) void topk_slice(const float* __restrict__ logits,
-                                                         TopkItem* __restrict__ cand,
-                                                         uint8_t* __restrict__ badf, int vocab,
-                                                         int n_slices, int k) {
-  __shared__ TkShared sh;
-  const int slice = blockIdx.x, row = blockIdx.y, t = threadIdx.x;
-  const float* x = logits + (size_t)row * (size_t)vocab;
-  const int base = slice * kTkSliceIds;
-  // group c of thread t: ids base + 4 (256 c + t) .. + 3 (1 KB per load instruction)
-  uint32_t key[4 * kTkChunks];
-  int bad = 0;
+// ---- wave-level select (no workgroup barriers): one wavefront, 64 lanes,
+// E elements per lane, a private 256-bin LDS histogram.  LDS instructions of
+// one wave execute in order, so clearing, counting and reading the histogram
+// need no barrier.
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int c = 0; c < kTkChunks; ++c) {
-    const f32x4 v = load4<kAligned>(x, base + 4 * (kTkThreads * c + t), vocab);
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+template <int E, typename KeyF, typename ActF>
+__device__ void wave_select(KeyF keyf, ActF act, uint32_t kk, uint32_t* hist, uint32_t& tau, uint32_t& gt,
+                            uint32_t& eq) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0, pmask = 0;
+  gt = 0;
+  eq = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    *reinterpret_cast<u32x4*>(hist + 4 * lane) = (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t k = keyf(e);
+      if (act(e) && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    // lane L reads bins 255 - 4L .. 252 - 4L (descending), so the running sums
+    // count the keys in higher bins
+    const u32x4 hv = *reinterpret_cast<const u32x4*>(hist + 252 - 4 * lane);
+    const uint32_t h[4] = {hv[3], hv[2], hv[1], hv[0]};
+    const uint32_t tot = h[0] + h[1] + h[2] + h[3];
+    uint32_t run = wave_scan(tot) - tot;
+    uint32_t b = 0, above = 0, cnt = 0;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!found && run < kk && run + h[j] >= kk) {
+        found = true;
+        b = 255u - 4u * (uint32_t)lane - (uint32_t)j;
+        above = run;
+        cnt = h[j];
+      }
+      run += h[j];
+    }
+    const uint64_t who = __builtin_amdgcn_ballot_w64(found);
+    const int src = who ? (int)__builtin_ctzll(who) : 0;   // exactly one lane holds the bin
+    b = __shfl(b, src);
+    above = __shfl(above, src);
+    cnt = __shfl(cnt, src);
+    prefix |= b << shift;
+    pmask |= 0xFFu << shift;
+    kk -= above;
+    gt += above;
+    eq = cnt;
+  }
+  tau = prefix;
+}
+
+template <int E, typename KeyF, typename IdF, typename ActF>
+__device__ TopkCut wave_topk_cut(KeyF keyf, IdF idf, ActF act, uint32_t k, uint32_t* hist) {
+  TopkCut c{0u, 0u};
+  uint32_t gt, eq;
+  wave_select<E>(keyf, act, k, hist, c.tau, gt, eq);
+  const uint32_t need = k - gt;   // equal keys to keep, 1 .. eq (uniform)
+  if (need < eq) {
+    uint32_t g2, e2;
+    const uint32_t tau = c.tau;
+    wave_select<E>([&](int e) { return ~idf(e); }, [&](int e) { return act(e) && keyf(e) == tau; }, need, hist,
+                   c.tau2, g2, e2);
+  }
+  return c;
+}
+
+// Per-lane R largest keys (sorted, descending) of E keys.
+template <int R, int E, typename KeyF>
+__device__ __forceinline__ void lane_top(KeyF keyf, uint32_t (&top)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) top[r] = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    uint32_t x = keyf(e);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t hi = max(top[r], x);
+      x = min(top[r], x);
+      top[r] = hi;
+    }
+  }
+}
+
+// Top k (k <= 256) of 4096-id sub-slices: grid (ceil(n_sub / 4), n_rows), one
+// sub-slice per wavefront.  Lane L holds the 4-id groups c = 0..15 starting at
+// id base + 4 (64 c + L) (each load instruction reads 1 KB of consecutive
+// logits).  The floor: the k-th largest of the lanes' top-R lists (R = k / 64
+// rounded up) is reached by at least k elements, so every member of the top k
+// reaches it and only those enter the radix select.
+constexpr int kTkWaveIds = 4096;
+constexpr int kTkWaveChunks = kTkWaveIds / (4 * kWave);   // 16
+
+// Per-wave LDS: the radix histogram and the compacted candidates.
+constexpr int kTkCap = 1024;   // candidates above the floor kept in LDS (fast path)
+struct TkWave {
+  uint32_t hist[256];
+  uint32_t ckey[kTkCap];
+  uint32_t cid[kTkCap];
+};
+
+// Marker left in a sub-slice's first candidate when more than kTkCap keys reach
+// the floor (many equal or near-equal logits); topk_slice_rest redoes those.
+constexpr int32_t kTkOverflow = -2;
+
+template <bool kAligned>
+__device__ __forceinline__ void topk_load_keys(const float* __restrict__ x, int vocab, int base,
+                                               uint32_t (&key)[4 * kTkWaveChunks], int& bad) {
+  const int lane = threadIdx.x & 63;
+  bad = 0;
+#pragma unroll
+  for (int c = 0; c < kTkWaveChunks; ++c) {
+    const f32x4 v = load4<kAligned>(x, base + 4 * (kWave * c + lane), vocab);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       bad |= (v[e] != v[e]) | (v[e] == INFINITY);
       key[4 * c + e] = order_key(v[e]);
     }
   }
-  auto idf = [&](int e) { return (uint32_t)(base + 4 * (kTkThreads * (e >> 2) + t) + (e & 3)); };
+}
+
+template <int R>
+__device__ __forceinline__ uint32_t topk_floor(const uint32_t (&key)[4 * kTkWaveChunks], int k, uint32_t* hist) {
+  uint32_t top[R];
+  lane_top<R, 4 * kTkWaveChunks>([&](int e) { return key[e]; }, top);
+  uint32_t fl, g0, e0;
+  wave_select<R>([&](int r) { return top[r]; }, [](int) { return true; }, (uint32_t)k, hist, fl, g0, e0);
+  return fl;
+}
+
+// Fast path: the keys above the floor (lanes in order, each lane's in id
+// order) go to LDS and the exact select runs on those alone.
+template <bool kAligned, int R>
+__device__ __forceinline__ void topk_wave_fast(const float* __restrict__ x, TopkItem* __restrict__ out,
+                                               uint8_t* __restrict__ badp, int vocab, int base, int k,
+                                               TkWave& L) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[4 * kTkWaveChunks];
+  int bad;
+  topk_load_keys<kAligned>(x, vocab, base, key, bad);
+  const bool any_bad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
+  if (lane == 0) *badp = any_bad ? 1 : 0;
+  auto idf = [&](int e) { return (uint32_t)(base + 4 * (kWave * (e >> 2) + lane) + (e & 3)); };
+  const uint32_t fl = topk_floor<R>(key, k, L.hist);
+  uint32_t n_act = 0;
+#pragma unroll
+  for (int e = 0; e < 4 * kTkWaveChunks; ++e) n_act += key[e] >= fl ? 1u : 0u;
+  const uint32_t act_incl = wave_scan(n_act);
+  const uint32_t total = __shfl(act_incl, 63);
+  if (total > (uint32_t)kTkCap) {
+    if (lane == 0) out[0] = TopkItem{0.f, kTkOverflow};
+    return;
+  }
+  uint32_t off = act_incl - n_act;
+#pragma unroll
+  for (int e = 0; e < 4 * kTkWaveChunks; ++e)
+    if (key[e] >= fl) { L.ckey[off] = key[e]; L.cid[off] = idf(e); ++off; }
+  constexpr int kPer = kTkCap / kWave;
+  uint32_t ck[kPer], ci[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint32_t i = (uint32_t)(lane + kWave * j);
+    ck[j] = i < total ? L.ckey[i] : 0u;
+    ci[j] = i < total ? L.cid[i] : 0xFFFFFFFFu;
+  }
+  auto cact = [&](int j) { return (uint32_t)(lane + kWave * j) < total; };
+  const TopkCut cut = wave_topk_cut<kPer>([&](int j) { return ck[j]; }, [&](int j) { return ci[j]; }, cact,
+                                          (uint32_t)k, L.hist);
+  auto kept = [&](int j) { return cact(j) && (ck[j] > cut.tau || (ck[j] == cut.tau && ~ci[j] >= cut.tau2)); };
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) cnt += kept(j) ? 1u : 0u;
+  uint32_t o = wave_scan(cnt) - cnt;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (kept(j) && o < (uint32_t)k) out[o++] = TopkItem{key_value(ck[j]), (int32_t)ci[j]};
+}
+
+// Overflowed sub-slices: the select over all 4096 register-held keys.
+template <bool kAligned, int R>
+__device__ __forceinline__ void topk_wave_full(const float* __restrict__ x, TopkItem* __restrict__ out, int vocab,
+                                               int base, int k, TkWave& L) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[4 * kTkWaveChunks];
+  int bad;
+  topk_load_keys<kAligned>(x, vocab, base, key, bad);
   auto keyf = [&](int e) { return key[e]; };
-  const uint32_t floor_key = wg_topk_floor<4 * kTkChunks>(keyf, [](int) { return true; }, (uint32_t)k, sh);
-  auto act = [&](int e) { return key[e] >= floor_key; };
-  const TopkCut cut = wg_topk_cut<4 * kTkChunks>(keyf, idf, act, (uint32_t)k, sh);
+  auto idf = [&](int e) { return (uint32_t)(base + 4 * (kWave * (e >> 2) + lane) + (e & 3)); };
+  const uint32_t fl = topk_floor<R>(key, k, L.hist);
+  auto act = [&](int e) { return key[e] >= fl; };
+  const TopkCut cut = wave_topk_cut<4 * kTkWaveChunks>(keyf, idf, act, (uint32_t)k, L.hist);
   auto kept = [&](int e) { return key[e] > cut.tau || (key[e] == cut.tau && ~idf(e) >= cut.tau2); };
   uint32_t cnt = 0;
 #pragma unroll
-  for (int e = 0; e < 4 * kTkChunks; ++e) cnt += kept(e) ? 1u : 0u;
-  uint32_t off = wg_scan(cnt, sh) - cnt;
-  TopkItem* out = cand + ((size_t)row * n_slices + slice) * k;
+  for (int e = 0; e < 4 * kTkWaveChunks; ++e) cnt += kept(e) ? 1u : 0u;
+  uint32_t o = wave_scan(cnt) - cnt;
 #pragma unroll
-  for (int e = 0; e < 4 * kTkChunks; ++e)
-    if (kept(e) && off < (uint32_t)k) out[off++] = TopkItem{key_value(key[e]), (int32_t)idf(e)};
-  bad = __syncthreads_or(bad);
-  if (t == 0) badf[(size_t)row * n_slices + slice] = bad ? 1 : 0;
+  for (int e = 0; e < 4 * kTkWaveChunks; ++e)
+    if (kept(e) && o < (uint32_t)k) out[o++] = TopkItem{key_value(key[e]), (int32_t)idf(e)};
 }
+
+// R = k / 64 rounded up: the length of the per-lane lists behind the floor.
+// grid (ceil(n_sub / 4), n_rows), one 4096-id sub-slice per wavefront.
+template <bool kAligned, int R>
+__global__ __launch_bounds__(kTkThreads) void topk_slice(const float* __restrict__ logits,
+                                                         TopkItem* __restrict__ cand,
+                                                         uint8_t* __restrict__ badf, int vocab, int n_sub,
+                                                         int k) {
+  __shared__ __attribute__((aligned(16))) TkWave lds_w[kTkThreads / kWave];
+  const int w = threadIdx.x >> 6;
+  const int sub = blockIdx.x * (kTkThreads / kWave) + w;
+  const int row = blockIdx.y;
+  if (sub >= n_sub) return;   // whole wavefront; no workgroup barrier follows
+  topk_wave_fast<kAligned, R>(logits + (size_t)row * (size_t)vocab, cand + ((size_t)row * n_sub + sub) * k,
+                              badf + (size_t)row * n_sub + sub, vocab, sub * kTkWaveIds, k, lds_w[w]);
+}
+
+// Same grid; only the sub-slices marked kTkOverflow do any work.
+template <bool kAligned, int R>
+__global__ __launch_bounds__(kTkThreads) void topk_slice_rest(const float* __restrict__ logits,
+                                                              TopkItem* __restrict__ cand, int vocab, int n_sub,
+                                                              int k) {
+  __shared__ __attribute__((aligned(16))) TkWave lds_w[kTkThreads / kWave];
+  const int w = threadIdx.x >> 6;
+  const int sub = blockIdx.x * (kTkThreads / kWave) + w;
+  const int row = blockIdx.y;
+  if (sub >= n_sub) return;
+  TopkItem* out = cand + ((size_t)row * n_sub + sub) * k;
+  if (out[0].id != kTkOverflow) return;   // uniform over the wavefront
+  topk_wave_full<kAligned, R>(logits + (size_t)row * (size_t)vocab, out, vocab, sub * kTkWaveIds, k, lds_w[w]);
+}
+
+template <bool kAligned, int R>
+static void launch_topk_slice_r(const TopkPlan& p, const float* logits, TopkItem* cand, uint8_t* badf,
+                                hipStream_t s) {
+  const dim3 grid((p.n_slices + 3) / 4, p.n);
+  topk_slice<kAligned, R><<<grid, kTkThreads, 0, s>>>(logits, cand, badf, p.vocab, p.n_slices, p.k);
+  topk_slice_rest<kAligned, R><<<grid, kTkThreads, 0, s>>>(logits, cand, p.vocab, p.n_slices, p.k);
+}
+
+template <bool kAligned>
+static void launch_topk_slice(const TopkPlan& p, const float* logits, TopkItem* cand, uint8_t* badf,
+                              hipStream_t s) {
+  if (p.k <= 64) launch_topk_slice_r<kAligned, 1>(p, logits, cand, badf, s);
+  else if (p.k <= 128) launch_topk_slice_r<kAligned, 2>(p, logits, cand, badf, s);
+  else if (p.k <= 192) launch_topk_slice_r<kAligned, 3>(p, logits, cand, badf, s);
+  else launch_topk_slice_r<kAligned, 4>(p, logits, cand, badf, s);
+}
+
+constexpr int kTkRowCap = 2048;   // candidates above the floor compacted into LDS (fast path)
 
 __global__ __launch_bounds__(kTkThreads) void topk_row(const TopkItem* __restrict__ cand,
                                                        const uint8_t* __restrict__ badf,
@@ -894,6 +1117,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_row(const TopkItem* __restric
                                                        int n_canvas, bool want_h) {
   __shared__ TkShared sh;
   __shared__ StatsPartial red[kTkThreads / kWave];
+  __shared__ uint32_t ckey[kTkRowCap], cid[kTkRowCap];
+  __shared__ uint32_t sel_key[256], sel_id[256];
   const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int count = n_slices * k;
   const TopkItem* src = cand + (size_t)row * count;
@@ -912,13 +1137,59 @@ __global__ __launch_bounds__(kTkThreads) void topk_row(const TopkItem* __restric
   }
   auto held = [&](int e) { return t + kTkThreads * e < count; };
   auto keyf = [&](int e) { return key[e]; };
+  auto idf = [&](int e) { return idv[e]; };
   const uint32_t floor_key = wg_topk_floor<kTkRowPer>(keyf, held, (uint32_t)k, sh);
-  auto act = [&](int e) { return held(e) && key[e] >= floor_key; };
-  const TopkCut cut = wg_topk_cut<kTkRowPer>(keyf, [&](int e) { return idv[e]; }, act, (uint32_t)k, sh);
-  auto kept = [&](int e) {
-    return act(e) && (key[e] > cut.tau || (key[e] == cut.tau && ~idv[e] >= cut.tau2));
-  };
+  uint32_t n_act = 0;
+#pragma unroll
+  for (int e = 0; e < kTkRowPer; ++e) n_act += (held(e) && key[e] >= floor_key) ? 1u : 0u;
+  const uint32_t act_incl = wg_scan(n_act, sh);
+  if (t == kTkThreads - 1) sh.res[0] = act_incl;
+  __syncthreads();
+  const uint32_t total = sh.res[0];
+  __syncthreads();
+  // the k kept items, in a fixed order, into sel_key / sel_id
+  if (total <= (uint32_t)kTkRowCap) {
+    uint32_t off = act_incl - n_act;
+#pragma unroll
+    for (int e = 0; e < kTkRowPer; ++e)
+      if (held(e) && key[e] >= floor_key) { ckey[off] = key[e]; cid[off] = idv[e]; ++off; }
+    __syncthreads();
+    constexpr int kPer = kTkRowCap / kTkThreads;   // 8
+    uint32_t ck[kPer], ci[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t i = (uint32_t)(t + kTkThreads * j);
+      ck[j] = i < total ? ckey[i] : 0u;
+      ci[j] = i < total ? cid[i] : 0xFFFFFFFFu;
+    }
+    auto cact = [&](int j) { return (uint32_t)(t + kTkThreads * j) < total; };
+    const TopkCut cut = wg_topk_cut<kPer>([&](int j) { return ck[j]; }, [&](int j) { return ci[j]; }, cact,
+                                          (uint32_t)k, sh);
+    auto kept = [&](int j) { return cact(j) && (ck[j] > cut.tau || (ck[j] == cut.tau && ~ci[j] >= cut.tau2)); };
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) cnt += kept(j) ? 1u : 0u;
+    uint32_t o = wg_scan(cnt, sh) - cnt;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (kept(j) && o < (uint32_t)k) { sel_key[o] = ck[j]; sel_id[o] = ci[j]; ++o; }
+  } else {
+    auto act = [&](int e) { return held(e) && key[e] >= floor_key; };
+    const TopkCut cut = wg_topk_cut<kTkRowPer>(keyf, idf, act, (uint32_t)k, sh);
+    auto kept = [&](int e) {
+      return act(e) && (key[e] > cut.tau || (key[e] == cut.tau && ~idv[e] >= cut.tau2));
+    };
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int e = 0; e < kTkRowPer; ++e) cnt += kept(e) ? 1u : 0u;
+    uint32_t o = wg_scan(cnt, sh) - cnt;
+#pragma unroll
+    for (int e = 0; e < kTkRowPer; ++e)
+      if (kept(e) && o < (uint32_t)k) { sel_key[o] = key[e]; sel_id[o] = idv[e]; ++o; }
+  }
+  __syncthreads();
 
+  // statistics over S, one kept item per thread (t < k)
   const dg_ctrl cb = ctrl[row / n_canvas];
   const uint32_t pos = (uint32_t)(row % n_canvas);
   const float temp = temperature(cb);
@@ -927,21 +1198,17 @@ __global__ __launch_bounds__(kTkThreads) void topk_row(const TopkItem* __restric
   const bool gumbel = (cb.flags & DG_GUMBEL) != 0;
   const float c_t = kLog2e * inv_t;
   const uint32_t k0 = seed_lo(cb.seed), k1 = seed_hi(cb.seed);
+  const bool mine = t < k;
+  const float v = mine ? key_value(sel_key[t]) : -INFINITY;
+  const uint32_t id = mine ? sel_id[t] : 0xFFFFFFFFu;
 
-  // max, argmax, Gumbel argmax over S
-  float m = -INFINITY, gbest = -INFINITY;
-  uint32_t bid = 0xFFFFFFFFu, gid = 0xFFFFFFFFu;
-#pragma unroll
-  for (int e = 0; e < kTkRowPer; ++e) {
-    if (!kept(e)) continue;
-    const float v = key_value(key[e]);
-    if (better(v, idv[e], m, bid)) { m = v; bid = idv[e]; }
-    if (gumbel) {
-      const Philox4 h = philox4x32_10(idv[e] >> 2, pos, cb.gstep, kStreamGumbel, k0, k1);
-      const uint32_t word = (idv[e] & 3u) == 0 ? h.w0 : (idv[e] & 3u) == 1 ? h.w1 : (idv[e] & 3u) == 2 ? h.w2 : h.w3;
-      const float sc = v * inv_t + gumbel_from_bits(word);
-      if (better(sc, idv[e], gbest, gid)) { gbest = sc; gid = idv[e]; }
-    }
+  float m = v, gbest = -INFINITY;
+  uint32_t bid = id, gid = 0xFFFFFFFFu;
+  if (gumbel && mine) {
+    const Philox4 h = philox4x32_10(id >> 2, pos, cb.gstep, kStreamGumbel, k0, k1);
+    const uint32_t word = (id & 3u) == 0 ? h.w0 : (id & 3u) == 1 ? h.w1 : (id & 3u) == 2 ? h.w2 : h.w3;
+    gbest = v * inv_t + gumbel_from_bits(word);
+    gid = id;
   }
   wave_argmax(m, bid);
   wave_argmax(gbest, gid);
@@ -963,26 +1230,19 @@ __global__ __launch_bounds__(kTkThreads) void topk_row(const TopkItem* __restric
   // weights exp(l - m) over S, their sums, and the row's list
   const float mc = (m == -INFINITY) ? 0.0f : -m * kLog2e;
   float s1 = 0.f, st = 0.f, sy = 0.f;
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int e = 0; e < kTkRowPer; ++e) cnt += kept(e) ? 1u : 0u;
-  uint32_t off = wg_scan(cnt, sh) - cnt;
-  TopkItem* out = list + (size_t)row * k;
-#pragma unroll
-  for (int e = 0; e < kTkRowPer; ++e) {
-    if (!kept(e)) continue;
-    const float v = key_value(key[e]);
+  if (mine) {
     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(v, kLog2e, mc));
-    s1 += p;
+    s1 = p;
     if (tempered || want_h) {
       const float y = fmaxf((v - m) * c_t, -200.f);
       const float et = tempered ? __builtin_amdgcn_exp2f(y) : p;
-      st += et;
-      if (want_h) sy += et * y;
+      st = et;
+      if (want_h) sy = et * y;
+    } else {
+      st = p;
     }
-    if (off < (uint32_t)k) out[off++] = TopkItem{p, (int32_t)idv[e]};
+    list[(size_t)row * k + t] = TopkItem{p, (int32_t)id};
   }
-  if (!tempered && !want_h) st = s1;
   s1 = wave_sum(s1);
   st = wave_sum(st);
   sy = wave_sum(sy);
@@ -1132,7 +1392,7 @@ hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void*
 TopkPlan topk_plan(int n_canvas, int batch, int vocab, int d, int k) {
   TopkPlan p{};
   p.n = n_canvas * batch; p.n_canvas = n_canvas; p.batch = batch; p.vocab = vocab; p.d = d; p.k = k;
-  p.n_slices = (vocab + kTkSliceIds - 1) / kTkSliceIds;
+  p.n_slices = (vocab + kTkWaveIds - 1) / kTkWaveIds;
   p.max_candidates = kTkThreads * kTkRowPer;
   p.off_part = 0;
   p.off_cand = align_up((size_t)p.n * sizeof(StatsPartial), 256);
@@ -1160,9 +1420,9 @@ hipError_t launch_sampler_topk(const TopkPlan& p, const float* logits, const flo
 
   prof_begin("topk_slice", s);
   if (p.vocab % 4 == 0)
-    topk_slice<true><<<dim3(p.n_slices, p.n), kTkThreads, 0, s>>>(logits, cand, badf, p.vocab, p.n_slices, p.k);
+    launch_topk_slice<true>(p, logits, cand, badf, s);
   else
-    topk_slice<false><<<dim3(p.n_slices, p.n), kTkThreads, 0, s>>>(logits, cand, badf, p.vocab, p.n_slices, p.k);
+    launch_topk_slice<false>(p, logits, cand, badf, s);
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

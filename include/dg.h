@@ -279,7 +279,7 @@ int dg_sampler_step_eb_batched(const float* logits, const void* emb_packed, int3
  *   top_k           in [1, 256]; top_k >= vocab keeps every id (untruncated)
  *   other arguments as in the batched calls above.
  * Limits: n_canvas in [1, 256], batch in [1, 4096],
- * n_canvas * batch * vocab * 4 < 2^32, and ceil(vocab / 8192) * top_k <= 16384.
+ * n_canvas * batch * vocab * 4 < 2^32, and ceil(vocab / 4096) * top_k <= 16384.
  */
 size_t dg_sampler_workspace_bytes_topk(int n_canvas, int batch, int vocab, int d_model, int top_k);
 int dg_sampler_step_topk(const float* logits, const float* emb, int32_t* canvas_ids,

@@ -179,7 +179,7 @@ def test_topk_sampler_arguments(lib):
     a = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE]
     assert lib.dg_sampler_step_topk(*a, 16, 1, 1000, 64, 0, FAKE, 1 << 30, None) == DG_EINVAL
     assert lib.dg_sampler_step_topk(*a, 16, 1, 1000, 64, 257, FAKE, 1 << 30, None) == DG_EUNSUPPORTED
-    # 66 slices of 8192 ids times 256 candidates exceed what one row pass holds
+    # 132 sub-slices of 4096 ids times 256 candidates exceed what one row pass holds
     assert lib.dg_sampler_step_topk(*a, 1, 1, 16384 * 33, 64, 256, FAKE, 1 << 30, None) == DG_EUNSUPPORTED
     assert b"top_k" in lib.dg_last_error()
     assert lib.dg_sampler_step_topk(*a, 16, 1, 1000, 64, 8, FAKE, 16, None) == DG_EWORKSPACE
