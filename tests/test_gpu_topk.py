@@ -152,3 +152,27 @@ def test_topk_entropy_bounded(n, batch, vocab, d, k):
         got["status"] = dg.read_eb_status(status, b)
         assert check_eb(ref, got) <= 2
         check_z(got["z"], ref["z"])
+
+
+def test_topk_degenerate_rows_take_the_overflow_paths():
+    """Rows of equal logits put every candidate at the cut: more than 1024 keys
+    reach a sub-slice's floor and more than 2048 the row's, so both fallback
+    selects run; the kept set is then decided by ids alone."""
+    torch, dg = require_gpu()
+    rng = np.random.default_rng(12)
+    n, vocab, d, k = 8, 40000, 32, 256
+    logits = (rng.standard_normal((n, vocab)) * 2).astype(np.float32)
+    logits[0] = 0.0                                        # all equal
+    logits[1] = 1.5
+    logits[1, rng.integers(0, vocab, 40)] = 3.0            # 40 at the top, the rest tied below
+    logits[2, 20000:] = logits[2].max() + 1.0              # the upper half tied at the top
+    logits[3] = -np.inf
+    logits[3, [5, 39999]] = [0.0, -1.0]                    # two finite logits
+    emb = (rng.standard_normal((vocab, d)) * 0.02).astype(np.float32)
+    ids = rng.integers(0, vocab, n)
+    ctrl = S.Ctrl(seed=21, flags=S.GUMBEL, tau=0.05, t_start=0.9, t_end=0.9)
+    g_ids, g_mask, g_kappa, g_z, _, _ = run_topk(torch, dg, logits, emb, ids, np.zeros(n, np.uint8), [ctrl], k)
+    ref = K.sampler_step_topk(logits, emb.astype(np.float64), ids, np.zeros(n, np.uint8), ctrl, k)
+    assert check_step(ids, np.zeros(n, np.uint8), g_ids, g_mask, g_kappa, ref, ctrl.tau) <= 1
+    check_z(g_z, ref["z"])
+    np.testing.assert_allclose(g_z[0], emb[:k].astype(np.float64).mean(0), rtol=1e-4, atol=1e-7)
