@@ -711,14 +711,16 @@ __global__ __launch_bounds__(256) void samp_eb_select(EbRows eb, int32_t* __rest
 // logits, ties to the smaller id; the step is then the full one on logits
 // with everything outside S at -inf, so the contraction shrinks to k rows of
 // E per canvas row.
-//   topk_slice   per (4096-id sub-slice, row), one wavefront each: the
-//                sub-slice's own top k by a radix select over order-preserving
-//                keys held in registers (then by id among equal keys); NaN /
-//                +inf flags.
-//   topk_row     per row: the top k of the slices' candidates (same select),
-//                then one split's statistics record (max, argmax, Gumbel
-//                argmax within S, sums at T = 1 and T, entropy term) and the
-//                weights exp(l - m) of S.
+//   topk_slice   per (4096-id sub-slice, row), one wavefront each: a floor
+//                that every member of the sub-slice's top k reaches, the keys
+//                at or above it compacted into LDS, and a radix select over
+//                those order-preserving keys (then by id among equal keys);
+//                NaN / +inf flags.  topk_slice_rest redoes the rare
+//                sub-slices where too many keys reach the floor.
+//   topk_row     per row: the top k of the sub-slices' candidates (floor,
+//                compaction, workgroup-wide select), then one split's
+//                statistics record (max, argmax, Gumbel argmax within S, sums
+//                at T = 1 and T, entropy term) and the weights exp(l - m) of S.
 //   topk_z       z_0 = sum over S of exp(l - m) E[id] from the fp32 table.
 //   samp_combine, samp_finalize / samp_eb_select as in the full sampler, with
 //                one split.
