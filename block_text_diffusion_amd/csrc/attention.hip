@@ -215,6 +215,11 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
   const int vbyte = 8 * (r16 & 1);
 
   kv_store<D, kF8>(ra, lds, t);
+  // blocks 1 and 2 in flight before the loop: every block's loads are issued
+  // two blocks ahead of their use
+  KvRegs<D, kF8> rb;
+  if (nb > 1) fetch(rb, 1);
+  if (nb > 2) fetch(ra, 2);
   __syncthreads();
 
   // one block: scores, online softmax, O^T update (reads one LDS stage)
@@ -308,14 +313,22 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
 
   };
 
-  // The next block's loads are in flight in registers while this one is
-  // multiplied; two LDS stages.
-  for (int b = 0; b < nb; ++b) {
-    if (b + 1 < nb) fetch(ra, b + 1);
+  // Two LDS stages; two register sets.  Iteration b multiplies block b,
+  // stores block b + 1 (loaded during the two previous iterations) into the
+  // other stage, and sends the loads of block b + 3 into the freed registers.
+  // rn holds block b + 1: rb for even b, ra for odd b.
+  auto iter = [&](int b, KvRegs<D, kF8>& rn) {
     step(b, lds + (b & 1) * G::kStageBytes);
-    if (b + 1 < nb) kv_store<D, kF8>(ra, lds + ((b + 1) & 1) * G::kStageBytes, t);
+    if (b + 1 < nb) kv_store<D, kF8>(rn, lds + ((b + 1) & 1) * G::kStageBytes, t);
+    if (b + 3 < nb) fetch(rn, b + 3);
     __syncthreads();
+  };
+  int b = 0;
+  for (; b + 1 < nb; b += 2) {
+    iter(b, rb);
+    iter(b + 1, ra);
   }
+  if (b < nb) iter(b, rb);
 
   // ---- merge the two key halves: waves 4-7 hand (m, l, O) to waves 0-3 ----
   f32x4* xo = reinterpret_cast<f32x4*>(lds);   // [row group][16 DB-chunks][64 lanes]
