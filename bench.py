@@ -171,6 +171,9 @@ def main():
     # ---- the decode run: 4096-token prefix, four 256-token canvases ----
     dec = decode_run_timing(torch, dg, T["emb"], vocab, dm)
     log(f"decode run: {dec['tokens']} tokens in {dec['steps']} steps, {dec['tokens_per_s']:.0f} tokens/s")
+    dec_eb = decode_run_timing(torch, dg, T["emb"], vocab, dm, entropy_bounded=True)
+    log(f"decode run, entropy-bounded: {dec_eb['tokens']} tokens in {dec_eb['steps']} steps, "
+        f"{dec_eb['tokens_per_s']:.0f} tokens/s")
 
     if a.copy_probe_mib:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters calibrate
@@ -224,6 +227,7 @@ def main():
                    "attention": attn,
                    "eb_sampler": eb,
                    "decode_run": dec,
+                   "decode_run_entropy_bounded": dec_eb,
                    "batched_sampler": batched,
                    "topk_sampler": topk,
                    "attention_fp8": attn_fp8,
@@ -234,11 +238,14 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def decode_run_timing(torch, dg, emb_packed, vocab, dm):
+def decode_run_timing(torch, dg, emb_packed, vocab, dm, entropy_bounded=False):
     """The decode-run workload end to end on the device: per canvas, attention
     over the growing prefix, canvas init, then steps of synthetic logits +
-    Gumbel sampler (T 0.8 -> 0.4) until no position is open (one host read of
-    the open count per step), then the KV append.  Tokens/s over the whole run."""
+    Gumbel sampler (T 0.8 -> 0.4) until the canvas is finished (one host read
+    per step), then the KV append.  Threshold mode: until no position is open.
+    Entropy-bounded mode (the pages' default): the accepted positions stand in
+    for the committed mask of the synthetic generator, and the canvas ends when
+    adaptive stopping fires (or after s_max steps).  Tokens/s over the whole run."""
     import workloads
     c = workloads.CONFIGS[5]
     n, p0, hq, hkv, hd = c["n"], c["n_prefix"], c["hq"], c["hkv"], c["head_dim"]
@@ -260,6 +267,9 @@ def decode_run_timing(torch, dg, emb_packed, vocab, dm):
     mask = torch.zeros(n, dtype=torch.uint8, device="cuda")
     z = torch.empty((n, dm), dtype=torch.float32, device="cuda")
     nu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ent = torch.empty(n, dtype=torch.float32, device="cuda")
+    amax = torch.empty(n, dtype=torch.int32, device="cuda")
+    status = torch.zeros(16, dtype=torch.uint8, device="cuda")
     attn = torch.empty((n, hq, hd), dtype=torch.float32, device="cuda")
     ctrl = dg.make_ctrl(seed=c["seed"], s_max=c["s_max"], tau=c["tau"], t_start=c["t_start"],
                         t_end=c["t_end"], flags=dg.DG_AUTO_ADVANCE | dg.DG_GUMBEL | dg.DG_T_SCHEDULE)
@@ -272,12 +282,21 @@ def decode_run_timing(torch, dg, emb_packed, vocab, dm):
     for q, kc, vc in blocks:
         dg.dg_canvas_attention(q, kbuf[:p], vbuf[:p], kc, vc, out=attn, workspace=ws)
         dg.dg_canvas_init(ids, mask, ctrl, vocab)
-        while True:
-            dg.dg_synth_logits(logits, ids, mask, ctrl, table)
-            dg.dg_sampler_step(logits, emb_packed, ids, mask, z, None, nu, ctrl, workspace=ws)
-            steps += 1
-            if int(nu.item()) == 0:
-                break
+        if entropy_bounded:
+            amax.fill_(-1)
+            for _ in range(c["s_max"]):
+                dg.dg_synth_logits(logits, ids, mask, ctrl, table)
+                dg.dg_sampler_step_eb(logits, emb_packed, ids, mask, z, ent, amax, status, ctrl, workspace=ws)
+                steps += 1
+                if dg.read_eb_status(status)["stop"]:
+                    break
+        else:
+            while True:
+                dg.dg_synth_logits(logits, ids, mask, ctrl, table)
+                dg.dg_sampler_step(logits, emb_packed, ids, mask, z, None, nu, ctrl, workspace=ws)
+                steps += 1
+                if int(nu.item()) == 0:
+                    break
         dg.dg_kv_append(kbuf, vbuf, kc, vc, p)
         p += n
     torch.cuda.synchronize()
@@ -285,7 +304,9 @@ def decode_run_timing(torch, dg, emb_packed, vocab, dm):
     tokens = c["blocks"] * n
     return {"tokens": tokens, "steps": steps, "seconds": round(dt, 5),
             "tokens_per_s": round(tokens / dt, 1), "ms_per_step": round(dt * 1e3 / steps, 4),
-            "note": "synthetic logits generated on the device inside the loop; one host read per step"}
+            "note": "synthetic logits generated on the device inside the loop; one host read per step"
+                    + ("; entropy-bounded sampler, budget 0.1, adaptive stop at mean entropy 0.005"
+                       if entropy_bounded else "")}
 
 
 def batched_sampler_timing(torch, dg, T, n, vocab, dm, steps, batches=(2, 4, 8)):
