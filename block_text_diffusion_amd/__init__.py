@@ -15,7 +15,7 @@ __all__ = [
     "dg_canvas_attention", "dg_canvas_attention_fp8", "dg_sampler_step", "dg_sampler_step_eb", "read_eb_status",
     "dg_sampler_step_batched", "dg_sampler_step_eb_batched", "dg_sampler_workspace_bytes_batched",
     "dg_sampler_step_topk", "dg_sampler_step_eb_topk", "dg_sampler_workspace_bytes_topk",
-    "stack_ctrl", "dg_embedding_pack", "dg_embedding_packed_bytes", "dg_denoise_step", "StepGraph", "dg_canvas_init",
+    "stack_ctrl", "dg_embedding_pack", "dg_embedding_packed_bytes", "dg_denoise_step", "dg_denoise_step_eb", "StepGraph", "StepGraphEB", "dg_canvas_init",
     "dg_kv_append", "dg_synth_logits", "dg_philox_fill", "dg_attention_workspace_bytes",
     "dg_sampler_workspace_bytes", "dg_denoise_workspace_bytes", "dg_profile_enable",
     "dg_profile_read", "make_ctrl", "read_ctrl", "write_ctrl", "DG_GUMBEL", "DG_COMMIT_ONLY",
@@ -334,6 +334,36 @@ def dg_denoise_step(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits,
     check(load().dg_denoise_step(*args, _stream(stream)))
 
 
+def _denoise_eb_args(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, scale, logits, emb, canvas_ids,
+                     accepted, selfcond, entropy, argmax, status, ctrl, budget, stop_entropy, ws):
+    n, hq, d = q.shape
+    hkv = k_canvas.shape[1]
+    n_prefix = 0 if k_prefix is None else k_prefix.shape[0]
+    vocab = logits.shape[1]
+    dm = selfcond.shape[1]
+    if emb.numel() < dg_embedding_packed_bytes(vocab, dm):
+        raise ValueError("emb_packed is smaller than dg_embedding_packed_bytes(vocab, d_model)")
+    return (_ptr(q), _ptr(k_prefix) if n_prefix else None, _ptr(v_prefix) if n_prefix else None,
+            _ptr(k_canvas), _ptr(v_canvas), _ptr(attn_out), n_prefix, hq, hkv, d, _qkv_dtype(q),
+            float(scale), _ptr(logits), _ptr(emb), _ptr(canvas_ids), _ptr(accepted), _ptr(selfcond),
+            _ptr(entropy), _ptr(argmax), _ptr(status), _ptr(ctrl), float(budget), float(stop_entropy),
+            n, vocab, dm, _ptr(ws), ws.numel())
+
+
+def dg_denoise_step_eb(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits, emb_packed, canvas_ids,
+                       accepted, selfcond, entropy, argmax, status, ctrl, budget=0.1, stop_entropy=0.005,
+                       scale=0.0, workspace=None, stream=None):
+    """Attention then the entropy-bounded sampler step (dg_sampler_step_eb)."""
+    n, hq, d = q.shape
+    nbytes = dg_denoise_workspace_bytes(n, 0 if k_prefix is None else k_prefix.shape[0], hq,
+                                        k_canvas.shape[1], d, logits.shape[1], selfcond.shape[1])
+    ws = _workspace(nbytes, q.device, workspace)
+    args = _denoise_eb_args(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, scale, logits, emb_packed,
+                            canvas_ids, accepted, selfcond, entropy, argmax, status, ctrl, budget, stop_entropy,
+                            ws)
+    check(load().dg_denoise_step_eb(*args, _stream(stream)))
+
+
 class StepGraph:
     """dg_step_graph_create / _launch / _destroy: one captured denoising step.
 
@@ -369,6 +399,27 @@ class StepGraph:
             self.close()
         except Exception:
             pass
+
+
+class StepGraphEB(StepGraph):
+    """dg_step_graph_create_eb: one captured step with the entropy-bounded sampler."""
+
+    def __init__(self, q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits, emb_packed, canvas_ids,
+                 accepted, selfcond, entropy, argmax, status, ctrl, budget=0.1, stop_entropy=0.005,
+                 scale=0.0, workspace=None):
+        n, hq, d = q.shape
+        nbytes = dg_denoise_workspace_bytes(n, 0 if k_prefix is None else k_prefix.shape[0], hq,
+                                            k_canvas.shape[1], d, logits.shape[1], selfcond.shape[1])
+        self.handle = None
+        self.ws = _workspace(nbytes, q.device, workspace)
+        self._keep = (q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits, emb_packed, canvas_ids,
+                      accepted, selfcond, entropy, argmax, status, ctrl)
+        args = _denoise_eb_args(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, scale, logits,
+                                emb_packed, canvas_ids, accepted, selfcond, entropy, argmax, status, ctrl,
+                                budget, stop_entropy, self.ws)
+        handle = ctypes.c_void_p()
+        check(load().dg_step_graph_create_eb(*args, ctypes.byref(handle)))
+        self.handle = handle
 
 
 # ---- block loop helpers ----

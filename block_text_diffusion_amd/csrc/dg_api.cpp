@@ -335,22 +335,46 @@ int dg_denoise_step(const void* q, const void* kp, const void* vp, const void* k
   return DG_OK;
 }
 
+int dg_denoise_step_eb(const void* q, const void* kp, const void* vp, const void* kc, const void* vc,
+                       float* attn_out, int np, int hq, int hkv, int d, int dtype, float scale,
+                       const float* logits, const void* emb, int32_t* ids, uint8_t* accepted, float* z,
+                       float* entropy, int32_t* argmax, dg_eb_status* status, dg_ctrl* ctrl, float budget,
+                       float stop_entropy, int n, int vocab, int dm, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  if (dtype == DG_FP8_E4M3) return fail(DG_EUNSUPPORTED, "denoise_eb: FP8 attention inputs take dg_canvas_attention_fp8");
+  int st = check_attention(q, kp, vp, kc, vc, attn_out, n, np, hq, hkv, d, dtype);
+  if (st != DG_OK) return st;
+  st = check_sampler(logits, emb, ids, accepted, z, reinterpret_cast<const uint32_t*>(status), ctrl, n, vocab, dm);
+  if (st != DG_OK) return st;
+  if (!argmax || !status) return fail(DG_EINVAL, "denoise_eb: null argmax or status");
+  if (!(budget >= 0.f) || !std::isfinite(budget)) return fail(DG_EINVAL, "denoise_eb: budget must be finite and >= 0");
+  if (!(stop_entropy >= 0.f) || !std::isfinite(stop_entropy))
+    return fail(DG_EINVAL, "denoise_eb: stop_entropy must be finite and >= 0");
+  const size_t need = dg_denoise_workspace_bytes(n, np, hq, hkv, d, vocab, dm);
+  if (!ws || ws_bytes < need) return fail(DG_EWORKSPACE, "denoise_eb: workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned16(ws)) return fail(DG_EINVAL, "denoise_eb: workspace misaligned");
+  if (!(scale > 0.f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)d);
+  const dg::AttnPlan ap = dg::attn_plan(n, np, hq, hkv, d);
+  hipError_t e = dg::launch_attention(ap, q, kp, vp, kc, vc, attn_out, dtype, scale, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "denoise_eb attention launch");
+  const dg::SamplerPlan sp = dg::sampler_plan(n, 1, vocab, dm);
+  const dg::EbCall eb{true, budget, stop_entropy, entropy, argmax, status};
+  e = dg::launch_sampler(sp, logits, emb, ids, accepted, z, nullptr, nullptr, ctrl, ws, stream, eb);
+  if (e != hipSuccess) return hip_fail(e, "denoise_eb sampler launch");
+  return DG_OK;
+}
+
 struct dg_step_graph {
   hipGraph_t graph;
   hipGraphExec_t exec;
 };
 
-int dg_step_graph_create(const void* q, const void* kp, const void* vp, const void* kc,
-                         const void* vc, float* attn_out, int np, int hq, int hkv, int d, int dtype,
-                         float scale, const float* logits, const void* emb, int32_t* ids,
-                         uint8_t* committed, float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl,
-                         int n, int vocab, int dm, void* ws, size_t ws_bytes, dg_step_graph** out) {
-  if (!out) return fail(DG_EINVAL, "graph: null output handle");
-  *out = nullptr;
-  int st = check_attention(q, kp, vp, kc, vc, attn_out, n, np, hq, hkv, d, dtype);
-  if (st != DG_OK) return st;
-  st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, dm);
-  if (st != DG_OK) return st;
+}  // extern "C"
+
+namespace {
+// Capture whatever `record` launches on a private stream into one graph.
+template <typename F>
+int capture_step(F record, dg_step_graph** out) {
   hipStream_t cs = nullptr;
   hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
   if (e != hipSuccess) return hip_fail(e, "graph: stream create");
@@ -360,8 +384,7 @@ int dg_step_graph_create(const void* q, const void* kp, const void* vp, const vo
     return hip_fail(e, "graph: begin capture");
   }
   g_capturing = true;
-  st = dg_denoise_step(q, kp, vp, kc, vc, attn_out, np, hq, hkv, d, dtype, scale, logits, emb, ids,
-                       committed, z, conf, n_unc, ctrl, n, vocab, dm, ws, ws_bytes, cs);
+  const int st = record(cs);
   g_capturing = false;
   hipGraph_t graph = nullptr;
   hipError_t e2 = hipStreamEndCapture(cs, &graph);
@@ -379,6 +402,45 @@ int dg_step_graph_create(const void* q, const void* kp, const void* vp, const vo
   }
   *out = new dg_step_graph{graph, exec};
   return DG_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int dg_step_graph_create(const void* q, const void* kp, const void* vp, const void* kc,
+                         const void* vc, float* attn_out, int np, int hq, int hkv, int d, int dtype,
+                         float scale, const float* logits, const void* emb, int32_t* ids,
+                         uint8_t* committed, float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl,
+                         int n, int vocab, int dm, void* ws, size_t ws_bytes, dg_step_graph** out) {
+  if (!out) return fail(DG_EINVAL, "graph: null output handle");
+  *out = nullptr;
+  int st = check_attention(q, kp, vp, kc, vc, attn_out, n, np, hq, hkv, d, dtype);
+  if (st != DG_OK) return st;
+  st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, dm);
+  if (st != DG_OK) return st;
+  return capture_step([&](hipStream_t cs) {
+    return dg_denoise_step(q, kp, vp, kc, vc, attn_out, np, hq, hkv, d, dtype, scale, logits, emb, ids,
+                           committed, z, conf, n_unc, ctrl, n, vocab, dm, ws, ws_bytes, cs);
+  }, out);
+}
+
+int dg_step_graph_create_eb(const void* q, const void* kp, const void* vp, const void* kc, const void* vc,
+                            float* attn_out, int np, int hq, int hkv, int d, int dtype, float scale,
+                            const float* logits, const void* emb, int32_t* ids, uint8_t* accepted, float* z,
+                            float* entropy, int32_t* argmax, dg_eb_status* status, dg_ctrl* ctrl, float budget,
+                            float stop_entropy, int n, int vocab, int dm, void* ws, size_t ws_bytes,
+                            dg_step_graph** out) {
+  if (!out) return fail(DG_EINVAL, "graph: null output handle");
+  *out = nullptr;
+  int st = check_attention(q, kp, vp, kc, vc, attn_out, n, np, hq, hkv, d, dtype);
+  if (st != DG_OK) return st;
+  st = check_sampler(logits, emb, ids, accepted, z, reinterpret_cast<const uint32_t*>(status), ctrl, n, vocab, dm);
+  if (st != DG_OK) return st;
+  return capture_step([&](hipStream_t cs) {
+    return dg_denoise_step_eb(q, kp, vp, kc, vc, attn_out, np, hq, hkv, d, dtype, scale, logits, emb, ids,
+                              accepted, z, entropy, argmax, status, ctrl, budget, stop_entropy, n, vocab, dm,
+                              ws, ws_bytes, cs);
+  }, out);
 }
 
 int dg_step_graph_launch(dg_step_graph* g, hipStream_t stream) {

@@ -313,6 +313,20 @@ int dg_denoise_step(const void* q, const void* k_prefix, const void* v_prefix,
                     int n_canvas, int vocab, int d_model,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * The same step with the entropy-bounded sampler (the pages' default):
+ * attention, then dg_sampler_step_eb, on one stream with one workspace
+ * (dg_denoise_workspace_bytes).  Sampler arguments as dg_sampler_step_eb.
+ */
+int dg_denoise_step_eb(const void* q, const void* k_prefix, const void* v_prefix,
+                       const void* k_canvas, const void* v_canvas, float* attn_out,
+                       int n_prefix, int hq, int hkv, int head_dim, int dtype, float scale,
+                       const float* logits, const void* emb_packed, int32_t* canvas_ids,
+                       uint8_t* accepted, float* selfcond, float* entropy, int32_t* argmax,
+                       dg_eb_status* status, dg_ctrl* ctrl, float budget, float stop_entropy,
+                       int n_canvas, int vocab, int d_model,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 typedef struct dg_step_graph dg_step_graph;
 
 /*
@@ -329,6 +343,15 @@ int dg_step_graph_create(const void* q, const void* k_prefix, const void* v_pref
                          uint32_t* n_uncommitted, dg_ctrl* ctrl,
                          int n_canvas, int vocab, int d_model,
                          void* workspace, size_t workspace_bytes, dg_step_graph** graph);
+/* Capture dg_denoise_step_eb (same arguments) into a graph, as above. */
+int dg_step_graph_create_eb(const void* q, const void* k_prefix, const void* v_prefix,
+                            const void* k_canvas, const void* v_canvas, float* attn_out,
+                            int n_prefix, int hq, int hkv, int head_dim, int dtype, float scale,
+                            const float* logits, const void* emb_packed, int32_t* canvas_ids,
+                            uint8_t* accepted, float* selfcond, float* entropy, int32_t* argmax,
+                            dg_eb_status* status, dg_ctrl* ctrl, float budget, float stop_entropy,
+                            int n_canvas, int vocab, int d_model,
+                            void* workspace, size_t workspace_bytes, dg_step_graph** graph);
 int dg_step_graph_launch(dg_step_graph* graph, hipStream_t stream);
 void dg_step_graph_destroy(dg_step_graph* graph);
 

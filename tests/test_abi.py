@@ -203,3 +203,14 @@ def test_fp8_attention_arguments(lib):
     # the bf16 entry points do not take FP8 (no scales there)
     assert lib.dg_canvas_attention_ex(*a[:11], DG_FP8_E4M3, 0.0, 0, FAKE, big, None) == DG_EINVAL
     assert b"fp8" in lib.dg_last_error()
+
+
+def test_entropy_bounded_step_and_graph_arguments(lib):
+    from block_text_diffusion_amd._lib import DG_EINVAL, DG_EUNSUPPORTED, DG_EWORKSPACE, DG_FP8_E4M3
+    a = [FAKE] * 6 + [64, 8, 8, 64, 1, 0.0] + [FAKE] * 9
+    assert lib.dg_denoise_step_eb(*a, 0.1, 0.005, 16, 1000, 64, FAKE, 16, None) == DG_EWORKSPACE
+    assert lib.dg_denoise_step_eb(*a, -1.0, 0.005, 16, 1000, 64, FAKE, 1 << 30, None) == DG_EINVAL
+    b = list(a)
+    b[10] = DG_FP8_E4M3
+    assert lib.dg_denoise_step_eb(*b, 0.1, 0.005, 16, 1000, 64, FAKE, 1 << 30, None) == DG_EUNSUPPORTED
+    assert lib.dg_step_graph_create_eb(*a, 0.1, 0.005, 16, 1000, 64, FAKE, 1 << 30, None) == DG_EINVAL

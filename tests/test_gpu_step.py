@@ -94,3 +94,59 @@ def test_eager_and_graph_steps(inputs, flags):
             assert dg.read_ctrl(st["ctrl"])["gstep"] == k + 1
     finally:
         graph.close()
+
+
+def test_entropy_bounded_step_eager_and_graph(inputs):
+    """The step with the entropy-bounded sampler: eager steps against the oracle,
+    then the same steps replayed from a captured graph, bit for bit."""
+    from oracle import eb as EB
+    from test_gpu_eb import BUDGET, STOP, check_eb
+    torch, dg = require_gpu()
+    flags = S.AUTO_ADVANCE | S.GUMBEL | S.T_SCHEDULE
+    ctrl = S.Ctrl(seed=8, s_max=48, flags=flags, t_start=0.8, t_end=0.4)
+    n = inputs["q"].shape[0]
+
+    def state():
+        st = device_state(torch, dg, inputs, ctrl)
+        st["ent"] = torch.empty(n, dtype=torch.float32, device="cuda")
+        st["amax"] = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+        st["status"] = torch.zeros(16, dtype=torch.uint8, device="cuda")
+        return st
+
+    def eb_args(st):
+        return (st["q"], st["kp"], st["vp"], st["kc"], st["vc"], st["attn"], st["logits"], st["emb"], st["ids"],
+                st["mask"], st["z"], st["ent"], st["amax"], st["status"], st["ctrl"])
+
+    def snap(st):
+        torch.cuda.synchronize()
+        return {k: st[k].cpu().numpy().copy() for k in ("attn", "ids", "mask", "z", "ent", "amax", "status", "ctrl")}
+
+    log("eb step: eager")
+    st = state()
+    eager = []
+    for _ in range(3):
+        dg.dg_denoise_step_eb(*eb_args(st), budget=BUDGET, stop_entropy=STOP)
+        eager.append(snap(st))
+    ref_attn = canvas_attention(inputs["q"], inputs["kp"], inputs["vp"], inputs["kc"], inputs["vc"])
+    assert np.abs(eager[0]["attn"] - ref_attn).max() <= ATTN_MAX_ABS
+    log("eb step: oracle step 0")
+    ref = EB.eb_step(inputs["logits"], inputs["emb"].astype(np.float64), inputs["ids"], ctrl, None, BUDGET, STOP,
+                     z_rows=ROWS)
+    got = dict(ids=eager[0]["ids"].astype(np.int64), accepted=eager[0]["mask"], entropy=eager[0]["ent"],
+               argmax=eager[0]["amax"].astype(np.int64), z=eager[0]["z"],
+               status=dg.read_eb_status(torch.from_numpy(eager[0]["status"])))
+    assert check_eb(ref, got) <= 2
+    check_z(got["z"][ROWS], ref["z"])
+
+    log("eb step: graph")
+    st = state()
+    graph = dg.StepGraphEB(*eb_args(st), budget=BUDGET, stop_entropy=STOP)
+    try:
+        for k in range(3):
+            graph.launch()
+            g = snap(st)
+            assert torch.ones(1 << 20, device="cuda").sum().item() == float(1 << 20)   # unrelated eager work
+            for key in g:
+                np.testing.assert_array_equal(g[key], eager[k][key], err_msg=f"replay {k} {key}")
+    finally:
+        graph.close()
