@@ -48,11 +48,15 @@ __device__ __forceinline__ int k_slot(int key, int c) {
   if constexpr (D == 128) return c ^ (key & 15);
   else return c ^ ((key ^ (key >> 3)) & 7);
 }
-// V rows: the transposing reads take two adjacent chunks of four consecutive
-// keys; this map sends those eight 16-byte pieces to eight different slots.
+// V rows: a 16-lane group of a transposing read takes four consecutive keys
+// (k & 3 = 0..3) in two adjacent chunks, and the two groups of a half-wave take
+// the same keys in the next two chunks.  For D = 128 the map sends the sixteen
+// 16-byte pieces of a half-wave to sixteen different slots (distinct modulo 8
+// within each group), so the reads are free of bank conflicts whether the LDS
+// serves 16 or 32 lanes of 8-byte reads per cycle.
 template <int D>
 __device__ __forceinline__ int v_slot(int key, int c) {
-  if constexpr (D == 128) return c ^ (((key & 7) << 1) | ((key >> 3) & 1));
+  if constexpr (D == 128) return c ^ ((4 * (key & 3)) ^ (2 * ((key ^ (key >> 1)) & 1)));
   else return c ^ (((key & 3) << 1) | ((key >> 2) & 1));
 }
 
