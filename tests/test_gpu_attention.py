@@ -43,6 +43,8 @@ def test_workloads(workload):
     (64, 200, 16, 4, 128, "bf16"),     # group of 4 query heads per KV head
     (130, 300, 8, 2, 64, "f32"),       # fp32 inputs staged as bf16, D=64, ragged
     (256, 5120, 16, 8, 128, "bf16"),   # largest prefix of the decode run
+    (64, 0, 16, 8, 128, "bf16"),       # one key block in all: one chunk, output written directly
+    (40, 0, 8, 2, 64, "f32"),          # the same single-chunk path at D=64, ragged block
 ])
 def test_shapes(n, p, hq, hkv, d, qkv):
     torch, dg = require_gpu()
@@ -86,6 +88,7 @@ def test_deterministic():
     (100, 37, 16, 8, 128, "bf16"),     # ragged tiles and blocks
     (130, 300, 8, 2, 64, "f32"),       # fp32 inputs, D=64
     (1, 5, 8, 8, 64, "bf16"),          # a single canvas position
+    (64, 0, 16, 8, 128, "bf16"),       # single chunk: the direct-output path with the causal mask
 ])
 def test_causal(n, p, hq, hkv, d, qkv):
     torch, dg = require_gpu()

@@ -44,6 +44,7 @@ def test_long_context_fp8_with_scales():
     (1, 5, 8, 8, 64, False),
     (256, 512, 16, 8, 128, True),
     (77, 130, 16, 4, 64, True),
+    (64, 0, 16, 8, 128, False),        # one key block: a single chunk, output written directly
 ])
 def test_fp8_shapes(n, p, hq, hkv, d, causal):
     torch, dg = require_gpu()
