@@ -12,9 +12,9 @@
 // Inside a workgroup.  Eight wavefronts: wave w owns query rows 32(w%4)..+31
 // and keys 32(w/4)..+31 of every block, with its own running max and sum; the
 // two key halves are merged through LDS at the end.  K and V blocks go to a
-// double-buffered LDS stage through registers (the next block's loads are in
-// flight while the current one is multiplied), both kept as [key][d] rows with
-// xor-swizzled 16-byte chunks.  Scores are formed
+// double-buffered LDS stage through registers (each block's loads are issued
+// two blocks ahead of its use), both kept as [key][d] rows with xor-swizzled
+// 16-byte chunks.  Scores are formed
 // transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16 (a lane holds 16 keys
 // of one query, so the row softmax needs one cross-lane exchange) and feed
 // O^T = V^T P^T straight from the score registers; the V^T operand comes from
