@@ -111,6 +111,17 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / a.steps
     steps_per_s = a.steps / elapsed
+    # spread of single replays (events between replays on the launch stream), after the timed region
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    evs[0].record()
+    for i in range(a.steps):
+        graph.launch()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_replay = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(a.steps)])
+    replay_ms = {"median": round(float(np.median(per_replay)), 4),
+                 "p10": round(float(np.percentile(per_replay, 10)), 4),
+                 "p90": round(float(np.percentile(per_replay, 90)), 4)}
 
     # ---- per-kernel durations (HIP events on the launch stream, eager calls,
     # as many steps as the timed region, right after it) ----
@@ -221,6 +232,7 @@ def main():
         "config": {"workload": "long_context_step: canvas 256, prefix 4096, 16q/8kv heads, head_dim 128 "
                                "bf16; vocab 262144, d_model 3072 fp32; one captured graph per step",
                    "canvas_tokens_per_s": round(256 * steps_per_s, 1),
+                   "replay_ms": replay_ms,
                    "per_kernel_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
                    "embedding_pack_ms_once": round(pack_ms, 2),
                    "attention": attn,
@@ -339,51 +351,57 @@ def batched_sampler_timing(torch, dg, T, n, vocab, dm, steps, batches=(2, 4, 8))
     return out
 
 
-def bf16_attention_timing(torch, dg, T, n, p, hq, hkv, hd, steps):
+def bf16_attention_timing(torch, dg, T, n, p, hq, hkv, hd, steps, n_sets=16):
     """Canvas attention of the headline step alone (bf16 inputs, the long-context
-    shapes): eager calls back to back between two events on the launch stream.
-    Per-kernel HIP events around each launch add a few microseconds of event
-    overhead to kernels this short, so the attention figure is taken this way."""
+    shapes): eager calls back to back between two events on the launch stream,
+    cycling through n_sets copies of Q/K/V (16 x 17.8 MB of K/V, more than the
+    256 MB last-level cache) so no call finds its K/V left in cache by the
+    previous one.  Per-kernel HIP events around each launch add a few
+    microseconds of event overhead to kernels this short, so the attention
+    figure is taken this way."""
     ws = torch.empty(dg.dg_attention_workspace_bytes(n, p, hq, hkv, hd), dtype=torch.uint8, device="cuda")
-    run = lambda: dg.dg_canvas_attention(T["q"], T["kp"], T["vp"], T["kc"], T["vc"], out=T["attn"],
-                                         workspace=ws)
-    for _ in range(3):
-        run()
+    sets = [tuple(T[k].clone() for k in ("q", "kp", "vp", "kc", "vc")) for _ in range(n_sets)]
+    run = lambda i: dg.dg_canvas_attention(*sets[i % n_sets], out=T["attn"], workspace=ws)
+    for i in range(n_sets):
+        run(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(steps):
-        run()
+    for i in range(steps):
+        run(i)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
     flops = 4.0 * n * (p + n) * hd * hq
     return {"us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 1),
             "frac_bf16_peak": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "timing": "eager calls back to back between two events (partial + combine)"}
+            "timing": f"eager calls back to back between two events (partial + combine), {n_sets} rotated Q/K/V sets"}
 
 
-def fp8_attention_timing(torch, dg, workloads, n, p, hq, hkv, hd, steps):
+def fp8_attention_timing(torch, dg, workloads, n, p, hq, hkv, hd, steps, n_sets=32):
     """Canvas attention with OCP E4M3 inputs (the long-context shapes), eager
-    calls between two events, and the per-kernel split."""
-    q, kp, vp, kc, vc = (torch.from_numpy(x).cuda() for x in workloads.attention_inputs_fp8(4))
+    calls between two events, and the per-kernel split.  The calls cycle
+    through n_sets copies of Q/K/V (32 x 8.9 MB of K/V, more than the 256 MB
+    last-level cache)."""
+    base = [torch.from_numpy(x).cuda() for x in workloads.attention_inputs_fp8(4)]
+    sets = [tuple(t.clone() for t in base) for _ in range(n_sets)]
     out = torch.empty((n, hq, hd), dtype=torch.float32, device="cuda")
     ws = torch.empty(dg.dg_attention_workspace_bytes(n, p, hq, hkv, hd), dtype=torch.uint8, device="cuda")
-    run = lambda: dg.dg_canvas_attention_fp8(q, kp, vp, kc, vc, 1.0, 1.0, 1.0, out=out, workspace=ws)
-    for _ in range(3):
-        run()
+    run = lambda i: dg.dg_canvas_attention_fp8(*sets[i % n_sets], 1.0, 1.0, 1.0, out=out, workspace=ws)
+    for i in range(n_sets):
+        run(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(steps):
-        run()
+    for i in range(steps):
+        run(i)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
     dg.dg_profile_enable(True)
     dg.dg_profile_read()
-    for _ in range(steps):
-        run()
+    for i in range(steps):
+        run(i)
     torch.cuda.synchronize()
     prof = dg.dg_profile_read()
     dg.dg_profile_enable(False)
