@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="eager steps timed kernel by kernel (default: as many as --steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="also time the tiny, mid and full-vocabulary-sampler workloads on the GPU and "
+                         "with the CPU oracle (context; not part of the headline line's value)")
     ap.add_argument("--blas-reference", action="store_true",
                     help="also time one plain bf16 GEMM of the contraction's shape through torch")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -215,6 +218,7 @@ def main():
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(q, kp, vp, kc, vc, emb, logits, ids, mask)
+    others = workload_sweep(torch, dg, workloads) if a.all_workloads else None
 
     out = {
         "metric": "denoise steps/s (attn+sampler) at 262k vocab, 4096 ctx",
@@ -236,6 +240,7 @@ def main():
                    "per_kernel_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
                    "embedding_pack_ms_once": round(pack_ms, 2),
                    "attention": attn,
+                   "other_workloads": others,
                    "eb_sampler": eb,
                    "decode_run": dec,
                    "decode_run_entropy_bounded": dec_eb,
@@ -533,6 +538,72 @@ def measured_traffic(kernel):
     if rec.get("sources_sha256") != sources_sha256() or kernel not in rec.get("kernels", {}):
         return None
     return rec["kernels"][kernel]["hbm_bytes"]
+
+
+def workload_sweep(torch, dg, workloads):
+    """GPU step time beside the CPU oracle's for the tiny (1), mid (2) and
+    full-vocabulary sampler (3) workloads.  GPU: eager steps (attention then
+    sampler; sampler only for 3) between two events, over the workload's own
+    per-step logits.  Oracle: the same steps in fp64 numpy, z for all rows."""
+    from oracle import sampler as S
+    from oracle.attention import canvas_attention
+    res = []
+    for w in (1, 2, 3):
+        c = workloads.CONFIGS[w]
+        n, vocab, dm, nsteps = c["n"], c["vocab"], c["d_model"], c["steps"]
+        log(f"workload {w} ({c['name']}): gpu")
+        emb = workloads.embedding(w)
+        logits = [workloads.step_logits(w, s) for s in range(nsteps)]
+        ids, mask = workloads.initial_canvas(w)
+        emb_t = torch.from_numpy(emb).cuda()
+        pk = dg.dg_embedding_pack(emb_t)
+        del emb_t
+        lg = [torch.from_numpy(x).cuda() for x in logits]
+        ids_t = torch.from_numpy(ids.astype(np.int32)).cuda()
+        mask_t = torch.from_numpy(mask).cuda()
+        z = torch.empty((n, dm), dtype=torch.float32, device="cuda")
+        kappa = torch.empty(n, dtype=torch.float32, device="cuda")
+        nu = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ctrl = dg.make_ctrl(seed=w, tau=c["tau"], flags=dg.DG_AUTO_ADVANCE)
+        if w != 3:
+            q, kp, vp, kc, vc = workloads.attention_inputs(w)
+            dt = torch.bfloat16 if c["qkv"] == "bf16" else torch.float32
+            A = [torch.from_numpy(x).to(dt).cuda() for x in (q, kp, vp, kc, vc)]
+            attn = torch.empty((n, c["hq"], c["head_dim"]), dtype=torch.float32, device="cuda")
+            ws = torch.empty(dg.dg_denoise_workspace_bytes(n, c["n_prefix"], c["hq"], c["hkv"], c["head_dim"],
+                                                           vocab, dm), dtype=torch.uint8, device="cuda")
+            step = lambda s: dg.dg_denoise_step(*A, attn, lg[s % nsteps], pk, ids_t, mask_t, z, kappa, nu, ctrl,
+                                                workspace=ws)
+        else:
+            ws = torch.empty(dg.dg_sampler_workspace_bytes(n, vocab, dm), dtype=torch.uint8, device="cuda")
+            step = lambda s: dg.dg_sampler_step(lg[0], pk, ids_t, mask_t, z, kappa, nu, ctrl, workspace=ws)
+        reps = 40
+        for s in range(4):
+            step(s)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(reps):
+            step(s)
+        e1.record()
+        torch.cuda.synchronize()
+        gpu_ms = e0.elapsed_time(e1) / reps
+        del lg, pk
+        log(f"workload {w} ({c['name']}): oracle")
+        e64 = emb.astype(np.float64)
+        octrl = S.Ctrl(seed=w, tau=c["tau"], flags=S.AUTO_ADVANCE)
+        o_steps = nsteps if w != 3 else 1
+        t0 = time.perf_counter()
+        for s in range(o_steps):
+            if w != 3:
+                canvas_attention(q, kp, vp, kc, vc)
+            S.sampler_step(logits[s], e64, ids, mask, octrl, z_rows="all")
+        cpu_ms = (time.perf_counter() - t0) * 1e3 / o_steps
+        res.append({"workload": w, "name": c["name"], "gpu_ms_per_step": round(gpu_ms, 4),
+                    "gpu_steps_per_s": round(1e3 / gpu_ms, 1), "oracle_ms_per_step": round(cpu_ms, 1),
+                    "oracle_steps": o_steps, "what": "attention + sampler" if w != 3 else "sampler only"})
+        log(f"workload {w}: gpu {gpu_ms:.3f} ms, oracle {cpu_ms:.0f} ms per step")
+    return res
 
 
 def cpu_baseline(q, kp, vp, kc, vc, emb, logits, ids, mask):
