@@ -428,8 +428,11 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
     const int rr = qtile * kARows + i;
     if (i >= kARows || rr >= rows) continue;
     const size_t row_o = (size_t)(rr / group) * hq + kvh * group + rr % group;
-    *reinterpret_cast<u32x4*>(base + row_o * D + 8 * c) =
-        *reinterpret_cast<const u32x4*>(tile + i * kTileRow + 16 * c);
+    // non-temporal: the partials leave as they are written instead of in one
+    // cache flush at the end of the kernel (measured ~1 us off this kernel,
+    // ~0.4 us onto the combine that reads them)
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(tile + i * kTileRow + 16 * c),
+                                reinterpret_cast<u32x4*>(base + row_o * D + 8 * c));
   }
 }
 
