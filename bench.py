@@ -176,6 +176,11 @@ def main():
     attn_fp8 = fp8_attention_timing(torch, dg, workloads, n, p, hq, hkv, hd, a.steps)
     log(f"fp8 attention: {attn_fp8['us']:.1f} us per call")
 
+    # ---- a denoising pass and a KV-update pass batched in one launch ----
+    attn_batched = batched_attention_timing(torch, dg, T, n, p, hq, hkv, hd, a.steps)
+    log(f"batched attention (denoise + KV update): {attn_batched['us_batched']:.1f} us in one launch, "
+        f"{attn_batched['us_two_calls']:.1f} us as two calls")
+
     # ---- the top-k truncated sampler (approximate), alone and after attention ----
     topk = topk_sampler_timing(torch, dg, T, n, p, hq, hkv, hd, vocab, dm, a.steps)
     log("top-k sampler: " + ", ".join(f"k={r['k']} B={r['batch']}: {r['sampler_ms']:.3f} ms"
@@ -247,6 +252,7 @@ def main():
                    "batched_sampler": batched,
                    "topk_sampler": topk,
                    "attention_fp8": attn_fp8,
+                   "attention_batched": attn_batched,
                    "blas_reference_bf16_gemm": blas},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -381,6 +387,45 @@ def bf16_attention_timing(torch, dg, T, n, p, hq, hkv, hd, steps, n_sets=16):
     return {"us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 1),
             "frac_bf16_peak": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "timing": f"eager calls back to back between two events (partial + combine), {n_sets} rotated Q/K/V sets"}
+
+
+def batched_attention_timing(torch, dg, T, n, p, hq, hkv, hd, steps, n_sets=8):
+    """A denoising pass (bidirectional) and a KV-update pass (causal) of two
+    long-context sequences: one batched launch against the same two passes as
+    two calls.  The calls cycle through n_sets copies (8 x 35.7 MB of K/V, more
+    than the 256 MB last-level cache).  Both passes are counted at the full key
+    length, since the kernel computes every block of the causal canvas too."""
+    two = lambda x: torch.stack([x, x]).contiguous()
+    sets = [tuple(two(T[k]) for k in ("q", "kp", "vp", "kc", "vc")) for _ in range(n_sets)]
+    out = torch.empty((2, n, hq, hd), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(dg.dg_attention_batched_workspace_bytes(2, n, p, hq, hkv, hd),
+                         dg.dg_attention_workspace_bytes(n, p, hq, hkv, hd)), dtype=torch.uint8, device="cuda")
+
+    def batched(i):
+        dg.dg_canvas_attention_batched(*sets[i % n_sets], [p, p], [False, True], out=out, workspace=ws)
+
+    def separate(i):
+        q, kp, vp, kc, vc = sets[i % n_sets]
+        dg.dg_canvas_attention(q[0], kp[0], vp[0], kc[0], vc[0], out=out[0], workspace=ws)
+        dg.dg_canvas_attention(q[1], kp[1], vp[1], kc[1], vc[1], out=out[1], workspace=ws, causal=True)
+
+    res = {}
+    for name, run in (("batched", batched), ("two_calls", separate)):
+        for i in range(n_sets):
+            run(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            run(i)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / steps
+    flops = 2 * 4.0 * n * (p + n) * hd * hq
+    return {"us_batched": round(res["batched"], 2), "us_two_calls": round(res["two_calls"], 2),
+            "tflops_batched": round(flops / (res["batched"] * 1e-6) / 1e12, 1),
+            "frac_bf16_peak_batched": round(flops / (res["batched"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "sequences": "2 x (canvas 256, prefix 4096): one bidirectional, one causal"}
 
 
 def fp8_attention_timing(torch, dg, workloads, n, p, hq, hkv, hd, steps, n_sets=32):

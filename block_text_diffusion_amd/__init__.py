@@ -12,7 +12,8 @@ from ._lib import (DG_ATTN_CAUSAL, DG_AUTO_ADVANCE, DG_BF16, DG_COMMIT_ONLY, DG_
                    DG_T_SCHEDULE, DgCtrl, DgError, check, load)
 
 __all__ = [
-    "dg_canvas_attention", "dg_canvas_attention_fp8", "dg_sampler_step", "dg_sampler_step_eb", "read_eb_status",
+    "dg_canvas_attention", "dg_canvas_attention_batched", "dg_attention_batched_workspace_bytes",
+    "dg_canvas_attention_fp8", "dg_sampler_step", "dg_sampler_step_eb", "read_eb_status",
     "dg_sampler_step_batched", "dg_sampler_step_eb_batched", "dg_sampler_workspace_bytes_batched",
     "dg_sampler_step_topk", "dg_sampler_step_eb_topk", "dg_sampler_workspace_bytes_topk",
     "stack_ctrl", "dg_embedding_pack", "dg_embedding_packed_bytes", "dg_denoise_step", "dg_denoise_step_eb", "StepGraph", "StepGraphEB", "dg_canvas_init",
@@ -159,6 +160,43 @@ def dg_canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, out=None, sca
                                         _ptr(v_canvas), _ptr(out), n, n_prefix, hq, hkv, d,
                                         _qkv_dtype(q), float(scale), DG_ATTN_CAUSAL if causal else 0,
                                         _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def dg_attention_batched_workspace_bytes(batch, n_canvas, prefix_stride, hq, hkv, head_dim):
+    return load().dg_attention_batched_workspace_bytes(batch, n_canvas, prefix_stride, hq, hkv, head_dim)
+
+
+def dg_canvas_attention_batched(q, k_prefix, v_prefix, k_canvas, v_canvas, n_prefix, causal=None, out=None,
+                                scale=0.0, workspace=None, stream=None):
+    """q [B, n, hq, d]; k_prefix / v_prefix [B, stride, hkv, d] or None (stride 0);
+    k_canvas / v_canvas [B, n, hkv, d]; n_prefix and causal: B host values.
+    Returns out [B, n, hq, d] float32."""
+    torch = _torch()
+    dt = (torch.bfloat16, torch.float32)
+    _need(q, "q", dt); _need(k_canvas, "k_canvas", dt); _need(v_canvas, "v_canvas", dt)
+    batch, n, hq, d = q.shape
+    hkv = k_canvas.shape[2]
+    stride = 0 if k_prefix is None else k_prefix.shape[1]
+    if stride:
+        _need(k_prefix, "k_prefix", dt); _need(v_prefix, "v_prefix", dt)
+    if len(n_prefix) != batch:
+        raise ValueError(f"n_prefix has {len(n_prefix)} entries for a batch of {batch}")
+    nps = (ctypes.c_int32 * batch)(*[int(x) for x in n_prefix])
+    flags = None
+    if causal is not None:
+        if len(causal) != batch:
+            raise ValueError(f"causal has {len(causal)} entries for a batch of {batch}")
+        flags = (ctypes.c_uint8 * batch)(*[1 if c else 0 for c in causal])
+    if out is None:
+        out = torch.empty((batch, n, hq, d), dtype=torch.float32, device=q.device)
+    nbytes = dg_attention_batched_workspace_bytes(batch, n, stride, hq, hkv, d)
+    ws = _workspace(nbytes, q.device, workspace)
+    check(load().dg_canvas_attention_batched(_ptr(q), _ptr(k_prefix) if stride else None,
+                                             _ptr(v_prefix) if stride else None, _ptr(k_canvas),
+                                             _ptr(v_canvas), _ptr(out), nps, flags, batch, n, stride, hq, hkv,
+                                             d, _qkv_dtype(q), float(scale), _ptr(ws), ws.numel(),
+                                             _stream(stream)))
     return out
 
 

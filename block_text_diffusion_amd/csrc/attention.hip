@@ -148,14 +148,15 @@ __device__ __forceinline__ void kv_store(const KvRegs<D, kF8>& r, uint8_t* stage
 
 // TQ: query element type (bf16 bits, float, or FP8 bytes); kF8: K/V are FP8
 // bytes (otherwise bf16).  out_scale multiplies the normalised output (the V
-// scale of FP8 inputs, 1 otherwise).
-template <int D, typename TQ, bool kF8>
+// scale of FP8 inputs, 1 otherwise).  kBatch: more than one sequence; without
+// it the sequence index is the constant 0, so a single sequence pays nothing
+// for the per-sequence lookups.
+template <int D, typename TQ, bool kF8, bool kBatch>
 __global__ __launch_bounds__(kAThreads) void attn_partial(
     const TQ* __restrict__ q, const void* __restrict__ kp, const void* __restrict__ vp,
     const void* __restrict__ kc, const void* __restrict__ vc, float* __restrict__ out,
-    _Float16* __restrict__ opart, float* __restrict__ ml, int n, int n_prefix, int hq, int hkv,
-    int blocks_prefix, int blocks_total, int blocks_per_chunk, int n_chunks, float scale_log2e,
-    bool causal, float out_scale) {
+    _Float16* __restrict__ opart, float* __restrict__ ml, const AttnSeqs seqs, int n, int hq, int hkv,
+    int blocks_per_chunk, int n_chunks, float scale_log2e, float out_scale) {
   using G = AGeom<D>;
   constexpr int KS = D / 16;   // 16-wide k steps over the head dimension
   constexpr int DB = D / 32;   // 32-row blocks of O^T
@@ -171,7 +172,14 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
   const int lin = xcd * (nwg >> 3) + min(xcd, nwg & 7) + xslot;
   const int chunk = lin % gridDim.x;
   const int qtile = (lin / gridDim.x) % gridDim.y;
-  const int kvh = lin / (gridDim.x * gridDim.y);
+  const int zi = lin / (gridDim.x * gridDim.y);   // sequence-major, then KV head
+  const int seq = kBatch ? zi / hkv : 0;
+  const int kvh = kBatch ? zi - seq * hkv : zi;
+  const int n_prefix = seqs.n_prefix[seq];
+  const bool causal = (seqs.causal >> seq) & 1u;
+  const int blocks_prefix = (n_prefix + kAKeys - 1) / kAKeys;
+  const int blocks_total = blocks_prefix + (n + kAKeys - 1) / kAKeys;
+  const size_t rows_all = (size_t)seqs.batch * n * hq;   // output rows of the launch
   const int group = hq / hkv;
   const int rows = n * group;
   const int t = threadIdx.x;
@@ -182,12 +190,19 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
   const int half = lane >> 5;
 
   const int gb0 = chunk * blocks_per_chunk;
-  const int nb = min(blocks_total, gb0 + blocks_per_chunk) - gb0;
+  // a chunk past the end of a shorter sequence's keys is empty: it writes
+  // m = -inf, l = 0 and a zero partial, which the merge weights by 0
+  const int nb = max(0, min(blocks_total, gb0 + blocks_per_chunk) - gb0);
 
-  const uint32_t pre_bytes = (uint32_t)n_prefix * hkv * D * (kF8 ? 1u : 2u);
-  const uint32_t can_bytes = (uint32_t)n * hkv * D * (kF8 ? 1u : 2u);
-  const __amdgpu_buffer_rsrc_t rkp = rsrc(kp, pre_bytes), rvp = rsrc(vp, pre_bytes);
-  const __amdgpu_buffer_rsrc_t rkc = rsrc(kc, can_bytes), rvc = rsrc(vc, can_bytes);
+  constexpr size_t kEl = kF8 ? 1 : 2;
+  const size_t pre_off = (size_t)seq * seqs.prefix_stride * hkv * D * kEl;
+  const size_t can_off = (size_t)seq * n * hkv * D * kEl;
+  const uint32_t pre_bytes = (uint32_t)((size_t)n_prefix * hkv * D * kEl);
+  const uint32_t can_bytes = (uint32_t)((size_t)n * hkv * D * kEl);
+  const __amdgpu_buffer_rsrc_t rkp = rsrc(static_cast<const uint8_t*>(kp) + pre_off, pre_bytes);
+  const __amdgpu_buffer_rsrc_t rvp = rsrc(static_cast<const uint8_t*>(vp) + pre_off, pre_bytes);
+  const __amdgpu_buffer_rsrc_t rkc = rsrc(static_cast<const uint8_t*>(kc) + can_off, can_bytes);
+  const __amdgpu_buffer_rsrc_t rvc = rsrc(static_cast<const uint8_t*>(vc) + can_off, can_bytes);
 
   KvRegs<D, kF8> ra;
   auto fetch = [&](KvRegs<D, kF8>& r, int b) {
@@ -197,7 +212,7 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
     else
       kv_fetch<D, kF8>(r, rkc, rvc, (gb - blocks_prefix) * kAKeys, n, hkv, kvh, t);
   };
-  fetch(ra, 0);
+  if (nb > 0) fetch(ra, 0);
 
   // this lane's query row (a column of S^T)
   const int r = qtile * kARows + wr * 32 + (lane & 31);
@@ -208,7 +223,7 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 w = (u32x4){0u, 0u, 0u, 0u};
-    if (r_ok) w = load8(q + ((size_t)qn * hq + qh) * D + 16 * ks + 8 * half);
+    if (r_ok) w = load8(q + (((size_t)seq * n + qn) * hq + qh) * D + 16 * ks + 8 * half);
     qf[ks] = __builtin_bit_cast(bf16x8, w);
   }
 
@@ -225,7 +240,7 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
   const int vkey0 = 32 * wh + 4 * (g16 >> 1) + (r16 >> 2);
   const int vbyte = 8 * (r16 & 1);
 
-  kv_store<D, kF8>(ra, lds, t);
+  if (nb > 0) kv_store<D, kF8>(ra, lds, t);
   // blocks 1 and 2 in flight before the loop: every block's loads are issued
   // two blocks ahead of their use
   KvRegs<D, kF8> rb;
@@ -354,7 +369,7 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
     lds_ml[wr][lane][1] = l_run;
   }
   __syncthreads();
-  const size_t orow = (size_t)qn * hq + qh;
+  const size_t orow = ((size_t)seq * n + qn) * hq + qh;
   float rmax = 0.f;
   if (wh == 0) {
     const float m2 = lds_ml[wr][lane][0];
@@ -415,19 +430,19 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
         *reinterpret_cast<f16x4*>(tile + i * kTileRow + dd * 2) = hv;
       }
     if (half == 0 && r_ok)
-      *reinterpret_cast<f32x4*>(ml + ((size_t)chunk * n * hq + orow) * 4) =
+      *reinterpret_cast<f32x4*>(ml + ((size_t)chunk * rows_all + orow) * 4) =
           (f32x4){m_run * scale_log2e, l_run, rmax, 0.f};
   }
   __syncthreads();
   constexpr int kCpr16 = D * 2 / 16;                 // 16-byte pieces per fp16 row
-  _Float16* base = reinterpret_cast<_Float16*>(opart) + (size_t)chunk * n * hq * D;
+  _Float16* base = reinterpret_cast<_Float16*>(opart) + (size_t)chunk * rows_all * D;
 #pragma unroll
   for (int k = 0; k < (kARows * kCpr16 + kAThreads - 1) / kAThreads; ++k) {
     const int idx = t + kAThreads * k;
     const int i = idx / kCpr16, c = idx % kCpr16;
     const int rr = qtile * kARows + i;
     if (i >= kARows || rr >= rows) continue;
-    const size_t row_o = (size_t)(rr / group) * hq + kvh * group + rr % group;
+    const size_t row_o = ((size_t)seq * n + rr / group) * hq + kvh * group + rr % group;
     // non-temporal: the partials leave as they are written instead of in one
     // cache flush at the end of the kernel (measured ~1 us off this kernel,
     // ~0.4 us onto the combine that reads them)
@@ -478,8 +493,9 @@ __global__ __launch_bounds__(256) void attn_to_bf16(const float* __restrict__ sr
   if (i < n8) *reinterpret_cast<u32x4*>(dst + 8 * i) = load8(src + 8 * i);
 }
 
-AttnPlan attn_plan(int n, int n_prefix, int hq, int hkv, int d) {
+AttnPlan attn_plan(int n, int n_prefix, int hq, int hkv, int d, int batch) {
   AttnPlan p{};
+  p.batch = batch;
   p.n = n; p.n_prefix = n_prefix; p.hq = hq; p.hkv = hkv; p.d = d;
   p.group = hq / hkv;
   p.rows = n * p.group;
@@ -488,20 +504,20 @@ AttnPlan attn_plan(int n, int n_prefix, int hq, int hkv, int d) {
   p.blocks_total = p.blocks_prefix + (n + kAKeys - 1) / kAKeys;
   // about one workgroup per CU: enough chunks to fill 256 CUs, no more (every
   // extra chunk adds a partial output to write and merge)
-  const int base = hkv * p.n_qtiles;
+  const int base = hkv * p.n_qtiles * batch;
   int want = 256 / base;
   if (want > p.blocks_total) want = p.blocks_total;
   if (want < 1) want = 1;
   p.blocks_per_chunk = (p.blocks_total + want - 1) / want;
   p.n_chunks = (p.blocks_total + p.blocks_per_chunk - 1) / p.blocks_per_chunk;
   // workspace: [bf16 copies of fp32 K/V][fp16 partial O][(m, l, s, -) per row]
-  const size_t kv_elems = (size_t)(n_prefix + n) * hkv * d;
+  const size_t kv_elems = (size_t)batch * (n_prefix + n) * hkv * d;
   p.off_kv16 = 0;
   p.kv16_bytes = align_up(2 * kv_elems * sizeof(uint16_t), 256);
   p.off_opart = p.kv16_bytes;
   if (p.n_chunks > 1) {
-    p.off_ml = p.off_opart + align_up((size_t)p.n_chunks * n * hq * d * sizeof(uint16_t), 256);
-    p.total = p.off_ml + align_up((size_t)p.n_chunks * n * hq * 4 * sizeof(float), 256);
+    p.off_ml = p.off_opart + align_up((size_t)p.n_chunks * batch * n * hq * d * sizeof(uint16_t), 256);
+    p.total = p.off_ml + align_up((size_t)p.n_chunks * batch * n * hq * 4 * sizeof(float), 256);
   } else {
     p.off_ml = p.off_opart;
     p.total = p.off_opart;
@@ -510,45 +526,54 @@ AttnPlan attn_plan(int n, int n_prefix, int hq, int hkv, int d) {
 }
 
 template <int D, typename TQ, bool kF8>
-static hipError_t launch_attn_t(const AttnPlan& p, const void* q, const void* kp, const void* vp,
-                                const void* kc, const void* vc, float* out, float scale, bool causal,
+static hipError_t launch_attn_t(const AttnPlan& p, const AttnSeqs& sq, const void* q, const void* kp,
+                                const void* vp, const void* kc, const void* vc, float* out, float scale,
                                 float out_scale, void* ws, hipStream_t s) {
   _Float16* opart = reinterpret_cast<_Float16*>(static_cast<uint8_t*>(ws) + p.off_opart);
   float* ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p.off_ml);
   const float sl2 = scale * kLog2e;
   prof_begin("attn_partial", s);
-  attn_partial<D, TQ, kF8><<<dim3(p.n_chunks, p.n_qtiles, p.hkv), kAThreads, 0, s>>>(
-      static_cast<const TQ*>(q), kp, vp, kc, vc, out, opart, ml, p.n, p.n_prefix, p.hq, p.hkv,
-      p.blocks_prefix, p.blocks_total, p.blocks_per_chunk, p.n_chunks, sl2, causal, out_scale);
+  const dim3 grid(p.n_chunks, p.n_qtiles, p.hkv * sq.batch);
+  if (sq.batch > 1)
+    attn_partial<D, TQ, kF8, true><<<grid, kAThreads, 0, s>>>(static_cast<const TQ*>(q), kp, vp, kc, vc, out,
+                                                              opart, ml, sq, p.n, p.hq, p.hkv,
+                                                              p.blocks_per_chunk, p.n_chunks, sl2, out_scale);
+  else
+    attn_partial<D, TQ, kF8, false><<<grid, kAThreads, 0, s>>>(static_cast<const TQ*>(q), kp, vp, kc, vc, out,
+                                                               opart, ml, sq, p.n, p.hq, p.hkv,
+                                                               p.blocks_per_chunk, p.n_chunks, sl2, out_scale);
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_chunks == 1) return e;
   const int rows_per_wg = kCThreads / (D / 4);
   prof_begin("attn_combine", s);
-  attn_combine<D><<<(p.n * p.hq + rows_per_wg - 1) / rows_per_wg, kCThreads, 0, s>>>(
-      opart, ml, out, p.n * p.hq, p.n_chunks, out_scale);
+  const int rows_all = sq.batch * p.n * p.hq;
+  attn_combine<D><<<(rows_all + rows_per_wg - 1) / rows_per_wg, kCThreads, 0, s>>>(
+      opart, ml, out, rows_all, p.n_chunks, out_scale);
   prof_end(s);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_attn_d(const AttnPlan& p, int dtype, const void* q, const void* kp, const void* vp,
-                                const void* kc, const void* vc, float* out, float scale, bool causal,
+static hipError_t launch_attn_d(const AttnPlan& p, const AttnSeqs& sq, int dtype, const void* q, const void* kp,
+                                const void* vp, const void* kc, const void* vc, float* out, float scale,
                                 float out_scale, void* ws, hipStream_t s) {
   if (dtype == DG_FP8_E4M3)
-    return launch_attn_t<D, uint8_t, true>(p, q, kp, vp, kc, vc, out, scale, causal, out_scale, ws, s);
+    return launch_attn_t<D, uint8_t, true>(p, sq, q, kp, vp, kc, vc, out, scale, out_scale, ws, s);
   if (dtype == DG_BF16)
-    return launch_attn_t<D, uint16_t, false>(p, q, kp, vp, kc, vc, out, scale, causal, out_scale, ws, s);
-  return launch_attn_t<D, float, false>(p, q, kp, vp, kc, vc, out, scale, causal, out_scale, ws, s);
+    return launch_attn_t<D, uint16_t, false>(p, sq, q, kp, vp, kc, vc, out, scale, out_scale, ws, s);
+  return launch_attn_t<D, float, false>(p, sq, q, kp, vp, kc, vc, out, scale, out_scale, ws, s);
 }
 
-hipError_t launch_attention(const AttnPlan& p, const void* q, const void* kp, const void* vp,
-                            const void* kc, const void* vc, float* out, int dtype, float scale,
-                            void* ws, hipStream_t s, bool causal, float out_scale) {
+hipError_t launch_attention_batched(const AttnPlan& p, const AttnSeqs& sq, const void* q, const void* kp,
+                                    const void* vp, const void* kc, const void* vc, float* out, int dtype,
+                                    float scale, void* ws, hipStream_t s, float out_scale) {
   if (dtype == DG_F32) {
-    // fp32 K/V: round to bf16 into the workspace first
+    // fp32 K/V: round to bf16 into the workspace first (the whole batched
+    // buffers, prefix padding included)
     uint16_t* base = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + p.off_kv16);
-    const size_t pre = (size_t)p.n_prefix * p.hkv * p.d, can = (size_t)p.n * p.hkv * p.d;
+    const size_t pre = (size_t)sq.batch * sq.prefix_stride * p.hkv * p.d;
+    const size_t can = (size_t)sq.batch * p.n * p.hkv * p.d;
     uint16_t* kp_w = base;
     uint16_t* vp_w = kp_w + pre;
     uint16_t* kc_w = vp_w + pre;
@@ -564,8 +589,19 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* kp, co
     if (e != hipSuccess) return e;
     kp = kp_w; vp = vp_w; kc = kc_w; vc = vc_w;
   }
-  if (p.d == 128) return launch_attn_d<128>(p, dtype, q, kp, vp, kc, vc, out, scale, causal, out_scale, ws, s);
-  return launch_attn_d<64>(p, dtype, q, kp, vp, kc, vc, out, scale, causal, out_scale, ws, s);
+  if (p.d == 128) return launch_attn_d<128>(p, sq, dtype, q, kp, vp, kc, vc, out, scale, out_scale, ws, s);
+  return launch_attn_d<64>(p, sq, dtype, q, kp, vp, kc, vc, out, scale, out_scale, ws, s);
+}
+
+hipError_t launch_attention(const AttnPlan& p, const void* q, const void* kp, const void* vp,
+                            const void* kc, const void* vc, float* out, int dtype, float scale,
+                            void* ws, hipStream_t s, bool causal, float out_scale) {
+  AttnSeqs sq{};
+  sq.n_prefix[0] = p.n_prefix;
+  sq.causal = causal ? 1u : 0u;
+  sq.prefix_stride = p.n_prefix;
+  sq.batch = 1;
+  return launch_attention_batched(p, sq, q, kp, vp, kc, vc, out, dtype, scale, ws, s, out_scale);
 }
 
 }  // namespace dg

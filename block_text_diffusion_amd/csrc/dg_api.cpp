@@ -154,6 +154,13 @@ size_t dg_attention_workspace_bytes(int n, int np, int hq, int hkv, int d) {
   return t == 0 ? 256 : t;
 }
 
+size_t dg_attention_batched_workspace_bytes(int batch, int n, int stride, int hq, int hkv, int d) {
+  if (batch < 1 || batch > dg::kMaxAttnSeqs) return 0;
+  if (n < 1 || n > 256 || stride < 0 || hq < 1 || hkv < 1 || hq % hkv || (d != 64 && d != 128)) return 0;
+  const size_t t = dg::attn_plan(n, stride, hq, hkv, d, batch).total;
+  return t == 0 ? 256 : t;
+}
+
 size_t dg_sampler_workspace_bytes(int n, int vocab, int d) {
   return dg_sampler_workspace_bytes_batched(n, 1, vocab, d);
 }
@@ -193,6 +200,39 @@ int dg_canvas_attention_ex(const void* q, const void* kp, const void* vp, const 
   hipError_t e = dg::launch_attention(p, q, kp, vp, kc, vc, out, dtype, scale, ws, stream,
                                       (attn_flags & DG_ATTN_CAUSAL) != 0);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return DG_OK;
+}
+
+int dg_canvas_attention_batched(const void* q, const void* kp, const void* vp, const void* kc,
+                                const void* vc, float* out, const int32_t* n_prefix, const uint8_t* causal,
+                                int batch, int n, int stride, int hq, int hkv, int d, int dtype, float scale,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (batch < 1) return fail(DG_EINVAL, "attention_batched: batch < 1");
+  if (batch > dg::kMaxAttnSeqs) return fail(DG_EUNSUPPORTED, "attention_batched: batch > %d", dg::kMaxAttnSeqs);
+  if (!n_prefix) return fail(DG_EINVAL, "attention_batched: null n_prefix");
+  if (stride < 0) return fail(DG_EINVAL, "attention_batched: prefix_stride < 0");
+  if (dtype == DG_FP8_E4M3) return fail(DG_EUNSUPPORTED, "attention_batched: FP8 inputs are not batched");
+  int st = check_attention(q, kp, vp, kc, vc, out, n, stride, hq, hkv, d, dtype);
+  if (st != DG_OK) return st;
+  if ((int64_t)hkv * batch > 65535) return fail(DG_EUNSUPPORTED, "attention_batched: hkv * batch > 65535");
+  dg::AttnSeqs sq{};
+  for (int s = 0; s < batch; ++s) {
+    if (n_prefix[s] < 0 || n_prefix[s] > stride)
+      return fail(DG_EINVAL, "attention_batched: n_prefix[%d] = %d outside [0, prefix_stride = %d]", s,
+                  n_prefix[s], stride);
+    if (causal && causal[s] > 1) return fail(DG_EINVAL, "attention_batched: causal[%d] must be 0 or 1", s);
+    sq.n_prefix[s] = n_prefix[s];
+    if (causal && causal[s]) sq.causal |= 1ull << s;
+  }
+  sq.prefix_stride = stride;
+  sq.batch = batch;
+  const dg::AttnPlan p = dg::attn_plan(n, stride, hq, hkv, d, batch);
+  if (p.total > 0 && (!ws || ws_bytes < p.total))
+    return fail(DG_EWORKSPACE, "attention_batched: workspace %zu < %zu bytes", ws_bytes, p.total);
+  if (p.total > 0 && !aligned16(ws)) return fail(DG_EINVAL, "attention_batched: workspace misaligned");
+  if (!(scale > 0.f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)d);
+  hipError_t e = dg::launch_attention_batched(p, sq, q, kp, vp, kc, vc, out, dtype, scale, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention_batched launch");
   return DG_OK;
 }
 

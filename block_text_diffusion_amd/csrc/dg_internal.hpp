@@ -60,7 +60,7 @@ hipError_t launch_sampler_topk(const TopkPlan& p, const float* logits, const flo
 
 // ---- attention ----
 struct AttnPlan {
-  int n, n_prefix, hq, hkv, d, group;
+  int n, n_prefix, hq, hkv, d, group, batch;
   int rows;          // n * group packed query rows per KV head
   int n_qtiles;      // 128-row query tiles per KV head
   int blocks_prefix;     // 64-key blocks of the prefix
@@ -70,7 +70,20 @@ struct AttnPlan {
   size_t off_kv16, kv16_bytes;  // bf16 copies of fp32 K/V
   size_t off_opart, off_ml, total;
 };
-AttnPlan attn_plan(int n, int n_prefix, int hq, int hkv, int d);
+// n_prefix is the prefix row stride of a batch (the longest prefix); the
+// partial outputs are sized for batch sequences.
+AttnPlan attn_plan(int n, int n_prefix, int hq, int hkv, int d, int batch = 1);
+// Per-sequence parameters of one launch over a batch of sequences: sequence s
+// owns rows [s n, (s + 1) n) of Q, O and the canvas K/V, and prefix rows
+// [s stride, s stride + n_prefix[s]) of the prefix K/V.  Passed by value in
+// the kernel arguments.
+constexpr int kMaxAttnSeqs = 64;
+struct AttnSeqs {
+  int n_prefix[kMaxAttnSeqs];
+  uint64_t causal;     // bit s: sequence s sees canvas keys 0..i only
+  int prefix_stride;   // prefix rows between consecutive sequences
+  int batch;
+};
 // dtype: DG_F32 (K/V rounded to bf16 into the workspace first), DG_BF16, or
 // DG_FP8_E4M3 (Q/K/V bytes converted exactly to bf16 while staged).
 // out_scale multiplies the normalised output.
@@ -78,6 +91,11 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* kp, co
                             const void* kc, const void* vc, float* out, int dtype,
                             float scale, void* ws, hipStream_t s, bool causal = false,
                             float out_scale = 1.0f);
+// The same over sq.batch sequences (p planned with n_prefix = sq.prefix_stride
+// and batch = sq.batch).
+hipError_t launch_attention_batched(const AttnPlan& p, const AttnSeqs& sq, const void* q, const void* kp,
+                                    const void* vp, const void* kc, const void* vc, float* out, int dtype,
+                                    float scale, void* ws, hipStream_t s, float out_scale = 1.0f);
 
 // ---- block loop helpers ----
 hipError_t launch_canvas_init(int32_t* ids, uint8_t* committed, dg_ctrl* ctrl, int n, int vocab,

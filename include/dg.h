@@ -133,6 +133,43 @@ int dg_canvas_attention_ex(const void* q, const void* k_prefix, const void* v_pr
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * A batch of sequences in one launch, each with its own prefix length and its
+ * own causal flag, so denoising passes and KV-update passes can share a batch
+ * (Technical Report part 4/6, paragraph "Eliminating CPU-GPU synchronization":
+ * both kinds of forward pass, with different attention masks, can occur in one
+ * batch; explainer "DiffusionGemma: Google's open diffusion LLM", section
+ * "Reference implementations in Transformers and vLLM": a per-sequence causal
+ * flag).  Sequence s computes exactly what dg_canvas_attention_ex computes for
+ * its own inputs:
+ *   q          [batch, n_canvas, hq, head_dim]          dtype
+ *   k_prefix   [batch, prefix_stride, hkv, head_dim]    dtype; sequence s uses
+ *   v_prefix   rows 0..n_prefix[s]-1 of its slab and never reads the rest
+ *              (NULL allowed iff prefix_stride == 0)
+ *   k_canvas   [batch, n_canvas, hkv, head_dim]         dtype
+ *   v_canvas   [batch, n_canvas, hkv, head_dim]         dtype
+ *   out        [batch, n_canvas, hq, head_dim]          float32 (written)
+ *   n_prefix   host array [batch], each in [0, prefix_stride]; read during the
+ *              call only
+ *   causal     host array [batch] of 0/1 (DG_ATTN_CAUSAL semantics for a 1),
+ *              or NULL for all bidirectional; read during the call only
+ *   batch in [1, 64]; dtype DG_BF16 or DG_F32 (DG_FP8_E4M3 returns
+ *   DG_EUNSUPPORTED); the other sizes and scale as dg_canvas_attention.
+ * Workspace: dg_attention_batched_workspace_bytes (0 if the sizes are
+ * invalid).  Errors: DG_EINVAL for a null pointer, a misaligned pointer, an
+ * n_prefix entry outside [0, prefix_stride] or a causal entry other than 0/1,
+ * DG_EUNSUPPORTED for batch > 64 or hkv * batch > 65535, DG_EWORKSPACE if the
+ * workspace is too small; nothing is launched on an error.
+ */
+size_t dg_attention_batched_workspace_bytes(int batch, int n_canvas, int prefix_stride, int hq, int hkv,
+                                            int head_dim);
+int dg_canvas_attention_batched(const void* q, const void* k_prefix, const void* v_prefix,
+                                const void* k_canvas, const void* v_canvas, float* out,
+                                const int32_t* n_prefix, const uint8_t* causal, int batch,
+                                int n_canvas, int prefix_stride, int hq, int hkv, int head_dim,
+                                int dtype, float scale, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
  * FP8 canvas attention: the pages' timings are taken in FP8 (explainer
  * "DiffusionGemma: Google's open diffusion LLM", section "Throughput flips at
  * about 32 concurrent users", Figure 12 caption).  q, k_prefix, v_prefix,

@@ -20,10 +20,22 @@ after another": a causal encoder reads the history).  Reading taken for the
 causal flag: canvas row i attends to every prefix key and to canvas keys
 0 .. i.
 
+A batch of sequences (Technical Report part 4/6, paragraph "Eliminating
+CPU-GPU synchronization": denoising passes and KV-update passes, with different
+masks, can share one batch; explainer "DiffusionGemma: Google's open diffusion
+LLM", section "Reference implementations in Transformers and vLLM": a
+per-sequence causal flag).  Sequence s is the single-sequence definition
+applied to its own inputs: prefix rows 0 .. n_prefix[s]-1 of its padded slab,
+its canvas rows, and its own causal flag; padding rows are not keys.
+
 Pins (tests/test_oracle_attention.py): explicit-loop brute force on tiny shapes;
 torch's CPU scaled_dot_product_attention with repeated KV heads; closed forms
 (one key gives v; scale 0 gives the mean of V; constant V gives that constant);
-invariance under a permutation applied to canvas (or prefix) keys and values.
+invariance under a permutation applied to canvas (or prefix) keys and values;
+for a batch, torch's CPU scaled_dot_product_attention over the padded layout
+with a boolean mask that hides each sequence's padding (and, where its flag is
+set, the canvas keys after each row), and the outputs of one sequence unchanged
+when another sequence's inputs or its own padding change.
 """
 import numpy as np
 
@@ -63,3 +75,19 @@ def canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, scale=None, caus
         w = w / w.sum(axis=1, keepdims=True)
         out[:, h, :] = w @ vals[:, kvh, :]
     return out
+
+
+def canvas_attention_batched(q, k_prefix, v_prefix, k_canvas, v_canvas, n_prefix, causal=None, scale=None):
+    """q [B,N,Hq,D]; k/v_prefix [B,S,Hkv,D] (S = prefix stride, may be 0 or None);
+    k/v_canvas [B,N,Hkv,D]; n_prefix: B lengths in [0, S]; causal: B flags or None
+    -> O [B,N,Hq,D] float64.  Sequence s uses prefix rows 0..n_prefix[s]-1 only."""
+    batch = np.asarray(q).shape[0]
+    out = []
+    for s in range(batch):
+        np_s = int(n_prefix[s])
+        kp = None if k_prefix is None else np.asarray(k_prefix)[s, :np_s]
+        vp = None if v_prefix is None else np.asarray(v_prefix)[s, :np_s]
+        flag = bool(causal[s]) if causal is not None else False
+        out.append(canvas_attention(np.asarray(q)[s], kp, vp, np.asarray(k_canvas)[s],
+                                    np.asarray(v_canvas)[s], scale=scale, causal=flag))
+    return np.stack(out)

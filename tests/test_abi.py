@@ -82,6 +82,41 @@ def test_attention_argument_errors(lib):
     assert b"workspace" in lib.dg_last_error()
 
 
+def attn_batched(lib, nps=(8, 0, 5), causal=(0, 1, 0), **kw):
+    a = dict(q=FAKE, kp=FAKE, vp=FAKE, kc=FAKE, vc=FAKE, out=FAKE, batch=3 if nps is None else len(nps),
+             n=16, stride=8, hq=8, hkv=4, d=64, dtype=1, scale=0.0, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    np_arr = None if nps is None else (ctypes.c_int32 * len(nps))(*nps)
+    c_arr = None if causal is None else (ctypes.c_uint8 * len(causal))(*causal)
+    return lib.dg_canvas_attention_batched(a["q"], a["kp"], a["vp"], a["kc"], a["vc"], a["out"], np_arr, c_arr,
+                                           a["batch"], a["n"], a["stride"], a["hq"], a["hkv"], a["d"],
+                                           a["dtype"], a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_batched_attention_workspace_and_errors(lib):
+    from block_text_diffusion_amd._lib import DG_EINVAL, DG_EUNSUPPORTED, DG_EWORKSPACE, DG_FP8_E4M3
+    one = lib.dg_attention_workspace_bytes(256, 4096, 16, 8, 128)
+    assert lib.dg_attention_batched_workspace_bytes(1, 256, 4096, 16, 8, 128) == one
+    # more sequences: fewer key chunks each, partials for every sequence
+    four = lib.dg_attention_batched_workspace_bytes(4, 256, 4096, 16, 8, 128)
+    assert four > 0 and four % 256 == 0
+    assert lib.dg_attention_batched_workspace_bytes(0, 16, 8, 8, 4, 64) == 0
+    assert lib.dg_attention_batched_workspace_bytes(65, 16, 8, 8, 4, 64) == 0
+    assert lib.dg_attention_batched_workspace_bytes(2, 16, -1, 8, 4, 64) == 0
+    assert attn_batched(lib, nps=None) == DG_EINVAL
+    assert attn_batched(lib, nps=(8, 9, 0), causal=(0, 0, 0)) == DG_EINVAL      # 9 > prefix stride 8
+    assert b"n_prefix[1]" in lib.dg_last_error()
+    assert attn_batched(lib, nps=(8, -1, 0)) == DG_EINVAL
+    assert attn_batched(lib, causal=(0, 2, 0)) == DG_EINVAL
+    assert attn_batched(lib, batch=0, nps=(), causal=()) == DG_EINVAL
+    assert attn_batched(lib, batch=65, nps=(0,) * 65, causal=None) == DG_EUNSUPPORTED
+    assert attn_batched(lib, dtype=DG_FP8_E4M3) == DG_EUNSUPPORTED
+    assert attn_batched(lib, kp=None) == DG_EINVAL                                # stride > 0 needs a prefix
+    assert attn_batched(lib, out=MIS) == DG_EINVAL
+    assert attn_batched(lib, stride=-1) == DG_EINVAL
+    assert attn_batched(lib, n=256, stride=4096, hq=16, hkv=8, d=128, wsb=1024) == DG_EWORKSPACE
+
+
 def samp(lib, **kw):
     a = dict(l=FAKE, e=FAKE, ids=FAKE, c=FAKE, z=FAKE, conf=None, nu=FAKE, ctrl=FAKE, n=16,
              v=1000, d=64, ws=FAKE, wsb=0, stream=None)

@@ -4,7 +4,7 @@ import pytest
 
 import workloads
 from gpu_util import ATTN_MAX_ABS, log, require_gpu, to_dev
-from oracle.attention import canvas_attention
+from oracle.attention import canvas_attention, canvas_attention_batched
 
 pytestmark = pytest.mark.gpu
 
@@ -99,3 +99,57 @@ def test_causal(n, p, hq, hkv, d, qkv):
     got = dg.dg_canvas_attention(t(q), t(kp) if p else None, t(vp) if p else None, t(kc), t(vc),
                                  causal=True).cpu().numpy()
     check(got, canvas_attention(q, kp, vp, kc, vc, causal=True), f"causal n={n} p={p}")
+
+
+def batched_inputs(qkv, n, stride, nps, hq, hkv, d):
+    """Per-sequence inputs in the padded batch layout; the prefix padding rows
+    are NaN, so a read of them would show in the output.  Each prefix is rolled
+    along the head dimension by its own amount, so equal-length prefixes differ."""
+    b = len(nps)
+    q = np.zeros((b, n, hq, d), np.float32)
+    kc = np.zeros((b, n, hkv, d), np.float32)
+    vc = np.zeros((b, n, hkv, d), np.float32)
+    kp = np.full((b, stride, hkv, d), np.nan, np.float32)
+    vp = np.full((b, stride, hkv, d), np.nan, np.float32)
+    for s_, np_s in enumerate(nps):
+        qs, kps, vps, kcs, vcs = workloads.attention_inputs(2, n=n, n_prefix=np_s, hq=hq, hkv=hkv, head_dim=d,
+                                                             qkv=qkv, block=s_)
+        q[s_], kc[s_], vc[s_] = qs, kcs, vcs
+        kp[s_, :np_s] = np.roll(kps, 5 * s_, axis=-1)
+        vp[s_, :np_s] = np.roll(vps, 3 * s_, axis=-1)
+    return q, kp, vp, kc, vc
+
+
+@pytest.mark.parametrize("qkv,n,stride,nps,flags,hq,hkv,d", [
+    ("bf16", 256, 320, [100, 0, 320], [0, 1, 0], 16, 8, 128),             # ragged prefixes, one empty
+    ("f32", 40, 130, [130, 7], [1, 0], 8, 2, 64),                          # fp32 staged, D=64, empty key chunks
+    ("bf16", 256, 512, [512, 0, 64, 257, 511, 1, 300, 128],
+     [0, 1, 0, 1, 1, 0, 0, 1], 16, 8, 128),                                # one chunk per sequence: direct output
+    ("bf16", 256, 4096, [4096, 4096, 2048, 0], [0, 1, 0, 1], 16, 8, 128),  # long context, both pass types
+])
+def test_batched_mixed_causal(qkv, n, stride, nps, flags, hq, hkv, d):
+    """Denoising (bidirectional) and KV-update (causal) passes of different
+    sequences in one launch, each against the oracle's per-sequence definition."""
+    torch, dg = require_gpu()
+    log(f"batched attention nps={nps} causal={flags} n={n} stride={stride} hq={hq} hkv={hkv} d={d} {qkv}")
+    q, kp, vp, kc, vc = batched_inputs(qkv, n, stride, nps, hq, hkv, d)
+    dt = torch.bfloat16 if qkv == "bf16" else torch.float32
+    out = dg.dg_canvas_attention_batched(to_dev(q, dt), to_dev(kp, dt), to_dev(vp, dt), to_dev(kc, dt),
+                                         to_dev(vc, dt), nps, [bool(f) for f in flags])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = canvas_attention_batched(q, kp, vp, kc, vc, nps, flags)
+    for s_ in range(len(nps)):
+        check(got[s_], ref[s_], f"sequence {s_} (n_prefix {nps[s_]}, causal {flags[s_]})")
+
+
+def test_batched_single_sequence_matches_the_single_call():
+    """A batch of one runs the same kernels with the same plan: bit-identical."""
+    torch, dg = require_gpu()
+    log("batched attention, batch of one against dg_canvas_attention (causal, long context)")
+    q, kp, vp, kc, vc = workloads.attention_inputs(4)
+    t = [to_dev(x, torch.bfloat16) for x in (q, kp, vp, kc, vc)]
+    one = dg.dg_canvas_attention(*t, causal=True)
+    bat = dg.dg_canvas_attention_batched(*[x[None] for x in t], [kp.shape[0]], [True])
+    torch.cuda.synchronize()
+    assert torch.equal(one, bat[0])

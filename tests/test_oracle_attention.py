@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import workloads
-from oracle.attention import canvas_attention
+from oracle.attention import canvas_attention, canvas_attention_batched
 
 
 def brute_force(q, kp, vp, kc, vc, scale):
@@ -136,3 +136,49 @@ def test_causal_special_cases():
     kc2[10:] = rng.standard_normal((n - 10, hkv, d)); vc2[10:] = 5.0
     c2 = canvas_attention(q, kp, vp, kc2, vc2, causal=True)
     np.testing.assert_allclose(c2[:10], causal[:10], rtol=1e-13, atol=1e-13)
+
+
+def test_batched_matches_torch_sdpa_over_the_padded_layout():
+    """A batch of sequences with ragged prefixes and mixed causal flags: torch's
+    SDPA over the padded [prefix slab ; canvas] layout with a boolean mask that
+    hides each sequence's padding rows, and its later canvas keys where the flag
+    is set.  Padding holds large finite values, so any leak would show."""
+    rng = np.random.default_rng(90)
+    b, n, stride, hq, hkv, d = 4, 24, 30, 8, 2, 32
+    nps, flags = [30, 0, 17, 5], [False, True, True, False]
+    q = rng.standard_normal((b, n, hq, d))
+    kp = rng.standard_normal((b, stride, hkv, d)); vp = rng.standard_normal((b, stride, hkv, d))
+    kc = rng.standard_normal((b, n, hkv, d)); vc = rng.standard_normal((b, n, hkv, d))
+    for s_, np_s in enumerate(nps):
+        kp[s_, np_s:] = 1e3; vp[s_, np_s:] = -1e3
+    got = canvas_attention_batched(q, kp, vp, kc, vc, nps, flags)
+    K = torch.from_numpy(np.concatenate([kp, kc], axis=1)).permute(0, 2, 1, 3).repeat_interleave(hq // hkv, dim=1)
+    V = torch.from_numpy(np.concatenate([vp, vc], axis=1)).permute(0, 2, 1, 3).repeat_interleave(hq // hkv, dim=1)
+    Q = torch.from_numpy(q).permute(0, 2, 1, 3)
+    allowed = np.zeros((b, 1, n, stride + n), dtype=bool)
+    for s_, (np_s, c) in enumerate(zip(nps, flags)):
+        allowed[s_, 0, :, :np_s] = True
+        allowed[s_, 0, :, stride:] = np.tril(np.ones((n, n), dtype=bool)) if c else True
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        Q, K, V, attn_mask=torch.from_numpy(allowed)).permute(0, 2, 1, 3).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-10)
+
+
+def test_batched_sequences_are_independent():
+    """Sequence 0's output depends neither on sequence 1's inputs nor on its own
+    padding rows; sequence 1's output does change with its inputs."""
+    rng = np.random.default_rng(91)
+    b, n, stride, hq, hkv, d = 2, 16, 20, 4, 4, 16
+    nps, flags = [11, 20], [True, False]
+    q = rng.standard_normal((b, n, hq, d))
+    kp = rng.standard_normal((b, stride, hkv, d)); vp = rng.standard_normal((b, stride, hkv, d))
+    kc = rng.standard_normal((b, n, hkv, d)); vc = rng.standard_normal((b, n, hkv, d))
+    o1 = canvas_attention_batched(q, kp, vp, kc, vc, nps, flags)
+    q2, kp2, vp2, kc2 = q.copy(), kp.copy(), vp.copy(), kc.copy()
+    q2[1] += 1.0; kc2[1] *= -1.0; kp2[1, 3] += 2.0
+    kp2[0, nps[0]:] = np.nan; vp2[0, nps[0]:] = np.inf
+    o2 = canvas_attention_batched(q2, kp2, vp2, kc2, vc, nps, flags)
+    assert np.array_equal(o1[0], o2[0])
+    assert not np.allclose(o1[1], o2[1])
+    # each sequence is the single-sequence definition with its own flag
+    np.testing.assert_array_equal(o1[0], canvas_attention(q[0], kp[0, :11], vp[0, :11], kc[0], vc[0], causal=True))
