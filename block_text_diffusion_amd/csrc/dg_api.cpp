@@ -116,7 +116,8 @@ void prof_begin(const char* name, hipStream_t s) {
   if (!g_prof_on || g_capturing) return;
   hipEvent_t e = take_event();
   if (!e) return;
-  hipEventRecord(e, s);
+  // best effort: a pair whose record failed is skipped by dg_profile_read
+  (void)hipEventRecord(e, s);
   g_prof_pending = name;
   g_prof_pending_start = e;
 }
@@ -125,7 +126,7 @@ void prof_end(hipStream_t s) {
   if (!g_prof_on || g_capturing || !g_prof_pending) return;
   hipEvent_t e = take_event();
   if (!e) return;
-  hipEventRecord(e, s);
+  (void)hipEventRecord(e, s);
   g_prof_recs.push_back(ProfRec{g_prof_pending, g_prof_pending_start, e});
   g_prof_pending = nullptr;
   g_prof_pending_start = nullptr;
@@ -420,7 +421,7 @@ int capture_step(F record, dg_step_graph** out) {
   if (e != hipSuccess) return hip_fail(e, "graph: stream create");
   e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
   if (e != hipSuccess) {
-    hipStreamDestroy(cs);
+    (void)hipStreamDestroy(cs);
     return hip_fail(e, "graph: begin capture");
   }
   g_capturing = true;
@@ -428,16 +429,16 @@ int capture_step(F record, dg_step_graph** out) {
   g_capturing = false;
   hipGraph_t graph = nullptr;
   hipError_t e2 = hipStreamEndCapture(cs, &graph);
-  hipStreamDestroy(cs);
+  (void)hipStreamDestroy(cs);
   if (st != DG_OK) {
-    if (graph) hipGraphDestroy(graph);
+    if (graph) (void)hipGraphDestroy(graph);
     return st;
   }
   if (e2 != hipSuccess) return hip_fail(e2, "graph: end capture");
   hipGraphExec_t exec = nullptr;
   e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
   if (e != hipSuccess) {
-    hipGraphDestroy(graph);
+    (void)hipGraphDestroy(graph);
     return hip_fail(e, "graph: instantiate");
   }
   *out = new dg_step_graph{graph, exec};
@@ -492,8 +493,8 @@ int dg_step_graph_launch(dg_step_graph* g, hipStream_t stream) {
 
 void dg_step_graph_destroy(dg_step_graph* g) {
   if (!g) return;
-  hipGraphExecDestroy(g->exec);
-  hipGraphDestroy(g->graph);
+  (void)hipGraphExecDestroy(g->exec);
+  (void)hipGraphDestroy(g->graph);
   delete g;
 }
 
