@@ -52,6 +52,38 @@ def _need(t, name, dtypes, device=True):
     return t
 
 
+def _check_attention_tensors(q, k_prefix, v_prefix, k_canvas, v_canvas, out, batched=False):
+    """Cross-tensor checks the C ABI cannot make from raw pointers: one dtype for
+    Q/K/V, matching head counts, head_dim and canvas length, and the shape and
+    dtype of a caller-supplied output.  Returns (n, hq, hkv, d, prefix rows)."""
+    torch = _torch()
+    lead = 1 if batched else 0
+    if q.dim() != 3 + lead or k_canvas.dim() != 3 + lead or v_canvas.dim() != 3 + lead:
+        raise ValueError("attention: q, k_canvas, v_canvas must be [%sn, heads, d]" % ("batch, " if batched else ""))
+    b = q.shape[0] if batched else 1
+    n, hq, d = q.shape[lead:]
+    hkv = k_canvas.shape[lead + 1]
+    tensors = [q, k_canvas, v_canvas]
+    if tuple(k_canvas.shape) != tuple(v_canvas.shape) or tuple(k_canvas.shape[lead:]) != (n, hkv, d) \
+            or (batched and k_canvas.shape[0] != b):
+        raise ValueError(f"attention: canvas K/V shape {tuple(k_canvas.shape)} does not match q {tuple(q.shape)}")
+    rows = 0
+    if k_prefix is not None:
+        if v_prefix is None or tuple(k_prefix.shape) != tuple(v_prefix.shape) or k_prefix.dim() != 3 + lead \
+                or tuple(k_prefix.shape[lead + 1:]) != (hkv, d) or (batched and k_prefix.shape[0] != b):
+            raise ValueError("attention: prefix K/V must both be [%sn_prefix, hkv, d]" % ("batch, " if batched else ""))
+        rows = k_prefix.shape[lead]
+        tensors += [k_prefix, v_prefix]
+    if len({t.dtype for t in tensors}) != 1:
+        raise ValueError("attention: q and every K/V tensor must share one dtype")
+    if out is not None:
+        want = (b, n, hq, d) if batched else (n, hq, d)
+        if tuple(out.shape) != want or out.dtype != torch.float32 or not out.is_contiguous() \
+                or out.device.type != "cuda":
+            raise ValueError(f"attention: out must be a contiguous float32 GPU tensor of shape {want}")
+    return n, hq, hkv, d, rows
+
+
 def _qkv_dtype(t):
     torch = _torch()
     return DG_BF16 if t.dtype == torch.bfloat16 else DG_F32
@@ -80,11 +112,9 @@ def dg_canvas_attention_fp8(q, k_prefix, v_prefix, k_canvas, v_canvas, q_scale=1
     torch = _torch()
     dt = (torch.uint8, torch.float8_e4m3fn)
     _need(q, "q", dt); _need(k_canvas, "k_canvas", dt); _need(v_canvas, "v_canvas", dt)
-    n, hq, d = q.shape
-    hkv = k_canvas.shape[1]
-    n_prefix = 0 if k_prefix is None else k_prefix.shape[0]
-    if n_prefix:
+    if k_prefix is not None and k_prefix.shape[0]:
         _need(k_prefix, "k_prefix", dt); _need(v_prefix, "v_prefix", dt)
+    n, hq, hkv, d, n_prefix = _check_attention_tensors(q, k_prefix, v_prefix, k_canvas, v_canvas, out)
     if out is None:
         out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
     ws = _workspace(dg_attention_workspace_bytes(n, n_prefix, hq, hkv, d), q.device, workspace)
@@ -146,11 +176,9 @@ def dg_canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, out=None, sca
     torch = _torch()
     dt = (torch.bfloat16, torch.float32)
     _need(q, "q", dt); _need(k_canvas, "k_canvas", dt); _need(v_canvas, "v_canvas", dt)
-    n, hq, d = q.shape
-    hkv = k_canvas.shape[1]
-    n_prefix = 0 if k_prefix is None else k_prefix.shape[0]
-    if n_prefix:
+    if k_prefix is not None and k_prefix.shape[0]:
         _need(k_prefix, "k_prefix", dt); _need(v_prefix, "v_prefix", dt)
+    n, hq, hkv, d, n_prefix = _check_attention_tensors(q, k_prefix, v_prefix, k_canvas, v_canvas, out)
     if out is None:
         out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
     nbytes = dg_attention_workspace_bytes(n, n_prefix, hq, hkv, d)
@@ -175,11 +203,10 @@ def dg_canvas_attention_batched(q, k_prefix, v_prefix, k_canvas, v_canvas, n_pre
     torch = _torch()
     dt = (torch.bfloat16, torch.float32)
     _need(q, "q", dt); _need(k_canvas, "k_canvas", dt); _need(v_canvas, "v_canvas", dt)
-    batch, n, hq, d = q.shape
-    hkv = k_canvas.shape[2]
-    stride = 0 if k_prefix is None else k_prefix.shape[1]
-    if stride:
+    if k_prefix is not None and k_prefix.shape[1]:
         _need(k_prefix, "k_prefix", dt); _need(v_prefix, "v_prefix", dt)
+    n, hq, hkv, d, stride = _check_attention_tensors(q, k_prefix, v_prefix, k_canvas, v_canvas, out, batched=True)
+    batch = q.shape[0]
     if len(n_prefix) != batch:
         raise ValueError(f"n_prefix has {len(n_prefix)} entries for a batch of {batch}")
     nps = (ctypes.c_int32 * batch)(*[int(x) for x in n_prefix])
@@ -467,9 +494,21 @@ def dg_canvas_init(canvas_ids, committed, ctrl, vocab, stream=None):
 
 
 def dg_kv_append(k_prefix, v_prefix, k_canvas, v_canvas, n_prefix, stream=None):
+    """Copy the canvas K/V [n, hkv, d] to rows n_prefix.. of the prefix buffers,
+    whose first dimension is the capacity the library checks against."""
+    torch = _torch()
+    dt = (torch.bfloat16, torch.float32)
+    for t, name in ((k_prefix, "k_prefix"), (v_prefix, "v_prefix"), (k_canvas, "k_canvas"), (v_canvas, "v_canvas")):
+        _need(t, name, dt)
     n, hkv, d = k_canvas.shape
+    cap = k_prefix.shape[0]
+    if tuple(v_prefix.shape) != tuple(k_prefix.shape) or tuple(v_canvas.shape) != (n, hkv, d) \
+            or tuple(k_prefix.shape[1:]) != (hkv, d):
+        raise ValueError("kv_append: prefix buffers must be [capacity, hkv, d] and canvas K/V [n, hkv, d]")
+    if len({k_prefix.dtype, v_prefix.dtype, k_canvas.dtype, v_canvas.dtype}) != 1:
+        raise ValueError("kv_append: all four tensors must share one dtype")
     check(load().dg_kv_append(_ptr(k_prefix), _ptr(v_prefix), _ptr(k_canvas), _ptr(v_canvas),
-                              int(n_prefix), n, hkv, d, _qkv_dtype(k_canvas), _stream(stream)))
+                              int(n_prefix), int(cap), n, hkv, d, _qkv_dtype(k_canvas), _stream(stream)))
 
 
 def dg_synth_logits(logits, canvas_ids, committed, ctrl, table, stream=None):

@@ -99,7 +99,7 @@ SIGNATURES = {
     "dg_step_graph_launch": (_i, [_vp, _vp]),
     "dg_step_graph_destroy": (None, [_vp]),
     "dg_canvas_init": (_i, [_vp, _vp, _vp, _i, _i, _vp]),
-    "dg_kv_append": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "dg_kv_append": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "dg_synth_logits": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "dg_philox_fill": (_i, [_vp, _sz, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
                             ctypes.c_uint32, _vp]),

@@ -97,6 +97,14 @@ int check_sampler(const float* logits, const void* emb, const int32_t* ids, cons
   return DG_OK;
 }
 
+// The plan's vocabulary splits must fit the combine kernel's per-split weights.
+int check_sampler_plan(const dg::SamplerPlan& p, const char* who) {
+  if (p.n_splits > dg::kMaxSamplerSplits)
+    return fail(DG_EUNSUPPORTED, "%s: vocab %d needs %d vocabulary splits, more than %d (vocab above 4194304)", who,
+                p.vocab, p.n_splits, dg::kMaxSamplerSplits);
+  return DG_OK;
+}
+
 int check_topk(int k, const dg::TopkPlan& p, void* ws, size_t ws_bytes, const char* who) {
   if (k < 1) return fail(DG_EINVAL, "%s: top_k < 1", who);
   if (k > 256) return fail(DG_EUNSUPPORTED, "%s: top_k > 256", who);
@@ -168,7 +176,8 @@ size_t dg_sampler_workspace_bytes(int n, int vocab, int d) {
 
 size_t dg_sampler_workspace_bytes_batched(int n, int batch, int vocab, int d) {
   if (n < 1 || n > 256 || batch < 1 || batch > 4096 || vocab < 2 || d < 1) return 0;
-  return dg::sampler_plan(n, batch, vocab, d).total;
+  const dg::SamplerPlan p = dg::sampler_plan(n, batch, vocab, d);
+  return p.n_splits > dg::kMaxSamplerSplits ? 0 : p.total;
 }
 
 size_t dg_denoise_workspace_bytes(int n, int np, int hq, int hkv, int d, int vocab, int dm) {
@@ -272,6 +281,8 @@ int dg_sampler_step_batched(const float* logits, const void* emb, int32_t* ids, 
   int st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, d, batch);
   if (st != DG_OK) return st;
   const dg::SamplerPlan p = dg::sampler_plan(n, batch, vocab, d);
+  st = check_sampler_plan(p, "sampler");
+  if (st != DG_OK) return st;
   if (!ws || ws_bytes < p.total)
     return fail(DG_EWORKSPACE, "sampler: workspace %zu < %zu bytes", ws_bytes, p.total);
   if (!aligned16(ws)) return fail(DG_EINVAL, "sampler: workspace misaligned");
@@ -301,6 +312,8 @@ int dg_sampler_step_eb_batched(const float* logits, const void* emb, int32_t* id
   if (!(stop_entropy >= 0.f) || !std::isfinite(stop_entropy))
     return fail(DG_EINVAL, "sampler_eb: stop_entropy must be finite and >= 0");
   const dg::SamplerPlan p = dg::sampler_plan(n, batch, vocab, d);
+  st = check_sampler_plan(p, "sampler_eb");
+  if (st != DG_OK) return st;
   if (!ws || ws_bytes < p.total)
     return fail(DG_EWORKSPACE, "sampler_eb: workspace %zu < %zu bytes", ws_bytes, p.total);
   if (!aligned16(ws)) return fail(DG_EINVAL, "sampler_eb: workspace misaligned");
@@ -363,6 +376,8 @@ int dg_denoise_step(const void* q, const void* kp, const void* vp, const void* k
   if (st != DG_OK) return st;
   st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, dm);
   if (st != DG_OK) return st;
+  st = check_sampler_plan(dg::sampler_plan(n, 1, vocab, dm), "denoise");
+  if (st != DG_OK) return st;
   const size_t need = dg_denoise_workspace_bytes(n, np, hq, hkv, d, vocab, dm);
   if (!ws || ws_bytes < need) return fail(DG_EWORKSPACE, "denoise: workspace %zu < %zu bytes", ws_bytes, need);
   if (!aligned16(ws)) return fail(DG_EINVAL, "denoise: workspace misaligned");
@@ -388,6 +403,8 @@ int dg_denoise_step_eb(const void* q, const void* kp, const void* vp, const void
   st = check_sampler(logits, emb, ids, accepted, z, reinterpret_cast<const uint32_t*>(status), ctrl, n, vocab, dm);
   if (st != DG_OK) return st;
   if (!argmax || !status) return fail(DG_EINVAL, "denoise_eb: null argmax or status");
+  st = check_sampler_plan(dg::sampler_plan(n, 1, vocab, dm), "denoise_eb");
+  if (st != DG_OK) return st;
   if (!(budget >= 0.f) || !std::isfinite(budget)) return fail(DG_EINVAL, "denoise_eb: budget must be finite and >= 0");
   if (!(stop_entropy >= 0.f) || !std::isfinite(stop_entropy))
     return fail(DG_EINVAL, "denoise_eb: stop_entropy must be finite and >= 0");
@@ -459,6 +476,8 @@ int dg_step_graph_create(const void* q, const void* kp, const void* vp, const vo
   if (st != DG_OK) return st;
   st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, dm);
   if (st != DG_OK) return st;
+  st = check_sampler_plan(dg::sampler_plan(n, 1, vocab, dm), "graph");
+  if (st != DG_OK) return st;
   return capture_step([&](hipStream_t cs) {
     return dg_denoise_step(q, kp, vp, kc, vc, attn_out, np, hq, hkv, d, dtype, scale, logits, emb, ids,
                            committed, z, conf, n_unc, ctrl, n, vocab, dm, ws, ws_bytes, cs);
@@ -476,6 +495,8 @@ int dg_step_graph_create_eb(const void* q, const void* kp, const void* vp, const
   int st = check_attention(q, kp, vp, kc, vc, attn_out, n, np, hq, hkv, d, dtype);
   if (st != DG_OK) return st;
   st = check_sampler(logits, emb, ids, accepted, z, reinterpret_cast<const uint32_t*>(status), ctrl, n, vocab, dm);
+  if (st != DG_OK) return st;
+  st = check_sampler_plan(dg::sampler_plan(n, 1, vocab, dm), "graph_eb");
   if (st != DG_OK) return st;
   return capture_step([&](hipStream_t cs) {
     return dg_denoise_step_eb(q, kp, vp, kc, vc, attn_out, np, hq, hkv, d, dtype, scale, logits, emb, ids,
@@ -524,10 +545,13 @@ int dg_canvas_init(int32_t* ids, uint8_t* committed, dg_ctrl* ctrl, int n, int v
   return DG_OK;
 }
 
-int dg_kv_append(void* kp, void* vp, const void* kc, const void* vc, int np, int n, int hkv, int d,
-                 int dtype, hipStream_t stream) {
+int dg_kv_append(void* kp, void* vp, const void* kc, const void* vc, int np, int capacity, int n, int hkv,
+                 int d, int dtype, hipStream_t stream) {
   if (!kp || !vp || !kc || !vc) return fail(DG_EINVAL, "kv_append: null pointer");
   if (np < 0 || n < 1 || hkv < 1 || d < 1) return fail(DG_EINVAL, "kv_append: bad sizes");
+  if ((int64_t)np + n > (int64_t)capacity)
+    return fail(DG_EINVAL, "kv_append: n_prefix %d + n_canvas %d exceeds the prefix capacity of %d rows", np, n,
+                capacity);
   if (dtype != DG_F32 && dtype != DG_BF16) return fail(DG_EUNSUPPORTED, "kv_append: dtype");
   const size_t es = dtype == DG_BF16 ? 2 : 4;
   const size_t row = (size_t)hkv * d * es;

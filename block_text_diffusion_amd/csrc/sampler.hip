@@ -507,7 +507,7 @@ __global__ __launch_bounds__(256) void samp_combine(const float* __restrict__ lo
                                                     int n_rows, int n_canvas, int vocab, int d,
                                                     EbRows eb) {
   const int row = blockIdx.y;
-  __shared__ float s_w[256];
+  __shared__ float s_w[kMaxSamplerSplits];
   __shared__ uint32_t s_bad;
   const dg_ctrl cb = ctrl[row / n_canvas];
   const float temp = temperature(cb);

@@ -408,10 +408,13 @@ int dg_canvas_init(int32_t* canvas_ids, uint8_t* committed, dg_ctrl* ctrl,
  * Append a finished canvas's K/V rows to the prefix cache (explainer section
  * "Block-autoregressive generation, one canvas after another"): copies
  * k_canvas/v_canvas [n_canvas, hkv, head_dim] to rows n_prefix.. of
- * k_prefix/v_prefix, which the caller sized for at least n_prefix + n_canvas rows.
+ * k_prefix/v_prefix [prefix_capacity, hkv, head_dim] (device, caller-owned).
+ * dtype DG_BF16 or DG_F32.  Returns DG_EINVAL when n_prefix + n_canvas exceeds
+ * prefix_capacity (nothing is copied), DG_EUNSUPPORTED for another dtype.
+ * Asynchronous on `stream` (two device-to-device copies).
  */
 int dg_kv_append(void* k_prefix, void* v_prefix, const void* k_canvas, const void* v_canvas,
-                 int n_prefix, int n_canvas, int hkv, int head_dim, int dtype,
+                 int n_prefix, int prefix_capacity, int n_canvas, int hkv, int head_dim, int dtype,
                  hipStream_t stream);
 
 /*

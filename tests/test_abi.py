@@ -142,7 +142,11 @@ def test_helper_argument_errors(lib):
     assert lib.dg_canvas_init(FAKE, FAKE, FAKE, 300, 100, None) == DG_EUNSUPPORTED
     assert lib.dg_synth_logits(FAKE, FAKE, FAKE, FAKE, FAKE, 1000, 16, 100, None) == DG_EINVAL
     assert lib.dg_philox_fill(FAKE, 6, 1, 0, 0, 0, None) == DG_EINVAL
-    assert lib.dg_kv_append(FAKE, FAKE, FAKE, FAKE, 0, 16, 8, 64, 9, None) == DG_EUNSUPPORTED
+    assert lib.dg_kv_append(FAKE, FAKE, FAKE, FAKE, 0, 16, 16, 8, 64, 9, None) == DG_EUNSUPPORTED
+    # the prefix buffer must hold n_prefix + n_canvas rows
+    assert lib.dg_kv_append(FAKE, FAKE, FAKE, FAKE, 4096, 4096 + 255, 256, 8, 128, 1, None) == DG_EINVAL
+    assert b"capacity" in lib.dg_last_error()
+    assert lib.dg_kv_append(FAKE, FAKE, FAKE, FAKE, -1, 4096, 256, 8, 128, 1, None) == DG_EINVAL
     h = ctypes.c_void_p()
     assert lib.dg_step_graph_create(None, None, None, None, None, None, 0, 8, 8, 64, 1, 0.0,
                                     None, None, None, None, None, None, None, None, 16, 100, 64,
@@ -249,3 +253,65 @@ def test_entropy_bounded_step_and_graph_arguments(lib):
     b[10] = DG_FP8_E4M3
     assert lib.dg_denoise_step_eb(*b, 0.1, 0.005, 16, 1000, 64, FAKE, 1 << 30, None) == DG_EUNSUPPORTED
     assert lib.dg_step_graph_create_eb(*a, 0.1, 0.005, 16, 1000, 64, FAKE, 1 << 30, None) == DG_EINVAL
+
+
+def test_vocabulary_splits_beyond_the_combine_limit_are_refused(lib):
+    """A vocabulary above 4194304 ids needs more than 256 vocabulary splits, more
+    merge weights than the combine kernel holds: every full-sampler entry point
+    refuses it on the host, and the workspace queries return 0."""
+    from block_text_diffusion_amd._lib import DG_EUNSUPPORTED
+    v = 8388608
+    assert lib.dg_sampler_workspace_bytes(1, v, 64) == 0
+    assert lib.dg_sampler_workspace_bytes_batched(1, 1, v, 64) == 0
+    assert lib.dg_denoise_workspace_bytes(1, 0, 8, 8, 64, v, 64) == 0
+    # the largest vocabulary that still fits is accepted by the query
+    assert lib.dg_sampler_workspace_bytes(1, 4194304, 64) > 0
+    big = 1 << 40
+    assert samp(lib, n=1, v=v, d=64, wsb=big) == DG_EUNSUPPORTED
+    assert b"splits" in lib.dg_last_error()
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE]
+    assert lib.dg_sampler_step_batched(*a, 1, 1, v, 64, FAKE, big, None) == DG_EUNSUPPORTED
+    assert samp_eb(lib, n=1, v=v, d=64, wsb=big) == DG_EUNSUPPORTED
+    d = [FAKE] * 6 + [0, 8, 8, 64, 1, 0.0] + [FAKE] * 8
+    assert lib.dg_denoise_step(*d, 1, v, 64, FAKE, big, None) == DG_EUNSUPPORTED
+    e = [FAKE] * 6 + [0, 8, 8, 64, 1, 0.0] + [FAKE] * 9
+    assert lib.dg_denoise_step_eb(*e, 0.1, 0.005, 1, v, 64, FAKE, big, None) == DG_EUNSUPPORTED
+    h = ctypes.c_void_p()
+    assert lib.dg_step_graph_create(*d, 1, v, 64, FAKE, big, ctypes.byref(h)) == DG_EUNSUPPORTED
+    assert h.value is None
+    assert lib.dg_step_graph_create_eb(*e, 0.1, 0.005, 1, v, 64, FAKE, big, ctypes.byref(h)) == DG_EUNSUPPORTED
+
+
+def test_binding_cross_checks_attention_tensors():
+    """The binding's cross-tensor checks (run before the C call, on any device):
+    one dtype for Q/K/V, matching heads and head_dim, and the output's shape."""
+    import torch
+    import block_text_diffusion_amd as dg
+    bf = torch.bfloat16
+    q = torch.zeros(16, 8, 64, dtype=bf)
+    kc = torch.zeros(16, 4, 64, dtype=bf)
+    kp = torch.zeros(8, 4, 64, dtype=bf)
+    assert dg._check_attention_tensors(q, kp, kp, kc, kc, None) == (16, 8, 4, 64, 8)
+    assert dg._check_attention_tensors(q, None, None, kc, kc, None) == (16, 8, 4, 64, 0)
+    with pytest.raises(ValueError, match="dtype"):
+        dg._check_attention_tensors(q.float(), kp, kp, kc, kc, None)
+    with pytest.raises(ValueError, match="dtype"):
+        dg._check_attention_tensors(q, kp.float(), kp.float(), kc, kc, None)
+    with pytest.raises(ValueError, match="canvas K/V"):
+        dg._check_attention_tensors(q, kp, kp, kc, torch.zeros(16, 4, 128, dtype=bf), None)
+    with pytest.raises(ValueError, match="canvas K/V"):
+        dg._check_attention_tensors(q, kp, kp, torch.zeros(15, 4, 64, dtype=bf), torch.zeros(15, 4, 64, dtype=bf),
+                                    None)
+    with pytest.raises(ValueError, match="prefix"):
+        dg._check_attention_tensors(q, kp, torch.zeros(9, 4, 64, dtype=bf), kc, kc, None)
+    with pytest.raises(ValueError, match="prefix"):
+        dg._check_attention_tensors(q, torch.zeros(8, 2, 64, dtype=bf), torch.zeros(8, 2, 64, dtype=bf), kc, kc,
+                                    None)
+    with pytest.raises(ValueError, match="out"):
+        dg._check_attention_tensors(q, kp, kp, kc, kc, torch.zeros(16, 8, 32))
+    with pytest.raises(ValueError, match="out"):
+        dg._check_attention_tensors(q, kp, kp, kc, kc, torch.zeros(16, 8, 64, dtype=bf))
+    qb, kcb, kpb = q[None].repeat(2, 1, 1, 1), kc[None].repeat(2, 1, 1, 1), kp[None].repeat(2, 1, 1, 1)
+    assert dg._check_attention_tensors(qb, kpb, kpb, kcb, kcb, None, batched=True) == (16, 8, 4, 64, 8)
+    with pytest.raises(ValueError, match="canvas K/V"):
+        dg._check_attention_tensors(qb, kpb, kpb, kcb[:1], kcb[:1], None, batched=True)
