@@ -8,8 +8,11 @@ commit / re-noise), replayed as one captured HIP graph.  Inputs are resident in
 HBM before timing starts.
 
 Prints one JSON line: steps/s, the roofline of the dominant kernel (the
-self-conditioning contraction) from per-kernel HIP events, and the CPU oracle's
-rate on the same workload.
+self-conditioning contraction, priced by the method's own bytes and flops) from
+per-kernel HIP events, roofline blocks for the whole sampler and for canvas
+attention, fractions against measured peaks (copy and matrix-core probes), the
+decode run through one captured step graph per canvas, and the CPU oracle's rate
+on the same workload.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -32,6 +35,7 @@ KERNEL_SOURCES = ["block_text_diffusion_amd/csrc/sampler.hip", "block_text_diffu
                   "block_text_diffusion_amd/csrc/attention.hip"]
 BF16_PEAK_TFLOPS = 2516.6
 FP32_MFMA_PEAK_TFLOPS = 157.3
+SAMPLER_KERNELS = ("samp_stats", "samp_gemm", "samp_combine", "samp_finalize")
 
 
 def parse():
@@ -47,8 +51,10 @@ def parse():
                          "with the CPU oracle (context; not part of the headline line's value)")
     ap.add_argument("--blas-reference", action="store_true",
                     help="also time one plain bf16 GEMM of the contraction's shape through torch")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--copy-probe-mib", type=int, default=1024,
+                    help="bytes each way of the plain copy probe (measured HBM peak, counter calibration)")
+    ap.add_argument("--no-probes", action="store_true", help="skip the copy and matrix-core peak probes")
+    ap.add_argument("--no-decode-run", action="store_true", help="skip the decode runs")
     return ap.parse_args()
 
 
@@ -140,28 +146,61 @@ def main():
     log("per-kernel us: " + ", ".join(f"{k}={v:.1f}" for k, v in per_kernel_us.items()))
     graph.close()
 
-    # algorithmic work of the dominant kernel, per launch (one step)
+    # Algorithmic work of the dominant kernel per launch (one step): the method
+    # reads the logits and E once and writes z, and does 2 N V d flops.  The
+    # contraction's operands are bf16 (three bf16 products per fp32-accurate
+    # one), so its roofline is the bf16 one: 412.3 GFLOP over 3.493 GB is an
+    # arithmetic intensity of 118 flop/B, below the bf16 ridge (2516.6 / 8 =
+    # 315 flop/B), so the bound is HBM bandwidth.
     gemm_us = per_kernel_us["samp_gemm"]
-    flops_fp32 = 2.0 * n * vocab * dm                          # softmax(l)·E contraction
-    flops_bf16x3 = 3.0 * flops_fp32                            # three bf16 products per fp32-accurate one
-    bytes_gemm = 4.0 * (n * vocab + vocab * dm + n * dm)       # logits + E + z, each once
-    achieved = flops_bf16x3 / (gemm_us * 1e-6) / 1e12
+    flops_method = 2.0 * n * vocab * dm                         # softmax(l)·E
+    flops_bf16x3 = 3.0 * flops_method                           # the products the matrix cores execute
+    bytes_method = 4.0 * (n * vocab + vocab * dm + n * dm)      # logits + E + z, each once
+    gbs = bytes_method / (gemm_us * 1e-6) / 1e9
     roofline = {
         "kernel": "samp_gemm",
-        "bound": "mfma",
-        "achieved": round(achieved, 1),
-        "peak": BF16_PEAK_TFLOPS,
-        "unit": "TFLOP/s",
-        "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+        "bound": "hbm",
+        "achieved": round(gbs, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(gbs / HBM_PEAK_GBS, 4),
         "traffic": measured_traffic("samp_gemm"),
         "avg_us": round(gemm_us, 2),
-        "hbm_gbs": round(bytes_gemm / (gemm_us * 1e-6) / 1e9, 1),
-        "hbm_frac": round(bytes_gemm / (gemm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-        "fp32_equiv_tflops": round(flops_fp32 / (gemm_us * 1e-6) / 1e12, 1),
+        "algorithmic_bytes": bytes_method,
+        "algorithmic_flops": flops_method,
+        "arithmetic_intensity": round(flops_method / bytes_method, 1),
+        "hbm_floor_us": round(bytes_method / (HBM_PEAK_GBS * 1e9) * 1e6, 1),
+        # the split-precision products against the bf16 matrix-core peak
+        "bf16x3_tflops": round(flops_bf16x3 / (gemm_us * 1e-6) / 1e12, 1),
+        "bf16x3_mfma_frac": round(flops_bf16x3 / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "bf16x3_floor_us": round(flops_bf16x3 / (BF16_PEAK_TFLOPS * 1e12) * 1e6, 1),
+        "timing": "HIP events around each launch on its stream, eager steps right after the timed region",
     }
+    # the whole sampler (four kernels) against the same HBM floor, and against
+    # max(HBM floor, bf16x3 matrix-core floor)
+    samp_us = sum(per_kernel_us[k] for k in SAMPLER_KERNELS if k in per_kernel_us)
+    floor_hbm_us = bytes_method / (HBM_PEAK_GBS * 1e9) * 1e6
+    floor_x3_us = max(floor_hbm_us, flops_bf16x3 / (BF16_PEAK_TFLOPS * 1e12) * 1e6)
+    sampler = {"kernels": list(SAMPLER_KERNELS), "us": round(samp_us, 2),
+               "bound": "hbm", "floor_us": round(floor_hbm_us, 1), "frac": round(floor_hbm_us / samp_us, 4),
+               "floor_bf16x3_us": round(floor_x3_us, 1), "frac_bf16x3": round(floor_x3_us / samp_us, 4)}
     attn = bf16_attention_timing(torch, dg, T, n, p, hq, hkv, hd, a.steps)
-    attn["per_kernel_us_in_step"] = {k: round(per_kernel_us[k], 2) for k in ("attn_partial", "attn_combine")
-                                     if k in per_kernel_us}
+    attn["per_kernel_us_eager_events"] = {k: round(per_kernel_us[k], 2)
+                                          for k in ("attn_partial", "attn_combine", "attn_fused")
+                                          if k in per_kernel_us}
+    log(f"roofline: samp_gemm {gemm_us:.1f} us = {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.3f} of HBM); "
+        f"sampler {samp_us:.1f} us ({floor_hbm_us / samp_us:.3f}); attention {attn['us']:.2f} us "
+        f"({attn['roofline']['frac']:.3f} of bf16 peak)")
+
+    probes = None if a.no_probes else peak_probes(torch, dg, a.copy_probe_mib)
+    if probes:
+        roofline["secondary"] = {"measured_peak": probes["copy_gbs"], "unit": "GB/s",
+                                 "frac": round(gbs / probes["copy_gbs"], 4),
+                                 "bf16x3_mfma_frac": round(flops_bf16x3 / (gemm_us * 1e-6) / 1e12
+                                                           / probes["mfma_tflops"], 4)}
+        sampler["frac_measured_hbm"] = round(bytes_method / (probes["copy_gbs"] * 1e9) * 1e6 / samp_us, 4)
+        attn["roofline"]["secondary"] = {"measured_peak": probes["mfma_tflops"], "unit": "TFLOP/s",
+                                         "frac": round(attn["tflops"] / probes["mfma_tflops"], 4)}
 
     # ---- the entropy-bounded sampler (the pages' default) on the same inputs ----
     eb = eb_sampler_timing(torch, dg, T, n, vocab, dm, a.steps)
@@ -186,22 +225,15 @@ def main():
     log("top-k sampler: " + ", ".join(f"k={r['k']} B={r['batch']}: {r['sampler_ms']:.3f} ms"
                                       for r in topk["runs"]))
 
-    # ---- the decode run: 4096-token prefix, four 256-token canvases ----
-    dec = decode_run_timing(torch, dg, T["emb"], vocab, dm)
-    log(f"decode run: {dec['tokens']} tokens in {dec['steps']} steps, {dec['tokens_per_s']:.0f} tokens/s")
-    dec_eb = decode_run_timing(torch, dg, T["emb"], vocab, dm, entropy_bounded=True)
-    log(f"decode run, entropy-bounded: {dec_eb['tokens']} tokens in {dec_eb['steps']} steps, "
-        f"{dec_eb['tokens_per_s']:.0f} tokens/s")
-
-    if a.copy_probe_mib:
-        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters calibrate
-        # the HBM byte counts read for the kernels above
-        src = torch.ones(a.copy_probe_mib << 18, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy probe: {a.copy_probe_mib} MiB read + {a.copy_probe_mib} MiB written per launch, 3 launches")
+    # ---- the decode run: 4096-token prefix, four 256-token canvases, one step graph per canvas ----
+    dec = dec_eb = None
+    if not a.no_decode_run:
+        dec = decode_run_timing(torch, dg, T["emb"], vocab, dm)
+        log(f"decode run: {dec['tokens']} tokens in {dec['steps']} steps, {dec['tokens_per_s_wall']:.0f} tokens/s "
+            f"wall, {dec['tokens_per_s_kernel']:.0f} tokens/s from step GPU time")
+        dec_eb = decode_run_timing(torch, dg, T["emb"], vocab, dm, entropy_bounded=True)
+        log(f"decode run, entropy-bounded: {dec_eb['tokens']} tokens in {dec_eb['steps']} steps, "
+            f"{dec_eb['tokens_per_s_wall']:.0f} tokens/s wall")
 
     blas = None
     if a.blas_reference:
@@ -220,9 +252,11 @@ def main():
         log(f"torch bf16 GEMM of the same shape: {us:.1f} us")
         del A, B
 
-    cpu = None
+    cpu = oracle_block0 = None
     if not a.no_cpu_baseline:
-        cpu = cpu_baseline(q, kp, vp, kc, vc, emb, logits, ids, mask)
+        cpu, e64 = cpu_baseline(q, kp, vp, kc, vc, emb, logits, ids, mask)
+        oracle_block0 = oracle_decode_block0(e64)
+        del e64
     others = workload_sweep(torch, dg, workloads) if a.all_workloads else None
 
     out = {
@@ -242,13 +276,19 @@ def main():
                                "bf16; vocab 262144, d_model 3072 fp32; one captured graph per step",
                    "canvas_tokens_per_s": round(256 * steps_per_s, 1),
                    "replay_ms": replay_ms,
-                   "per_kernel_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
+                   "per_kernel_us_eager_events": {k: round(v, 2) for k, v in per_kernel_us.items()},
+                   "per_kernel_note": "HIP events around each kernel of eager steps on the launch stream; "
+                                      "the event pairs add a few us to the short kernels, the graph replays "
+                                      "run them back to back (rocprofv3 in-graph durations in profiles/)",
+                   "sampler": sampler,
+                   "peak_probes": probes,
                    "embedding_pack_ms_once": round(pack_ms, 2),
                    "attention": attn,
                    "other_workloads": others,
                    "eb_sampler": eb,
                    "decode_run": dec,
                    "decode_run_entropy_bounded": dec_eb,
+                   "oracle_decode_block0": oracle_block0,
                    "batched_sampler": batched,
                    "topk_sampler": topk,
                    "attention_fp8": attn_fp8,
@@ -261,13 +301,22 @@ def main():
 
 
 def decode_run_timing(torch, dg, emb_packed, vocab, dm, entropy_bounded=False):
-    """The decode-run workload end to end on the device: per canvas, attention
-    over the growing prefix, canvas init, then steps of synthetic logits +
-    Gumbel sampler (T 0.8 -> 0.4) until the canvas is finished (one host read
-    per step), then the KV append.  Threshold mode: until no position is open.
-    Entropy-bounded mode (the pages' default): the accepted positions stand in
-    for the committed mask of the synthetic generator, and the canvas ends when
-    adaptive stopping fires (or after s_max steps).  Tokens/s over the whole run."""
+    """The decode-run workload on the device: a 4096-token prefix, then four
+    256-token canvases.  Each canvas gets one captured step graph (canvas
+    attention over the prefix as it stands, then the Gumbel sampler with T
+    0.8 -> 0.4), captured before the timed region; the prefix grows by 256
+    rows per canvas through the KV append.  Per step: the synthetic logits
+    (eagerly, outside the graph: they stand in for the model), then one graph
+    replay bracketed by two events, then one host read of the open count (or
+    the stop flag).  Threshold mode runs until no position is open;
+    entropy-bounded mode (the pages' default; the accepted positions stand in
+    for the committed mask of the synthetic generator) until adaptive stopping
+    fires or s_max steps.
+
+    tokens_per_s_kernel follows Eq. 12 of the Technical Report: tokens per
+    forward pass over the mean step GPU time (the graph replays, attention and
+    sampler).  tokens_per_s_wall is the whole loop on the host clock, with the
+    synthetic logits, canvas starts, host reads and KV appends."""
     import workloads
     c = workloads.CONFIGS[5]
     n, p0, hq, hkv, hd = c["n"], c["n_prefix"], c["hq"], c["hkv"], c["head_dim"]
@@ -288,6 +337,7 @@ def decode_run_timing(torch, dg, emb_packed, vocab, dm, entropy_bounded=False):
     ids = torch.zeros(n, dtype=torch.int32, device="cuda")
     mask = torch.zeros(n, dtype=torch.uint8, device="cuda")
     z = torch.empty((n, dm), dtype=torch.float32, device="cuda")
+    kappa = torch.empty(n, dtype=torch.float32, device="cuda")
     nu = torch.zeros(1, dtype=torch.int32, device="cuda")
     ent = torch.empty(n, dtype=torch.float32, device="cuda")
     amax = torch.empty(n, dtype=torch.int32, device="cuda")
@@ -295,40 +345,60 @@ def decode_run_timing(torch, dg, emb_packed, vocab, dm, entropy_bounded=False):
     attn = torch.empty((n, hq, hd), dtype=torch.float32, device="cuda")
     ctrl = dg.make_ctrl(seed=c["seed"], s_max=c["s_max"], tau=c["tau"], t_start=c["t_start"],
                         t_end=c["t_end"], flags=dg.DG_AUTO_ADVANCE | dg.DG_GUMBEL | dg.DG_T_SCHEDULE)
-    ws = torch.empty(max(dg.dg_sampler_workspace_bytes(n, vocab, dm),
-                         dg.dg_attention_workspace_bytes(n, total, hq, hkv, hd)), dtype=torch.uint8,
+    ws = torch.empty(dg.dg_denoise_workspace_bytes(n, total - n, hq, hkv, hd, vocab, dm), dtype=torch.uint8,
                      device="cuda")
+    # one step graph per canvas, each over the prefix length that canvas sees
+    graphs = []
+    for b, (q, kc, vc) in enumerate(blocks):
+        p = p0 + b * n
+        if entropy_bounded:
+            graphs.append(dg.StepGraphEB(q, kbuf[:p], vbuf[:p], kc, vc, attn, logits, emb_packed, ids, mask, z,
+                                         ent, amax, status, ctrl, workspace=ws))
+        else:
+            graphs.append(dg.StepGraph(q, kbuf[:p], vbuf[:p], kc, vc, attn, logits, emb_packed, ids, mask, z,
+                                       kappa, nu, ctrl, workspace=ws))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(c["blocks"] * c["s_max"])]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     steps, p = 0, p0
-    for q, kc, vc in blocks:
-        dg.dg_canvas_attention(q, kbuf[:p], vbuf[:p], kc, vc, out=attn, workspace=ws)
+    per_block = []
+    for b, (q, kc, vc) in enumerate(blocks):
         dg.dg_canvas_init(ids, mask, ctrl, vocab)
         if entropy_bounded:
             amax.fill_(-1)
-            for _ in range(c["s_max"]):
-                dg.dg_synth_logits(logits, ids, mask, ctrl, table)
-                dg.dg_sampler_step_eb(logits, emb_packed, ids, mask, z, ent, amax, status, ctrl, workspace=ws)
-                steps += 1
+        s_block = 0
+        for _ in range(c["s_max"]):
+            dg.dg_synth_logits(logits, ids, mask, ctrl, table)
+            evs[steps][0].record()
+            graphs[b].launch()
+            evs[steps][1].record()
+            steps += 1
+            s_block += 1
+            if entropy_bounded:
                 if dg.read_eb_status(status)["stop"]:
                     break
-        else:
-            while True:
-                dg.dg_synth_logits(logits, ids, mask, ctrl, table)
-                dg.dg_sampler_step(logits, emb_packed, ids, mask, z, None, nu, ctrl, workspace=ws)
-                steps += 1
-                if int(nu.item()) == 0:
-                    break
+            elif int(nu.item()) == 0:
+                break
         dg.dg_kv_append(kbuf, vbuf, kc, vc, p)
         p += n
+        per_block.append(s_block)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    step_ms = np.array([evs[k][0].elapsed_time(evs[k][1]) for k in range(steps)])
+    for g in graphs:
+        g.close()
     tokens = c["blocks"] * n
-    return {"tokens": tokens, "steps": steps, "seconds": round(dt, 5),
-            "tokens_per_s": round(tokens / dt, 1), "ms_per_step": round(dt * 1e3 / steps, 4),
-            "note": "synthetic logits generated on the device inside the loop; one host read per step"
-                    + ("; entropy-bounded sampler, budget 0.1, adaptive stop at mean entropy 0.005"
-                       if entropy_bounded else "")}
+    tpf = tokens / steps                        # tokens per forward pass
+    t_fwd_ms = float(step_ms.mean())
+    return {"tokens": tokens, "steps": steps, "steps_per_canvas": per_block, "tokens_per_forward": round(tpf, 2),
+            "seconds_wall": round(dt, 5), "tokens_per_s_wall": round(tokens / dt, 1),
+            "step_gpu_ms_mean": round(t_fwd_ms, 4), "step_gpu_ms_median": round(float(np.median(step_ms)), 4),
+            "tokens_per_s_kernel": round(tpf / (t_fwd_ms * 1e-3), 1),
+            "note": "one captured step graph (attention + sampler) per canvas, prefix 4096 + 256 b; synthetic "
+                    "logits written on the device before each replay (outside the step GPU time); one host read "
+                    "per step" + ("; entropy-bounded sampler, budget 0.1, adaptive stop at mean entropy 0.005"
+                                  if entropy_bounded else "")}
 
 
 def batched_sampler_timing(torch, dg, T, n, vocab, dm, steps, batches=(2, 4, 8)):
@@ -383,10 +453,53 @@ def bf16_attention_timing(torch, dg, T, n, p, hq, hkv, hd, steps, n_sets=16):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
+    # algorithmic work per call: QK^T and PV over the 4352 keys for 256 x 16
+    # query rows; bytes: Q, prefix and canvas K/V once (bf16), O (fp32)
     flops = 4.0 * n * (p + n) * hd * hq
-    return {"us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 1),
-            "frac_bf16_peak": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "timing": f"eager calls back to back between two events (partial + combine), {n_sets} rotated Q/K/V sets"}
+    nbytes = 2.0 * n * hq * hd + 2.0 * 2.0 * (p + n) * hkv * hd + 4.0 * n * hq * hd
+    tflops = flops / (us * 1e-6) / 1e12
+    return {"us": round(us, 2), "tflops": round(tflops, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops,
+                         "algorithmic_bytes": nbytes, "arithmetic_intensity": round(flops / nbytes, 1),
+                         "floor_us": round(flops / (BF16_PEAK_TFLOPS * 1e12) * 1e6, 2)},
+            "timing": f"eager calls back to back between two events (every kernel of a call), "
+                      f"{n_sets} rotated Q/K/V sets"}
+
+
+def peak_probes(torch, dg, copy_mib):
+    """Measured peaks on this machine: a plain copy (bytes read + written per
+    second) and the matrix-core loop probe (bf16 flops per second), each timed
+    with events over several launches after a warm-up."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    src = torch.ones(copy_mib << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dg.dg_probe_copy(dst, src)
+    torch.cuda.synchronize()
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        dg.dg_probe_copy(dst, src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1) / reps
+    copy_gbs = 2.0 * (copy_mib << 20) / (copy_ms * 1e-3) / 1e9
+    del src, dst
+    for _ in range(2):
+        dg.dg_probe_mfma_bf16()
+    torch.cuda.synchronize()
+    e0.record()
+    flops = 0.0
+    for _ in range(reps):
+        flops += dg.dg_probe_mfma_bf16()
+    e1.record()
+    torch.cuda.synchronize()
+    mfma_tflops = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    log(f"probes: copy {copy_gbs:.0f} GB/s, matrix cores {mfma_tflops:.0f} TFLOP/s (bf16)")
+    return {"copy_gbs": round(copy_gbs, 1), "copy_mib_each_way": copy_mib, "copy_ms": round(copy_ms, 4),
+            "mfma_tflops": round(mfma_tflops, 1),
+            "mfma_probe": "1024 workgroups x 4 waves x 2048 iterations x 4 independent 32x32x16 bf16 MFMA chains"}
 
 
 def batched_attention_timing(torch, dg, T, n, p, hq, hkv, hd, steps, n_sets=8):
@@ -651,15 +764,37 @@ def workload_sweep(torch, dg, workloads):
     return res
 
 
-def cpu_baseline(q, kp, vp, kc, vc, emb, logits, ids, mask):
-    """The CPU oracle on the same workload: one full step (attention + sampler, z for all rows)."""
-    from oracle import sampler as S
-    from oracle.attention import canvas_attention
+def host_cpu():
+    """The host's CPU: cores this process may run on, the core count, and the model name."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"nproc": usable, "cpu_count": os.cpu_count(), "model": model}
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        cores = os.cpu_count()
+        return os.cpu_count()
+
+
+def cpu_baseline(q, kp, vp, kc, vc, emb, logits, ids, mask):
+    """The CPU oracle on the same workload: one full step (attention + sampler,
+    z for all rows).  Returns the record and E widened to fp64 (reused)."""
+    from oracle import sampler as S
+    from oracle.attention import canvas_attention
     log("cpu baseline: widening E to fp64 (untimed input preparation)")
     e64 = emb.astype(np.float64)
     ctrl = S.Ctrl(seed=4, tau=0.9, flags=S.AUTO_ADVANCE)
@@ -673,10 +808,33 @@ def cpu_baseline(q, kp, vp, kc, vc, emb, logits, ids, mask):
         dt = time.perf_counter() - t0
         if dt >= 10.0 or steps >= 30:
             break
-    return {"value": round(steps / dt, 4), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+    hc = host_cpu()
+    return {"value": round(steps / dt, 4), "unit": "steps/s", "cores": int(blas_threads()), "kind": "oracle",
+            "nproc": hc["nproc"], "cpu_model": hc["model"],
             "sample": f"{steps} full steps of the same workload (attention over 4352 keys for 256x16 query "
                       f"rows + sampler over 256x262144 logits with z for all rows) in {dt:.1f} s, "
-                      f"fp64 numpy; E widened to fp64 before timing"}
+                      f"fp64 numpy with {blas_threads()} BLAS threads; E widened to fp64 before timing"}, e64
+
+
+def oracle_decode_block0(e64):
+    """The oracle on the decode run's first canvas (prefix 4096): attention once
+    (its Q/K/V are fixed for the canvas), then synthetic logits and a sampler
+    step with z for all rows until the canvas is committed."""
+    import workloads
+    from oracle import decode, sampler as S
+    c = workloads.CONFIGS[5]
+    q, kp, vp, kc, vc = workloads.attention_inputs(5, block=0)
+    ctrl = S.Ctrl(seed=c["seed"], s_max=c["s_max"], flags=S.AUTO_ADVANCE | S.GUMBEL | S.T_SCHEDULE,
+                  tau=c["tau"], t_start=c["t_start"], t_end=c["t_end"])
+    log("oracle: decode run, first canvas")
+    t0 = time.perf_counter()
+    recs, _ = decode.decode_run(kp, vp, [dict(q=q, k_canvas=kc, v_canvas=vc)], e64, workloads.synth_table(),
+                                c["vocab"], ctrl, z_rows="all", max_blocks=1)
+    dt = time.perf_counter() - t0
+    steps = len(recs[0]["steps"])
+    return {"seconds": round(dt, 2), "steps": steps, "tokens": c["n"], "tokens_per_s": round(c["n"] / dt, 2),
+            "ms_per_step": round(dt * 1e3 / steps, 1), "cores": int(blas_threads()),
+            "what": "attention once + per step synthetic logits and a sampler step with z for all 256 rows"}
 
 
 if __name__ == "__main__":

@@ -19,7 +19,7 @@ __all__ = [
     "stack_ctrl", "dg_embedding_pack", "dg_embedding_packed_bytes", "dg_denoise_step", "dg_denoise_step_eb", "StepGraph", "StepGraphEB", "dg_canvas_init",
     "dg_kv_append", "dg_synth_logits", "dg_philox_fill", "dg_attention_workspace_bytes",
     "dg_sampler_workspace_bytes", "dg_denoise_workspace_bytes", "dg_profile_enable",
-    "dg_profile_read", "make_ctrl", "read_ctrl", "write_ctrl", "DG_GUMBEL", "DG_COMMIT_ONLY",
+    "dg_profile_read", "dg_probe_mfma_bf16", "dg_probe_copy", "make_ctrl", "read_ctrl", "write_ctrl", "DG_GUMBEL", "DG_COMMIT_ONLY",
     "DG_AUTO_ADVANCE", "DG_T_SCHEDULE", "DG_ATTN_CAUSAL", "DG_F32", "DG_BF16", "DG_FP8_E4M3", "DgError", "load",
 ]
 
@@ -520,6 +520,22 @@ def dg_synth_logits(logits, canvas_ids, committed, ctrl, table, stream=None):
 def dg_philox_fill(out, seed, c1, c2, c3, stream=None):
     check(load().dg_philox_fill(_ptr(out), out.numel(), int(seed), int(c1), int(c2), int(c3),
                                 _stream(stream)))
+
+
+# ---- peak probes ----
+def dg_probe_mfma_bf16(n_workgroups=1024, iters=2048, stream=None):
+    """Launch the matrix-core probe; returns its flop count (time it with events)."""
+    torch = _torch()
+    sink = torch.empty(n_workgroups * 256, dtype=torch.float32, device="cuda")
+    check(load().dg_probe_mfma_bf16(_ptr(sink), int(n_workgroups), int(iters), _stream(stream)))
+    return float(n_workgroups) * 4 * iters * 4 * 32768
+
+
+def dg_probe_copy(dst, src, stream=None):
+    """Copy src to dst (same byte size, GPU tensors) with the plain copy probe."""
+    if dst.numel() * dst.element_size() != src.numel() * src.element_size():
+        raise ValueError("probe_copy: dst and src must have the same byte size")
+    check(load().dg_probe_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(), _stream(stream)))
 
 
 # ---- profiling ----

@@ -103,6 +103,8 @@ SIGNATURES = {
     "dg_synth_logits": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "dg_philox_fill": (_i, [_vp, _sz, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
                             ctypes.c_uint32, _vp]),
+    "dg_probe_mfma_bf16": (_i, [_vp, _i, _i, _vp]),
+    "dg_probe_copy": (_i, [_vp, _vp, _sz, _vp]),
     "dg_profile_enable": (_i, [_i]),
     "dg_profile_read": (_i, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                              ctypes.POINTER(ctypes.c_int), _i]),

@@ -77,6 +77,57 @@ __global__ __launch_bounds__(256) void philox_fill_kernel(uint32_t* __restrict__
   *reinterpret_cast<u32x4*>(out + 4 * m) = (u32x4){h.w0, h.w1, h.w2, h.w3};
 }
 
+// ---- peak probes (measurement only) ----
+// Matrix cores: every wave keeps four independent accumulator chains of
+// v_mfma_f32_32x32x16_bf16 on register operands (a chain on one accumulator
+// cannot issue back to back), so the loop runs at the rate the matrix cores
+// sustain at the clock the chip holds under this load.
+constexpr int kProbeWaves = 4;
+__global__ __launch_bounds__(64 * kProbeWaves) void probe_mfma_kernel(float* __restrict__ sink, int iters) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(1.0f + 0.0078125f * (float)((lane + e) & 7));
+    b[e] = (__bf16)(0.5f - 0.0078125f * (float)((lane * 3 + e) & 7));
+  }
+  f32x16 c0, c1, c2, c3;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) { c0[v] = 0.f; c1[v] = 0.f; c2[v] = 0.f; c3[v] = 0.f; }
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c3, 0, 0, 0);
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc += c0[v] + c1[v] + c2[v] + c3[v];
+  // every lane's sum is written: the loop's results are live
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+// HBM: a plain copy, 16 bytes per lane per iteration, grid-stride.
+__global__ __launch_bounds__(256) void probe_copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                         size_t n16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+hipError_t launch_probe_mfma(float* sink, int n_wg, int iters, hipStream_t s) {
+  probe_mfma_kernel<<<n_wg, 64 * kProbeWaves, 0, s>>>(sink, iters);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  probe_copy_kernel<<<(unsigned)blocks, 256, 0, s>>>(static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), n16);
+  return hipGetLastError();
+}
+
 hipError_t launch_canvas_init(int32_t* ids, uint8_t* committed, dg_ctrl* ctrl, int n, int vocab,
                               hipStream_t s) {
   prof_begin("canvas_init", s);

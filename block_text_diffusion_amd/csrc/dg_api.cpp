@@ -588,6 +588,24 @@ int dg_philox_fill(uint32_t* out, size_t n_words, uint64_t seed, uint32_t c1, ui
   return DG_OK;
 }
 
+int dg_probe_mfma_bf16(float* sink, int n_workgroups, int iters, hipStream_t stream) {
+  if (!sink) return fail(DG_EINVAL, "probe_mfma: null sink");
+  if (n_workgroups < 1 || n_workgroups > 65535 || iters < 1)
+    return fail(DG_EINVAL, "probe_mfma: n_workgroups must be in [1, 65535] and iters >= 1");
+  hipError_t e = dg::launch_probe_mfma(sink, n_workgroups, iters, stream);
+  if (e != hipSuccess) return hip_fail(e, "probe_mfma launch");
+  return DG_OK;
+}
+
+int dg_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (!dst || !src) return fail(DG_EINVAL, "probe_copy: null pointer");
+  if (bytes % 16 != 0) return fail(DG_EINVAL, "probe_copy: bytes must be a multiple of 16");
+  if (!aligned16(dst) || !aligned16(src)) return fail(DG_EINVAL, "probe_copy: pointers must be 16-byte aligned");
+  hipError_t e = dg::launch_probe_copy(dst, src, bytes, stream);
+  if (e != hipSuccess) return hip_fail(e, "probe_copy launch");
+  return DG_OK;
+}
+
 int dg_profile_enable(int on) {
   g_prof_on = on != 0;
   return DG_OK;

@@ -438,6 +438,27 @@ int dg_philox_fill(uint32_t* out, size_t n_words, uint64_t seed, uint32_t c1, ui
                    uint32_t c3, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Peak probes (measurement only)                                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The matrix-core rate the chip sustains: n_workgroups workgroups of 4 waves,
+ * each wave running `iters` iterations of four independent
+ * v_mfma_f32_32x32x16_bf16 chains on register operands, i.e.
+ * n_workgroups * 4 * iters * 4 * 32768 flops.  sink: device float32 buffer of
+ * n_workgroups * 256 entries (written, values meaningless).  n_workgroups in
+ * [1, 65535], iters >= 1.  Asynchronous on `stream`.
+ */
+int dg_probe_mfma_bf16(float* sink, int n_workgroups, int iters, hipStream_t stream);
+
+/*
+ * The HBM rate of a plain copy: `bytes` (a multiple of 16) from src to dst,
+ * both device pointers, 16-byte aligned, not overlapping; 16 bytes per lane
+ * per load and store.  Asynchronous on `stream`.
+ */
+int dg_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Profiling and errors                                                      */
 /* ------------------------------------------------------------------------ */
 

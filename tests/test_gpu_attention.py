@@ -1,10 +1,10 @@
-"""Canvas attention on the GPU against the fp64 oracle (max-abs 2e-2, bf16 in, fp32 accumulate)."""
+"""Canvas attention on the GPU against the fp64 oracle: the max-abs 2e-2 contract (bf16 in,
+fp32 accumulate) and the secondary rounding bounds (element and row) of tests/gpu_util.py."""
 import numpy as np
 import pytest
 
 import workloads
-from gpu_util import ATTN_MAX_ABS, log, require_gpu, to_dev
-from oracle.attention import canvas_attention, canvas_attention_batched
+from gpu_util import ATTN_MAX_ABS, attention_reference, check_attention, log, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -19,11 +19,10 @@ def run_gpu(torch, dg, q, kp, vp, kc, vc, qkv, scale=0.0):
     return out.cpu().numpy()
 
 
-def check(got, ref, label):
-    err = np.abs(got.astype(np.float64) - ref).max()
-    log(f"{label}: max abs err {err:.3e}")
-    assert np.all(np.isfinite(got))
-    assert err <= ATTN_MAX_ABS, f"{label}: max abs err {err}"
+def check(got, inputs, label, qkv="bf16", causal=False, scale=None):
+    """The contract and the secondary bounds against the oracle on these inputs."""
+    ref, ref_r, bound = attention_reference(*inputs, causal=causal, scale=scale, staged_bf16=(qkv == "f32"))
+    return check_attention(got, ref, ref_r, bound, label)
 
 
 @pytest.mark.parametrize("workload", [1, 2, 4])
@@ -33,7 +32,7 @@ def test_workloads(workload):
     log(f"attention workload {workload}")
     q, kp, vp, kc, vc = workloads.attention_inputs(workload)
     got = run_gpu(torch, dg, q, kp, vp, kc, vc, c["qkv"])
-    check(got, canvas_attention(q, kp, vp, kc, vc), f"workload {workload}")
+    check(got, (q, kp, vp, kc, vc), f"workload {workload}", qkv=c["qkv"])
 
 
 @pytest.mark.parametrize("n,p,hq,hkv,d,qkv", [
@@ -51,14 +50,14 @@ def test_shapes(n, p, hq, hkv, d, qkv):
     log(f"attention n={n} p={p} hq={hq} hkv={hkv} d={d} {qkv}")
     q, kp, vp, kc, vc = workloads.attention_inputs(2, n=n, n_prefix=p, hq=hq, hkv=hkv, head_dim=d, qkv=qkv)
     got = run_gpu(torch, dg, q, kp, vp, kc, vc, qkv)
-    check(got, canvas_attention(q, kp, vp, kc, vc), f"n={n} p={p}")
+    check(got, (q, kp, vp, kc, vc), f"n={n} p={p}", qkv=qkv)
 
 
 def test_explicit_scale():
     torch, dg = require_gpu()
     q, kp, vp, kc, vc = workloads.attention_inputs(2, n=64, n_prefix=64)
     got = run_gpu(torch, dg, q, kp, vp, kc, vc, "bf16", scale=0.05)
-    check(got, canvas_attention(q, kp, vp, kc, vc, scale=0.05), "scale 0.05")
+    check(got, (q, kp, vp, kc, vc), "scale 0.05", scale=0.05)
 
 
 def test_permutation_invariance_and_equivariance():
@@ -69,6 +68,7 @@ def test_permutation_invariance_and_equivariance():
     pc = rng.permutation(kc.shape[0])
     permuted = run_gpu(torch, dg, q, kp, vp, kc[pc], vc[pc], "bf16")
     assert np.abs(permuted - base).max() <= ATTN_MAX_ABS
+    check(permuted, (q, kp, vp, kc[pc], vc[pc]), "permuted canvas keys")
     pq = rng.permutation(q.shape[0])
     # query rows are independent: permuting queries permutes the output exactly
     np.testing.assert_array_equal(run_gpu(torch, dg, q[pq], kp, vp, kc, vc, "bf16"), base[pq])
@@ -98,7 +98,7 @@ def test_causal(n, p, hq, hkv, d, qkv):
     t = lambda x: to_dev(x, dt)
     got = dg.dg_canvas_attention(t(q), t(kp) if p else None, t(vp) if p else None, t(kc), t(vc),
                                  causal=True).cpu().numpy()
-    check(got, canvas_attention(q, kp, vp, kc, vc, causal=True), f"causal n={n} p={p}")
+    check(got, (q, kp, vp, kc, vc), f"causal n={n} p={p}", qkv=qkv, causal=True)
 
 
 def batched_inputs(qkv, n, stride, nps, hq, hkv, d):
@@ -138,9 +138,10 @@ def test_batched_mixed_causal(qkv, n, stride, nps, flags, hq, hkv, d):
                                          to_dev(vc, dt), nps, [bool(f) for f in flags])
     torch.cuda.synchronize()
     got = out.cpu().numpy()
-    ref = canvas_attention_batched(q, kp, vp, kc, vc, nps, flags)
     for s_ in range(len(nps)):
-        check(got[s_], ref[s_], f"sequence {s_} (n_prefix {nps[s_]}, causal {flags[s_]})")
+        np_s = nps[s_]
+        check(got[s_], (q[s_], kp[s_, :np_s], vp[s_, :np_s], kc[s_], vc[s_]),
+              f"sequence {s_} (n_prefix {np_s}, causal {flags[s_]})", qkv=qkv, causal=bool(flags[s_]))
 
 
 def test_batched_single_sequence_matches_the_single_call():

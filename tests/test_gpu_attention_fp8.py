@@ -1,12 +1,13 @@
 """FP8 (OCP E4M3) canvas attention on the GPU against the oracle: attention of
 the decoded, scaled inputs in fp64 (oracle.fp8).  The kernel stages E4M3 as
-bf16 exactly, so the bf16 path's bound applies: max-abs 2e-2 on outputs of
-unit-scale values, scaled by v_scale."""
+bf16 exactly, so the bf16 path's bounds apply to the decoded, scaled inputs:
+max-abs 2e-2 on outputs of unit-scale values (scaled by v_scale) and the
+secondary rounding bounds of tests/gpu_util.py."""
 import numpy as np
 import pytest
 
 import workloads
-from gpu_util import ATTN_MAX_ABS, log, require_gpu, to_dev
+from gpu_util import ATTN_MAX_ABS, ATTN_ROW_REL, attention_errors, attention_reference, log, require_gpu, to_dev
 from oracle import fp8 as F
 
 pytestmark = pytest.mark.gpu
@@ -21,11 +22,21 @@ def run_fp8(torch, dg, q, kp, vp, kc, vc, scales=(1.0, 1.0, 1.0), causal=False):
     return out.cpu().numpy()
 
 
-def check(got, ref, label, tol):
-    err = np.abs(got.astype(np.float64) - ref).max()
-    log(f"{label}: max abs err {err:.3e}")
+def check(got, codes, scales, label, tol, causal=False):
+    """The contract (tol) and the secondary bounds around the oracle on the
+    decoded, scaled inputs (the kernel stages them exactly)."""
+    q, kp, vp, kc, vc = codes
+    qs, ks, vs = scales
+    dq = lambda x, sc: F.e4m3_to_float(x) * float(np.float32(sc))
+    ref = F.canvas_attention_fp8(q, kp, vp, kc, vc, *scales, causal=causal)
+    _, ref_r, bound = attention_reference(dq(q, qs), dq(kp, ks), dq(vp, vs), dq(kc, ks), dq(vc, vs), causal=causal,
+                                          scale=1.0 / np.sqrt(q.shape[2]))
     assert np.all(np.isfinite(got))
+    err, ratio, row = attention_errors(got, ref, ref_r, bound)
+    log(f"{label}: max abs err {err:.3e}, error / element bound {ratio:.3f}, row rel L2 {row:.3e}")
     assert err <= tol, f"{label}: max abs err {err}"
+    assert ratio <= 1.0, f"{label}: error exceeds the rounding bound by {ratio:.2f}x"
+    assert row <= ATTN_ROW_REL, f"{label}: row relative L2 {row:.3e}"
 
 
 def test_long_context_fp8_with_scales():
@@ -33,8 +44,7 @@ def test_long_context_fp8_with_scales():
     q, kp, vp, kc, vc = workloads.attention_inputs_fp8(4)
     scales = (0.5, 0.75, 2.0)
     got = run_fp8(torch, dg, q, kp, vp, kc, vc, scales)
-    ref = F.canvas_attention_fp8(q, kp, vp, kc, vc, *scales)
-    check(got, ref, "long context, fp8", ATTN_MAX_ABS * scales[2])
+    check(got, (q, kp, vp, kc, vc), scales, "long context, fp8", ATTN_MAX_ABS * scales[2])
 
 
 @pytest.mark.parametrize("n,p,hq,hkv,d,causal", [
@@ -51,7 +61,7 @@ def test_fp8_shapes(n, p, hq, hkv, d, causal):
     log(f"fp8 attention n={n} p={p} hq={hq} hkv={hkv} d={d} causal={causal}")
     q, kp, vp, kc, vc = workloads.attention_inputs_fp8(2, n=n, n_prefix=p, hq=hq, hkv=hkv, head_dim=d)
     got = run_fp8(torch, dg, q, kp, vp, kc, vc, causal=causal)
-    check(got, F.canvas_attention_fp8(q, kp, vp, kc, vc, causal=causal), f"n={n} p={p}", ATTN_MAX_ABS)
+    check(got, (q, kp, vp, kc, vc), (1.0, 1.0, 1.0), f"n={n} p={p}", ATTN_MAX_ABS, causal=causal)
 
 
 def test_every_code_decodes_exactly():

@@ -3,20 +3,23 @@ until committed with Gumbel candidates and the linear temperature schedule, the
 logits drawn on the device by the threshold-tuned synthetic generator, and each
 finished canvas appended to the KV cache before the next one starts.
 
+Each canvas runs through one captured step graph (canvas attention over the
+prefix as it stands, then the sampler; the prefix grows by 256 rows per canvas)
+replayed once per step, with the synthetic logits written before each replay.
 Every step is compared with the oracle from the same entry state: the device's
-synthetic logits bit for bit, ids / commit mask / confidence under the
-comparison rules, z on sampled rows, the counter of open positions and the
-control block.  Each test runs one canvas; they share the run's state and go in
-order.
+synthetic logits bit for bit, the attention output (against the oracle on the
+first step of a canvas, bit-identical on the later replays), ids / commit mask /
+confidence under the comparison rules, z on sampled rows, the counter of open
+positions and the control block.  Each test runs one canvas; they share the
+run's state and go in order.
 """
 import numpy as np
 import pytest
 
 import workloads
-from gpu_util import ATTN_MAX_ABS, check_step, check_z, log, require_gpu, to_dev
+from gpu_util import attention_reference, check_attention, check_step, check_z, log, require_gpu, to_dev
 from oracle import sampler as S
 from oracle import synth
-from oracle.attention import canvas_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -52,8 +55,10 @@ def run():
         nu=torch.zeros(1, dtype=torch.int32, device="cuda"),
         ctrl=dg.make_ctrl(seed=ctrl.seed, s_max=ctrl.s_max, flags=ctrl.flags, tau=ctrl.tau,
                           t_start=ctrl.t_start, t_end=ctrl.t_end),
-        ws=torch.empty(dg.dg_sampler_workspace_bytes(n, vocab, emb.shape[1]), dtype=torch.uint8,
-                       device="cuda"),
+        attn=torch.empty((n, CFG["hq"], hd), dtype=torch.float32, device="cuda"),
+        # one workspace for every canvas's step graph: sized for the longest prefix
+        ws=torch.empty(dg.dg_denoise_workspace_bytes(n, total - n, CFG["hq"], hkv, hd, vocab, emb.shape[1]),
+                       dtype=torch.uint8, device="cuda"),
         # oracle side
         e64=emb.astype(np.float64), table_np=table, kp=kp, vp=vp, ctrl_ref=ctrl,
         steps=[], torch=torch, dg=dg)
@@ -76,14 +81,9 @@ def test_decode_block(run, block):
     q, _, _, kc, vc = workloads.attention_inputs(5, block=block)
     p = run["n_prefix"]
 
-    # attention of this canvas over the prefix as it stands, then the oracle's
     kp_d, vp_d = run["kbuf"][:p], run["vbuf"][:p]
-    kc_d, vc_d = to_dev(kc, bf), to_dev(vc, bf)
-    attn = dg.dg_canvas_attention(to_dev(q, bf), kp_d, vp_d, kc_d, vc_d)
-    ref_attn = canvas_attention(q, run["kp"], run["vp"], kc, vc)
-    err = float(np.abs(attn.cpu().numpy() - ref_attn).max())
-    log(f"decode block {block}: prefix {p}, attention max abs err {err:.2e}")
-    assert err <= ATTN_MAX_ABS
+    q_d, kc_d, vc_d = to_dev(q, bf), to_dev(kc, bf), to_dev(vc, bf)
+    attn_ref = attention_reference(q, run["kp"], run["vp"], kc, vc)
 
     # a fresh canvas
     dg.dg_canvas_init(run["ids"], run["mask"], run["ctrl"], vocab)
@@ -93,30 +93,43 @@ def test_decode_block(run, block):
     assert not run["mask"].cpu().numpy().any()
     assert ctrl_matches(dg, run["ctrl"], c)
 
+    # this canvas's step graph: attention over the prefix of p rows, then the sampler
+    graph = dg.StepGraph(q_d, kp_d, vp_d, kc_d, vc_d, run["attn"], run["logits"], run["emb"], run["ids"],
+                         run["mask"], run["z"], run["kappa"], run["nu"], run["ctrl"], workspace=run["ws"])
     accepted = []
-    while True:
-        dg.dg_synth_logits(run["logits"], run["ids"], run["mask"], run["ctrl"], run["table"])
-        dg.dg_sampler_step(run["logits"], run["emb"], run["ids"], run["mask"], run["z"], run["kappa"],
-                           run["nu"], run["ctrl"], workspace=run["ws"])
-        torch.cuda.synchronize()
-        logits = synth.synth_logits(ids, mask, c.gstep, c.seed, run["table_np"], vocab)
-        assert np.array_equal(run["logits"].cpu().numpy(), logits), "synthetic logits differ"
-        ref = S.sampler_step(logits, run["e64"], ids, mask, c, z_rows=ROWS)
-        g_ids, g_mask = run["ids"].cpu().numpy(), run["mask"].cpu().numpy()
-        exempt = check_step(ids, mask, g_ids, g_mask, run["kappa"].cpu().numpy(), ref, c.tau)
-        check_z(run["z"].cpu().numpy()[ROWS], ref["z"])
-        assert int(run["nu"].cpu()[0]) == int(n - g_mask.sum())
-        c = ref["ctrl"]
-        assert ctrl_matches(dg, run["ctrl"], c)
-        accepted.append(int(g_mask.sum() - mask.sum()))
-        # both sides continue from the device's state (identical unless a decision
-        # fell inside the comparison band)
-        ids, mask = g_ids.astype(np.int64), g_mask
-        if exempt:
-            log(f"decode block {block}: step {len(accepted)}: {exempt} in-band decisions")
-        if int(run["nu"].cpu()[0]) == 0:
-            break
-        assert len(accepted) < CFG["s_max"], "canvas did not finish within the step budget"
+    attn0 = None
+    try:
+        while True:
+            dg.dg_synth_logits(run["logits"], run["ids"], run["mask"], run["ctrl"], run["table"])
+            torch.cuda.synchronize()
+            logits = synth.synth_logits(ids, mask, c.gstep, c.seed, run["table_np"], vocab)
+            assert np.array_equal(run["logits"].cpu().numpy(), logits), "synthetic logits differ"
+            graph.launch()
+            torch.cuda.synchronize()
+            attn = run["attn"].cpu().numpy()
+            if attn0 is None:
+                check_attention(attn, *attn_ref, f"decode block {block} (prefix {p}) attention")
+                attn0 = attn
+            else:
+                assert np.array_equal(attn, attn0), "attention differs between replays"
+            ref = S.sampler_step(logits, run["e64"], ids, mask, c, z_rows=ROWS)
+            g_ids, g_mask = run["ids"].cpu().numpy(), run["mask"].cpu().numpy()
+            exempt = check_step(ids, mask, g_ids, g_mask, run["kappa"].cpu().numpy(), ref, c.tau)
+            check_z(run["z"].cpu().numpy()[ROWS], ref["z"])
+            assert int(run["nu"].cpu()[0]) == int(n - g_mask.sum())
+            c = ref["ctrl"]
+            assert ctrl_matches(dg, run["ctrl"], c)
+            accepted.append(int(g_mask.sum() - mask.sum()))
+            # both sides continue from the device's state (identical unless a decision
+            # fell inside the comparison band)
+            ids, mask = g_ids.astype(np.int64), g_mask
+            if exempt:
+                log(f"decode block {block}: step {len(accepted)}: {exempt} in-band decisions")
+            if int(run["nu"].cpu()[0]) == 0:
+                break
+            assert len(accepted) < CFG["s_max"], "canvas did not finish within the step budget"
+    finally:
+        graph.close()
     run["ctrl_ref"] = c
     log(f"decode block {block}: {len(accepted)} steps, accepted per step {accepted}")
     # about 20 tokens per forward pass, as the generator is tuned for

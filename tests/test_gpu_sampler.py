@@ -75,7 +75,7 @@ def test_workload2_eight_steps():
 
 
 def test_workload3_full_vocab():
-    """262144 x 3072 at full size: every decision, z on sampled rows."""
+    """262144 x 3072 at full size: every decision, and z on all 256 rows."""
     torch, dg = require_gpu()
     log("sampler workload 3: generating inputs")
     emb = workloads.embedding(3)
@@ -83,13 +83,13 @@ def test_workload3_full_vocab():
     ids, mask = workloads.initial_canvas(3)
     ctrl = S.Ctrl(seed=3, tau=0.9, flags=S.AUTO_ADVANCE)
     g = GpuSampler(torch, dg, emb, ids, mask, ctrl)
-    rows = np.array([0, 1, 37, 100, 128, 200, 254, 255])
     log("sampler workload 3: gpu step")
     gids, gmask, gk, gz, gnu = g.step(logits)
-    log("sampler workload 3: oracle")
-    ref = S.sampler_step(logits, emb, ids, mask, ctrl, z_rows=rows)
+    log("sampler workload 3: oracle (z for all 256 rows)")
+    ref = S.sampler_step(logits, emb, ids, mask, ctrl, z_rows="all")
     assert check_step(ids, mask, gids, gmask, gk, ref, 0.9) == 0
-    check_z(gz[rows], ref["z"])
+    worst, total = check_z(gz, ref["z"])
+    log(f"workload 3: z relative L2 worst row {worst:.3e}, whole tensor {total:.3e}")
     assert gnu == ref["n_uncommitted"]
     log(f"workload 3: {int(gmask.sum())} committed of 256")
 

@@ -4,9 +4,8 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_util import ATTN_MAX_ABS, check_step, check_z, log, require_gpu, to_dev
+from gpu_util import attention_reference, check_attention, check_step, check_z, log, require_gpu, to_dev
 from oracle import sampler as S
-from oracle.attention import canvas_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -20,7 +19,8 @@ def inputs():
     emb = workloads.embedding(3)
     logits = workloads.step_logits(4, 0)
     ids, mask = workloads.initial_canvas(4)
-    return dict(q=q, kp=kp, vp=vp, kc=kc, vc=vc, emb=emb, logits=logits, ids=ids, mask=mask)
+    attn_ref = attention_reference(q, kp, vp, kc, vc)
+    return dict(q=q, kp=kp, vp=vp, kc=kc, vc=vc, emb=emb, logits=logits, ids=ids, mask=mask, attn_ref=attn_ref)
 
 
 def device_state(torch, dg, x, ctrl):
@@ -53,7 +53,6 @@ def snapshot(torch, st):
 def test_eager_and_graph_steps(inputs, flags):
     torch, dg = require_gpu()
     ctrl = S.Ctrl(seed=4, tau=0.9, flags=flags, t_start=0.8, t_end=0.4)
-    ref_attn = canvas_attention(inputs["q"], inputs["kp"], inputs["vp"], inputs["kc"], inputs["vc"])
     e64 = inputs["emb"].astype(np.float64)
 
     # eager: three steps on the same logits
@@ -70,8 +69,7 @@ def test_eager_and_graph_steps(inputs, flags):
         log(f"step: oracle step {k}")
         ref = S.sampler_step(inputs["logits"], e64, ids, mask, c, z_rows=ROWS)
         got = eager[k]
-        err = np.abs(got["attn"] - ref_attn).max()
-        assert err <= ATTN_MAX_ABS, err
+        check_attention(got["attn"], *inputs["attn_ref"], f"step {k} attention")
         assert check_step(ids, mask, got["ids"], got["mask"], got["kappa"], ref, 0.9) <= 2
         # both sides continue from the device's state (identical unless a decision fell in the band)
         ref = dict(ref, ids=got["ids"].astype(np.int64), committed=got["mask"])
@@ -127,8 +125,7 @@ def test_entropy_bounded_step_eager_and_graph(inputs):
     for _ in range(3):
         dg.dg_denoise_step_eb(*eb_args(st), budget=BUDGET, stop_entropy=STOP)
         eager.append(snap(st))
-    ref_attn = canvas_attention(inputs["q"], inputs["kp"], inputs["vp"], inputs["kc"], inputs["vc"])
-    assert np.abs(eager[0]["attn"] - ref_attn).max() <= ATTN_MAX_ABS
+    check_attention(eager[0]["attn"], *inputs["attn_ref"], "eb step attention")
     log("eb step: oracle step 0")
     ref = EB.eb_step(inputs["logits"], inputs["emb"].astype(np.float64), inputs["ids"], ctrl, None, BUDGET, STOP,
                      z_rows=ROWS)

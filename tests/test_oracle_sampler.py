@@ -92,6 +92,64 @@ def test_gumbel_candidates_sample_p_t():
     assert pval > 1e-4
 
 
+@pytest.mark.parametrize("temp", [1.0, 0.8, 0.4])
+@pytest.mark.parametrize("a,b", [(1.7, -0.4), (-3.0, 2.25), (0.5, 0.5), (12.0, -7.5)])
+def test_greedy_gap_two_logit_closed_form(temp, a, b):
+    """Greedy mode: the top-2 gap is in probability units of p_T.  For two logits
+    p_T = (sigma((a-b)/T), sigma((b-a)/T)), so the gap is |2 sigma((a-b)/T) - 1|
+    = |tanh((a - b) / (2T))|, with T the float32 temperature."""
+    l = np.array([[a, b]], np.float32)
+    ctrl = S.Ctrl(t_start=temp, t_end=temp)
+    t32 = S.temperature(ctrl)
+    cand, gap = S.candidates(l, ctrl, t32)
+    a32, b32 = float(l[0, 0]), float(l[0, 1])
+    want = abs(np.tanh((a32 - b32) / (2.0 * float(t32))))
+    np.testing.assert_allclose(gap[0], want, rtol=1e-12, atol=1e-15)
+    assert cand[0] == (0 if a32 >= b32 else 1)
+
+
+def test_greedy_gap_three_logit_closed_form():
+    """Three logits a > b > c at temperature T: gap = (1 - e^{(b-a)/T}) /
+    (1 + e^{(b-a)/T} + e^{(c-a)/T}), which no two-logit case distinguishes
+    from a gap taken at T = 1 or over the raw logits."""
+    a, b, c, temp = 2.0, 1.25, -0.5, 0.4
+    l = np.array([[c, a, b]], np.float32)
+    ctrl = S.Ctrl(t_start=temp, t_end=temp)
+    t = float(S.temperature(ctrl))
+    _, gap = S.candidates(l, ctrl, S.temperature(ctrl))
+    eb, ec = np.exp((b - a) / t), np.exp((c - a) / t)
+    np.testing.assert_allclose(gap[0], (1 - eb) / (1 + eb + ec), rtol=1e-12)
+
+
+@pytest.mark.parametrize("temp", [1.0, 0.5])
+def test_gumbel_gap_is_in_score_units(temp):
+    """Gumbel mode: the gap is the difference of the two best perturbed scores
+    l_j / T + g_j, with g_j = -ln(-ln u_j) from the Philox word of id j (stream
+    0, counter (j >> 2, position, gstep, 0), word j & 3) and u_j = (2 (h >> 9) + 1)
+    2^-24.  The scores are computed here in float64 from those words; the oracle
+    takes them in float32, so they agree to float32 rounding."""
+    seed, gstep, pos = 77, 5, 3
+    l = np.full((pos + 1, 5), -1.0, np.float32)
+    l[pos] = np.array([10.0, 0.0, 0.25, -2.0, 9.5], np.float32)
+    ctrl = S.Ctrl(seed=seed, gstep=gstep, flags=S.GUMBEL, t_start=temp, t_end=temp)
+    t32 = S.temperature(ctrl)
+    cand, gap = S.candidates(l, ctrl, t32)
+    k0, k1 = seed & 0xFFFFFFFF, seed >> 32
+    scores = []
+    for j in range(5):
+        words = philox.philox4x32_10(j >> 2, pos, gstep, 0, k0, k1)
+        h = int(words[j & 3])
+        u = (2 * (h >> 9) + 1) * 2.0 ** -24
+        g = -np.log(-np.log(u))
+        scores.append(float(l[pos, j]) / float(t32) + g)
+    order = np.argsort(scores)[::-1]
+    assert cand[pos] == order[0]
+    np.testing.assert_allclose(gap[pos], scores[order[0]] - scores[order[1]], rtol=0, atol=1e-5)
+    if temp == 0.5:
+        # 10 / 0.5 against at most 9.5 / 0.5: a gap of this size exists only in score units
+        assert gap[pos] > 1.0 or scores[order[1]] > 15
+
+
 def test_greedy_ties_go_to_smallest_id():
     l = np.zeros((3, 10), np.float32)
     l[0, [4, 7]] = 5
