@@ -12,7 +12,7 @@ from ._lib import (DG_ATTN_CAUSAL, DG_AUTO_ADVANCE, DG_BF16, DG_COMMIT_ONLY, DG_
                    DG_T_SCHEDULE, DgCtrl, DgError, check, load)
 
 __all__ = [
-    "dg_canvas_attention", "dg_canvas_attention_batched", "dg_attention_batched_workspace_bytes",
+    "dg_canvas_attention", "dg_canvas_attention_noalloc", "dg_static_scratch_bytes", "dg_canvas_attention_batched", "dg_attention_batched_workspace_bytes",
     "dg_canvas_attention_fp8", "dg_sampler_step", "dg_sampler_step_eb", "read_eb_status",
     "dg_sampler_step_batched", "dg_sampler_step_eb_batched", "dg_sampler_workspace_bytes_batched",
     "dg_sampler_step_topk", "dg_sampler_step_eb_topk", "dg_sampler_workspace_bytes_topk",
@@ -188,6 +188,29 @@ def dg_canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, out=None, sca
                                         _ptr(v_canvas), _ptr(out), n, n_prefix, hq, hkv, d,
                                         _qkv_dtype(q), float(scale), DG_ATTN_CAUSAL if causal else 0,
                                         _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def dg_static_scratch_bytes():
+    return load().dg_static_scratch_bytes()
+
+
+def dg_canvas_attention_noalloc(q, k_prefix, v_prefix, k_canvas, v_canvas, out, scale=0.0, stream=None,
+                                causal=False):
+    """dg_canvas_attention without a workspace: the library's static device
+    scratch serves as workspace.  out [N, Hq, D] float32 is required (the call
+    allocates nothing); calls that overlap in time on one GPU race."""
+    torch = _torch()
+    dt = (torch.bfloat16, torch.float32)
+    _need(q, "q", dt); _need(k_canvas, "k_canvas", dt); _need(v_canvas, "v_canvas", dt)
+    _need(out, "out", (torch.float32,))
+    if k_prefix is not None and k_prefix.shape[0]:
+        _need(k_prefix, "k_prefix", dt); _need(v_prefix, "v_prefix", dt)
+    n, hq, hkv, d, n_prefix = _check_attention_tensors(q, k_prefix, v_prefix, k_canvas, v_canvas, out)
+    check(load().dg_canvas_attention_noalloc(_ptr(q), _ptr(k_prefix) if n_prefix else None,
+                                             _ptr(v_prefix) if n_prefix else None, _ptr(k_canvas),
+                                             _ptr(v_canvas), _ptr(out), n, n_prefix, hq, hkv, d, _qkv_dtype(q),
+                                             float(scale), DG_ATTN_CAUSAL if causal else 0, _stream(stream)))
     return out
 
 

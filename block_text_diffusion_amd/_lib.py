@@ -67,6 +67,9 @@ SIGNATURES = {
     "dg_canvas_attention": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "dg_canvas_attention_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
                                     ctypes.c_uint32, _vp, _sz, _vp]),
+    "dg_static_scratch_bytes": (_sz, []),
+    "dg_canvas_attention_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
+                                         ctypes.c_uint32, _vp]),
     "dg_attention_batched_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "dg_canvas_attention_batched": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                          _f, _vp, _sz, _vp]),

@@ -6,11 +6,21 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "dg.h"
 #include "dg_internal.hpp"
+
+// Workspace of dg_canvas_attention_noalloc, for callers that cannot allocate
+// device memory: a file-scope device array of fixed size.  Every GPU the
+// library runs on holds its own copy until the process ends.  Host code never
+// passes the array's name to a kernel or a copy (in host code it is only a
+// host-side stand-in); it uses the device address looked up per device with
+// hipGetSymbolAddress.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -103,6 +113,29 @@ int check_sampler_plan(const dg::SamplerPlan& p, const char* who) {
     return fail(DG_EUNSUPPORTED, "%s: vocab %d needs %d vocabulary splits, more than %d (vocab above 4194304)", who,
                 p.vocab, p.n_splits, dg::kMaxSamplerSplits);
   return DG_OK;
+}
+
+// The device address of the current device's scratch array, looked up on the
+// first call on that device, with that device current, and kept per device.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 int check_topk(int k, const dg::TopkPlan& p, void* ws, size_t ws_bytes, const char* who) {
@@ -210,6 +243,29 @@ int dg_canvas_attention_ex(const void* q, const void* kp, const void* vp, const 
   hipError_t e = dg::launch_attention(p, q, kp, vp, kc, vc, out, dtype, scale, ws, stream,
                                       (attn_flags & DG_ATTN_CAUSAL) != 0);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return DG_OK;
+}
+
+size_t dg_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+int dg_canvas_attention_noalloc(const void* q, const void* kp, const void* vp, const void* kc, const void* vc,
+                                float* out, int n, int np, int hq, int hkv, int d, int dtype, float scale,
+                                uint32_t attn_flags, hipStream_t stream) {
+  if (attn_flags & ~(uint32_t)DG_ATTN_CAUSAL) return fail(DG_EINVAL, "attention_noalloc: unknown flag bits");
+  if (dtype == DG_FP8_E4M3)
+    return fail(DG_EINVAL, "attention_noalloc: FP8 inputs take dg_canvas_attention_fp8 (scales)");
+  int st = check_attention(q, kp, vp, kc, vc, out, n, np, hq, hkv, d, dtype);
+  if (st != DG_OK) return st;
+  const dg::AttnPlan p = dg::attn_plan(n, np, hq, hkv, d);
+  if (p.total > kStaticScratchBytes)
+    return fail(DG_EUNSUPPORTED, "attention_noalloc: these sizes need %zu workspace bytes, more than the %zu-byte "
+                "static scratch (use dg_canvas_attention with a workspace)", p.total, kStaticScratchBytes);
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e, "attention_noalloc: scratch address");
+  if (!(scale > 0.f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)d);
+  e = dg::launch_attention(p, q, kp, vp, kc, vc, out, dtype, scale, ws, stream, (attn_flags & DG_ATTN_CAUSAL) != 0);
+  if (e != hipSuccess) return hip_fail(e, "attention_noalloc launch");
   return DG_OK;
 }
 

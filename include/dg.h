@@ -133,6 +133,24 @@ int dg_canvas_attention_ex(const void* q, const void* k_prefix, const void* v_pr
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * dg_canvas_attention_ex without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a static device array
+ * of dg_static_scratch_bytes() bytes (64 MiB) inside the library; each GPU
+ * holds its own copy from the first call on it until the process ends.  Inputs,
+ * output, flags, results and errors as dg_canvas_attention_ex; sizes whose
+ * workspace (dg_attention_workspace_bytes) exceeds the static scratch return
+ * DG_EUNSUPPORTED before any HIP call.  The call allocates nothing.  Every
+ * call on one GPU shares that GPU's scratch: calls that overlap in time on one
+ * GPU (several streams or threads) race and must be serialised by the caller.
+ */
+size_t dg_static_scratch_bytes(void);
+int dg_canvas_attention_noalloc(const void* q, const void* k_prefix, const void* v_prefix,
+                                const void* k_canvas, const void* v_canvas, float* out,
+                                int n_canvas, int n_prefix, int hq, int hkv, int head_dim,
+                                int dtype, float scale, uint32_t attn_flags, hipStream_t stream);
+
+/*
  * A batch of sequences in one launch, each with its own prefix length and its
  * own causal flag, so denoising passes and KV-update passes can share a batch
  * (Technical Report part 4/6, paragraph "Eliminating CPU-GPU synchronization":

@@ -315,3 +315,25 @@ def test_binding_cross_checks_attention_tensors():
     assert dg._check_attention_tensors(qb, kpb, kpb, kcb, kcb, None, batched=True) == (16, 8, 4, 64, 8)
     with pytest.raises(ValueError, match="canvas K/V"):
         dg._check_attention_tensors(qb, kpb, kpb, kcb[:1], kcb[:1], None, batched=True)
+
+
+def test_noalloc_attention_arguments(lib):
+    """The no-allocation attention variant: the static scratch size, the same
+    argument checks as dg_canvas_attention_ex, and sizes beyond the scratch
+    refused before any HIP call."""
+    from block_text_diffusion_amd._lib import DG_EINVAL, DG_EUNSUPPORTED, DG_F32, DG_FP8_E4M3
+    assert lib.dg_static_scratch_bytes() == 64 << 20
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert lib.dg_canvas_attention_noalloc(None, *a[1:], 16, 8, 8, 4, 64, 1, 0.0, 0, None) == DG_EINVAL
+    assert lib.dg_canvas_attention_noalloc(*a, 16, 8, 8, 4, 96, 1, 0.0, 0, None) == DG_EUNSUPPORTED
+    assert lib.dg_canvas_attention_noalloc(*a, 16, 8, 8, 4, 64, 1, 0.0, 2, None) == DG_EINVAL   # unknown flag
+    assert lib.dg_canvas_attention_noalloc(*a, 16, 8, 8, 4, 64, DG_FP8_E4M3, 0.0, 0, None) == DG_EINVAL
+    assert lib.dg_canvas_attention_noalloc(MIS, *a[1:], 16, 8, 8, 4, 64, 1, 0.0, 0, None) == DG_EINVAL
+    # float32 K/V are copied to bf16 in the workspace: a 500000-row prefix needs
+    # far more than the 64 MiB scratch
+    need = lib.dg_attention_workspace_bytes(256, 500000, 16, 8, 128)
+    assert need > 64 << 20
+    assert lib.dg_canvas_attention_noalloc(*a, 256, 500000, 16, 8, 128, DG_F32, 0.0, 0, None) == DG_EUNSUPPORTED
+    assert b"static scratch" in lib.dg_last_error()
+    # the long-context shape fits
+    assert lib.dg_attention_workspace_bytes(256, 4096, 16, 8, 128) <= 64 << 20
