@@ -34,6 +34,7 @@ COUNTERS = os.path.join(ROOT, "profiles", "long_context_step_counters.json")
 KERNEL_SOURCES = ["block_text_diffusion_amd/csrc/sampler.hip", "block_text_diffusion_amd/csrc/dg_common.hpp",
                   "block_text_diffusion_amd/csrc/attention.hip"]
 BF16_PEAK_TFLOPS = 2516.6
+FP8_PEAK_TFLOPS = 5000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
 SAMPLER_KERNELS = ("samp_stats", "samp_gemm", "samp_combine", "samp_finalize")
 
@@ -570,11 +571,18 @@ def fp8_attention_timing(torch, dg, workloads, n, p, hq, hkv, hd, steps, n_sets=
     dg.dg_profile_enable(False)
     flops = 4.0 * n * (p + n) * hd * hq
     kv_bytes = 2.0 * (p + n) * hkv * hd          # K and V, one byte per element
-    return {"us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 1),
-            "frac_bf16_peak": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+    tflops = flops / (us * 1e-6) / 1e12
+    # half the flops (Q.K^T) run on the FP8 matrix cores, half (P.V) on bf16:
+    # the floor is (F/2)/fp8 peak + (F/2)/bf16 peak
+    mixed_peak = 1.0 / (0.5 / FP8_PEAK_TFLOPS + 0.5 / BF16_PEAK_TFLOPS)
+    return {"us": round(us, 2), "tflops": round(tflops, 1),
+            "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+            "frac_mixed_peak": round(tflops / mixed_peak, 4), "mixed_peak_tflops": round(mixed_peak, 1),
+            "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
             "kv_mb": round(kv_bytes / 1e6, 2),
             "per_kernel_us": {k: round(1e3 * t / c, 2) for k, (t, c) in prof.items()},
-            "note": "E4M3 Q/K/V staged exactly as bf16; bf16 MFMA, fp32 softmax"}
+            "note": "E4M3 Q/K/V; Q.K^T on the FP8 matrix cores (v_mfma_f32_32x32x64_f8f6f4), V staged exactly "
+                    "as bf16 and P.V on bf16; fp32 softmax"}
 
 
 def topk_sampler_timing(torch, dg, T, n, p, hq, hkv, hd, vocab, dm, steps, ks=(64, 256), batches=(1, 8)):

@@ -16,7 +16,8 @@ __all__ = [
     "dg_canvas_attention_fp8", "dg_sampler_step", "dg_sampler_step_eb", "read_eb_status",
     "dg_sampler_step_batched", "dg_sampler_step_eb_batched", "dg_sampler_workspace_bytes_batched",
     "dg_sampler_step_topk", "dg_sampler_step_eb_topk", "dg_sampler_workspace_bytes_topk",
-    "stack_ctrl", "dg_embedding_pack", "dg_embedding_packed_bytes", "dg_denoise_step", "dg_denoise_step_eb", "StepGraph", "StepGraphEB", "dg_canvas_init",
+    "stack_ctrl", "dg_embedding_pack", "dg_embedding_packed_bytes", "dg_denoise_step", "dg_denoise_step_eb", "dg_denoise_step_fp8", "StepGraph", "StepGraphEB",
+    "StepGraphFP8", "dg_canvas_init",
     "dg_kv_append", "dg_synth_logits", "dg_philox_fill", "dg_attention_workspace_bytes",
     "dg_sampler_workspace_bytes", "dg_denoise_workspace_bytes", "dg_profile_enable",
     "dg_profile_read", "dg_probe_mfma_bf16", "dg_probe_copy", "make_ctrl", "read_ctrl", "write_ctrl", "DG_GUMBEL", "DG_COMMIT_ONLY",
@@ -452,6 +453,38 @@ def dg_denoise_step_eb(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logi
     check(load().dg_denoise_step_eb(*args, _stream(stream)))
 
 
+def _denoise_fp8_args(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, scale, q_scale, k_scale, v_scale,
+                      logits, emb, canvas_ids, committed, selfcond, confidence, n_uncommitted, ctrl, ws):
+    torch = _torch()
+    dt = (torch.uint8, torch.float8_e4m3fn)
+    _need(q, "q", dt); _need(k_canvas, "k_canvas", dt); _need(v_canvas, "v_canvas", dt)
+    if k_prefix is not None and k_prefix.shape[0]:
+        _need(k_prefix, "k_prefix", dt); _need(v_prefix, "v_prefix", dt)
+    n, hq, hkv, d, n_prefix = _check_attention_tensors(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out)
+    vocab = logits.shape[1]
+    dm = selfcond.shape[1]
+    if emb.numel() < dg_embedding_packed_bytes(vocab, dm):
+        raise ValueError("emb_packed is smaller than dg_embedding_packed_bytes(vocab, d_model)")
+    return (_ptr(q), _ptr(k_prefix) if n_prefix else None, _ptr(v_prefix) if n_prefix else None,
+            _ptr(k_canvas), _ptr(v_canvas), _ptr(attn_out), n_prefix, hq, hkv, d, float(scale), float(q_scale),
+            float(k_scale), float(v_scale), _ptr(logits), _ptr(emb), _ptr(canvas_ids), _ptr(committed),
+            _ptr(selfcond), _ptr(confidence), _ptr(n_uncommitted), _ptr(ctrl), n, vocab, dm, _ptr(ws), ws.numel())
+
+
+def dg_denoise_step_fp8(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits, emb_packed, canvas_ids,
+                        committed, selfcond, confidence, n_uncommitted, ctrl, q_scale=1.0, k_scale=1.0,
+                        v_scale=1.0, scale=0.0, workspace=None, stream=None):
+    """FP8 (E4M3) attention inputs with per-tensor scales, then the sampler step."""
+    n, hq, d = q.shape
+    nbytes = dg_denoise_workspace_bytes(n, 0 if k_prefix is None else k_prefix.shape[0], hq,
+                                        k_canvas.shape[1], d, logits.shape[1], selfcond.shape[1])
+    ws = _workspace(nbytes, q.device, workspace)
+    args = _denoise_fp8_args(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, scale, q_scale, k_scale, v_scale,
+                             logits, emb_packed, canvas_ids, committed, selfcond, confidence, n_uncommitted, ctrl,
+                             ws)
+    check(load().dg_denoise_step_fp8(*args, _stream(stream)))
+
+
 class StepGraph:
     """dg_step_graph_create / _launch / _destroy: one captured denoising step.
 
@@ -507,6 +540,27 @@ class StepGraphEB(StepGraph):
                                 budget, stop_entropy, self.ws)
         handle = ctypes.c_void_p()
         check(load().dg_step_graph_create_eb(*args, ctypes.byref(handle)))
+        self.handle = handle
+
+
+class StepGraphFP8(StepGraph):
+    """dg_step_graph_create_fp8: one captured step with FP8 attention inputs."""
+
+    def __init__(self, q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits, emb_packed, canvas_ids,
+                 committed, selfcond, confidence, n_uncommitted, ctrl, q_scale=1.0, k_scale=1.0, v_scale=1.0,
+                 scale=0.0, workspace=None):
+        n, hq, d = q.shape
+        nbytes = dg_denoise_workspace_bytes(n, 0 if k_prefix is None else k_prefix.shape[0], hq,
+                                            k_canvas.shape[1], d, logits.shape[1], selfcond.shape[1])
+        self.handle = None
+        self.ws = _workspace(nbytes, q.device, workspace)
+        self._keep = (q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, logits, emb_packed, canvas_ids,
+                      committed, selfcond, confidence, n_uncommitted, ctrl)
+        args = _denoise_fp8_args(q, k_prefix, v_prefix, k_canvas, v_canvas, attn_out, scale, q_scale, k_scale,
+                                 v_scale, logits, emb_packed, canvas_ids, committed, selfcond, confidence,
+                                 n_uncommitted, ctrl, self.ws)
+        handle = ctypes.c_void_p()
+        check(load().dg_step_graph_create_fp8(*args, ctypes.byref(handle)))
         self.handle = handle
 
 

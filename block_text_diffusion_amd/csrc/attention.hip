@@ -20,6 +20,11 @@
 // O^T = V^T P^T straight from the score registers; the V^T operand comes from
 // ds_read_b64_tr_b16, which transposes 16-bit elements across 16 lanes, so V
 // needs no transposition pass.  Online softmax in fp32, base 2.
+//
+// FP8 (E4M3) inputs: K stays FP8 in LDS and the scores run on the FP8 matrix
+// cores (v_mfma_f32_32x32x64_f8f6f4, four times the depth of a bf16 step at
+// twice the rate); V is converted exactly to bf16 when staged and P.V stays on
+// bf16 (P rounded to bf16, as for bf16 inputs).
 #include <type_traits>
 
 #include "dg_common.hpp"
@@ -40,6 +45,27 @@ struct AGeom {
   static constexpr int kStageBytes = 2 * kBlockBytes;           // K then V
   static_assert(kCpr * kAKeys % kAThreads == 0, "block does not split evenly over the threads");
 };
+
+// LDS stage of one block: K (bf16 rows, or raw FP8 rows of D bytes when the
+// scores run on the FP8 matrix cores), then V (bf16 rows).
+template <int D, bool kF8>
+struct AStage {
+  static constexpr int kKRowBytes = kF8 ? D : 2 * D;
+  static constexpr int kKBytes = kAKeys * kKRowBytes;
+  static constexpr int kVOffset = kKBytes;
+  static constexpr int kBytes = kKBytes + AGeom<D>::kBlockBytes;
+};
+
+// FP8 K rows (D bytes): 16-byte chunk c of key k sits at slot c ^ f(k).  A
+// 16-lane pass of a score-fragment read takes one chunk column over 16
+// consecutive keys; with rows of 128 (64) bytes, key bits 0 (0-1) pick the half
+// (quarter) of a 256-byte line and f supplies the other bits, so the 16 pieces
+// land on 16 different slots.
+template <int D>
+__device__ __forceinline__ int k8_slot(int key, int c) {
+  if constexpr (D == 128) return c ^ ((key >> 1) & 7);
+  else return c ^ ((key >> 2) & 3);
+}
 
 // K rows: chunk c of key k sits at slot c ^ f(k); a wave's 16-byte reads of one
 // chunk column over 32 consecutive keys spread over all banks.
@@ -84,6 +110,7 @@ __device__ __forceinline__ u32x4 load8(const uint8_t* p) {
   return fp8x8_to_bf16(w[0], w[1]);
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
@@ -129,20 +156,22 @@ __device__ __forceinline__ void kv_fetch(KvRegs<D, kF8>& r, __amdgpu_buffer_rsrc
 template <int D, bool kF8>
 __device__ __forceinline__ void kv_store(const KvRegs<D, kF8>& r, uint8_t* stage, int t) {
   using G = AGeom<D>;
+  using S = AStage<D, kF8>;
 #pragma unroll
   for (int i = 0; i < KvRegs<D, kF8>::kPer; ++i) {
     const int idx = t + kAThreads * i;
-    const int key = idx / G::kCpr, c = idx % G::kCpr;
-    u32x4 kw, vw;
+    const int key = idx / G::kCpr, c = idx % G::kCpr;   // c: 8-element chunk of the row
+    u32x4 vw;
     if constexpr (kF8) {
-      kw = fp8x8_to_bf16(r.k[i][0], r.k[i][1]);
+      // K stays FP8 for the FP8 matrix cores: 8 bytes into half of a 16-byte slot
+      *reinterpret_cast<u32x2*>(stage + key * S::kKRowBytes + (k8_slot<D>(key, c >> 1) << 4) + 8 * (c & 1)) =
+          r.k[i];
       vw = fp8x8_to_bf16(r.v[i][0], r.v[i][1]);
     } else {
-      kw = r.k[i];
+      *reinterpret_cast<u32x4*>(stage + key * G::kRowBytes + (k_slot<D>(key, c) << 4)) = r.k[i];
       vw = r.v[i];
     }
-    *reinterpret_cast<u32x4*>(stage + key * G::kRowBytes + (k_slot<D>(key, c) << 4)) = kw;
-    *reinterpret_cast<u32x4*>(stage + G::kBlockBytes + key * G::kRowBytes + (v_slot<D>(key, c) << 4)) = vw;
+    *reinterpret_cast<u32x4*>(stage + S::kVOffset + key * G::kRowBytes + (v_slot<D>(key, c) << 4)) = vw;
   }
 }
 
@@ -158,9 +187,13 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
     _Float16* __restrict__ opart, float* __restrict__ ml, const AttnSeqs seqs, int n, int hq, int hkv,
     int blocks_per_chunk, int n_chunks, float scale_log2e, float out_scale) {
   using G = AGeom<D>;
-  constexpr int KS = D / 16;   // 16-wide k steps over the head dimension
+  using S = AStage<D, kF8>;
+  constexpr int KS = D / 16;   // 16-wide k steps over the head dimension (bf16 scores)
+  constexpr int KS8 = D / 64;  // 64-wide k steps (FP8 scores)
   constexpr int DB = D / 32;   // 32-row blocks of O^T
+  // two stages, and the key-half merge of the epilogue (64 KB at D = 128)
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * G::kStageBytes];
+  static_assert(2 * S::kBytes <= 2 * G::kStageBytes, "stages exceed the LDS array");
   __shared__ float lds_ml[4][64][2];
 
   // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that the
@@ -219,12 +252,30 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
   const bool r_ok = r < rows;
   const int qn = r_ok ? r / group : 0;
   const int qh = kvh * group + (r_ok ? r % group : 0);
+  // bf16 scores: lane half h holds elements 16 ks + 8 h .. +7 of its query row
+  // in k step ks.  FP8 scores: 32 bytes, elements 64 ks + 32 h .. +31 (the FP8
+  // matrix-core operands pair the same register bytes of the K and Q lanes, so
+  // the K fragments below take the same elements of their key rows).
   bf16x8 qf[KS];
+  i32x8 qf8[KS8];
+  const size_t qrow = (((size_t)seq * n + qn) * hq + qh) * D;
+  if constexpr (kF8) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 w = (u32x4){0u, 0u, 0u, 0u};
-    if (r_ok) w = load8(q + (((size_t)seq * n + qn) * hq + qh) * D + 16 * ks + 8 * half);
-    qf[ks] = __builtin_bit_cast(bf16x8, w);
+    for (int ks = 0; ks < KS8; ++ks) {
+      u32x4 lo = (u32x4){0u, 0u, 0u, 0u}, hi = lo;
+      if (r_ok) {
+        lo = *reinterpret_cast<const u32x4*>(q + qrow + 64 * ks + 32 * half);
+        hi = *reinterpret_cast<const u32x4*>(q + qrow + 64 * ks + 32 * half + 16);
+      }
+      qf8[ks] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 w = (u32x4){0u, 0u, 0u, 0u};
+      if (r_ok) w = load8(q + qrow + 16 * ks + 8 * half);
+      qf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
   }
 
   f32x16 acc_o[DB];
@@ -250,7 +301,7 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
 
   // one block: scores, online softmax, O^T update (reads one LDS stage)
   auto step = [&](int b, const uint8_t* ks_lds) {
-    const uint8_t* vs_lds = ks_lds + G::kBlockBytes;
+    const uint8_t* vs_lds = ks_lds + S::kVOffset;
     const int gb = gb0 + b;
     const int seg_left = (gb < blocks_prefix) ? n_prefix - gb * kAKeys
                                               : n - (gb - blocks_prefix) * kAKeys;
@@ -259,14 +310,32 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
     f32x16 sa, sb;
 #pragma unroll
     for (int v = 0; v < 16; ++v) { sa[v] = 0.f; sb[v] = 0.f; }
+    if constexpr (kF8) {
+      // E4M3 x E4M3 on the FP8 matrix cores (products exact in fp32); format
+      // selectors 0 = E4M3 for both operands, no block scales
 #pragma unroll
-    for (int ks = 0; ks < KS; ks += 2) {
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(
-          ks_lds + kkey * G::kRowBytes + (k_slot<D>(kkey, 2 * ks + half) << 4));
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(
-          ks_lds + kkey * G::kRowBytes + (k_slot<D>(kkey, 2 * ks + 2 + half) << 4));
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks + 1], sb, 0, 0, 0);
+      for (int ks = 0; ks < KS8; ++ks) {
+        const int c0 = 4 * ks + 2 * half;   // 16-byte chunks c0, c0 + 1 of the key row
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(ks_lds + kkey * S::kKRowBytes + (k8_slot<D>(kkey, c0) << 4));
+        const u32x4 hi =
+            *reinterpret_cast<const u32x4*>(ks_lds + kkey * S::kKRowBytes + (k8_slot<D>(kkey, c0 + 1) << 4));
+        const i32x8 kf = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        if (ks & 1)
+          sb = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf8[ks], sb, 0, 0, 0, 0, 0, 0);
+        else
+          sa = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf8[ks], sa, 0, 0, 0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ks += 2) {
+        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(
+            ks_lds + kkey * G::kRowBytes + (k_slot<D>(kkey, 2 * ks + half) << 4));
+        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(
+            ks_lds + kkey * G::kRowBytes + (k_slot<D>(kkey, 2 * ks + 2 + half) << 4));
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks + 1], sb, 0, 0, 0);
+      }
     }
     float s[16];
 #pragma unroll
@@ -344,8 +413,8 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
   // other stage, and sends the loads of block b + 3 into the freed registers.
   // rn holds block b + 1: rb for even b, ra for odd b.
   auto iter = [&](int b, KvRegs<D, kF8>& rn) {
-    step(b, lds + (b & 1) * G::kStageBytes);
-    if (b + 1 < nb) kv_store<D, kF8>(rn, lds + ((b + 1) & 1) * G::kStageBytes, t);
+    step(b, lds + (b & 1) * S::kBytes);
+    if (b + 1 < nb) kv_store<D, kF8>(rn, lds + ((b + 1) & 1) * S::kBytes, t);
     if (b + 3 < nb) fetch(rn, b + 3);
     __syncthreads();
   };

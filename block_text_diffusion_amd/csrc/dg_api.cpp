@@ -447,6 +447,34 @@ int dg_denoise_step(const void* q, const void* kp, const void* vp, const void* k
   return DG_OK;
 }
 
+int dg_denoise_step_fp8(const void* q, const void* kp, const void* vp, const void* kc, const void* vc,
+                        float* attn_out, int np, int hq, int hkv, int d, float scale, float q_scale, float k_scale,
+                        float v_scale, const float* logits, const void* emb, int32_t* ids, uint8_t* committed,
+                        float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl, int n, int vocab, int dm, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  int st = check_attention(q, kp, vp, kc, vc, attn_out, n, np, hq, hkv, d, DG_FP8_E4M3);
+  if (st != DG_OK) return st;
+  if (!(q_scale > 0.f) || !std::isfinite(q_scale) || !(k_scale > 0.f) || !std::isfinite(k_scale) ||
+      !(v_scale > 0.f) || !std::isfinite(v_scale))
+    return fail(DG_EINVAL, "denoise_fp8: q_scale, k_scale and v_scale must be finite and > 0");
+  st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, dm);
+  if (st != DG_OK) return st;
+  st = check_sampler_plan(dg::sampler_plan(n, 1, vocab, dm), "denoise_fp8");
+  if (st != DG_OK) return st;
+  const size_t need = dg_denoise_workspace_bytes(n, np, hq, hkv, d, vocab, dm);
+  if (!ws || ws_bytes < need) return fail(DG_EWORKSPACE, "denoise_fp8: workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned16(ws)) return fail(DG_EINVAL, "denoise_fp8: workspace misaligned");
+  if (!(scale > 0.f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)d);
+  const dg::AttnPlan ap = dg::attn_plan(n, np, hq, hkv, d);
+  hipError_t e = dg::launch_attention(ap, q, kp, vp, kc, vc, attn_out, DG_FP8_E4M3, scale * q_scale * k_scale, ws,
+                                      stream, false, v_scale);
+  if (e != hipSuccess) return hip_fail(e, "denoise_fp8 attention launch");
+  const dg::SamplerPlan sp = dg::sampler_plan(n, 1, vocab, dm);
+  e = dg::launch_sampler(sp, logits, emb, ids, committed, z, conf, n_unc, ctrl, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "denoise_fp8 sampler launch");
+  return DG_OK;
+}
+
 int dg_denoise_step_eb(const void* q, const void* kp, const void* vp, const void* kc, const void* vc,
                        float* attn_out, int np, int hq, int hkv, int d, int dtype, float scale,
                        const float* logits, const void* emb, int32_t* ids, uint8_t* accepted, float* z,
@@ -537,6 +565,25 @@ int dg_step_graph_create(const void* q, const void* kp, const void* vp, const vo
   return capture_step([&](hipStream_t cs) {
     return dg_denoise_step(q, kp, vp, kc, vc, attn_out, np, hq, hkv, d, dtype, scale, logits, emb, ids,
                            committed, z, conf, n_unc, ctrl, n, vocab, dm, ws, ws_bytes, cs);
+  }, out);
+}
+
+int dg_step_graph_create_fp8(const void* q, const void* kp, const void* vp, const void* kc, const void* vc,
+                             float* attn_out, int np, int hq, int hkv, int d, float scale, float q_scale,
+                             float k_scale, float v_scale, const float* logits, const void* emb, int32_t* ids,
+                             uint8_t* committed, float* z, float* conf, uint32_t* n_unc, dg_ctrl* ctrl, int n,
+                             int vocab, int dm, void* ws, size_t ws_bytes, dg_step_graph** out) {
+  if (!out) return fail(DG_EINVAL, "graph: null output handle");
+  *out = nullptr;
+  int st = check_attention(q, kp, vp, kc, vc, attn_out, n, np, hq, hkv, d, DG_FP8_E4M3);
+  if (st != DG_OK) return st;
+  st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, dm);
+  if (st != DG_OK) return st;
+  st = check_sampler_plan(dg::sampler_plan(n, 1, vocab, dm), "graph_fp8");
+  if (st != DG_OK) return st;
+  return capture_step([&](hipStream_t cs) {
+    return dg_denoise_step_fp8(q, kp, vp, kc, vc, attn_out, np, hq, hkv, d, scale, q_scale, k_scale, v_scale, logits,
+                               emb, ids, committed, z, conf, n_unc, ctrl, n, vocab, dm, ws, ws_bytes, cs);
   }, out);
 }
 

@@ -194,10 +194,11 @@ int dg_canvas_attention_batched(const void* q, const void* k_prefix, const void*
  * k_canvas and v_canvas are OCP FP8 E4M3 bytes (1 sign, 4 exponent bits with
  * bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN) in the layouts of
  * dg_canvas_attention; the real values are q_scale * q, k_scale * k and
- * v_scale * v.  Every E4M3 value is exactly a bf16 value, so the kernel stages
- * them as bf16 without rounding and computes as the bf16 path does (bf16
- * products, float32 softmax and accumulation); the K/V bytes read are half
- * those of bf16.  The scales must be finite and > 0.  attn_flags, scale,
+ * v_scale * v.  The scores q.k run on the FP8 matrix cores
+ * (v_mfma_f32_32x32x64_f8f6f4: E4M3 products are exact in float32, summed in
+ * float32); V is converted exactly to bf16 when staged and P.V runs on bf16
+ * (P rounded to bf16, float32 softmax and accumulation).  The K/V bytes read
+ * are half those of bf16.  The scales must be finite and > 0.  attn_flags, scale,
  * workspace (dg_attention_workspace_bytes) and errors as dg_canvas_attention_ex.
  */
 int dg_canvas_attention_fp8(const void* q, const void* k_prefix, const void* v_prefix,
@@ -382,6 +383,25 @@ int dg_denoise_step_eb(const void* q, const void* k_prefix, const void* v_prefix
                        int n_canvas, int vocab, int d_model,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * The step with FP8 attention inputs: dg_canvas_attention_fp8 (E4M3 Q/K/V with
+ * per-tensor scales, the scores on the FP8 matrix cores) then dg_sampler_step,
+ * on one stream with one workspace (dg_denoise_workspace_bytes).  The pages'
+ * timings are taken in FP8 (explainer "DiffusionGemma: Google's open diffusion
+ * LLM", section "Throughput flips at about 32 concurrent users", Figure 12
+ * caption).  Attention arguments as dg_canvas_attention_fp8 (bidirectional),
+ * sampler arguments as dg_sampler_step; the scales must be finite and > 0.
+ */
+int dg_denoise_step_fp8(const void* q, const void* k_prefix, const void* v_prefix,
+                        const void* k_canvas, const void* v_canvas, float* attn_out,
+                        int n_prefix, int hq, int hkv, int head_dim, float scale,
+                        float q_scale, float k_scale, float v_scale,
+                        const float* logits, const void* emb_packed, int32_t* canvas_ids,
+                        uint8_t* committed, float* selfcond, float* confidence,
+                        uint32_t* n_uncommitted, dg_ctrl* ctrl,
+                        int n_canvas, int vocab, int d_model,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 typedef struct dg_step_graph dg_step_graph;
 
 /*
@@ -407,6 +427,16 @@ int dg_step_graph_create_eb(const void* q, const void* k_prefix, const void* v_p
                             dg_eb_status* status, dg_ctrl* ctrl, float budget, float stop_entropy,
                             int n_canvas, int vocab, int d_model,
                             void* workspace, size_t workspace_bytes, dg_step_graph** graph);
+/* Capture dg_denoise_step_fp8 (same arguments) into a graph, as above. */
+int dg_step_graph_create_fp8(const void* q, const void* k_prefix, const void* v_prefix,
+                             const void* k_canvas, const void* v_canvas, float* attn_out,
+                             int n_prefix, int hq, int hkv, int head_dim, float scale,
+                             float q_scale, float k_scale, float v_scale,
+                             const float* logits, const void* emb_packed, int32_t* canvas_ids,
+                             uint8_t* committed, float* selfcond, float* confidence,
+                             uint32_t* n_uncommitted, dg_ctrl* ctrl,
+                             int n_canvas, int vocab, int d_model,
+                             void* workspace, size_t workspace_bytes, dg_step_graph** graph);
 int dg_step_graph_launch(dg_step_graph* graph, hipStream_t stream);
 void dg_step_graph_destroy(dg_step_graph* graph);
 

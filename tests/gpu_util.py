@@ -11,19 +11,22 @@ if ROOT not in sys.path:
 
 ATTN_MAX_ABS = 2e-2      # attention outputs, bf16 in / fp32 accumulate (the contract)
 # Secondary attention bound, from the kernel's roundings (bf16 inputs are exact):
-#  - P is rounded to bf16 before the P.V product while the softmax sum uses the
-#    float32 P, so O moves by at most 2^-9 * sum_j w_j |v_jd| (w = softmax weights);
+#  - P is rounded to bf16 (unit roundoff 2^-8) before the P.V product while the
+#    softmax sum uses the float32 P, so O moves by at most 2^-8 * sum_j w_j |v_jd|
+#    (w = softmax weights);
 #  - key-chunk partial outputs scaled by their row's largest |O| and stored as
-#    fp16 move O by at most 2^-12 * sum_j w_j max_d |v_jd|;
-#  - float32 score sums over head_dim and the hardware exp2 move p by ~1e-4
-#    relative at most, inside a factor-2 margin on both terms above.
-# The element bound is 2^-8 * A + 2^-11 * B + 1e-6 with A = sum_j w_j |v_jd| and
-# B = sum_j w_j max_d |v_jd|.  Per output row (one query position and head) the
-# P rounding has an rms of 2^-9 / sqrt(3) = 1.1e-3 relative for incoherent
-# values; the worst of the 4096 rows of the long-context shape reaches 2.3e-3 in
-# a CPU model of that rounding.  The row bound leaves 4x headroom over that,
-# while dropping a single key moves the worst row by 0.16-0.25
-# (tests/test_attention_bound.py).
+#    fp16 (values in [-1, 1], absolute error at most 2^-12) move O by at most
+#    2^-12 * sum_j w_j max_d |v_jd|;
+#  - float32 score sums over head_dim, the exponent reference and the hardware
+#    exp2 move p by about 1e-4 relative at most: 2^-11 of A covers them, and the
+#    fp16 term gets a factor 2.
+# The element bound is (2^-8 + 2^-11) * A + 2^-11 * B + 1e-6 with
+# A = sum_j w_j |v_jd| and B = sum_j w_j max_d |v_jd|.  Per output row (one
+# query position and head) the P rounding has an rms of about
+# 2^-8 / sqrt(6) = 1.6e-3 relative for incoherent values; the worst of the 4096
+# rows of the long-context shape reaches 2.3e-3 in a CPU model of that
+# rounding.  The row bound leaves 4x headroom over that, while dropping a
+# single key moves the worst row by 0.16-0.25 (tests/test_attention_bound.py).
 ATTN_ROW_REL = 1e-2
 Z_REL_L2 = 1e-4          # self-conditioning z, per row and over the tensor
 BAND = 1e-4              # threshold band and top-2 gap below which decisions may differ
@@ -130,7 +133,7 @@ def attention_reference(q, kp, vp, kc, vc, causal=False, scale=None, staged_bf16
     inf_vp = np.broadcast_to(abs_vp.max(axis=-1, keepdims=True), abs_vp.shape) if has_p else None
     inf_vc = np.broadcast_to(abs_vc.max(axis=-1, keepdims=True), abs_vc.shape)
     b = canvas_attention(q, kp, inf_vp, kc, inf_vc, scale=scale, causal=causal)
-    bound = 2.0 ** -8 * a + 2.0 ** -11 * b + 1e-6
+    bound = (2.0 ** -8 + 2.0 ** -11) * a + 2.0 ** -11 * b + 1e-6
     return ref, ref_r, bound
 
 

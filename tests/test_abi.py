@@ -337,3 +337,20 @@ def test_noalloc_attention_arguments(lib):
     assert b"static scratch" in lib.dg_last_error()
     # the long-context shape fits
     assert lib.dg_attention_workspace_bytes(256, 4096, 16, 8, 128) <= 64 << 20
+
+
+def test_fp8_step_and_graph_arguments(lib):
+    from block_text_diffusion_amd._lib import DG_EINVAL, DG_EUNSUPPORTED, DG_EWORKSPACE
+    att = [FAKE] * 6 + [64, 8, 8, 64, 0.0]
+    smp = [FAKE] * 8
+    big = 1 << 30
+    assert lib.dg_denoise_step_fp8(*att, 1.0, 1.0, 1.0, *smp, 16, 1000, 64, FAKE, 16, None) == DG_EWORKSPACE
+    assert lib.dg_denoise_step_fp8(*att, 0.0, 1.0, 1.0, *smp, 16, 1000, 64, FAKE, big, None) == DG_EINVAL
+    assert lib.dg_denoise_step_fp8(*att, 1.0, float("nan"), 1.0, *smp, 16, 1000, 64, FAKE, big, None) == DG_EINVAL
+    bad_d = [FAKE] * 6 + [64, 8, 8, 96, 0.0]
+    assert lib.dg_denoise_step_fp8(*bad_d, 1.0, 1.0, 1.0, *smp, 16, 1000, 64, FAKE, big, None) == DG_EUNSUPPORTED
+    assert lib.dg_denoise_step_fp8(*att, 1.0, 1.0, 1.0, *smp, 300, 1000, 64, FAKE, big, None) == DG_EUNSUPPORTED
+    h = ctypes.c_void_p()
+    assert lib.dg_step_graph_create_fp8(*att, 1.0, 1.0, 1.0, None, *smp[1:], 16, 1000, 64, FAKE, big,
+                                        ctypes.byref(h)) == DG_EINVAL
+    assert h.value is None

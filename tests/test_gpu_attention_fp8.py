@@ -79,3 +79,43 @@ def test_every_code_decodes_exactly():
     got = run_fp8(torch, dg, q, empty, empty, kc, vc)
     ref = F.canvas_attention_fp8(q, empty, empty, kc, vc)
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-3)
+
+
+def every_code_inputs(d):
+    """Q row i holds one nonzero E4M3 code, at element i, and key j holds code
+    (3j + 5c) mod 254 of the finite codes at element c, so score (i, j) is the
+    single product q_i * k_j[i]: exact in float32 whatever the accumulation
+    order, and every finite code of K (subnormals, zeros, +-448) meets the FP8
+    matrix cores.  V is the identity, so O row i is query i's weight vector."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    n = d
+    q = np.zeros((n, 1, d), np.uint8)
+    for i in range(n):
+        q[i, 0, i] = codes[(7 * i + 3) % len(codes)]
+    j, c = np.meshgrid(np.arange(n), np.arange(d), indexing="ij")
+    kc = codes[(3 * j + 5 * c) % len(codes)][:, None, :]
+    eye = workloads.fp8_codes(np.eye(n, d, dtype=np.float32))[:, None, :]
+    return q, kc, eye, codes
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_every_code_through_the_fp8_scores(d):
+    """The FP8 matrix-core scores, element by element: O = the softmax weights
+    of exact single-product scores (scale 1/64), against the oracle on the
+    decoded codes.  Each weight is rounded to bf16 for the P.V product (unit
+    roundoff 2^-8) and divided by the float32 sum: (2^-8 + 2^-11) relative, the
+    second term for the exponent and sum roundings, plus float32 noise, bounds
+    the difference."""
+    torch, dg = require_gpu()
+    log(f"fp8 scores over every code, d={d}")
+    q, kc, eye, codes = every_code_inputs(d)
+    assert set(np.unique(kc).tolist()) == set(codes.tolist())
+    empty = np.zeros((0, 1, d), np.uint8)
+    out = dg.dg_canvas_attention_fp8(to_dev(q), None, None, to_dev(kc), to_dev(eye), scale=1.0 / 64)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = F.canvas_attention_fp8(q, empty, empty, kc, eye, scale=1.0 / 64)
+    err = np.abs(got - ref)
+    worst = float((err / ((2.0 ** -8 + 2.0 ** -11) * np.abs(ref) + 1e-6)).max())
+    log(f"every code, d={d}: worst error / ((2^-8 + 2^-11) |w| + 1e-6) = {worst:.3f}")
+    assert worst <= 1.0

@@ -147,3 +147,54 @@ def test_entropy_bounded_step_eager_and_graph(inputs):
                 np.testing.assert_array_equal(g[key], eager[k][key], err_msg=f"replay {k} {key}")
     finally:
         graph.close()
+
+
+def test_fp8_step_eager_and_graph(inputs):
+    """The step with FP8 attention inputs (scores on the FP8 matrix cores): the
+    attention against the oracle on the decoded, scaled codes under the
+    contract and the rounding bounds, the sampler against the oracle, then the
+    same steps replayed from a captured graph, bit for bit."""
+    from oracle import fp8 as F
+    torch, dg = require_gpu()
+    codes = workloads.attention_inputs_fp8(4)
+    scales = (0.5, 0.75, 2.0)
+    ctrl = S.Ctrl(seed=12, tau=0.9, flags=S.AUTO_ADVANCE)
+
+    def state():
+        st = device_state(torch, dg, inputs, ctrl)
+        for k, c in zip(("q", "kp", "vp", "kc", "vc"), codes):
+            st[k] = to_dev(c)
+        return st
+
+    def snap(st):
+        torch.cuda.synchronize()
+        return {k: st[k].cpu().numpy().copy() for k in ("attn", "ids", "mask", "kappa", "z", "nu", "ctrl")}
+
+    log("fp8 step: eager")
+    st = state()
+    eager = []
+    for _ in range(2):
+        dg.dg_denoise_step_fp8(*args(st), *scales)
+        eager.append(snap(st))
+    qd, kpd, vpd, kcd, vcd = (F.e4m3_to_float(c) * float(np.float32(sc))
+                              for c, sc in zip(codes, (scales[0], scales[1], scales[2], scales[1], scales[2])))
+    ref_attn = attention_reference(qd, kpd, vpd, kcd, vcd)
+    check_attention(eager[0]["attn"], ref_attn[0], ref_attn[1], ref_attn[2] * 1.0, "fp8 step attention")
+    ref = S.sampler_step(inputs["logits"], inputs["emb"].astype(np.float64), inputs["ids"], inputs["mask"], ctrl,
+                         z_rows=ROWS)
+    assert check_step(inputs["ids"], inputs["mask"], eager[0]["ids"], eager[0]["mask"], eager[0]["kappa"], ref,
+                      0.9) <= 2
+    check_z(eager[0]["z"][ROWS], ref["z"])
+
+    log("fp8 step: graph")
+    st = state()
+    graph = dg.StepGraphFP8(*args(st), *scales)
+    try:
+        for k in range(2):
+            graph.launch()
+            g = snap(st)
+            assert torch.ones(1 << 20, device="cuda").sum().item() == float(1 << 20)   # unrelated eager work
+            for key in g:
+                np.testing.assert_array_equal(g[key], eager[k][key], err_msg=f"replay {k} {key}")
+    finally:
+        graph.close()
