@@ -31,8 +31,13 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, calibrated
 # on a plain copy; valid only for the kernel sources they were taken from
 COUNTERS = os.path.join(ROOT, "profiles", "long_context_step_counters.json")
-KERNEL_SOURCES = ["block_text_diffusion_amd/csrc/sampler.hip", "block_text_diffusion_amd/csrc/dg_common.hpp",
-                  "block_text_diffusion_amd/csrc/attention.hip"]
+# the source files each kernel family is built from: a kernel's recorded counters
+# stay valid while these files are unchanged
+_CSRC = "block_text_diffusion_amd/csrc/"
+KERNEL_SOURCES = {
+    "samp": [_CSRC + "sampler.hip", _CSRC + "dg_common.hpp"],
+    "attn": [_CSRC + "attention.hip", _CSRC + "dg_common.hpp"],
+}
 BF16_PEAK_TFLOPS = 2516.6
 FP8_PEAK_TFLOPS = 5000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
@@ -56,6 +61,9 @@ def parse():
                     help="bytes each way of the plain copy probe (measured HBM peak, counter calibration)")
     ap.add_argument("--no-probes", action="store_true", help="skip the copy and matrix-core peak probes")
     ap.add_argument("--no-decode-run", action="store_true", help="skip the decode runs")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the headline step, its per-kernel timing, the attention timing and the probes "
+                         "(for counter runs under a profiler); implies --no-cpu-baseline and --no-decode-run")
     return ap.parse_args()
 
 
@@ -65,6 +73,8 @@ def log(msg):
 
 def main():
     a = parse()
+    if a.headline_only:
+        a.no_cpu_baseline = a.no_decode_run = True
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {a.gpus}).",
               file=sys.stderr)
@@ -185,7 +195,16 @@ def main():
     sampler = {"kernels": list(SAMPLER_KERNELS), "us": round(samp_us, 2),
                "bound": "hbm", "floor_us": round(floor_hbm_us, 1), "frac": round(floor_hbm_us / samp_us, 4),
                "floor_bf16x3_us": round(floor_x3_us, 1), "frac_bf16x3": round(floor_x3_us / samp_us, 4)}
+    samp_traffic = [measured_traffic(k) for k in SAMPLER_KERNELS]
+    if all(t is not None for t in samp_traffic):
+        sampler["traffic"] = sum(samp_traffic)
+        sampler["traffic_over_algorithmic"] = round(sum(samp_traffic) / bytes_method, 3)
     attn = bf16_attention_timing(torch, dg, T, n, p, hq, hkv, hd, a.steps)
+    attn_traffic = [measured_traffic(k) for k in ("attn_partial", "attn_combine")]
+    if all(t is not None for t in attn_traffic):
+        attn["roofline"]["traffic"] = sum(attn_traffic)
+        attn["roofline"]["traffic_over_algorithmic"] = round(sum(attn_traffic) / attn["roofline"]["algorithmic_bytes"],
+                                                             3)
     attn["per_kernel_us_eager_events"] = {k: round(per_kernel_us[k], 2)
                                           for k in ("attn_partial", "attn_combine", "attn_fused")
                                           if k in per_kernel_us}
@@ -203,28 +222,30 @@ def main():
         attn["roofline"]["secondary"] = {"measured_peak": probes["mfma_tflops"], "unit": "TFLOP/s",
                                          "frac": round(attn["tflops"] / probes["mfma_tflops"], 4)}
 
-    # ---- the entropy-bounded sampler (the pages' default) on the same inputs ----
-    eb = eb_sampler_timing(torch, dg, T, n, vocab, dm, a.steps)
-    log(f"entropy-bounded sampler: {eb['ms_per_step']:.3f} ms per step")
+    eb = batched = attn_fp8 = attn_batched = topk = None
+    if not a.headline_only:
+        # ---- the entropy-bounded sampler (the pages' default) on the same inputs ----
+        eb = eb_sampler_timing(torch, dg, T, n, vocab, dm, a.steps)
+        log(f"entropy-bounded sampler: {eb['ms_per_step']:.3f} ms per step")
 
-    # ---- batches of canvases sharing one pass over E ----
-    batched = batched_sampler_timing(torch, dg, T, n, vocab, dm, a.steps)
-    log("batched sampler: " + ", ".join(f"B={r['batch']}: {r['ms_per_step']:.3f} ms ({r['canvas_steps_per_s']:.0f} canvas-steps/s)"
-                                        for r in batched))
+        # ---- batches of canvases sharing one pass over E ----
+        batched = batched_sampler_timing(torch, dg, T, n, vocab, dm, a.steps)
+        log("batched sampler: " + ", ".join(f"B={r['batch']}: {r['ms_per_step']:.3f} ms "
+                                            f"({r['canvas_steps_per_s']:.0f} canvas-steps/s)" for r in batched))
 
-    # ---- FP8 (E4M3) attention on the same draws ----
-    attn_fp8 = fp8_attention_timing(torch, dg, workloads, n, p, hq, hkv, hd, a.steps)
-    log(f"fp8 attention: {attn_fp8['us']:.1f} us per call")
+        # ---- FP8 (E4M3) attention on the same draws ----
+        attn_fp8 = fp8_attention_timing(torch, dg, workloads, n, p, hq, hkv, hd, a.steps)
+        log(f"fp8 attention: {attn_fp8['us']:.1f} us per call")
 
-    # ---- a denoising pass and a KV-update pass batched in one launch ----
-    attn_batched = batched_attention_timing(torch, dg, T, n, p, hq, hkv, hd, a.steps)
-    log(f"batched attention (denoise + KV update): {attn_batched['us_batched']:.1f} us in one launch, "
-        f"{attn_batched['us_two_calls']:.1f} us as two calls")
+        # ---- a denoising pass and a KV-update pass batched in one launch ----
+        attn_batched = batched_attention_timing(torch, dg, T, n, p, hq, hkv, hd, a.steps)
+        log(f"batched attention (denoise + KV update): {attn_batched['us_batched']:.1f} us in one launch, "
+            f"{attn_batched['us_two_calls']:.1f} us as two calls")
 
-    # ---- the top-k truncated sampler (approximate), alone and after attention ----
-    topk = topk_sampler_timing(torch, dg, T, n, p, hq, hkv, hd, vocab, dm, a.steps)
-    log("top-k sampler: " + ", ".join(f"k={r['k']} B={r['batch']}: {r['sampler_ms']:.3f} ms"
-                                      for r in topk["runs"]))
+        # ---- the top-k truncated sampler (approximate), alone and after attention ----
+        topk = topk_sampler_timing(torch, dg, T, n, p, hq, hkv, hd, vocab, dm, a.steps)
+        log("top-k sampler: " + ", ".join(f"k={r['k']} B={r['batch']}: {r['sampler_ms']:.3f} ms"
+                                          for r in topk["runs"]))
 
     # ---- the decode run: 4096-token prefix, four 256-token canvases, one step graph per canvas ----
     dec = dec_eb = None
@@ -684,10 +705,11 @@ def eb_sampler_timing(torch, dg, T, n, vocab, dm, steps):
             "per_kernel_us": {k: round(1e3 * t / c, 2) for k, (t, c) in prof.items()}}
 
 
-def sources_sha256():
+def sources_sha256(kernel):
+    """SHA-256 of the concatenated source files the kernel is built from."""
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel.split("_")[0]]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -695,15 +717,16 @@ def sources_sha256():
 
 def measured_traffic(kernel):
     """HBM bytes per launch from the committed counter summary, or None if the
-    kernel sources changed since the counters were taken."""
+    kernel's sources changed since its counters were taken."""
     try:
         with open(COUNTERS) as f:
             rec = json.load(f)
-    except (OSError, ValueError):
+        k = rec["kernels"][kernel]
+    except (OSError, ValueError, KeyError):
         return None
-    if rec.get("sources_sha256") != sources_sha256() or kernel not in rec.get("kernels", {}):
+    if k.get("sources_sha256") != sources_sha256(kernel):
         return None
-    return rec["kernels"][kernel]["hbm_bytes"]
+    return k["hbm_bytes"]
 
 
 def workload_sweep(torch, dg, workloads):
