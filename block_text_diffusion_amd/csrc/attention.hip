@@ -192,8 +192,10 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
   constexpr int KS8 = D / 64;  // 64-wide k steps (FP8 scores)
   constexpr int DB = D / 32;   // 32-row blocks of O^T
   // two stages, and the key-half merge of the epilogue (64 KB at D = 128)
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * G::kStageBytes];
-  static_assert(2 * S::kBytes <= 2 * G::kStageBytes, "stages exceed the LDS array");
+  constexpr int kLdsBytes = 2 * G::kStageBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+  static_assert(2 * S::kBytes <= kLdsBytes, "stages exceed the LDS array");
+  static_assert(4 * 4 * DB * 64 * 16 <= kLdsBytes, "key-half merge exceeds the LDS array");
   __shared__ float lds_ml[4][64][2];
 
   // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that the
@@ -299,14 +301,15 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
   if (nb > 2) fetch(ra, 2);
   __syncthreads();
 
-  // one block: scores, online softmax, O^T update (reads one LDS stage)
-  auto step = [&](int b, const uint8_t* ks_lds) {
-    const uint8_t* vs_lds = ks_lds + S::kVOffset;
+  // ---- one block in three phases: scores (matrix cores), online softmax
+  // (vector ALU), O^T update (matrix cores) ----
+  // scores of block b from its LDS stage: this wave's 32 keys of the block,
+  // masked past the segment end (and after the row under the causal flag)
+  auto scores = [&](int b, const uint8_t* ks_lds, float (&s)[16]) {
     const int gb = gb0 + b;
     const int seg_left = (gb < blocks_prefix) ? n_prefix - gb * kAKeys
                                               : n - (gb - blocks_prefix) * kAKeys;
-
-    // ---- S^T = K Q^T over this wave's 32 keys: two accumulators, even / odd k steps ----
+    // S^T = K Q^T: two accumulators, even / odd k steps
     f32x16 sa, sb;
 #pragma unroll
     for (int v = 0; v < 16; ++v) { sa[v] = 0.f; sb[v] = 0.f; }
@@ -337,7 +340,6 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
         sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks + 1], sb, 0, 0, 0);
       }
     }
-    float s[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = sa[v] + sb[v];
     // lane holds keys 32wh + 8(v/4) + 4half + v%4 of query r; with the causal
@@ -352,8 +354,12 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
         if (key >= lim) s[v] = -INFINITY;
       }
     }
+  };
 
-    // ---- online softmax (raw score units; exp2 folds in the scale) ----
+  // online softmax of one block's scores (raw score units; exp2 folds in the
+  // scale): updates the running max / sum, rescales O when the reference
+  // moves, and returns P as bf16 operands
+  auto softmax = [&](const float (&s)[16], bf16x8 (&pf)[2]) {
     float mloc = s[0];
 #pragma unroll
     for (int v = 1; v < 16; ++v) mloc = fmaxf(mloc, s[v]);
@@ -374,7 +380,6 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
     }
     const float mc = (m_run == -INFINITY) ? 0.f : -m_run * scale_log2e;
     float lsum = 0.f;
-    bf16x8 pf[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       float p[8];
@@ -389,8 +394,12 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
     }
     lsum += __shfl_xor(lsum, 32);
     l_run += lsum;
+  };
 
-    // ---- O^T += V^T P^T: 16-key steps; lane half h supplies keys 16tt+4h+{0..3}, 16tt+8+4h+{0..3} ----
+  // O^T += V^T P^T from a block's LDS stage: 16-key steps; lane half h
+  // supplies keys 16tt+4h+{0..3}, 16tt+8+4h+{0..3}
+  auto pv = [&](const uint8_t* st, const bf16x8 (&pf)[2]) {
+    const uint8_t* vs_lds = st + S::kVOffset;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
@@ -405,7 +414,6 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, pf[tt], acc_o[db], 0, 0, 0);
       }
     }
-
   };
 
   // Two LDS stages; two register sets.  Iteration b multiplies block b,
@@ -413,7 +421,12 @@ __global__ __launch_bounds__(kAThreads) void attn_partial(
   // other stage, and sends the loads of block b + 3 into the freed registers.
   // rn holds block b + 1: rb for even b, ra for odd b.
   auto iter = [&](int b, KvRegs<D, kF8>& rn) {
-    step(b, lds + (b & 1) * S::kBytes);
+    const uint8_t* st = lds + (b & 1) * S::kBytes;
+    float s[16];
+    bf16x8 pf[2];
+    scores(b, st, s);
+    softmax(s, pf);
+    pv(st, pf);
     if (b + 1 < nb) kv_store<D, kF8>(rn, lds + ((b + 1) & 1) * S::kBytes, t);
     if (b + 3 < nb) fetch(rn, b + 3);
     __syncthreads();
