@@ -44,6 +44,7 @@ def test_workloads(workload):
     (256, 5120, 16, 8, 128, "bf16"),   # largest prefix of the decode run
     (64, 0, 16, 8, 128, "bf16"),       # one key block in all: one chunk, output written directly
     (40, 0, 8, 2, 64, "f32"),          # the same single-chunk path at D=64, ragged block
+    (64, 2048, 4, 2, 64, "bf16"),      # 33 key chunks: the merge beyond its 16-chunk one-pass form
 ])
 def test_shapes(n, p, hq, hkv, d, qkv):
     torch, dg = require_gpu()
