@@ -8,7 +8,9 @@ missing, and there is no fallback implementation.
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdg.so")
+# DG_LIBRARY may name another build of the same sources (the AddressSanitizer
+# variant the CPU ABI tests run under); by default the in-tree libdg.so.
+LIB_PATH = os.environ.get("DG_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdg.so")
 
 DG_OK = 0
 DG_EINVAL = -1
