@@ -13,7 +13,7 @@ from ._lib import (DG_ATTN_CAUSAL, DG_AUTO_ADVANCE, DG_BF16, DG_COMMIT_ONLY, DG_
 
 __all__ = [
     "dg_canvas_attention", "dg_canvas_attention_noalloc", "dg_static_scratch_bytes", "dg_canvas_attention_batched", "dg_attention_batched_workspace_bytes",
-    "dg_canvas_attention_fp8", "dg_sampler_step", "dg_sampler_step_eb", "read_eb_status",
+    "dg_canvas_attention_fp8", "dg_sampler_step", "dg_sampler_step_f32", "dg_sampler_step_eb", "read_eb_status",
     "dg_sampler_step_batched", "dg_sampler_step_eb_batched", "dg_sampler_workspace_bytes_batched",
     "dg_sampler_step_topk", "dg_sampler_step_eb_topk", "dg_sampler_workspace_bytes_topk",
     "stack_ctrl", "dg_embedding_pack", "dg_embedding_packed_bytes", "dg_denoise_step", "dg_denoise_step_eb", "dg_denoise_step_fp8", "StepGraph", "StepGraphEB",
@@ -269,6 +269,26 @@ def dg_sampler_step(logits, emb_packed, canvas_ids, committed, selfcond, confide
     check(load().dg_sampler_step(_ptr(logits), _ptr(emb_packed), _ptr(canvas_ids), _ptr(committed),
                                  _ptr(selfcond), _ptr(confidence), _ptr(n_uncommitted), _ptr(ctrl),
                                  n, vocab, d, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def dg_sampler_step_f32(logits, emb, canvas_ids, committed, selfcond, confidence, n_uncommitted, ctrl,
+                        workspace=None, stream=None):
+    """dg_sampler_step on the plain float32 table E [V, d] (d a multiple of 4)."""
+    torch = _torch()
+    _need(logits, "logits", (torch.float32,)); _need(emb, "emb", (torch.float32,))
+    _need(canvas_ids, "canvas_ids", (torch.int32,)); _need(committed, "committed", (torch.uint8,))
+    _need(selfcond, "selfcond", (torch.float32,)); _need(n_uncommitted, "n_uncommitted", (torch.int32, torch.uint32))
+    _need(ctrl, "ctrl", (torch.uint8,))
+    if confidence is not None:
+        _need(confidence, "confidence", (torch.float32,))
+    n, vocab = logits.shape
+    d = selfcond.shape[1]
+    if tuple(emb.shape) != (vocab, d):
+        raise ValueError("emb must be [vocab, d_model]")
+    ws = _workspace(dg_sampler_workspace_bytes(n, vocab, d), logits.device, workspace)
+    check(load().dg_sampler_step_f32(_ptr(logits), _ptr(emb), _ptr(canvas_ids), _ptr(committed), _ptr(selfcond),
+                                     _ptr(confidence), _ptr(n_uncommitted), _ptr(ctrl), n, vocab, d, _ptr(ws),
+                                     ws.numel(), _stream(stream)))
 
 
 def dg_sampler_step_eb(logits, emb_packed, canvas_ids, accepted, selfcond, entropy, argmax, status,

@@ -81,6 +81,7 @@ SIGNATURES = {
     "dg_embedding_packed_bytes": (_sz, [_i, _i]),
     "dg_embedding_pack": (_i, [_vp, _vp, _i, _i, _vp]),
     "dg_sampler_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]),
+    "dg_sampler_step_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]),
     "dg_sampler_step_eb": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _i, _i, _i,
                                 _vp, _sz, _vp]),
     "dg_sampler_workspace_bytes_batched": (_sz, [_i, _i, _i, _i]),

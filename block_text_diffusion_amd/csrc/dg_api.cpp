@@ -347,6 +347,25 @@ int dg_sampler_step_batched(const float* logits, const void* emb, int32_t* ids, 
   return DG_OK;
 }
 
+int dg_sampler_step_f32(const float* logits, const float* emb, int32_t* ids, uint8_t* committed, float* z,
+                        float* conf, uint32_t* n_unc, dg_ctrl* ctrl, int n, int vocab, int d, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  int st = check_sampler(logits, emb, ids, committed, z, n_unc, ctrl, n, vocab, d, 1);
+  if (st != DG_OK) return st;
+  if (d % 4 != 0) return fail(DG_EUNSUPPORTED, "sampler_f32: d_model must be a multiple of 4 for the float32 table");
+  const dg::SamplerPlan p = dg::sampler_plan(n, 1, vocab, d);
+  st = check_sampler_plan(p, "sampler_f32");
+  if (st != DG_OK) return st;
+  if (!ws || ws_bytes < p.total)
+    return fail(DG_EWORKSPACE, "sampler_f32: workspace %zu < %zu bytes", ws_bytes, p.total);
+  if (!aligned16(ws)) return fail(DG_EINVAL, "sampler_f32: workspace misaligned");
+  dg::EbCall call{false, 0.f, 0.f, nullptr, nullptr, nullptr};
+  call.emb_f32 = true;
+  hipError_t e = dg::launch_sampler(p, logits, emb, ids, committed, z, conf, n_unc, ctrl, ws, stream, call);
+  if (e != hipSuccess) return hip_fail(e, "sampler_f32 launch");
+  return DG_OK;
+}
+
 int dg_sampler_step_eb(const float* logits, const void* emb, int32_t* ids, uint8_t* accepted,
                        float* z, float* entropy, int32_t* argmax, dg_eb_status* status,
                        dg_ctrl* ctrl, float budget, float stop_entropy, int n, int vocab, int d,

@@ -36,6 +36,7 @@ struct EbCall {
   float* entropy_out;       // [n] or null
   int32_t* argmax;          // [n] in/out
   dg_eb_status* status;
+  bool emb_f32 = false;     // E is the plain float32 table [V, d] (not the packed image)
 };
 SamplerPlan sampler_plan(int n_canvas, int batch, int vocab, int d);
 // The combine kernel keeps one merge weight per vocabulary split in LDS; a plan

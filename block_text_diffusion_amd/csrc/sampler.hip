@@ -323,17 +323,41 @@ constexpr int kDmaPerStep = 4;         // LDS DMA instructions per wave per k st
 // directly (lane i of an instruction lands at destination + 16 i).  Wave w
 // moves rows 32w..32w+31 of the p image and columns 32w..32w+31 of the E
 // image; lane i fetches the global chunk that belongs at its swizzled slot.
-__device__ __forceinline__ void gemm_dma(uint8_t* stage, const uint8_t* __restrict__ pimg,
-                                         const uint8_t* __restrict__ eimg, int kb, int n_kb,
-                                         int col_pad, int col0, const uint32_t (&voff)[2],
+// The E operand comes either as the packed image (the same [column][64 B]
+// form as the p images) or, with kF32E, as the plain float32 table [V, d]: then
+// wave w moves id rows 2w and 2w + 1 of the k-block, 1 KB each (the tile's 256
+// columns), into LDS rows of 1 KB; lane i fetches the 16-byte chunk i ^ f(row)
+// so id rows r and r + 8 sit 128 bytes apart in the banks.  Ids past the
+// vocabulary and columns past d read as zero (buffer range checks; d is a
+// multiple of 4).
+struct EOperand {
+  const uint8_t* base;  // packed image, or float32 E
+  int d;                // row length of float32 E (elements)
+  int vocab;
+};
+
+__device__ __forceinline__ int e32_chunk(int row, int lane) { return lane ^ (row & 8); }
+
+template <bool kF32E>
+__device__ __forceinline__ void gemm_dma(uint8_t* stage, const uint8_t* __restrict__ pimg, const EOperand& eo,
+                                         int kb, int n_kb, int col_pad, int col0, const uint32_t (&voff)[2],
                                          const uint32_t (&poff)[2], int wave) {
   const __amdgpu_buffer_rsrc_t ra = rsrc(pimg + (size_t)kb * kPImg, kPImg);
-  const __amdgpu_buffer_rsrc_t rb = rsrc(eimg + ((size_t)kb * col_pad + col0) * kImgRow, kArr);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     uint8_t* dst = stage + (32 * wave + 16 * j) * kImgRow;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)dst, 16, poff[j], 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[j], 0, 0, 0);
+    if constexpr (kF32E) {
+      const int row = 2 * wave + j;                       // id row of the k-block
+      const int id = kb * kKB + row;
+      const uint32_t valid = (id < eo.vocab && col0 < eo.d) ? (uint32_t)(eo.d - col0) * 4u : 0u;
+      const __amdgpu_buffer_rsrc_t rb =
+          rsrc(eo.base + ((size_t)min(id, eo.vocab - 1) * eo.d + col0) * 4, valid < 1024u ? valid : 1024u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[j], 0, 0, 0);
+    } else {
+      const __amdgpu_buffer_rsrc_t rb = rsrc(eo.base + ((size_t)kb * col_pad + col0) * kImgRow, kArr);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[j], 0, 0, 0);
+    }
   }
 }
 
@@ -341,6 +365,7 @@ struct Frags {
   bf16x8 ah[4], al[4], bh[2], bl[2];
 };
 
+template <bool kF32E>
 __device__ __forceinline__ void gemm_frags(Frags& f, const uint8_t* stage, int wm, int wn, int lane) {
   const int h = lane >> 5;
 #pragma unroll
@@ -349,11 +374,38 @@ __device__ __forceinline__ void gemm_frags(Frags& f, const uint8_t* stage, int w
     f.ah[i] = *reinterpret_cast<const bf16x8*>(stage + swz_off(ra, h));
     f.al[i] = *reinterpret_cast<const bf16x8*>(stage + swz_off(ra, 2 + h));
   }
+  if constexpr (kF32E) {
+    // The lane's two column fragments are the adjacent columns 64 wn + 2 c and
+    // + 1 (c = lane % 32; the epilogue maps them back), so one 8-byte read per
+    // id row serves both.  Ids 8h .. 8h + 7 come from their float32 rows and
+    // are split into the bf16 hi / lo pairs exactly as dg_embedding_pack forms
+    // them.
+    const int cb = 64 * wn + 2 * (lane & 31);
+    float x0[8], x1[8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rb = 64 * wn + 32 * i + (lane & 31);
-    f.bh[i] = *reinterpret_cast<const bf16x8*>(stage + kArr + swz_off(rb, h));
-    f.bl[i] = *reinterpret_cast<const bf16x8*>(stage + kArr + swz_off(rb, 2 + h));
+    for (int e = 0; e < 8; ++e) {
+      const int row = 8 * h + e;
+      const f32x2 v = *reinterpret_cast<const f32x2*>(stage + kArr + row * 1024 + (e32_chunk(row, cb >> 2) << 4) +
+                                                      (cb & 3) * 4);
+      x0[e] = v[0];
+      x1[e] = v[1];
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split2(x0[2 * e], x0[2 * e + 1], hi[e], lo[e]);
+    f.bh[0] = __builtin_bit_cast(bf16x8, (u32x4){hi[0], hi[1], hi[2], hi[3]});
+    f.bl[0] = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], lo[2], lo[3]});
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split2(x1[2 * e], x1[2 * e + 1], hi[e], lo[e]);
+    f.bh[1] = __builtin_bit_cast(bf16x8, (u32x4){hi[0], hi[1], hi[2], hi[3]});
+    f.bl[1] = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], lo[2], lo[3]});
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rb = 64 * wn + 32 * i + (lane & 31);
+      f.bh[i] = *reinterpret_cast<const bf16x8*>(stage + kArr + swz_off(rb, h));
+      f.bl[i] = *reinterpret_cast<const bf16x8*>(stage + kArr + swz_off(rb, 2 + h));
+    }
   }
 }
 
@@ -375,10 +427,10 @@ __device__ __forceinline__ void gemm_mma(const Frags& f, f32x16 (&acc)[4][2]) {
 // fragments of step s+1 are read (kFrags).  kAhead = number of DMA steps
 // issued beyond s+1 at the wait.  Every variant is straight-line code, so the
 // compiler's wait-count tracking stays exact across the unrolled iterations.
-template <int kAhead, bool kDma, bool kFrags>
+template <int kAhead, bool kDma, bool kFrags, bool kF32E>
 __device__ __forceinline__ void gemm_iter(int s, uint8_t* smem, Frags& cur, Frags& nxt,
                                           f32x16 (&acc)[4][2], const uint8_t* __restrict__ pimg,
-                                          const uint8_t* __restrict__ eimg, int kb0, int kb_last,
+                                          const EOperand& eo, int kb0, int kb_last,
                                           int n_kb, int col_pad, int col0,
                                           const uint32_t (&voff)[2], const uint32_t (&poff)[2],
                                           int wave, int wm, int wn, int lane) {
@@ -389,14 +441,14 @@ __device__ __forceinline__ void gemm_iter(int s, uint8_t* smem, Frags& cur, Frag
   // past the split's last k-block the DMA repeats that block into a stage that
   // is never read again, so every iteration runs the same code
   if (kDma)
-    gemm_dma(smem + ((s + kDist) % kStages) * kStage, pimg, eimg, min(kb0 + s + kDist, kb_last), n_kb,
-             col_pad, col0, voff, poff, wave);
-  if (kFrags) gemm_frags(nxt, smem + ((s + 1) % kStages) * kStage, wm, wn, lane);
+    gemm_dma<kF32E>(smem + ((s + kDist) % kStages) * kStage, pimg, eo, min(kb0 + s + kDist, kb_last), n_kb,
+                    col_pad, col0, voff, poff, wave);
+  if (kFrags) gemm_frags<kF32E>(nxt, smem + ((s + 1) % kStages) * kStage, wm, wn, lane);
   gemm_mma(cur, acc);
   // issue order: the next step's fragment reads first, then the MFMAs with the
   // LDS DMA instructions spread between them, so a DMA that has to wait for
   // queue space never holds back more than a few MFMAs
-  if (kFrags) __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+  if (kFrags) __builtin_amdgcn_sched_group_barrier(0x100, kF32E ? 16 : 12, 0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
@@ -404,11 +456,13 @@ __device__ __forceinline__ void gemm_iter(int s, uint8_t* smem, Frags& cur, Frag
   }
 }
 
+template <bool kF32E>
 __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restrict__ pimg,
                                                           const uint8_t* __restrict__ eimg,
                                                           float* __restrict__ zp, int n_rows, int d,
                                                           int col_pad, int n_tiles, int n_mt,
-                                                          int kb_per_split, int n_kb) {
+                                                          int kb_per_split, int n_kb, int vocab) {
+  const EOperand eo{eimg, d, vocab};
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
 
   // Workgroups are dealt round-robin to the 8 XCDs; renumber them so the
@@ -440,8 +494,9 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
   for (int j = 0; j < 2; ++j) {
     const int row = 32 * wave + 16 * j + (lane >> 2);
     const int chunk = (lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
-    voff[j] = (uint32_t)(row * kImgRow + chunk * 16);
-    poff[j] = voff[j];
+    poff[j] = (uint32_t)(row * kImgRow + chunk * 16);
+    // float32 E: id row 2 wave + j, lane's slot holds 16-byte chunk e32_chunk
+    voff[j] = kF32E ? (uint32_t)(e32_chunk(2 * wave + j, lane) * 16) : poff[j];
   }
 
   f32x16 acc[4][2];
@@ -457,15 +512,15 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
   const int kb_last = kb0 + nsteps - 1;
 #pragma unroll
   for (int k = 0; k < kDist; ++k)
-    gemm_dma(smem + k * kStage, pimg, eimg, min(kb0 + k, kb_last), n_kb, col_pad, col0, voff, poff, wave);
+    gemm_dma<kF32E>(smem + k * kStage, pimg, eo, min(kb0 + k, kb_last), n_kb, col_pad, col0, voff, poff, wave);
   Frags fa, fb;
   wait_vmcnt<(kDist - 1) * kDmaPerStep>();
   raw_barrier();
-  gemm_frags(fa, smem, wm, wn, lane);
+  gemm_frags<kF32E>(fa, smem, wm, wn, lane);
 
 #define DG_ITER(S, C, N) \
-  gemm_iter<1, true, true>(S, smem, C, N, acc, pimg, eimg, kb0, kb_last, n_kb, col_pad, col0, voff, poff, \
-                           wave, wm, wn, lane)
+  gemm_iter<1, true, true, kF32E>(S, smem, C, N, acc, pimg, eo, kb0, kb_last, n_kb, col_pad, col0, voff, poff, \
+                                  wave, wm, wn, lane)
   // every iteration sends a DMA step and reads the next step's fragments (the
   // last ones read data that is never used)
   int s = 0;
@@ -483,7 +538,8 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int col = col0 + 64 * wn + 32 * nb + (lane & 31);
+      // float32 E: fragment nb holds the columns of parity nb (see gemm_frags)
+      const int col = kF32E ? col0 + 64 * wn + 2 * (lane & 31) + nb : col0 + 64 * wn + 32 * nb + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = kGM * mt + 128 * wm + 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -1363,9 +1419,14 @@ hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void*
   if (e != hipSuccess) return e;
 
   prof_begin("samp_gemm", s);
-  samp_gemm<<<p.n_mt * p.n_tiles * p.n_splits, kGThreads, 0, s>>>(
-      pimg, static_cast<const uint8_t*>(emb_packed), zp, p.n, p.d, p.col_pad, p.n_tiles, p.n_mt,
-      p.kb_per_split, p.n_kb);
+  if (eb.emb_f32)
+    samp_gemm<true><<<p.n_mt * p.n_tiles * p.n_splits, kGThreads, 0, s>>>(
+        pimg, static_cast<const uint8_t*>(emb_packed), zp, p.n, p.d, p.col_pad, p.n_tiles, p.n_mt,
+        p.kb_per_split, p.n_kb, p.vocab);
+  else
+    samp_gemm<false><<<p.n_mt * p.n_tiles * p.n_splits, kGThreads, 0, s>>>(
+        pimg, static_cast<const uint8_t*>(emb_packed), zp, p.n, p.d, p.col_pad, p.n_tiles, p.n_mt,
+        p.kb_per_split, p.n_kb, p.vocab);
   prof_end(s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

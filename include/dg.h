@@ -257,6 +257,22 @@ int dg_sampler_step(const float* logits, const void* emb_packed, int32_t* canvas
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * dg_sampler_step on the plain float32 embedding table instead of the packed
+ * image:
+ *   emb             [vocab, d_model] float32, row-major, 16-byte aligned
+ * The contraction splits each element of E into its bf16 hi / lo pair while it
+ * streams (the same split dg_embedding_pack makes), so z equals
+ * dg_sampler_step's z bit for bit.  d_model must be a multiple of 4
+ * (DG_EUNSUPPORTED otherwise).  Other arguments, workspace
+ * (dg_sampler_workspace_bytes) and errors as dg_sampler_step.
+ */
+int dg_sampler_step_f32(const float* logits, const float* emb, int32_t* canvas_ids,
+                        uint8_t* committed, float* selfcond, float* confidence,
+                        uint32_t* n_uncommitted, dg_ctrl* ctrl,
+                        int n_canvas, int vocab, int d_model,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Entropy-bounded sampler step: the pages' default sampler (explainer
  * "DiffusionGemma: Google's open diffusion LLM", section "A diffusion language
  * model refines 256 tokens in 12 steps" and Table 2 "Sampler settings that

@@ -354,3 +354,12 @@ def test_fp8_step_and_graph_arguments(lib):
     assert lib.dg_step_graph_create_fp8(*att, 1.0, 1.0, 1.0, None, *smp[1:], 16, 1000, 64, FAKE, big,
                                         ctypes.byref(h)) == DG_EINVAL
     assert h.value is None
+
+
+def test_float32_table_sampler_arguments(lib):
+    from block_text_diffusion_amd._lib import DG_EINVAL, DG_EUNSUPPORTED, DG_EWORKSPACE
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE]
+    assert lib.dg_sampler_step_f32(*a, 16, 1000, 64, FAKE, 16, None) == DG_EWORKSPACE
+    assert lib.dg_sampler_step_f32(*a, 16, 1000, 66, FAKE, 1 << 30, None) == DG_EUNSUPPORTED   # d % 4
+    assert lib.dg_sampler_step_f32(*a, 1, 8388608, 64, FAKE, 1 << 40, None) == DG_EUNSUPPORTED  # splits
+    assert lib.dg_sampler_step_f32(None, *a[1:], 16, 1000, 64, FAKE, 1 << 30, None) == DG_EINVAL

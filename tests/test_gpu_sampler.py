@@ -246,3 +246,45 @@ def test_embedding_pack_layout(vocab, d):
     recon = hi.astype(np.float64) + lo.astype(np.float64)
     assert np.all(np.abs(recon - ref) <= 2.0 ** -16 * np.abs(ref) + 1e-30)
     np.testing.assert_array_equal(hi.astype(np.float32), (workloads.round_bf16(ref.astype(np.float32))))
+
+
+@pytest.mark.parametrize("n,vocab,d", [(256, 262144, 3072), (256, 4097, 260), (17, 12345, 516), (1, 2, 4)])
+def test_float32_table_matches_the_packed_image(n, vocab, d):
+    """dg_sampler_step_f32 splits E while streaming it, exactly as the packing
+    kernel does: every output equals dg_sampler_step's on the packed image bit
+    for bit, and both meet the oracle."""
+    torch, dg = require_gpu()
+    log(f"sampler float32 table n={n} V={vocab} d={d}")
+    if vocab == 262144:
+        emb = workloads.embedding(3)
+        logits = workloads.step_logits(3, 0)
+        rows = np.array([0, 5, 77, 128, 255])
+    else:
+        rng = np.random.default_rng(vocab + d)
+        logits = (rng.standard_normal((n, vocab)) * 3).astype(np.float32)
+        logits[::3, vocab // 2] += 12.0
+        emb = (rng.standard_normal((vocab, d)) * 0.02).astype(np.float32)
+        rows = None
+    ids = (np.arange(n) * 7919 % vocab).astype(np.int32)
+    mask = (np.arange(n) % 5 == 0).astype(np.uint8)
+    ctrl = S.Ctrl(seed=21, gstep=3, tau=0.9, flags=S.AUTO_ADVANCE)
+    tl, te = to_dev(logits), to_dev(emb)
+    outs = []
+    for f32 in (False, True):
+        t_ids, t_mask = to_dev(ids), to_dev(mask)
+        z = torch.empty((n, d), dtype=torch.float32, device="cuda")
+        kappa = torch.empty(n, dtype=torch.float32, device="cuda")
+        nu = torch.zeros(1, dtype=torch.int32, device="cuda")
+        c = dg.make_ctrl(seed=ctrl.seed, gstep=ctrl.gstep, tau=ctrl.tau, flags=ctrl.flags)
+        if f32:
+            dg.dg_sampler_step_f32(tl, te, t_ids, t_mask, z, kappa, nu, c)
+        else:
+            dg.dg_sampler_step(tl, dg.dg_embedding_pack(te), t_ids, t_mask, z, kappa, nu, c)
+        torch.cuda.synchronize()
+        outs.append([x.cpu().numpy() for x in (t_ids, t_mask, z, kappa, nu, c)])
+    for a, b, name in zip(outs[0], outs[1], ("ids", "mask", "z", "kappa", "n_uncommitted", "ctrl")):
+        np.testing.assert_array_equal(a, b, err_msg=f"float32 table differs from the packed image: {name}")
+    ref = S.sampler_step(logits, emb, ids, mask, ctrl, z_rows="all" if rows is None else rows)
+    gids, gmask, gz, gk = outs[1][0], outs[1][1], outs[1][2], outs[1][3]
+    assert check_step(ids, mask, gids, gmask, gk, ref, 0.9) == 0
+    check_z(gz if rows is None else gz[rows], ref["z"])
