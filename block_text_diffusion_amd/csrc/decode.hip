@@ -41,16 +41,23 @@ __global__ __launch_bounds__(kSynThreads) void synth_logits_kernel(
   const int open = (t < n && !committed[t]) ? 1 : 0;
   const uint32_t n_open = (uint32_t)__syncthreads_count(open);
 
-  int target = -1;
-  if (committed[row]) {
-    target = ids[row];
-  } else {
-    const Philox4 hc = philox4x32_10(0u, (uint32_t)row, gstep, kStreamSynChoose, k0, k1);
-    if (range_draw(hc.w0, n_open) < kChoosePerStep) {
-      const Philox4 ht = philox4x32_10(0u, (uint32_t)row, gstep, kStreamSynTarget, k0, k1);
-      target = (int)range_draw(ht.w0, (uint32_t)vocab);
+  // the row's spike target, drawn once per workgroup
+  __shared__ int s_target;
+  if (t == 0) {
+    int target = -1;
+    if (committed[row]) {
+      target = ids[row];
+    } else {
+      const Philox4 hc = philox4x32_10(0u, (uint32_t)row, gstep, kStreamSynChoose, k0, k1);
+      if (range_draw(hc.w0, n_open) < kChoosePerStep) {
+        const Philox4 ht = philox4x32_10(0u, (uint32_t)row, gstep, kStreamSynTarget, k0, k1);
+        target = (int)range_draw(ht.w0, (uint32_t)vocab);
+      }
     }
+    s_target = target;
   }
+  __syncthreads();
+  const int target = s_target;
   const int j = 4 * (blockIdx.x * kSynThreads + t);
   if (j >= vocab) return;
   const Philox4 h = philox4x32_10((uint32_t)j >> 2, (uint32_t)row, gstep, kStreamSynNoise, k0, k1);
