@@ -159,13 +159,14 @@ def main():
 
     # Algorithmic work of the dominant kernel per launch (one step): the method
     # reads the logits and E once and writes z, and does 2 N V d flops.  The
-    # contraction's operands are bf16 (three bf16 products per fp32-accurate
-    # one), so its roofline is the bf16 one: 412.3 GFLOP over 3.493 GB is an
-    # arithmetic intensity of 118 flop/B, below the bf16 ridge (2516.6 / 8 =
-    # 315 flop/B), so the bound is HBM bandwidth.
+    # contraction runs one fp16 product and two fp8 correction products per
+    # fp32-accurate one; at 412.3 GFLOP over 3.493 GB (118 flop/B) it is below
+    # the fp16 ridge (2516.6 / 8 = 315 flop/B), so the bound is HBM bandwidth.
     gemm_us = per_kernel_us["samp_gemm"]
     flops_method = 2.0 * n * vocab * dm                         # softmax(l)·E
-    flops_bf16x3 = 3.0 * flops_method                           # the products the matrix cores execute
+    flops_fp16, flops_fp8 = flops_method, 2.0 * flops_method    # the products the matrix cores execute
+    # matrix-core time at the datasheet peaks (fp16 = bf16 rate, fp8 twice it)
+    split_floor_us = (flops_fp16 / BF16_PEAK_TFLOPS + flops_fp8 / FP8_PEAK_TFLOPS) / 1e12 * 1e6
     bytes_method = 4.0 * (n * vocab + vocab * dm + n * dm)      # logits + E + z, each once
     gbs = bytes_method / (gemm_us * 1e-6) / 1e9
     roofline = {
@@ -181,20 +182,20 @@ def main():
         "algorithmic_flops": flops_method,
         "arithmetic_intensity": round(flops_method / bytes_method, 1),
         "hbm_floor_us": round(bytes_method / (HBM_PEAK_GBS * 1e9) * 1e6, 1),
-        # the split-precision products against the bf16 matrix-core peak
-        "bf16x3_tflops": round(flops_bf16x3 / (gemm_us * 1e-6) / 1e12, 1),
-        "bf16x3_mfma_frac": round(flops_bf16x3 / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
-        "bf16x3_floor_us": round(flops_bf16x3 / (BF16_PEAK_TFLOPS * 1e12) * 1e6, 1),
+        # the split-precision products (fp16 + two fp8) against the datasheet
+        # matrix-core peaks: the time they need at peak over the time taken
+        "split_mfma_floor_us": round(split_floor_us, 1),
+        "split_mfma_frac": round(split_floor_us / gemm_us, 4),
         "timing": "HIP events around each launch on its stream, eager steps right after the timed region",
     }
     # the whole sampler (four kernels) against the same HBM floor, and against
-    # max(HBM floor, bf16x3 matrix-core floor)
+    # max(HBM floor, split-precision matrix-core floor)
     samp_us = sum(per_kernel_us[k] for k in SAMPLER_KERNELS if k in per_kernel_us)
     floor_hbm_us = bytes_method / (HBM_PEAK_GBS * 1e9) * 1e6
-    floor_x3_us = max(floor_hbm_us, flops_bf16x3 / (BF16_PEAK_TFLOPS * 1e12) * 1e6)
+    floor_split_us = max(floor_hbm_us, split_floor_us)
     sampler = {"kernels": list(SAMPLER_KERNELS), "us": round(samp_us, 2),
                "bound": "hbm", "floor_us": round(floor_hbm_us, 1), "frac": round(floor_hbm_us / samp_us, 4),
-               "floor_bf16x3_us": round(floor_x3_us, 1), "frac_bf16x3": round(floor_x3_us / samp_us, 4)}
+               "floor_split_us": round(floor_split_us, 1), "frac_split": round(floor_split_us / samp_us, 4)}
     samp_traffic = [measured_traffic(k) for k in SAMPLER_KERNELS]
     if all(t is not None for t in samp_traffic):
         sampler["traffic"] = sum(samp_traffic)
@@ -216,8 +217,9 @@ def main():
     if probes:
         roofline["secondary"] = {"measured_peak": probes["copy_gbs"], "unit": "GB/s",
                                  "frac": round(gbs / probes["copy_gbs"], 4),
-                                 "bf16x3_mfma_frac": round(flops_bf16x3 / (gemm_us * 1e-6) / 1e12
-                                                           / probes["mfma_tflops"], 4)}
+                                 # the probe measures bf16; fp16 runs at that rate, fp8 at twice it
+                                 "split_mfma_frac": round((flops_fp16 + flops_fp8 / 2) / (gemm_us * 1e-6) / 1e12
+                                                          / probes["mfma_tflops"], 4)}
         sampler["frac_measured_hbm"] = round(bytes_method / (probes["copy_gbs"] * 1e9) * 1e6 / samp_us, 4)
         attn["roofline"]["secondary"] = {"measured_peak": probes["mfma_tflops"], "unit": "TFLOP/s",
                                          "frac": round(attn["tflops"] / probes["mfma_tflops"], 4)}

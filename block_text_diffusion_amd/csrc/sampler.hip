@@ -12,18 +12,32 @@
 //   samp_stats     per (split, row), from one read of the logits held in
 //                  registers: the max, the greedy argmax and the Gumbel-perturbed
 //                  argmax, then the sums of exp(l - m_s) at T = 1 and at T, and
-//                  p = exp(l - m_s) written as bf16 hi/lo "images": per k-block of
-//                  16 ids, 256 row slots of 64 bytes (16 hi, 16 lo).
-//   samp_gemm      z_s = sum_j p_j E_j over one split for a 256 x 256 tile: p
-//                  and E (packed once by dg_embedding_pack into the same image
-//                  form) stream through LDS; bf16x3 split precision on
-//                  v_mfma_f32_32x32x16_bf16: p_hi E_hi + p_hi E_lo + p_lo E_hi
-//                  accumulated in fp32.  No exponentials or conversions in the
-//                  loop: 16-byte loads, LDS stores, fragment reads and MFMAs.
+//                  the weights p = exp(l - m_s) written as split-precision
+//                  "images": per k-block of 16 ids, 256 row slots of 64 bytes.
+//   samp_gemm      z_s = sum_j p_j E_j over one split for a 256 x 256 tile, both
+//                  operands streamed through LDS, fp32 accumulation.  On the
+//                  packed table (dg_embedding_pack) each product is one fp16
+//                  term plus two fp8 corrections (below); on the plain float32
+//                  table E is split into bf16 hi / lo while it streams and the
+//                  product is bf16x3 (p_hi E_hi + p_hi E_lo + p_lo E_hi).
 //   samp_combine   per row: merge the split statistics (log-sum-exp), the
 //                  candidate, its confidence, commit / re-noise, and
 //                  z = sum_s 2^((m_s - m) log2 e) z_s / S.
 //   samp_finalize  count open positions; advance the step counters.
+//
+// fp16 + fp8 split precision.  With P = p 2^14 (p <= 1) and Q = E 2^c, where
+// c puts max|Q| in [2^12, 2^13), P16 = fp16(P), Pe = P - P16, Q16 = fp16(Q),
+// Qe = Q - Q16, the contraction sums
+//     P16 Q16  +  fp8(P 2^-6) fp8(Qe 2^6)  +  fp8(Pe 2^5) fp8(Q 2^-5)
+// = PQ + Pe Qe + (the fp8 roundings of the two correction terms).
+// fp16 x fp16 products are exact in fp32; the corrections are 2^-11 of a term
+// and carry fp8 (e4m3) relative error <= 2^-4, so each term is within about
+// 2^-14 of P Q.  The exponents are chosen so every fp8 operand is at most 256
+// (e4m3 holds 448) and the two correction terms need no scale factor: one
+// v_mfma_f32_32x32x16_f16 per 16 ids and one v_mfma_f32_32x32x64_f8f6f4 per
+// 32 ids (corrections of two k-blocks side by side in K), the work of two
+// bf16 products instead of bf16x3's three.  The combine multiplies by
+// 2^-(14 + c), which dg_embedding_pack stores after the image.
 #include "dg_common.hpp"
 #include "dg_internal.hpp"
 
@@ -51,7 +65,7 @@ struct EbRows {
 };
 
 constexpr int kKB = 16;            // vocabulary ids per k-block
-constexpr int kImgRow = 64;        // bytes per row slot of a k-block image: 16 bf16 hi, 16 bf16 lo
+constexpr int kImgRow = 64;        // bytes per row slot of a k-block image (16 ids)
 constexpr int kGM = 256;           // canvas row slots per image / rows per contraction tile
 constexpr int kGN = 256;           // embedding columns per contraction tile
 constexpr int kPImg = kGM * kImgRow;   // 16 KB: the p image of one k-block
@@ -59,6 +73,49 @@ constexpr int kGThreads = 512;     // 8 waves (two per SIMD): 2 x 4, 128 x 64 ea
 constexpr int kArr = kGM * kImgRow;    // 16 KB: one operand of one LDS stage
 constexpr int kStage = 2 * kArr;       // p tile + E tile
 constexpr int kStatsThreads = 256;
+
+// Record layouts of one 64-byte slot (16 ids of one row of p, or one column of E):
+//   bf16x3:    bf16 hi of ids 0-15 | bf16 lo of ids 0-15
+//   fp16 + fp8 (p side):  fp16 P16 of ids 0-15 | fp8 P 2^-6 | fp8 Pe 2^5
+//   fp16 + fp8 (E side):  fp16 Q16 of ids 0-15 | fp8 Qe 2^6 | fp8 Q 2^-5
+constexpr float kPScale = 16384.0f;    // P = p 2^14
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, (f16x2){(_Float16)a, (_Float16)b});
+}
+
+// four fp32 values to four e4m3 bytes (round to nearest even), id order
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// x = v 2^k (k = 14 for p, c for E) as fp16 x16 | fp8 first | fp8 second for
+// four ids: first = fp8(x 2^f1), second = fp8((x - fp16(x)) 2^e1) on the p
+// side (f1 = -6, e1 = 5); the E side swaps the two (fp8 of the residual
+// first, e1 = 6; then fp8(x 2^-5)).
+template <bool kESide>
+__device__ __forceinline__ void split_f16f8(const float (&x)[4], uint32_t (&h16)[2], uint32_t& first,
+                                            uint32_t& second) {
+  h16[0] = pack_f16x2(x[0], x[1]);
+  h16[1] = pack_f16x2(x[2], x[3]);
+  float r[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const f16x2 h = __builtin_bit_cast(f16x2, h16[e >> 1]);
+    r[e] = x[e] - (float)h[e & 1];
+  }
+  if (kESide) {
+    first = pack_fp8x4(r[0] * 64.0f, r[1] * 64.0f, r[2] * 64.0f, r[3] * 64.0f);
+    second = pack_fp8x4(x[0] * 0.03125f, x[1] * 0.03125f, x[2] * 0.03125f, x[3] * 0.03125f);
+  } else {
+    first = pack_fp8x4(x[0] * 0.015625f, x[1] * 0.015625f, x[2] * 0.015625f, x[3] * 0.015625f);
+    second = pack_fp8x4(r[0] * 32.0f, r[1] * 32.0f, r[2] * 32.0f, r[3] * 32.0f);
+  }
+}
 
 __device__ __forceinline__ float rescale_factor(float m_old, float m_new, float c) {
   return (m_old == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_old - m_new) * c);
@@ -120,12 +177,13 @@ constexpr int kStatsThreadsWG = 64 * kStatsRows * kStatsWavesPerRow;
 // 16 kb0 + 4 (256 c + L): every load instruction of the row reads 1 KB of
 // consecutive logits, and lanes 4k .. 4k + 3 hold one k-block.  The logits
 // are read from HBM once and kept in registers: the split maximum is reduced
-// first, then the same registers give exp(l - m_s), the sums and the bf16
-// hi/lo p images.  Each round's image slots are staged in LDS as
+// first, then the same registers give exp(l - m_s), the sums and the p
+// image records (kF16: fp16 + fp8, else bf16 hi / lo).  Each round's image
+// slots are staged in LDS as
 // [k-block][2 rows][64 B] and leave as 1 KB per store instruction (8 k-blocks'
 // 128-byte lines; staging through LDS measured faster than storing from the
 // registers, and whole lines measured faster than one row's 64-byte halves).
-template <bool kAligned>
+template <bool kAligned, bool kF16>
 __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __restrict__ logits,
                                                               const dg_ctrl* __restrict__ ctrl,
                                                               StatsPartial* __restrict__ part,
@@ -212,7 +270,7 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
     m = acc.m; bid = acc.best_id; gbest = acc.gscore; gid = acc.gid; bad = acc.bad;
   }
 
-  // exp(l - m_s), its sums, the bf16 hi/lo image rows, round by round
+  // exp(l - m_s), its sums, the p image records, round by round
   const float mc = (m == -INFINITY) ? 0.0f : -m * kLog2e;
   float s1 = 0.f, st = 0.f, sy = 0.f;
 #pragma unroll
@@ -234,13 +292,22 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
           if (want_h) sy += et * y;
         }
       }
-      uint32_t hi[2], lo[2];
-      split2(pp[0], pp[1], hi[0], lo[0]);
-      split2(pp[2], pp[3], hi[1], lo[1]);
       // k-block 64 q + L / 4 of the round, ids 4 (L % 4) .. 4 (L % 4) + 3 of it
-      uint8_t* dst = stage + ((kStatsLanes / 4 * q + L / 4) * kStatsRows + r) * kImgRow + (L % 4) * 8;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(hi[0], hi[1]);
-      *reinterpret_cast<uint2*>(dst + 32) = make_uint2(lo[0], lo[1]);
+      uint8_t* slot = stage + ((kStatsLanes / 4 * q + L / 4) * kStatsRows + r) * kImgRow;
+      if constexpr (kF16) {
+        const float P[4] = {pp[0] * kPScale, pp[1] * kPScale, pp[2] * kPScale, pp[3] * kPScale};
+        uint32_t h16[2], c8, e8;
+        split_f16f8<false>(P, h16, c8, e8);
+        *reinterpret_cast<uint2*>(slot + (L % 4) * 8) = make_uint2(h16[0], h16[1]);
+        *reinterpret_cast<uint32_t*>(slot + 32 + (L % 4) * 4) = c8;
+        *reinterpret_cast<uint32_t*>(slot + 48 + (L % 4) * 4) = e8;
+      } else {
+        uint32_t hi[2], lo[2];
+        split2(pp[0], pp[1], hi[0], lo[0]);
+        split2(pp[2], pp[3], hi[1], lo[1]);
+        *reinterpret_cast<uint2*>(slot + (L % 4) * 8) = make_uint2(hi[0], hi[1]);
+        *reinterpret_cast<uint2*>(slot + 32 + (L % 4) * 8) = make_uint2(lo[0], lo[1]);
+      }
     }
     __syncthreads();
     // write-out: the row slots of k-block kbl are contiguous; thread T moves
@@ -275,32 +342,99 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
 }
 
 // ---------------------------------------------------------------------------
-// E packing: the embedding table as bf16 hi/lo k-block images, columns padded
-// to a multiple of 256 (zeros), ids padded to a multiple of 16 (zeros).
+// E packing: the embedding table as fp16 + fp8 k-block records (E side of the
+// layout above), columns padded to a multiple of 256 (zeros), ids padded to a
+// multiple of 16 (zeros).  After the image: kAmaxParts partial maxima of |E|
+// (working space of the pack) and the PackTail record.
 // ---------------------------------------------------------------------------
+constexpr int kAmaxParts = 1024;
+struct PackTail {
+  float zscale;    // 2^-(14 + c): undoes P = p 2^14 and Q = E 2^c in the combine
+  int32_t c;       // the table's exponent shift
+};
+constexpr size_t kPackTailBytes = 256;
+
+__device__ __forceinline__ float block_max256(float m, float* red) {
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Partial maxima of |E| over a grid-stride sweep (NaN entries are skipped;
+// they reach z through the records all the same).
+__global__ __launch_bounds__(256) void emb_amax_kernel(const float* __restrict__ emb, size_t n,
+                                                       float* __restrict__ part) {
+  __shared__ float red[4];
+  const size_t stride = (size_t)gridDim.x * 256;
+  float m = 0.0f;
+  if ((reinterpret_cast<uintptr_t>(emb) & 15) == 0) {
+    const f32x4* e4 = reinterpret_cast<const f32x4*>(emb);
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n / 4; i += stride) {
+      const f32x4 v = e4[i];
+      m = fmaxf(fmaxf(m, fmaxf(fabsf(v[0]), fabsf(v[1]))), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    }
+    for (size_t i = n / 4 * 4 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+      m = fmaxf(m, fabsf(emb[i]));
+  } else {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) m = fmaxf(m, fabsf(emb[i]));
+  }
+  m = block_max256(m, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = m;
+}
+
+// c = 13 - e for max|E| in [2^(e-1), 2^e), so max|Q| lies in [2^12, 2^13);
+// capped at 80 so that the combine's weight 2^-(14 + c) / S (S <= 2^31) stays
+// a normal float (tables with max|E| < 2^-67 keep fewer fp16 bits).  A zero or
+// non-finite maximum leaves the table unscaled.
+__global__ __launch_bounds__(256) void emb_scale_kernel(const float* __restrict__ part,
+                                                        PackTail* __restrict__ tail) {
+  __shared__ float red[4];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < kAmaxParts; i += 256) m = fmaxf(m, part[i]);
+  m = block_max256(m, red);
+  if (threadIdx.x == 0) {
+    int c = 0;
+    if (m > 0.0f && m <= 3.4028234663852886e38f) {
+      int e;
+      (void)frexpf(m, &e);
+      c = min(13 - e, 80);
+    }
+    tail->c = c;
+    tail->zscale = ldexpf(1.0f, -(14 + c));
+  }
+}
+
 __global__ __launch_bounds__(256) void emb_pack_kernel(const float* __restrict__ emb,
                                                        uint8_t* __restrict__ out, int vocab, int d,
-                                                       int col_pad) {
+                                                       int col_pad, const PackTail* __restrict__ tail) {
   const int col = blockIdx.x * 256 + threadIdx.x;
   const int kb = blockIdx.y;
-  float v[16];
+  const float sc = ldexpf(1.0f, tail->c);
+  uint32_t h16[8], qe8[4], q8[4];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int k = kb * kKB + e;
-    v[e] = (k < vocab && col < d) ? emb[(size_t)k * d + col] : 0.0f;
+  for (int g = 0; g < 4; ++g) {
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = kb * kKB + 4 * g + e;
+      x[e] = (k < vocab && col < d) ? emb[(size_t)k * d + col] * sc : 0.0f;
+    }
+    uint32_t h[2];
+    split_f16f8<true>(x, h, qe8[g], q8[g]);
+    h16[2 * g] = h[0];
+    h16[2 * g + 1] = h[1];
   }
-  uint32_t hi[8], lo[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) split2(v[2 * e], v[2 * e + 1], hi[e], lo[e]);
   uint8_t* dst = out + ((size_t)kb * col_pad + col) * kImgRow;
-  *reinterpret_cast<u32x4*>(dst) = (u32x4){hi[0], hi[1], hi[2], hi[3]};
-  *reinterpret_cast<u32x4*>(dst + 16) = (u32x4){hi[4], hi[5], hi[6], hi[7]};
-  *reinterpret_cast<u32x4*>(dst + 32) = (u32x4){lo[0], lo[1], lo[2], lo[3]};
-  *reinterpret_cast<u32x4*>(dst + 48) = (u32x4){lo[4], lo[5], lo[6], lo[7]};
+  *reinterpret_cast<u32x4*>(dst) = (u32x4){h16[0], h16[1], h16[2], h16[3]};
+  *reinterpret_cast<u32x4*>(dst + 16) = (u32x4){h16[4], h16[5], h16[6], h16[7]};
+  *reinterpret_cast<u32x4*>(dst + 32) = (u32x4){qe8[0], qe8[1], qe8[2], qe8[3]};
+  *reinterpret_cast<u32x4*>(dst + 48) = (u32x4){q8[0], q8[1], q8[2], q8[3]};
 }
 
 // ---------------------------------------------------------------------------
-// z_s = p · E over one split, bf16x3 on MFMA.  A four-stage LDS pipeline fed
+// z_s = p · E over one split on MFMA (fp16 + fp8 on the packed table, bf16x3
+// on the float32 table).  A four-stage LDS pipeline fed
 // by direct global-to-LDS loads: no staging registers and no LDS store
 // instructions; the fragments of the next step are read while the MFMAs of
 // the current one run.
@@ -421,6 +555,94 @@ __device__ __forceinline__ void gemm_mma(const Frags& f, f32x16 (&acc)[4][2]) {
     }
 }
 
+// fp16 + fp8 operands.  The fp16 fragments of one k step are the first two
+// chunks of the slots (ids 8h .. 8h + 7 for lane half h, as in the bf16 case).
+// The fp8 corrections of k-blocks s and s + 1 feed one 32 x 32 x 64 MFMA: lane
+// half h supplies the 32 correction bytes (chunks 2 and 3) of k-block s + h,
+// read from that k-block's stage, and A and B pair byte for byte.
+struct Frags16 {
+  f16x8 a[4], b[2];
+};
+struct Frags8 {
+  i32x8 a[4], b[2];
+};
+
+__device__ __forceinline__ void gemm_frags16(Frags16& f, const uint8_t* stage, int wm, int wn, int lane) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.a[i] = *reinterpret_cast<const f16x8*>(stage + swz_off(128 * wm + 32 * i + (lane & 31), h));
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    f.b[i] = *reinterpret_cast<const f16x8*>(stage + kArr + swz_off(64 * wn + 32 * i + (lane & 31), h));
+}
+
+__device__ __forceinline__ i32x8 frag8_at(const uint8_t* stage, int row) {
+  const u32x4 x = *reinterpret_cast<const u32x4*>(stage + swz_off(row, 2));
+  const u32x4 y = *reinterpret_cast<const u32x4*>(stage + swz_off(row, 3));
+  return (i32x8){(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+}
+
+// stage_h: this lane's stage (that of k-block s + lane / 32).  kLone: k-block
+// s is the split's last and has no partner, so lane half 1 contributes zero.
+template <bool kLone>
+__device__ __forceinline__ void gemm_frags8(Frags8& f, const uint8_t* stage_h, int wm, int wn, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = frag8_at(stage_h, 128 * wm + 32 * i + (lane & 31));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    f.b[i] = frag8_at(stage_h + kArr, 64 * wn + 32 * i + (lane & 31));
+    if (kLone && lane >= 32) f.b[i] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
+  }
+}
+
+__device__ __forceinline__ void gemm_mma16(const Frags16& f, f32x16 (&acc)[4][2]) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[mb], f.b[nb], acc[mb][nb], 0, 0, 0);
+}
+
+// e4m3 x e4m3 (format selectors 0), no block scales
+__device__ __forceinline__ void gemm_mma8(const Frags8& f, f32x16 (&acc)[4][2]) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[mb], f.b[nb], acc[mb][nb], 0, 0, 0, 0,
+                                                                    0, 0);
+}
+
+// One iteration of the fp16 + fp8 pipeline (same staging as gemm_iter).  Steps
+// come in pairs: the first (kRead8) also reads the pair's fp8 fragments, the
+// second (kMma8) also issues the pair's fp8 MFMAs.
+template <bool kRead8, bool kMma8, bool kLone>
+__device__ __forceinline__ void gemm_iter16(int s, uint8_t* smem, Frags16& cur, Frags16& nxt, Frags8& f8,
+                                            f32x16 (&acc)[4][2], const uint8_t* __restrict__ pimg,
+                                            const EOperand& eo, int kb0, int kb_last, int n_kb, int col_pad,
+                                            int col0, const uint32_t (&voff)[2], const uint32_t (&poff)[2],
+                                            int wave, int wm, int wn, int lane) {
+  // the MFMAs touch no memory: keep the scheduler from moving them across the
+  // workgroup barrier into the next iteration
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt_lgkm0<kDmaPerStep>();
+  raw_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  gemm_dma<false>(smem + ((s + kDist) % kStages) * kStage, pimg, eo, min(kb0 + s + kDist, kb_last), n_kb, col_pad,
+                  col0, voff, poff, wave);
+  gemm_frags16(nxt, smem + ((s + 1) % kStages) * kStage, wm, wn, lane);
+  if (kRead8) gemm_frags8<kLone>(f8, smem + ((s + (lane >> 5)) % kStages) * kStage, wm, wn, lane);
+  gemm_mma16(cur, acc);
+  if (kMma8) gemm_mma8(f8, acc);
+  __builtin_amdgcn_sched_group_barrier(0x100, kRead8 ? 18 : 6, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, kMma8 ? 4 : 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+}
+
 // Iteration s of the pipeline: step s+1 has landed in LDS (waited before the
 // barrier), step s+kDist is sent to the stage step s-1 used (kDma), the MFMAs
 // consume the fragments of step s (read during iteration s-1) while the
@@ -513,23 +735,43 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
 #pragma unroll
   for (int k = 0; k < kDist; ++k)
     gemm_dma<kF32E>(smem + k * kStage, pimg, eo, min(kb0 + k, kb_last), n_kb, col_pad, col0, voff, poff, wave);
-  Frags fa, fb;
   wait_vmcnt<(kDist - 1) * kDmaPerStep>();
   raw_barrier();
-  gemm_frags<kF32E>(fa, smem, wm, wn, lane);
 
+  // every iteration sends a DMA step and reads the next step's fragments (the
+  // last ones read data that is never used)
+  if constexpr (kF32E) {
+    Frags fa, fb;
+    gemm_frags<kF32E>(fa, smem, wm, wn, lane);
 #define DG_ITER(S, C, N) \
   gemm_iter<1, true, true, kF32E>(S, smem, C, N, acc, pimg, eo, kb0, kb_last, n_kb, col_pad, col0, voff, poff, \
                                   wave, wm, wn, lane)
-  // every iteration sends a DMA step and reads the next step's fragments (the
-  // last ones read data that is never used)
-  int s = 0;
-  for (; s + 1 < nsteps; s += 2) {
-    DG_ITER(s, fa, fb);
-    DG_ITER(s + 1, fb, fa);
-  }
-  if (s < nsteps) DG_ITER(s, fa, fb);
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+      DG_ITER(s, fa, fb);
+      DG_ITER(s + 1, fb, fa);
+    }
+    if (s < nsteps) DG_ITER(s, fa, fb);
 #undef DG_ITER
+  } else {
+    Frags16 ga, gb;
+    Frags8 g8;
+    gemm_frags16(ga, smem, wm, wn, lane);
+#define DG_ITER16(R, M, L, S, C, N)                                                                              \
+  gemm_iter16<R, M, L>(S, smem, C, N, g8, acc, pimg, eo, kb0, kb_last, n_kb, col_pad, col0, voff, poff, wave, wm, \
+                       wn, lane)
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+      DG_ITER16(true, false, false, s, ga, gb);
+      DG_ITER16(false, true, false, s + 1, gb, ga);
+    }
+    if (s < nsteps) {
+      // the split's last k-block has no partner: its corrections go alone
+      DG_ITER16(true, false, true, s, ga, gb);
+      gemm_mma8(g8, acc);
+    }
+#undef DG_ITER16
+  }
   wait_vmcnt<0>();
 
   // epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block, column lane%32
@@ -561,7 +803,7 @@ __global__ __launch_bounds__(256) void samp_combine(const float* __restrict__ lo
                                                     uint8_t* __restrict__ committed,
                                                     float* __restrict__ z, float* __restrict__ conf,
                                                     int n_rows, int n_canvas, int vocab, int d,
-                                                    EbRows eb) {
+                                                    EbRows eb, const PackTail* __restrict__ tail) {
   const int row = blockIdx.y;
   __shared__ float s_w[kMaxSamplerSplits];
   __shared__ uint32_t s_bad;
@@ -583,7 +825,8 @@ __global__ __launch_bounds__(256) void samp_combine(const float* __restrict__ lo
       merge_partial(r, q, c_t);
     }
     const bool bad = r.bad || !(r.m > -INFINITY);
-    const float inv_s1 = 1.0f / r.s1;
+    // z_s of the fp16 + fp8 contraction is in units of 2^(14 + c)
+    const float inv_s1 = (1.0f / r.s1) * (tail ? tail->zscale : 1.0f);
     for (int sp = threadIdx.x; sp < n_splits; sp += kWave)
       s_w[sp] = rescale_factor(pr[sp].m, r.m, kLog2e) * inv_s1;
     if (threadIdx.x == 0) {
@@ -1350,20 +1593,40 @@ __global__ __launch_bounds__(256) void topk_z(const TopkItem* __restrict__ list,
 }
 
 // ---------------------------------------------------------------------------
-size_t embedding_packed_bytes(int vocab, int d) {
+static size_t embedding_image_bytes(int vocab, int d) {
   const size_t n_kb = (size_t)(vocab + kKB - 1) / kKB;
   const size_t col_pad = (size_t)(d + kGN - 1) / kGN * kGN;
-  return n_kb * col_pad * kImgRow;
+  return n_kb * col_pad * kImgRow;   // a multiple of 16 KB
+}
+
+size_t embedding_packed_bytes(int vocab, int d) {
+  return embedding_image_bytes(vocab, d) + kAmaxParts * sizeof(float) + kPackTailBytes;
+}
+
+static const PackTail* pack_tail(const void* packed, int vocab, int d) {
+  return reinterpret_cast<const PackTail*>(static_cast<const uint8_t*>(packed) + embedding_image_bytes(vocab, d) +
+                                           kAmaxParts * sizeof(float));
 }
 
 hipError_t launch_embedding_pack(const float* emb, void* packed, int vocab, int d, hipStream_t s) {
   const int n_kb = (vocab + kKB - 1) / kKB;
   const int col_pad = (d + kGN - 1) / kGN * kGN;
+  uint8_t* base = static_cast<uint8_t*>(packed);
+  float* part = reinterpret_cast<float*>(base + embedding_image_bytes(vocab, d));
+  PackTail* tail = const_cast<PackTail*>(pack_tail(packed, vocab, d));
   prof_begin("emb_pack", s);
-  emb_pack_kernel<<<dim3(col_pad / 256, n_kb), 256, 0, s>>>(emb, static_cast<uint8_t*>(packed), vocab,
-                                                            d, col_pad);
+  emb_amax_kernel<<<kAmaxParts, 256, 0, s>>>(emb, (size_t)vocab * (size_t)d, part);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) {
+    emb_scale_kernel<<<1, 256, 0, s>>>(part, tail);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    emb_pack_kernel<<<dim3(col_pad / 256, n_kb), 256, 0, s>>>(emb, base, vocab, d, col_pad, tail);
+    e = hipGetLastError();
+  }
   prof_end(s);
-  return hipGetLastError();
+  return e;
 }
 
 SamplerPlan sampler_plan(int n_canvas, int batch, int vocab, int d) {
@@ -1408,12 +1671,17 @@ hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void*
 
   prof_begin("samp_stats", s);
   const dim3 sgrid(p.n_splits, (p.n + kStatsRows - 1) / kStatsRows);
-  if (aligned)
-    samp_stats<true><<<sgrid, kStatsThreadsWG, 0, s>>>(logits, ctrl, part, pimg, p.n, p.n_canvas, p.vocab,
-                                                       p.kb_per_split, p.n_kb, eb.on);
-  else
-    samp_stats<false><<<sgrid, kStatsThreadsWG, 0, s>>>(logits, ctrl, part, pimg, p.n, p.n_canvas, p.vocab,
-                                                        p.kb_per_split, p.n_kb, eb.on);
+#define DG_STATS(A, F)                                                                                  \
+  samp_stats<A, F><<<sgrid, kStatsThreadsWG, 0, s>>>(logits, ctrl, part, pimg, p.n, p.n_canvas, p.vocab, \
+                                                     p.kb_per_split, p.n_kb, eb.on)
+  if (eb.emb_f32) {
+    if (aligned) DG_STATS(true, false);
+    else DG_STATS(false, false);
+  } else {
+    if (aligned) DG_STATS(true, true);
+    else DG_STATS(false, true);
+  }
+#undef DG_STATS
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1432,9 +1700,9 @@ hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void*
   if (e != hipSuccess) return e;
 
   prof_begin("samp_combine", s);
-  samp_combine<<<dim3((p.d + 1023) / 1024, p.n), 256, 0, s>>>(logits, part, p.n_splits, zp, ctrl, ids,
-                                                              committed, z, conf, p.n, p.n_canvas,
-                                                              p.vocab, p.d, rows);
+  samp_combine<<<dim3((p.d + 1023) / 1024, p.n), 256, 0, s>>>(
+      logits, part, p.n_splits, zp, ctrl, ids, committed, z, conf, p.n, p.n_canvas, p.vocab, p.d, rows,
+      eb.emb_f32 ? nullptr : pack_tail(emb_packed, p.vocab, p.d));
   prof_end(s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1501,7 +1769,7 @@ hipError_t launch_sampler_topk(const TopkPlan& p, const float* logits, const flo
   if (e != hipSuccess) return e;
   prof_begin("samp_combine", s);
   samp_combine<<<dim3((p.d + 1023) / 1024, p.n), 256, 0, s>>>(logits, part, 1, zp, ctrl, ids, committed, z, conf,
-                                                              p.n, p.n_canvas, p.vocab, p.d, rows);
+                                                              p.n, p.n_canvas, p.vocab, p.d, rows, nullptr);
   prof_end(s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

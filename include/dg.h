@@ -217,15 +217,21 @@ size_t dg_sampler_workspace_bytes(int n_canvas, int vocab, int d_model);
 
 /*
  * The embedding table E in the layout the sampler streams.  The contraction
- * z = softmax(logits)·E runs on bf16 matrix cores in split precision
- * (E = E_hi + E_lo, both bf16, E_hi = round(E), E_lo = round(E - E_hi)), so E is
- * converted once, when the weights are loaded, rather than on every step:
+ * z = softmax(logits)·E runs on fp16 and fp8 matrix cores in split precision:
+ * with Q = E·2^c (c chosen so that max|Q| lies in [2^12, 2^13)), each element
+ * is held as Q16 = fp16(Q) plus two e4m3 bytes, fp8((Q - Q16)·2^6) and
+ * fp8(Q·2^-5), so E is converted once, when the weights are loaded, rather
+ * than on every step:
  *   emb        [vocab, d_model] float32 (input)
  *   packed     dg_embedding_packed_bytes(vocab, d_model) bytes (output): for
  *              each block of 16 ids and each column (d_model rounded up to a
- *              multiple of 256, zero padded), 16 bf16 E_hi then 16 bf16 E_lo;
- *              ids past vocab are zero.
- * The caller owns both buffers.  Asynchronous on `stream`.
+ *              multiple of 256, zero padded), a 64-byte record: 16 fp16 Q16,
+ *              16 bytes fp8((Q - Q16)·2^6), 16 bytes fp8(Q·2^-5); ids past
+ *              vocab are zero.  Then 4096 bytes the pack uses as working space
+ *              and a 256-byte record: float 2^-(14 + c), int32 c.
+ * A zero or non-finite max|E| gives c = 0; c is at most 80 (tables with
+ * max|E| below 2^-67 keep fewer bits).  The caller owns both buffers.
+ * Asynchronous on `stream`.
  */
 size_t dg_embedding_packed_bytes(int vocab, int d_model);
 int dg_embedding_pack(const float* emb, void* packed, int vocab, int d_model, hipStream_t stream);
@@ -260,9 +266,11 @@ int dg_sampler_step(const float* logits, const void* emb_packed, int32_t* canvas
  * dg_sampler_step on the plain float32 embedding table instead of the packed
  * image:
  *   emb             [vocab, d_model] float32, row-major, 16-byte aligned
- * The contraction splits each element of E into its bf16 hi / lo pair while it
- * streams (the same split dg_embedding_pack makes), so z equals
- * dg_sampler_step's z bit for bit.  d_model must be a multiple of 4
+ * The contraction splits each element of E into a bf16 pair (E_hi = bf16(E),
+ * E_lo = bf16(E - E_hi)) while it streams and sums p_hi E_hi + p_hi E_lo +
+ * p_lo E_hi.  Ids, commit mask, confidence, counts and ctrl equal
+ * dg_sampler_step's bit for bit (they come from the same statistics pass); z
+ * meets the same bound by another rounding.  d_model must be a multiple of 4
  * (DG_EUNSUPPORTED otherwise).  Other arguments, workspace
  * (dg_sampler_workspace_bytes) and errors as dg_sampler_step.
  */
