@@ -217,6 +217,9 @@ def main():
     if probes:
         roofline["secondary"] = {"measured_peak": probes["copy_gbs"], "unit": "GB/s",
                                  "frac": round(gbs / probes["copy_gbs"], 4),
+                                 # the contraction's bytes are almost all reads
+                                 "measured_read_peak": probes["read_gbs"],
+                                 "frac_of_read": round(gbs / probes["read_gbs"], 4),
                                  # the probe measures bf16; fp16 runs at that rate, fp8 at twice it
                                  "split_mfma_frac": round((flops_fp16 + flops_fp8 / 2) / (gemm_us * 1e-6) / 1e12
                                                           / probes["mfma_tflops"], 4)}
@@ -493,8 +496,8 @@ def bf16_attention_timing(torch, dg, T, n, p, hq, hkv, hd, steps, n_sets=16):
 
 def peak_probes(torch, dg, copy_mib):
     """Measured peaks on this machine: a plain copy (bytes read + written per
-    second) and the matrix-core loop probe (bf16 flops per second), each timed
-    with events over several launches after a warm-up."""
+    second), a plain read, and the matrix-core loop probe (bf16 flops per
+    second), each timed with events over several launches after a warm-up."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     src = torch.ones(copy_mib << 18, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -509,7 +512,22 @@ def peak_probes(torch, dg, copy_mib):
     torch.cuda.synchronize()
     copy_ms = e0.elapsed_time(e1) / reps
     copy_gbs = 2.0 * (copy_mib << 20) / (copy_ms * 1e-3) / 1e9
-    del src, dst
+    del dst
+    # a plain read of 4x the copy's buffer (more than the 256 MB last-level cache)
+    big = torch.empty(4 * (copy_mib << 18), dtype=torch.float32, device="cuda")
+    big.fill_(1.0)
+    sink = dg.dg_probe_read(big)
+    for _ in range(2):
+        dg.dg_probe_read(big, sink)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dg.dg_probe_read(big, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    read_ms = e0.elapsed_time(e1) / reps
+    read_gbs = 4.0 * (copy_mib << 20) / (read_ms * 1e-3) / 1e9
+    del src, big, sink
     for _ in range(2):
         dg.dg_probe_mfma_bf16()
     torch.cuda.synchronize()
@@ -520,8 +538,9 @@ def peak_probes(torch, dg, copy_mib):
     e1.record()
     torch.cuda.synchronize()
     mfma_tflops = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
-    log(f"probes: copy {copy_gbs:.0f} GB/s, matrix cores {mfma_tflops:.0f} TFLOP/s (bf16)")
+    log(f"probes: copy {copy_gbs:.0f} GB/s, read {read_gbs:.0f} GB/s, matrix cores {mfma_tflops:.0f} TFLOP/s (bf16)")
     return {"copy_gbs": round(copy_gbs, 1), "copy_mib_each_way": copy_mib, "copy_ms": round(copy_ms, 4),
+            "read_gbs": round(read_gbs, 1), "read_mib": 4 * copy_mib, "read_ms": round(read_ms, 4),
             "mfma_tflops": round(mfma_tflops, 1),
             "mfma_probe": "1024 workgroups x 4 waves x 2048 iterations x 4 independent 32x32x16 bf16 MFMA chains"}
 

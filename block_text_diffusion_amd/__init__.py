@@ -20,7 +20,7 @@ __all__ = [
     "StepGraphFP8", "dg_canvas_init",
     "dg_kv_append", "dg_synth_logits", "dg_philox_fill", "dg_attention_workspace_bytes",
     "dg_sampler_workspace_bytes", "dg_denoise_workspace_bytes", "dg_profile_enable",
-    "dg_profile_read", "dg_probe_mfma_bf16", "dg_probe_copy", "make_ctrl", "read_ctrl", "write_ctrl", "DG_GUMBEL", "DG_COMMIT_ONLY",
+    "dg_profile_read", "dg_probe_mfma_bf16", "dg_probe_copy", "dg_probe_read", "make_ctrl", "read_ctrl", "write_ctrl", "DG_GUMBEL", "DG_COMMIT_ONLY",
     "DG_AUTO_ADVANCE", "DG_T_SCHEDULE", "DG_ATTN_CAUSAL", "DG_F32", "DG_BF16", "DG_FP8_E4M3", "DgError", "load",
 ]
 
@@ -633,6 +633,21 @@ def dg_probe_copy(dst, src, stream=None):
     if dst.numel() * dst.element_size() != src.numel() * src.element_size():
         raise ValueError("probe_copy: dst and src must have the same byte size")
     check(load().dg_probe_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(), _stream(stream)))
+
+
+PROBE_READ_SINK_WORDS = 16384
+
+
+def dg_probe_read(src, sink=None, stream=None):
+    """Read src (a GPU tensor, 16-byte aligned, byte size a multiple of 16) with
+    the plain read probe; sink: int32 GPU tensor of PROBE_READ_SINK_WORDS (made
+    here if not given)."""
+    if sink is None:
+        sink = _torch().empty(PROBE_READ_SINK_WORDS, dtype=_torch().int32, device="cuda")
+    if sink.numel() * sink.element_size() < 4 * PROBE_READ_SINK_WORDS:
+        raise ValueError("probe_read: sink must hold 16384 uint32 words")
+    check(load().dg_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)))
+    return sink
 
 
 # ---- profiling ----

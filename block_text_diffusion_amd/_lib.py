@@ -116,6 +116,7 @@ SIGNATURES = {
                             ctypes.c_uint32, _vp]),
     "dg_probe_mfma_bf16": (_i, [_vp, _i, _i, _vp]),
     "dg_probe_copy": (_i, [_vp, _vp, _sz, _vp]),
+    "dg_probe_read": (_i, [_vp, _sz, _vp, _vp]),
     "dg_profile_enable": (_i, [_i]),
     "dg_profile_read": (_i, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                              ctypes.POINTER(ctypes.c_int), _i]),

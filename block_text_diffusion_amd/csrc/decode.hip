@@ -121,6 +121,35 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(u32x4* __restrict__ dst
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// HBM: a plain read, 16 bytes per lane per load, four loads in flight per
+// lane, grid-stride.  Each wave writes the xor of everything it read, so no
+// load is dead.
+constexpr int kProbeReadBlocks = 4096;
+__global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                         uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4 acc = (u32x4){0u, 0u, 0u, 0u};
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) acc ^= src[i];
+  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = x;
+}
+
+hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > kProbeReadBlocks) blocks = kProbeReadBlocks;
+  probe_read_kernel<<<(unsigned)blocks, 256, 0, s>>>(static_cast<const u32x4*>(src), n16, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_probe_mfma(float* sink, int n_wg, int iters, hipStream_t s) {
   probe_mfma_kernel<<<n_wg, 64 * kProbeWaves, 0, s>>>(sink, iters);
   return hipGetLastError();

@@ -728,6 +728,15 @@ int dg_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) 
   return DG_OK;
 }
 
+int dg_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink) return fail(DG_EINVAL, "probe_read: null pointer");
+  if (bytes % 16 != 0) return fail(DG_EINVAL, "probe_read: bytes must be a multiple of 16");
+  if (!aligned16(src)) return fail(DG_EINVAL, "probe_read: src must be 16-byte aligned");
+  hipError_t e = dg::launch_probe_read(src, bytes, sink, stream);
+  if (e != hipSuccess) return hip_fail(e, "probe_read launch");
+  return DG_OK;
+}
+
 int dg_profile_enable(int on) {
   g_prof_on = on != 0;
   return DG_OK;

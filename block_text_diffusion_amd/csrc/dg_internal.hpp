@@ -109,6 +109,7 @@ hipError_t launch_synth_logits(float* logits, const int32_t* ids, const uint8_t*
                                int vocab, hipStream_t s);
 hipError_t launch_probe_mfma(float* sink, int n_wg, int iters, hipStream_t s);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_philox_fill(uint32_t* out, size_t n_words, uint64_t seed, uint32_t c1,
                               uint32_t c2, uint32_t c3, hipStream_t s);
 

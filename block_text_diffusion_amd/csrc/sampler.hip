@@ -26,18 +26,19 @@
 //   samp_finalize  count open positions; advance the step counters.
 //
 // fp16 + fp8 split precision.  With P = p 2^14 (p <= 1) and Q = E 2^c, where
-// c puts max|Q| in [2^12, 2^13), P16 = fp16(P), Pe = P - P16, Q16 = fp16(Q),
+// c puts max|Q| in [2^7, 2^8), P16 = fp16(P), Pe = P - P16, Q16 = fp16(Q),
 // Qe = Q - Q16, the contraction sums
-//     P16 Q16  +  fp8(P 2^-6) fp8(Qe 2^6)  +  fp8(Pe 2^5) fp8(Q 2^-5)
+//     P16 Q16  +  2^-5 [ fp8(P 2^-6) fp8(Qe 2^11)  +  fp8(Pe 2^5) fp8(Q16) ]
 // = PQ + Pe Qe + (the fp8 roundings of the two correction terms).
 // fp16 x fp16 products are exact in fp32; the corrections are 2^-11 of a term
 // and carry fp8 (e4m3) relative error <= 2^-4, so each term is within about
-// 2^-14 of P Q.  The exponents are chosen so every fp8 operand is at most 256
-// (e4m3 holds 448) and the two correction terms need no scale factor: one
-// v_mfma_f32_32x32x16_f16 per 16 ids and one v_mfma_f32_32x32x64_f8f6f4 per
-// 32 ids (corrections of two k-blocks side by side in K), the work of two
-// bf16 products instead of bf16x3's three.  The combine multiplies by
-// 2^-(14 + c), which dg_embedding_pack stores after the image.
+// 2^-14 of P Q.  The exponents keep every fp8 operand at most 256 (e4m3 holds
+// 448).  The table stores Q16 and fp8(Qe 2^11), 3 bytes per element;
+// fp8(Q16) is formed in the contraction.  One v_mfma_f32_32x32x16_f16 per 16
+// ids and one v_mfma_scale_f32_32x32x64_f8f6f4 per 32 ids (corrections of two
+// k-blocks side by side in K, block scale 2^-5 on A): the work of two bf16
+// products instead of bf16x3's three.  The combine multiplies by 2^-(14 + c),
+// which dg_embedding_pack stores after the table.
 #include "dg_common.hpp"
 #include "dg_internal.hpp"
 
@@ -74,10 +75,12 @@ constexpr int kArr = kGM * kImgRow;    // 16 KB: one operand of one LDS stage
 constexpr int kStage = 2 * kArr;       // p tile + E tile
 constexpr int kStatsThreads = 256;
 
-// Record layouts of one 64-byte slot (16 ids of one row of p, or one column of E):
+// Record layouts of one 64-byte slot (16 ids of one row of p, or one column of E
+// in LDS):
 //   bf16x3:    bf16 hi of ids 0-15 | bf16 lo of ids 0-15
 //   fp16 + fp8 (p side):  fp16 P16 of ids 0-15 | fp8 P 2^-6 | fp8 Pe 2^5
-//   fp16 + fp8 (E side):  fp16 Q16 of ids 0-15 | fp8 Qe 2^6 | fp8 Q 2^-5
+//   fp16 + fp8 (E side, in LDS):  fp16 Q16 of ids 0-15 | fp8 Qe 2^11 of this
+//              k-block and of the next (even k-blocks only)
 constexpr float kPScale = 16384.0f;    // P = p 2^14
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -93,13 +96,9 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-// x = v 2^k (k = 14 for p, c for E) as fp16 x16 | fp8 first | fp8 second for
-// four ids: first = fp8(x 2^f1), second = fp8((x - fp16(x)) 2^e1) on the p
-// side (f1 = -6, e1 = 5); the E side swaps the two (fp8 of the residual
-// first, e1 = 6; then fp8(x 2^-5)).
-template <bool kESide>
-__device__ __forceinline__ void split_f16f8(const float (&x)[4], uint32_t (&h16)[2], uint32_t& first,
-                                            uint32_t& second) {
+// Four weights P = p 2^14 as fp16 P16 (two dwords), e4m3 of P 2^-6 and e4m3 of
+// (P - P16) 2^5 (one dword each, id order).
+__device__ __forceinline__ void split_p(const float (&x)[4], uint32_t (&h16)[2], uint32_t& p8, uint32_t& pe8) {
   h16[0] = pack_f16x2(x[0], x[1]);
   h16[1] = pack_f16x2(x[2], x[3]);
   float r[4];
@@ -108,13 +107,32 @@ __device__ __forceinline__ void split_f16f8(const float (&x)[4], uint32_t (&h16)
     const f16x2 h = __builtin_bit_cast(f16x2, h16[e >> 1]);
     r[e] = x[e] - (float)h[e & 1];
   }
-  if (kESide) {
-    first = pack_fp8x4(r[0] * 64.0f, r[1] * 64.0f, r[2] * 64.0f, r[3] * 64.0f);
-    second = pack_fp8x4(x[0] * 0.03125f, x[1] * 0.03125f, x[2] * 0.03125f, x[3] * 0.03125f);
-  } else {
-    first = pack_fp8x4(x[0] * 0.015625f, x[1] * 0.015625f, x[2] * 0.015625f, x[3] * 0.015625f);
-    second = pack_fp8x4(r[0] * 32.0f, r[1] * 32.0f, r[2] * 32.0f, r[3] * 32.0f);
+  p8 = pack_fp8x4(x[0] * 0.015625f, x[1] * 0.015625f, x[2] * 0.015625f, x[3] * 0.015625f);
+  pe8 = pack_fp8x4(r[0] * 32.0f, r[1] * 32.0f, r[2] * 32.0f, r[3] * 32.0f);
+}
+
+// Four table values Q as fp16 Q16 (two dwords) and e4m3 of (Q - Q16) 2^11.
+__device__ __forceinline__ void split_q(const float (&x)[4], uint32_t (&h16)[2], uint32_t& qe8) {
+  h16[0] = pack_f16x2(x[0], x[1]);
+  h16[1] = pack_f16x2(x[2], x[3]);
+  float r[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const f16x2 h = __builtin_bit_cast(f16x2, h16[e >> 1]);
+    r[e] = (x[e] - (float)h[e & 1]) * 2048.0f;
   }
+  qe8 = pack_fp8x4(r[0], r[1], r[2], r[3]);
+}
+
+// Four fp16 values (two dwords) to four e4m3 bytes, round to nearest even, no
+// scale (v_cvt_scalef32_pk_fp8_f16 with scale 1).
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f16x4_to_fp8(uint32_t lo, uint32_t hi) {
+  // the first conversion's upper word is overwritten by the second
+  i16x2 r = __builtin_bit_cast(i16x2, lo);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, __builtin_bit_cast(f16x2, lo), 1.0f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, __builtin_bit_cast(f16x2, hi), 1.0f, true);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ float rescale_factor(float m_old, float m_new, float c) {
@@ -297,7 +315,7 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
       if constexpr (kF16) {
         const float P[4] = {pp[0] * kPScale, pp[1] * kPScale, pp[2] * kPScale, pp[3] * kPScale};
         uint32_t h16[2], c8, e8;
-        split_f16f8<false>(P, h16, c8, e8);
+        split_p(P, h16, c8, e8);
         *reinterpret_cast<uint2*>(slot + (L % 4) * 8) = make_uint2(h16[0], h16[1]);
         *reinterpret_cast<uint32_t*>(slot + 32 + (L % 4) * 4) = c8;
         *reinterpret_cast<uint32_t*>(slot + 48 + (L % 4) * 4) = e8;
@@ -342,11 +360,18 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
 }
 
 // ---------------------------------------------------------------------------
-// E packing: the embedding table as fp16 + fp8 k-block records (E side of the
-// layout above), columns padded to a multiple of 256 (zeros), ids padded to a
-// multiple of 16 (zeros).  After the image: kAmaxParts partial maxima of |E|
-// (working space of the pack) and the PackTail record.
+// E packing: Q = E 2^c as fp16 Q16 plus e4m3 of (Q - Q16) 2^11.  Columns are
+// padded to whole 256-column tiles and ids to whole pairs of 16-id k-blocks
+// (zeros).  For each k-block pair j and column tile t, one 24 KB block at
+// ((j n_tiles + t) 24 KB): the Q16 records of k-block 2j (256 columns x 32 B:
+// ids 0-7, ids 8-15), those of k-block 2j + 1, then 256 columns x 32 B of
+// residual bytes (16 for k-block 2j, 16 for 2j + 1).  After the blocks:
+// kAmaxParts partial maxima of |E| (working space of the pack) and the
+// PackTail record.
 // ---------------------------------------------------------------------------
+constexpr int kEBlock = 24576;          // bytes per (k-block pair, column tile)
+constexpr int kEHalf = 8192;            // Q16 records of one k-block and tile
+constexpr int kEResid = 16384;          // offset of the residual bytes in a block
 constexpr int kAmaxParts = 1024;
 struct PackTail {
   float zscale;    // 2^-(14 + c): undoes P = p 2^14 and Q = E 2^c in the combine
@@ -383,9 +408,9 @@ __global__ __launch_bounds__(256) void emb_amax_kernel(const float* __restrict__
   if (threadIdx.x == 0) part[blockIdx.x] = m;
 }
 
-// c = 13 - e for max|E| in [2^(e-1), 2^e), so max|Q| lies in [2^12, 2^13);
-// capped at 80 so that the combine's weight 2^-(14 + c) / S (S <= 2^31) stays
-// a normal float (tables with max|E| < 2^-67 keep fewer fp16 bits).  A zero or
+// c = 8 - e for max|E| in [2^(e-1), 2^e), so max|Q| lies in [2^7, 2^8); capped
+// at 80 so that the combine's weight 2^-(14 + c) / S (S <= 2^31) stays a normal
+// float (tables with max|E| below 2^-72 keep fewer fp16 bits).  A zero or
 // non-finite maximum leaves the table unscaled.
 __global__ __launch_bounds__(256) void emb_scale_kernel(const float* __restrict__ part,
                                                         PackTail* __restrict__ tail) {
@@ -398,20 +423,22 @@ __global__ __launch_bounds__(256) void emb_scale_kernel(const float* __restrict_
     if (m > 0.0f && m <= 3.4028234663852886e38f) {
       int e;
       (void)frexpf(m, &e);
-      c = min(13 - e, 80);
+      c = min(8 - e, 80);
     }
     tail->c = c;
     tail->zscale = ldexpf(1.0f, -(14 + c));
   }
 }
 
+// grid (n_tiles, 2 n_pairs): one thread per column and k-block.
 __global__ __launch_bounds__(256) void emb_pack_kernel(const float* __restrict__ emb,
                                                        uint8_t* __restrict__ out, int vocab, int d,
-                                                       int col_pad, const PackTail* __restrict__ tail) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
+                                                       int n_tiles, const PackTail* __restrict__ tail) {
+  const int cl = threadIdx.x;                 // column within the tile
+  const int col = blockIdx.x * 256 + cl;
   const int kb = blockIdx.y;
   const float sc = ldexpf(1.0f, tail->c);
-  uint32_t h16[8], qe8[4], q8[4];
+  uint32_t h16[8], qe8[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     float x[4];
@@ -421,15 +448,15 @@ __global__ __launch_bounds__(256) void emb_pack_kernel(const float* __restrict__
       x[e] = (k < vocab && col < d) ? emb[(size_t)k * d + col] * sc : 0.0f;
     }
     uint32_t h[2];
-    split_f16f8<true>(x, h, qe8[g], q8[g]);
+    split_q(x, h, qe8[g]);
     h16[2 * g] = h[0];
     h16[2 * g + 1] = h[1];
   }
-  uint8_t* dst = out + ((size_t)kb * col_pad + col) * kImgRow;
-  *reinterpret_cast<u32x4*>(dst) = (u32x4){h16[0], h16[1], h16[2], h16[3]};
-  *reinterpret_cast<u32x4*>(dst + 16) = (u32x4){h16[4], h16[5], h16[6], h16[7]};
-  *reinterpret_cast<u32x4*>(dst + 32) = (u32x4){qe8[0], qe8[1], qe8[2], qe8[3]};
-  *reinterpret_cast<u32x4*>(dst + 48) = (u32x4){q8[0], q8[1], q8[2], q8[3]};
+  uint8_t* blk = out + ((size_t)(kb >> 1) * n_tiles + blockIdx.x) * kEBlock;
+  uint8_t* q = blk + (kb & 1) * kEHalf + cl * 32;
+  *reinterpret_cast<u32x4*>(q) = (u32x4){h16[0], h16[1], h16[2], h16[3]};
+  *reinterpret_cast<u32x4*>(q + 16) = (u32x4){h16[4], h16[5], h16[6], h16[7]};
+  *reinterpret_cast<u32x4*>(blk + kEResid + cl * 32 + (kb & 1) * 16) = (u32x4){qe8[0], qe8[1], qe8[2], qe8[3]};
 }
 
 // ---------------------------------------------------------------------------
@@ -440,15 +467,16 @@ __global__ __launch_bounds__(256) void emb_pack_kernel(const float* __restrict__
 // the current one run.
 // ---------------------------------------------------------------------------
 
-// LDS rows are 64 bytes (four 16-byte chunks: hi k0-7, hi k8-15, lo k0-7,
-// lo k8-15); the chunk index is xor-swizzled with row bits so a wavefront's
-// 16-byte reads of one chunk column spread over all banks.
+// LDS rows are 64 bytes (four 16-byte chunks: ids 0-7 and 8-15 of the fp16 or
+// bf16-hi values, then the two correction chunks); the chunk index is
+// xor-swizzled with row bits so a wavefront's 16-byte reads of one chunk
+// column spread over all banks.
 __device__ __forceinline__ int swz_off(int row, int chunk) {
   return row * 64 + ((chunk ^ (((row >> 1) ^ (row >> 2)) & 3)) << 4);
 }
 
-constexpr int kStages = 4;            // LDS stages of 32 KB
-constexpr int kDist = kStages - 1;     // DMA runs this many steps ahead
+constexpr int kStages = 4;            // LDS stages of 32 KB (float32-table path)
+constexpr int kDist = kStages - 1;     // DMA runs this many steps ahead (float32-table path; prologue of both)
 constexpr int kDmaPerStep = 4;         // LDS DMA instructions per wave per k step
 
 
@@ -456,25 +484,31 @@ constexpr int kDmaPerStep = 4;         // LDS DMA instructions per wave per k st
 // DMA one k step into an LDS stage: 16-byte buffer loads that write LDS
 // directly (lane i of an instruction lands at destination + 16 i).  Wave w
 // moves rows 32w..32w+31 of the p image and columns 32w..32w+31 of the E
-// image; lane i fetches the global chunk that belongs at its swizzled slot.
-// The E operand comes either as the packed image (the same [column][64 B]
-// form as the p images) or, with kF32E, as the plain float32 table [V, d]: then
-// wave w moves id rows 2w and 2w + 1 of the k-block, 1 KB each (the tile's 256
-// columns), into LDS rows of 1 KB; lane i fetches the 16-byte chunk i ^ f(row)
-// so id rows r and r + 8 sit 128 bytes apart in the banks.  Ids past the
-// vocabulary and columns past d read as zero (buffer range checks; d is a
-// multiple of 4).
+// tile; lane i fetches the global chunk that belongs at its swizzled slot.
+// The E operand comes either as the packed table, whose (k-block pair, tile)
+// blocks give each LDS column row its Q16 chunks (and, for an even k-block,
+// the residual bytes of the pair; an odd k-block's residual lanes point past
+// the block's range, so they load zeros and move no memory), or, with kF32E,
+// as the plain float32 table [V, d]: then wave w moves id rows 2w and 2w + 1
+// of the k-block, 1 KB each (the tile's 256 columns), into LDS rows of 1 KB;
+// lane i fetches the 16-byte chunk i ^ f(row) so id rows r and r + 8 sit 128
+// bytes apart in the banks.  Ids past the vocabulary and columns past d read
+// as zero (buffer range checks; d is a multiple of 4).
 struct EOperand {
-  const uint8_t* base;  // packed image, or float32 E
+  const uint8_t* base;  // packed table, or float32 E
   int d;                // row length of float32 E (elements)
   int vocab;
+  int n_tiles;          // column tiles of the packed table
 };
 
 __device__ __forceinline__ int e32_chunk(int row, int lane) { return lane ^ (row & 8); }
 
-template <bool kF32E>
+// kOdd (packed table): the step is an odd one of its split, whose k-block is
+// odd (splits start at even k-blocks).  Past a split's last k-block the clamped
+// block may have the other parity; such stages are never read.
+template <bool kF32E, bool kOdd = false>
 __device__ __forceinline__ void gemm_dma(uint8_t* stage, const uint8_t* __restrict__ pimg, const EOperand& eo,
-                                         int kb, int n_kb, int col_pad, int col0, const uint32_t (&voff)[2],
+                                         int kb, int n_kb, int col_pad, int col0, const uint32_t (&voff)[2][2],
                                          const uint32_t (&poff)[2], int wave) {
   const __amdgpu_buffer_rsrc_t ra = rsrc(pimg + (size_t)kb * kPImg, kPImg);
 #pragma unroll
@@ -487,10 +521,11 @@ __device__ __forceinline__ void gemm_dma(uint8_t* stage, const uint8_t* __restri
       const uint32_t valid = (id < eo.vocab && col0 < eo.d) ? (uint32_t)(eo.d - col0) * 4u : 0u;
       const __amdgpu_buffer_rsrc_t rb =
           rsrc(eo.base + ((size_t)min(id, eo.vocab - 1) * eo.d + col0) * 4, valid < 1024u ? valid : 1024u);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[0][j], 0, 0, 0);
     } else {
-      const __amdgpu_buffer_rsrc_t rb = rsrc(eo.base + ((size_t)kb * col_pad + col0) * kImgRow, kArr);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[j], 0, 0, 0);
+      const __amdgpu_buffer_rsrc_t rb =
+          rsrc(eo.base + ((size_t)(kb >> 1) * eo.n_tiles + col0 / kGN) * kEBlock, kEBlock);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[kOdd ? 1 : 0][j], 0, 0, 0);
     }
   }
 }
@@ -557,14 +592,14 @@ __device__ __forceinline__ void gemm_mma(const Frags& f, f32x16 (&acc)[4][2]) {
 
 // fp16 + fp8 operands.  The fp16 fragments of one k step are the first two
 // chunks of the slots (ids 8h .. 8h + 7 for lane half h, as in the bf16 case).
-// The fp8 corrections of k-blocks s and s + 1 feed one 32 x 32 x 64 MFMA: lane
-// half h supplies the 32 correction bytes (chunks 2 and 3) of k-block s + h,
-// read from that k-block's stage, and A and B pair byte for byte.
+// The fp8 corrections of k-blocks s and s + 1 (s even) feed one 32 x 32 x 64
+// MFMA per output block: lane half h supplies the 32 correction bytes of
+// k-block s + h, and A and B pair byte for byte: A = [fp8(P 2^-6) | fp8(Pe 2^5)]
+// (chunks 2 and 3 of the p slot, in k-block s + h's stage), B = [fp8(Qe 2^11) |
+// fp8(Q16)] (the residual chunk 2 + h in stage s, and Q16 of k-block s + h
+// converted).
 struct Frags16 {
   f16x8 a[4], b[2];
-};
-struct Frags8 {
-  i32x8 a[4], b[2];
 };
 
 __device__ __forceinline__ void gemm_frags16(Frags16& f, const uint8_t* stage, int wm, int wn, int lane) {
@@ -577,22 +612,58 @@ __device__ __forceinline__ void gemm_frags16(Frags16& f, const uint8_t* stage, i
     f.b[i] = *reinterpret_cast<const f16x8*>(stage + kArr + swz_off(64 * wn + 32 * i + (lane & 31), h));
 }
 
-__device__ __forceinline__ i32x8 frag8_at(const uint8_t* stage, int row) {
-  const u32x4 x = *reinterpret_cast<const u32x4*>(stage + swz_off(row, 2));
-  const u32x4 y = *reinterpret_cast<const u32x4*>(stage + swz_off(row, 3));
+__device__ __forceinline__ i32x8 join8(const u32x4& x, const u32x4& y) {
   return (i32x8){(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
 }
 
-// stage_h: this lane's stage (that of k-block s + lane / 32).  kLone: k-block
-// s is the split's last and has no partner, so lane half 1 contributes zero.
-template <bool kLone>
-__device__ __forceinline__ void gemm_frags8(Frags8& f, const uint8_t* stage_h, int wm, int wn, int lane) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = frag8_at(stage_h, 128 * wm + 32 * i + (lane & 31));
+// A bytes of row blocks kMb0 and kMb0 + 1, from this lane's stage (k-block s + h)
+template <int kMb0>
+__device__ __forceinline__ void gemm_reads8a(i32x8 (&a)[2], const uint8_t* stage_h, int wm, int lane) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    f.b[i] = frag8_at(stage_h + kArr, 64 * wn + 32 * i + (lane & 31));
-    if (kLone && lane >= 32) f.b[i] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
+    const int ra = 128 * wm + 32 * (kMb0 + i) + (lane & 31);
+    a[i] = join8(*reinterpret_cast<const u32x4*>(stage_h + swz_off(ra, 2)),
+                 *reinterpret_cast<const u32x4*>(stage_h + swz_off(ra, 3)));
+  }
+}
+
+// B: the residual bytes (chunk 2 + h of stage s) now, and the 16 Q16 values of
+// k-block s + h (two chunks) raw, for gemm_convert8b.  The Q16 chunks are read
+// first, so their conversion waits for the fewest reads.
+struct Raw8 {
+  u32x4 q0[2], q1[2];
+};
+
+__device__ __forceinline__ void gemm_reads8b(i32x8 (&b)[2], Raw8& r, const uint8_t* stage_s,
+                                             const uint8_t* stage_h, int wn, int lane) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rb = 64 * wn + 32 * i + (lane & 31);
+    r.q0[i] = *reinterpret_cast<const u32x4*>(stage_h + kArr + swz_off(rb, 0));
+    r.q1[i] = *reinterpret_cast<const u32x4*>(stage_h + kArr + swz_off(rb, 1));
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rb = 64 * wn + 32 * i + (lane & 31);
+    const u32x4 qe = *reinterpret_cast<const u32x4*>(stage_s + kArr + swz_off(rb, 2 + h));
+    // the upper half is written by gemm_convert8b
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[i][e] = (int)qe[e];
+  }
+}
+
+// B's second half, fp8(Q16).  kLone: k-block s is the split's last and has no
+// partner, so lane half 1 contributes zero.
+template <bool kLone>
+__device__ __forceinline__ void gemm_convert8b(i32x8 (&b)[2], const Raw8& r, int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    b[i][4] = (int)f16x4_to_fp8(r.q0[i][0], r.q0[i][1]);
+    b[i][5] = (int)f16x4_to_fp8(r.q0[i][2], r.q0[i][3]);
+    b[i][6] = (int)f16x4_to_fp8(r.q1[i][0], r.q1[i][1]);
+    b[i][7] = (int)f16x4_to_fp8(r.q1[i][2], r.q1[i][3]);
+    if (kLone && lane >= 32) b[i] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
   }
 }
 
@@ -604,43 +675,84 @@ __device__ __forceinline__ void gemm_mma16(const Frags16& f, f32x16 (&acc)[4][2]
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[mb], f.b[nb], acc[mb][nb], 0, 0, 0);
 }
 
-// e4m3 x e4m3 (format selectors 0), no block scales
-__device__ __forceinline__ void gemm_mma8(const Frags8& f, f32x16 (&acc)[4][2]) {
+// fp8 MFMAs of row blocks kMb0, kMb0 + 1: e4m3 x e4m3 (format selectors 0),
+// block scale 2^-5 on A (E8M0 122), 1 on B
+template <int kMb0>
+__device__ __forceinline__ void gemm_mma8(const i32x8 (&a)[2], const i32x8 (&b)[2], f32x16 (&acc)[4][2]) {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
-      acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[mb], f.b[nb], acc[mb][nb], 0, 0, 0, 0,
-                                                                    0, 0);
+      acc[kMb0 + i][nb] =
+          __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[nb], acc[kMb0 + i][nb], 0, 0, 0, 122, 0, 127);
 }
 
-// One iteration of the fp16 + fp8 pipeline (same staging as gemm_iter).  Steps
-// come in pairs: the first (kRead8) also reads the pair's fp8 fragments, the
-// second (kMma8) also issues the pair's fp8 MFMAs.
-template <bool kRead8, bool kMma8, bool kLone>
-__device__ __forceinline__ void gemm_iter16(int s, uint8_t* smem, Frags16& cur, Frags16& nxt, Frags8& f8,
+// The packed-table pipeline keeps five LDS stages and synchronises once per
+// pair of steps.  The even step s waits until every step sent so far (up to
+// s + 2) has landed, passes the barrier and sends steps s + 3 and s + 4 (into
+// the stages of s - 2 and s - 1, last read before the barrier).  A step's
+// stage thus stays intact through the pair that reads it, and the fp8 work of
+// a pair (s, s + 1) spreads over both steps:
+//   even s:  fp8 MFMAs of the previous pair's row blocks 2-3 (zeros before
+//            the first pair); read this pair's B and the A bytes of row
+//            blocks 0-1; fp16 MFMAs of step s; then convert B's Q16 half.
+//   odd s+1: read the A bytes of row blocks 2-3; fp16 MFMAs of step s + 1;
+//            fp8 MFMAs of row blocks 0-1.
+// Each step issues 12 MFMAs (8 fp16, 4 fp8) and 16 or 10 fragment reads; every
+// step is sent two steps before the pair that needs it.
+constexpr int kStages16 = 5;
+__device__ __forceinline__ uint8_t* stage16(uint8_t* smem, int k) { return smem + (k % kStages16) * kStage; }
+
+struct Ops8 {
+  i32x8 a01[2], a23[2], b[2];
+};
+
+template <bool kLone>
+__device__ __forceinline__ void gemm_even16(int s, uint8_t* smem, Frags16& cur, Frags16& nxt, Ops8& o,
                                             f32x16 (&acc)[4][2], const uint8_t* __restrict__ pimg,
                                             const EOperand& eo, int kb0, int kb_last, int n_kb, int col_pad,
-                                            int col0, const uint32_t (&voff)[2], const uint32_t (&poff)[2],
+                                            int col0, const uint32_t (&voff)[2][2], const uint32_t (&poff)[2],
                                             int wave, int wm, int wn, int lane) {
   // the MFMAs touch no memory: keep the scheduler from moving them across the
-  // workgroup barrier into the next iteration
+  // workgroup barrier into another iteration
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt_lgkm0<kDmaPerStep>();
+  wait_vmcnt_lgkm0<0>();
   raw_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  gemm_dma<false>(smem + ((s + kDist) % kStages) * kStage, pimg, eo, min(kb0 + s + kDist, kb_last), n_kb, col_pad,
-                  col0, voff, poff, wave);
-  gemm_frags16(nxt, smem + ((s + 1) % kStages) * kStage, wm, wn, lane);
-  if (kRead8) gemm_frags8<kLone>(f8, smem + ((s + (lane >> 5)) % kStages) * kStage, wm, wn, lane);
+  gemm_dma<false, true>(stage16(smem, s + 3), pimg, eo, min(kb0 + s + 3, kb_last), n_kb, col_pad, col0, voff, poff,
+                        wave);
+  gemm_dma<false, false>(stage16(smem, s + 4), pimg, eo, min(kb0 + s + 4, kb_last), n_kb, col_pad, col0, voff,
+                         poff, wave);
+  gemm_mma8<2>(o.a23, o.b, acc);
+  // the previous pair's B is consumed before this pair's is read over it
+  __builtin_amdgcn_sched_barrier(0);
+  // reads in the order they are needed: B (converted at the end of this
+  // step), the next step's fp16 fragments (first MFMAs of the odd step), the A
+  // bytes of row blocks 0-1 (last MFMAs of the odd step)
+  const int h = lane >> 5;
+  Raw8 raw;
+  gemm_reads8b(o.b, raw, stage16(smem, s), stage16(smem, s + h), wn, lane);
+  gemm_frags16(nxt, stage16(smem, s + 1), wm, wn, lane);
+  gemm_reads8a<0>(o.a01, stage16(smem, s + h), wm, lane);
   gemm_mma16(cur, acc);
-  if (kMma8) gemm_mma8(f8, acc);
-  __builtin_amdgcn_sched_group_barrier(0x100, kRead8 ? 18 : 6, 0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, kMma8 ? 4 : 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-  }
+  __builtin_amdgcn_sched_barrier(0);
+  gemm_convert8b<kLone>(o.b, raw, lane);
+}
+
+__device__ __forceinline__ void gemm_odd16(int s1, uint8_t* smem, Frags16& cur, Frags16& nxt, Ops8& o,
+                                           f32x16 (&acc)[4][2], const uint8_t* __restrict__ pimg,
+                                           const EOperand& eo, int kb0, int kb_last, int n_kb, int col_pad,
+                                           int col0, const uint32_t (&voff)[2][2], const uint32_t (&poff)[2],
+                                           int wave, int wm, int wn, int lane) {
+  __builtin_amdgcn_sched_barrier(0);
+  // reads first (consumed after the next barrier), then the fp16 MFMAs on
+  // fragments read early in the even step, then the fp8 ones on the A bytes
+  // read last there
+  gemm_reads8a<2>(o.a23, stage16(smem, s1 - 1 + (lane >> 5)), wm, lane);
+  gemm_frags16(nxt, stage16(smem, s1 + 1), wm, wn, lane);
+  gemm_mma16(cur, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  gemm_mma8<0>(o.a01, o.b, acc);
 }
 
 // Iteration s of the pipeline: step s+1 has landed in LDS (waited before the
@@ -654,7 +766,7 @@ __device__ __forceinline__ void gemm_iter(int s, uint8_t* smem, Frags& cur, Frag
                                           f32x16 (&acc)[4][2], const uint8_t* __restrict__ pimg,
                                           const EOperand& eo, int kb0, int kb_last,
                                           int n_kb, int col_pad, int col0,
-                                          const uint32_t (&voff)[2], const uint32_t (&poff)[2],
+                                          const uint32_t (&voff)[2][2], const uint32_t (&poff)[2],
                                           int wave, int wm, int wn, int lane) {
   // the fragments of step s were read an iteration ago: drain them here, before
   // this iteration's reads are queued behind them
@@ -684,8 +796,8 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
                                                           float* __restrict__ zp, int n_rows, int d,
                                                           int col_pad, int n_tiles, int n_mt,
                                                           int kb_per_split, int n_kb, int vocab) {
-  const EOperand eo{eimg, d, vocab};
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
+  const EOperand eo{eimg, d, vocab, n_tiles};
+  __shared__ __attribute__((aligned(16))) uint8_t smem[(kF32E ? kStages : kStages16) * kStage];
 
   // Workgroups are dealt round-robin to the 8 XCDs; renumber them so the
   // d-tiles of one vocabulary split sit on the same XCD and share its L2 copy
@@ -710,15 +822,24 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   // lane offsets of the 16-byte chunk that belongs at this lane's swizzled LDS
-  // slot (p images and E tiles are both [row or column][64 B] per k-block)
-  uint32_t voff[2], poff[2];
+  // slot (p images and E tiles are both [row or column][64 B] per k-block in
+  // LDS); voff[parity of the k-block][instruction]
+  uint32_t voff[2][2], poff[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int row = 32 * wave + 16 * j + (lane >> 2);
     const int chunk = (lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
     poff[j] = (uint32_t)(row * kImgRow + chunk * 16);
-    // float32 E: id row 2 wave + j, lane's slot holds 16-byte chunk e32_chunk
-    voff[j] = kF32E ? (uint32_t)(e32_chunk(2 * wave + j, lane) * 16) : poff[j];
+    if (kF32E) {
+      // float32 E: id row 2 wave + j, lane's slot holds 16-byte chunk e32_chunk
+      voff[0][j] = voff[1][j] = (uint32_t)(e32_chunk(2 * wave + j, lane) * 16);
+    } else {
+      // packed table, column row: Q16 chunks of k-block 2j' or 2j' + 1, or the
+      // pair's residual chunks (even k-blocks only; odd ones load zeros)
+      const uint32_t q16 = (uint32_t)(row * 32 + (chunk & 1) * 16);
+      voff[0][j] = chunk < 2 ? q16 : (uint32_t)(kEResid + row * 32 + (chunk - 2) * 16);
+      voff[1][j] = chunk < 2 ? (uint32_t)kEHalf + q16 : (1u << 30);
+    }
   }
 
   f32x16 acc[4][2];
@@ -732,9 +853,10 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
   // prologue: steps 0..kDist-1 in flight (clamped to the last k-block), step 0
   // landed, its fragments read
   const int kb_last = kb0 + nsteps - 1;
-#pragma unroll
-  for (int k = 0; k < kDist; ++k)
-    gemm_dma<kF32E>(smem + k * kStage, pimg, eo, min(kb0 + k, kb_last), n_kb, col_pad, col0, voff, poff, wave);
+  gemm_dma<kF32E, false>(smem, pimg, eo, min(kb0, kb_last), n_kb, col_pad, col0, voff, poff, wave);
+  gemm_dma<kF32E, true>(smem + kStage, pimg, eo, min(kb0 + 1, kb_last), n_kb, col_pad, col0, voff, poff, wave);
+  gemm_dma<kF32E, false>(smem + 2 * kStage, pimg, eo, min(kb0 + 2, kb_last), n_kb, col_pad, col0, voff, poff, wave);
+  static_assert(kDist == 3, "the prologue sends three steps");
   wait_vmcnt<(kDist - 1) * kDmaPerStep>();
   raw_barrier();
 
@@ -755,22 +877,31 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
 #undef DG_ITER
   } else {
     Frags16 ga, gb;
-    Frags8 g8;
+    Ops8 o;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      o.a01[i] = o.a23[i] = o.b[i] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
+    }
     gemm_frags16(ga, smem, wm, wn, lane);
-#define DG_ITER16(R, M, L, S, C, N)                                                                              \
-  gemm_iter16<R, M, L>(S, smem, C, N, g8, acc, pimg, eo, kb0, kb_last, n_kb, col_pad, col0, voff, poff, wave, wm, \
-                       wn, lane)
+#define DG_EVEN(L, S) \
+  gemm_even16<L>(S, smem, ga, gb, o, acc, pimg, eo, kb0, kb_last, n_kb, col_pad, col0, voff, poff, wave, wm, wn, lane)
+#define DG_ODD(S) \
+  gemm_odd16(S, smem, gb, ga, o, acc, pimg, eo, kb0, kb_last, n_kb, col_pad, col0, voff, poff, wave, wm, wn, lane)
     int s = 0;
     for (; s + 1 < nsteps; s += 2) {
-      DG_ITER16(true, false, false, s, ga, gb);
-      DG_ITER16(false, true, false, s + 1, gb, ga);
+      DG_EVEN(false, s);
+      DG_ODD(s + 1);
     }
     if (s < nsteps) {
-      // the split's last k-block has no partner: its corrections go alone
-      DG_ITER16(true, false, true, s, ga, gb);
-      gemm_mma8(g8, acc);
+      // the split's last k-block has no partner: its corrections go alone.  Its
+      // stage and the next (the clamped repeat) stay intact, as no DMA follows.
+      DG_EVEN(true, s);
+      gemm_reads8a<2>(o.a23, stage16(smem, s + (lane >> 5)), wm, lane);
+      gemm_mma8<0>(o.a01, o.b, acc);
     }
-#undef DG_ITER16
+    gemm_mma8<2>(o.a23, o.b, acc);
+#undef DG_EVEN
+#undef DG_ODD
   }
   wait_vmcnt<0>();
 
@@ -1594,9 +1725,9 @@ __global__ __launch_bounds__(256) void topk_z(const TopkItem* __restrict__ list,
 
 // ---------------------------------------------------------------------------
 static size_t embedding_image_bytes(int vocab, int d) {
-  const size_t n_kb = (size_t)(vocab + kKB - 1) / kKB;
-  const size_t col_pad = (size_t)(d + kGN - 1) / kGN * kGN;
-  return n_kb * col_pad * kImgRow;   // a multiple of 16 KB
+  const size_t n_pairs = ((size_t)(vocab + kKB - 1) / kKB + 1) / 2;
+  const size_t n_tiles = (size_t)(d + kGN - 1) / kGN;
+  return n_pairs * n_tiles * kEBlock;
 }
 
 size_t embedding_packed_bytes(int vocab, int d) {
@@ -1609,8 +1740,8 @@ static const PackTail* pack_tail(const void* packed, int vocab, int d) {
 }
 
 hipError_t launch_embedding_pack(const float* emb, void* packed, int vocab, int d, hipStream_t s) {
-  const int n_kb = (vocab + kKB - 1) / kKB;
-  const int col_pad = (d + kGN - 1) / kGN * kGN;
+  const int n_pairs = ((vocab + kKB - 1) / kKB + 1) / 2;
+  const int n_tiles = (d + kGN - 1) / kGN;
   uint8_t* base = static_cast<uint8_t*>(packed);
   float* part = reinterpret_cast<float*>(base + embedding_image_bytes(vocab, d));
   PackTail* tail = const_cast<PackTail*>(pack_tail(packed, vocab, d));
@@ -1622,7 +1753,7 @@ hipError_t launch_embedding_pack(const float* emb, void* packed, int vocab, int 
     e = hipGetLastError();
   }
   if (e == hipSuccess) {
-    emb_pack_kernel<<<dim3(col_pad / 256, n_kb), 256, 0, s>>>(emb, base, vocab, d, col_pad, tail);
+    emb_pack_kernel<<<dim3(n_tiles, 2 * n_pairs), 256, 0, s>>>(emb, base, vocab, d, n_tiles, tail);
     e = hipGetLastError();
   }
   prof_end(s);
@@ -1646,6 +1777,8 @@ SamplerPlan sampler_plan(int n_canvas, int batch, int vocab, int d) {
   if (splits < by_regs) splits = by_regs;
   if (splits < 1) splits = 1;
   p.kb_per_split = (p.n_kb + splits - 1) / splits;
+  // an even count: the contraction takes k-blocks in pairs from an even start
+  p.kb_per_split += p.kb_per_split & 1;
   p.n_splits = (p.n_kb + p.kb_per_split - 1) / p.kb_per_split;
   p.off_stats = 0;
   p.off_pimg = align_up((size_t)n * p.n_splits * sizeof(StatsPartial), 256);

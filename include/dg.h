@@ -218,19 +218,23 @@ size_t dg_sampler_workspace_bytes(int n_canvas, int vocab, int d_model);
 /*
  * The embedding table E in the layout the sampler streams.  The contraction
  * z = softmax(logits)·E runs on fp16 and fp8 matrix cores in split precision:
- * with Q = E·2^c (c chosen so that max|Q| lies in [2^12, 2^13)), each element
- * is held as Q16 = fp16(Q) plus two e4m3 bytes, fp8((Q - Q16)·2^6) and
- * fp8(Q·2^-5), so E is converted once, when the weights are loaded, rather
- * than on every step:
+ * with Q = E·2^c (c chosen so that max|Q| lies in [2^7, 2^8)), each element
+ * is held as Q16 = fp16(Q) plus one e4m3 byte, fp8((Q - Q16)·2^11) (3 bytes;
+ * the contraction forms fp8(Q16) itself), so E is converted once, when the
+ * weights are loaded, rather than on every step:
  *   emb        [vocab, d_model] float32 (input)
- *   packed     dg_embedding_packed_bytes(vocab, d_model) bytes (output): for
- *              each block of 16 ids and each column (d_model rounded up to a
- *              multiple of 256, zero padded), a 64-byte record: 16 fp16 Q16,
- *              16 bytes fp8((Q - Q16)·2^6), 16 bytes fp8(Q·2^-5); ids past
- *              vocab are zero.  Then 4096 bytes the pack uses as working space
- *              and a 256-byte record: float 2^-(14 + c), int32 c.
+ *   packed     dg_embedding_packed_bytes(vocab, d_model) bytes (output).  Ids
+ *              are grouped in blocks of 16 and the blocks in pairs (ids past
+ *              vocab are zero); columns in tiles of 256 (d_model rounded up,
+ *              zero padded).  For pair j and tile t, a 24576-byte block at
+ *              (j·n_tiles + t)·24576: the 256 columns' fp16 Q16 of the pair's
+ *              first 16 ids (32 bytes per column, id order), the same for the
+ *              second 16 ids, then per column the 16 residual bytes of the
+ *              first block and the 16 of the second.  After the blocks: 4096
+ *              bytes the pack uses as working space, then a 256-byte record:
+ *              float 2^-(14 + c), int32 c.
  * A zero or non-finite max|E| gives c = 0; c is at most 80 (tables with
- * max|E| below 2^-67 keep fewer bits).  The caller owns both buffers.
+ * max|E| below 2^-72 keep fewer bits).  The caller owns both buffers.
  * Asynchronous on `stream`.
  */
 size_t dg_embedding_packed_bytes(int vocab, int d_model);
@@ -529,6 +533,14 @@ int dg_probe_mfma_bf16(float* sink, int n_workgroups, int iters, hipStream_t str
  * per load and store.  Asynchronous on `stream`.
  */
 int dg_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+/*
+ * The HBM rate of a plain read: `bytes` (a multiple of 16) from src (device,
+ * 16-byte aligned), 16 bytes per lane per load, grid-stride over at most 4096
+ * workgroups of 256 lanes.  sink: device uint32 buffer of 16384 entries (one
+ * per wave; written, values meaningless).  Asynchronous on `stream`.
+ */
+int dg_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Profiling and errors                                                      */

@@ -235,33 +235,37 @@ def _fp8_bytes(torch, x):
 
 
 @pytest.mark.parametrize("vocab,d,scale", [(37, 260, 0.02), (4096, 512, 0.02), (16, 1, 0.02), (300, 64, 700.0),
-                                           (64, 8, 3e-6)])
+                                           (64, 8, 3e-6), (48, 300, 0.5)])
 def test_embedding_pack_layout(vocab, d, scale):
-    """The packed table: per 16-id block and column, fp16 Q16 of ids 0-15, e4m3
-    of (Q - Q16) 2^6, e4m3 of Q 2^-5, with Q = E 2^c and max|Q| in [2^12, 2^13);
-    after the image, 1024 floats of pack workspace and the record (2^-(14+c), c).
-    Every byte is compared with numpy's fp16 and torch's e4m3 rounding."""
+    """The packed table: Q = E 2^c with max|Q| in [2^7, 2^8); for each pair of
+    16-id k-blocks and 256-column tile a 24 KB block holding the fp16 Q16 of
+    k-block 2j (256 columns x 16 ids), those of k-block 2j + 1, then per column
+    the e4m3 bytes of (Q - Q16) 2^11 for k-block 2j and for 2j + 1; after the
+    blocks, 1024 floats of pack workspace and the record (2^-(14+c), c).  Every
+    byte is compared with numpy's fp16 and torch's e4m3 rounding."""
     torch, dg = require_gpu()
     rng = np.random.default_rng(vocab + d)
     emb = (rng.standard_normal((vocab, d)) * scale).astype(np.float32)
     packed = dg.dg_embedding_pack(to_dev(emb)).cpu().numpy()
-    n_kb, col_pad = -(-vocab // 16), -(-d // 256) * 256
-    image = n_kb * col_pad * 64
+    n_pairs, n_tiles = -(-vocab // 32), -(-d // 256)
+    image = n_pairs * n_tiles * 24576
     assert packed.size == image + 4096 + 256 == dg.dg_embedding_packed_bytes(vocab, d)
     zscale = packed[image + 4096:image + 4100].view(np.float32)[0]
     c = int(packed[image + 4100:image + 4104].view(np.int32)[0])
     top = float(np.abs(emb).max()) * 2.0 ** c
-    assert 4096.0 <= top < 8192.0, (c, top)
+    assert 128.0 <= top < 256.0, (c, top)
     assert zscale == np.float32(2.0 ** -(14 + c))
-    full = np.zeros((n_kb * 16, col_pad), np.float32)
+    full = np.zeros((n_pairs * 32, n_tiles * 256), np.float32)
     full[:vocab, :d] = emb
-    q = (full * np.float32(2.0 ** c)).reshape(n_kb, 16, col_pad).transpose(0, 2, 1)   # [kb, col, id]
-    rec = packed[:image].reshape(n_kb, col_pad, 64)
+    q = full * np.float32(2.0 ** c)                                   # [id, column]
     q16 = q.astype(np.float16)
-    np.testing.assert_array_equal(rec[:, :, :32].copy().view(np.float16), q16)
-    qe = (q - q16.astype(np.float32)).astype(np.float32)
-    np.testing.assert_array_equal(rec[:, :, 32:48], _fp8_bytes(torch, qe * np.float32(64.0)))
-    np.testing.assert_array_equal(rec[:, :, 48:64], _fp8_bytes(torch, q * np.float32(0.03125)))
+    qe8 = _fp8_bytes(torch, (q - q16.astype(np.float32)) * np.float32(2048.0))
+    # reference blocks [pair, tile, 24576]
+    q16_kb = q16.reshape(n_pairs, 2, 16, n_tiles, 256).transpose(0, 3, 1, 4, 2)     # [pair, tile, kb&1, col, id]
+    qe_kb = qe8.reshape(n_pairs, 2, 16, n_tiles, 256).transpose(0, 3, 4, 1, 2)      # [pair, tile, col, kb&1, id]
+    blocks = packed[:image].reshape(n_pairs, n_tiles, 24576)
+    np.testing.assert_array_equal(blocks[:, :, :16384].copy().view(np.float16).reshape(q16_kb.shape), q16_kb)
+    np.testing.assert_array_equal(blocks[:, :, 16384:].reshape(qe_kb.shape), qe_kb)
 
 
 @pytest.mark.parametrize("n,vocab,d", [(256, 262144, 3072), (256, 4097, 260), (17, 12345, 516), (1, 2, 4)])
