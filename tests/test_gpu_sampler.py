@@ -113,6 +113,26 @@ def test_ragged_shapes(n, vocab, d):
     check_z(gz, ref["z"])
 
 
+@pytest.mark.parametrize("scale", [300.0, 1e-5, 0.02])
+def test_table_scales(scale):
+    """The packed table's exponent shift at both ends: z of tables with entries
+    of order 300 and 1e-5 meets the bound like the 0.02 table (the shift c is
+    chosen from max|E| when the table is packed)."""
+    torch, dg = require_gpu()
+    n, vocab, d = 64, 20000, 96
+    rng = np.random.default_rng(int(scale * 1e6) % 997)
+    logits = (rng.standard_normal((n, vocab)) * 2).astype(np.float32)
+    logits[::4, 123] += 10.0
+    emb = (rng.standard_normal((vocab, d)) * scale).astype(np.float32)
+    ctrl = S.Ctrl(seed=5, tau=0.9, flags=S.AUTO_ADVANCE)
+    g = GpuSampler(torch, dg, emb, np.zeros(n), np.zeros(n), ctrl)
+    gids, gmask, gk, gz, _ = g.step(logits)
+    ref = S.sampler_step(logits, emb, np.zeros(n), np.zeros(n), ctrl, z_rows="all")
+    assert check_step(np.zeros(n), np.zeros(n), gids, gmask, gk, ref, 0.9) == 0
+    worst, total = check_z(gz, ref["z"])
+    log(f"table scale {scale}: z relative L2 worst row {worst:.3e}, whole tensor {total:.3e}")
+
+
 def test_identity_embedding_and_probability_sum():
     """E = I gives z = p; an all-ones column of E gives sum(p) = 1 (through the ABI)."""
     torch, dg = require_gpu()
