@@ -101,6 +101,9 @@ int check_sampler(const float* logits, const void* emb, const int32_t* ids, cons
   // the logits are addressed with 32-bit byte offsets
   if ((uint64_t)n * (uint64_t)batch * (uint64_t)vocab * 4ull >= (1ull << 32))
     return fail(DG_EUNSUPPORTED, "sampler: n_canvas * batch * vocab * 4 must be below 2^32");
+  // rows are a launch-grid dimension of the per-row kernels
+  if ((int64_t)n * batch > dg::kMaxSamplerRows)
+    return fail(DG_EUNSUPPORTED, "sampler: n_canvas * batch above %d rows", dg::kMaxSamplerRows);
   if (!aligned16(logits) || !aligned16(emb) || !aligned16(z))
     return fail(DG_EINVAL, "sampler: logits/emb_packed/selfcond must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(ctrl) & 7u) != 0) return fail(DG_EINVAL, "sampler: ctrl misaligned");
@@ -209,6 +212,7 @@ size_t dg_sampler_workspace_bytes(int n, int vocab, int d) {
 
 size_t dg_sampler_workspace_bytes_batched(int n, int batch, int vocab, int d) {
   if (n < 1 || n > 256 || batch < 1 || batch > 4096 || vocab < 2 || d < 1) return 0;
+  if ((int64_t)n * batch > dg::kMaxSamplerRows) return 0;
   const dg::SamplerPlan p = dg::sampler_plan(n, batch, vocab, d);
   return p.n_splits > dg::kMaxSamplerSplits ? 0 : p.total;
 }
@@ -400,6 +404,7 @@ int dg_sampler_step_eb_batched(const float* logits, const void* emb, int32_t* id
 
 size_t dg_sampler_workspace_bytes_topk(int n, int batch, int vocab, int d, int k) {
   if (n < 1 || n > 256 || batch < 1 || batch > 4096 || vocab < 2 || d < 1 || k < 1 || k > 256) return 0;
+  if ((int64_t)n * batch > dg::kMaxSamplerRows) return 0;
   return dg::topk_plan(n, batch, vocab, d, k).total;
 }
 

@@ -42,6 +42,7 @@ SamplerPlan sampler_plan(int n_canvas, int batch, int vocab, int d);
 // The combine kernel keeps one merge weight per vocabulary split in LDS; a plan
 // with more splits (a vocabulary above 4194304 ids) is refused on the host.
 constexpr int kMaxSamplerSplits = 256;
+constexpr int kMaxSamplerRows = 65535;   // rows over a batch: the y extent of the per-row launch grids
 size_t embedding_packed_bytes(int vocab, int d);
 hipError_t launch_embedding_pack(const float* emb, void* packed, int vocab, int d, hipStream_t s);
 hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void* emb_packed,

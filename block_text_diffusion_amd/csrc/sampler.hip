@@ -430,13 +430,15 @@ __global__ __launch_bounds__(256) void emb_scale_kernel(const float* __restrict_
   }
 }
 
-// grid (n_tiles, 2 n_pairs): one thread per column and k-block.
+// grid (2 n_pairs, n_tiles): one thread per column and k-block (k-blocks on x,
+// which takes the large count).
 __global__ __launch_bounds__(256) void emb_pack_kernel(const float* __restrict__ emb,
                                                        uint8_t* __restrict__ out, int vocab, int d,
                                                        int n_tiles, const PackTail* __restrict__ tail) {
   const int cl = threadIdx.x;                 // column within the tile
-  const int col = blockIdx.x * 256 + cl;
-  const int kb = blockIdx.y;
+  const int tile = blockIdx.y;
+  const int col = tile * 256 + cl;
+  const int kb = blockIdx.x;
   const float sc = ldexpf(1.0f, tail->c);
   uint32_t h16[8], qe8[4];
 #pragma unroll
@@ -452,7 +454,7 @@ __global__ __launch_bounds__(256) void emb_pack_kernel(const float* __restrict__
     h16[2 * g] = h[0];
     h16[2 * g + 1] = h[1];
   }
-  uint8_t* blk = out + ((size_t)(kb >> 1) * n_tiles + blockIdx.x) * kEBlock;
+  uint8_t* blk = out + ((size_t)(kb >> 1) * n_tiles + tile) * kEBlock;
   uint8_t* q = blk + (kb & 1) * kEHalf + cl * 32;
   *reinterpret_cast<u32x4*>(q) = (u32x4){h16[0], h16[1], h16[2], h16[3]};
   *reinterpret_cast<u32x4*>(q + 16) = (u32x4){h16[4], h16[5], h16[6], h16[7]};
@@ -1753,7 +1755,7 @@ hipError_t launch_embedding_pack(const float* emb, void* packed, int vocab, int 
     e = hipGetLastError();
   }
   if (e == hipSuccess) {
-    emb_pack_kernel<<<dim3(n_tiles, 2 * n_pairs), 256, 0, s>>>(emb, base, vocab, d, n_tiles, tail);
+    emb_pack_kernel<<<dim3(2 * n_pairs, n_tiles), 256, 0, s>>>(emb, base, vocab, d, n_tiles, tail);
     e = hipGetLastError();
   }
   prof_end(s);

@@ -331,7 +331,8 @@ int dg_sampler_step_eb(const float* logits, const void* emb_packed, int32_t* can
  * so canvas b's results are exactly those of dg_sampler_step on canvas b
  * alone.  The batch shares one pass over the embedding table, which raises
  * the contraction's arithmetic intensity by `batch`.
- *   batch in [1, 4096]; n_canvas * batch * vocab * 4 < 2^32.
+ *   batch in [1, 4096]; n_canvas * batch * vocab * 4 < 2^32; n_canvas * batch <= 65535
+ *   (DG_EUNSUPPORTED otherwise).
  */
 size_t dg_sampler_workspace_bytes_batched(int n_canvas, int batch, int vocab, int d_model);
 int dg_sampler_step_batched(const float* logits, const void* emb_packed, int32_t* canvas_ids,
@@ -362,7 +363,7 @@ int dg_sampler_step_eb_batched(const float* logits, const void* emb_packed, int3
  *   emb             [vocab, d_model] float32, row-major (not the packed image)
  *   top_k           in [1, 256]; top_k >= vocab keeps every id (untruncated)
  *   other arguments as in the batched calls above.
- * Limits: n_canvas in [1, 256], batch in [1, 4096],
+ * Limits: n_canvas in [1, 256], batch in [1, 4096], n_canvas * batch <= 65535,
  * n_canvas * batch * vocab * 4 < 2^32, and ceil(vocab / 4096) * top_k <= 16384.
  */
 size_t dg_sampler_workspace_bytes_topk(int n_canvas, int batch, int vocab, int d_model, int top_k);

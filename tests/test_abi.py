@@ -206,6 +206,13 @@ def test_batched_sampler_arguments(lib):
     assert lib.dg_sampler_step_batched(*a, 16, 0, 1000, 64, FAKE, 0, None) == DG_EINVAL
     assert lib.dg_sampler_step_batched(*a, 256, 64, 262144, 64, FAKE, 0, None) == DG_EUNSUPPORTED  # > 2^32 bytes
     assert lib.dg_sampler_step_batched(*a, 16, 4, 1000, 64, FAKE, 16, None) == DG_EWORKSPACE
+    # more than 65535 rows over the batch (small vocabulary, many canvases): refused on the host,
+    # before the per-row launch grids would exceed their y extent
+    assert lib.dg_sampler_workspace_bytes_batched(256, 256, 64, 64) == 0
+    assert lib.dg_sampler_workspace_bytes_batched(255, 257, 64, 64) > 0
+    assert lib.dg_sampler_step_batched(*a, 256, 256, 64, 64, FAKE, 1 << 40, None) == DG_EUNSUPPORTED
+    assert b"rows" in lib.dg_last_error()
+    assert lib.dg_sampler_workspace_bytes_topk(256, 256, 64, 64, 8) == 0
 
 
 def test_topk_sampler_arguments(lib):

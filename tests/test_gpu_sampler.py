@@ -133,6 +133,25 @@ def test_table_scales(scale):
     log(f"table scale {scale}: z relative L2 worst row {worst:.3e}, whole tensor {total:.3e}")
 
 
+def test_vocab_past_65536_blocks():
+    """A vocabulary of more than 65536 16-id blocks (1048600 ids): the packing
+    grid takes the blocks on its x dimension, and the step meets the oracle."""
+    torch, dg = require_gpu()
+    n, vocab, d = 4, 1048600, 8
+    rng = np.random.default_rng(65537)
+    logits = (rng.standard_normal((n, vocab)) * 2).astype(np.float32)
+    logits[1, vocab - 1] += 20.0               # the winner in the last block
+    emb = (rng.standard_normal((vocab, d)) * 0.02).astype(np.float32)
+    emb[vocab - 16:] += 1.0                    # the last block's rows stand out in z
+    ctrl = S.Ctrl(seed=9, tau=0.5, flags=S.AUTO_ADVANCE)
+    g = GpuSampler(torch, dg, emb, np.zeros(n), np.zeros(n), ctrl)
+    gids, gmask, gk, gz, _ = g.step(logits)
+    ref = S.sampler_step(logits, emb, np.zeros(n), np.zeros(n), ctrl, z_rows="all")
+    assert check_step(np.zeros(n), np.zeros(n), gids, gmask, gk, ref, 0.5) == 0
+    assert gids[1] == vocab - 1 and gmask[1] == 1
+    check_z(gz, ref["z"])
+
+
 def test_identity_embedding_and_probability_sum():
     """E = I gives z = p; an all-ones column of E gives sum(p) = 1 (through the ABI)."""
     torch, dg = require_gpu()
