@@ -297,7 +297,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+f32",
+        # attention in bf16; the sampler's contraction in fp16 + fp8 products
+        # with fp32 accumulation, its softmax statistics in fp32
+        "dtype": "bf16+fp16+fp8+f32",
         "data": "synthetic",
         "config": {"workload": "long_context_step: canvas 256, prefix 4096, 16q/8kv heads, head_dim 128 "
                                "bf16; vocab 262144, d_model 3072 fp32; one captured graph per step",
