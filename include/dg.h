@@ -233,8 +233,9 @@ size_t dg_sampler_workspace_bytes(int n_canvas, int vocab, int d_model);
  *              first block and the 16 of the second.  After the blocks: 4096
  *              bytes the pack uses as working space, then a 256-byte record:
  *              float 2^-(14 + c), int32 c.
- * A zero or non-finite max|E| gives c = 0; c is at most 80 (tables with
- * max|E| below 2^-72 keep fewer bits).  The caller owns both buffers.
+ * E is expected finite: a non-finite entry makes z undefined (c = 0 then; a
+ * zero table also gives c = 0).  c is at most 80 (tables with max|E| below
+ * 2^-72 keep fewer bits).  The caller owns both buffers.
  * Asynchronous on `stream`.
  */
 size_t dg_embedding_packed_bytes(int vocab, int d_model);
