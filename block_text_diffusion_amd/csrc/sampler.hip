@@ -127,9 +127,10 @@ __device__ __forceinline__ void split_q(const float (&x)[4], uint32_t (&h16)[2],
 // Four fp16 values (two dwords) to four e4m3 bytes, round to nearest even, no
 // scale (v_cvt_scalef32_pk_fp8_f16 with scale 1).
 typedef short i16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t f16x4_to_fp8(uint32_t lo, uint32_t hi) {
-  // the first conversion's upper word is overwritten by the second
-  i16x2 r = __builtin_bit_cast(i16x2, lo);
+// Both words of old are replaced; passing the value the result overwrites lets
+// the conversions write that register in place.
+__device__ __forceinline__ uint32_t f16x4_to_fp8(uint32_t old, uint32_t lo, uint32_t hi) {
+  i16x2 r = __builtin_bit_cast(i16x2, old);
   r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, __builtin_bit_cast(f16x2, lo), 1.0f, false);
   r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, __builtin_bit_cast(f16x2, hi), 1.0f, true);
   return __builtin_bit_cast(uint32_t, r);
@@ -478,24 +479,24 @@ __device__ __forceinline__ int swz_off(int row, int chunk) {
 }
 
 constexpr int kStages = 4;            // LDS stages of 32 KB (float32-table path)
-constexpr int kDist = kStages - 1;     // DMA runs this many steps ahead (float32-table path; prologue of both)
-constexpr int kDmaPerStep = 4;         // LDS DMA instructions per wave per k step
-
-
+constexpr int kDist = kStages - 1;     // DMA runs this many steps ahead (float32-table path)
+constexpr int kDmaPerStep = 4;         // LDS DMA instructions per wave per k step (float32-table path)
 
 // DMA one k step into an LDS stage: 16-byte buffer loads that write LDS
-// directly (lane i of an instruction lands at destination + 16 i).  Wave w
-// moves rows 32w..32w+31 of the p image and columns 32w..32w+31 of the E
-// tile; lane i fetches the global chunk that belongs at its swizzled slot.
-// The E operand comes either as the packed table, whose (k-block pair, tile)
-// blocks give each LDS column row its Q16 chunks (and, for an even k-block,
-// the residual bytes of the pair; an odd k-block's residual lanes point past
-// the block's range, so they load zeros and move no memory), or, with kF32E,
-// as the plain float32 table [V, d]: then wave w moves id rows 2w and 2w + 1
-// of the k-block, 1 KB each (the tile's 256 columns), into LDS rows of 1 KB;
-// lane i fetches the 16-byte chunk i ^ f(row) so id rows r and r + 8 sit 128
-// bytes apart in the banks.  Ids past the vocabulary and columns past d read
-// as zero (buffer range checks; d is a multiple of 4).
+// directly (lane i of an instruction lands at destination + 16 i); lane i
+// fetches the global chunk that belongs at its swizzled slot.
+//   float32-table path (gemm_dma): wave w moves rows 32w..32w+31 of the p
+//     image, and id rows 2w and 2w + 1 of the k-block from the plain float32
+//     table [V, d], 1 KB each (the tile's 256 columns), into LDS rows of 1 KB;
+//     lane i fetches the 16-byte chunk i ^ f(row) so id rows r and r + 8 sit
+//     128 bytes apart in the banks.  Ids past the vocabulary and columns past
+//     d read as zero (buffer range checks; d is a multiple of 4).
+//   packed-table path (gemm_dma16): waves 0-3 alone move the step, wave w
+//     the p rows and E columns 64w..64w+63.  The table's (k-block pair,
+//     tile) blocks give each LDS column row its Q16 chunks and, for an even
+//     k-block, the residual bytes of the pair; an odd k-block's residual
+//     lanes point past the block's range, so they load zeros and move no
+//     memory.
 struct EOperand {
   const uint8_t* base;  // packed table, or float32 E
   int d;                // row length of float32 E (elements)
@@ -505,30 +506,39 @@ struct EOperand {
 
 __device__ __forceinline__ int e32_chunk(int row, int lane) { return lane ^ (row & 8); }
 
-// kOdd (packed table): the step is an odd one of its split, whose k-block is
-// odd (splits start at even k-blocks).  Past a split's last k-block the clamped
-// block may have the other parity; such stages are never read.
-template <bool kF32E, bool kOdd = false>
 __device__ __forceinline__ void gemm_dma(uint8_t* stage, const uint8_t* __restrict__ pimg, const EOperand& eo,
-                                         int kb, int n_kb, int col_pad, int col0, const uint32_t (&voff)[2][2],
-                                         const uint32_t (&poff)[2], int wave) {
+                                         int kb, int col0, const uint32_t (&voff)[2], const uint32_t (&poff)[2],
+                                         int wave) {
   const __amdgpu_buffer_rsrc_t ra = rsrc(pimg + (size_t)kb * kPImg, kPImg);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     uint8_t* dst = stage + (32 * wave + 16 * j) * kImgRow;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)dst, 16, poff[j], 0, 0, 0);
-    if constexpr (kF32E) {
-      const int row = 2 * wave + j;                       // id row of the k-block
-      const int id = kb * kKB + row;
-      const uint32_t valid = (id < eo.vocab && col0 < eo.d) ? (uint32_t)(eo.d - col0) * 4u : 0u;
-      const __amdgpu_buffer_rsrc_t rb =
-          rsrc(eo.base + ((size_t)min(id, eo.vocab - 1) * eo.d + col0) * 4, valid < 1024u ? valid : 1024u);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[0][j], 0, 0, 0);
-    } else {
-      const __amdgpu_buffer_rsrc_t rb =
-          rsrc(eo.base + ((size_t)(kb >> 1) * eo.n_tiles + col0 / kGN) * kEBlock, kEBlock);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[kOdd ? 1 : 0][j], 0, 0, 0);
-    }
+    const int row = 2 * wave + j;                       // id row of the k-block
+    const int id = kb * kKB + row;
+    const uint32_t valid = (id < eo.vocab && col0 < eo.d) ? (uint32_t)(eo.d - col0) * 4u : 0u;
+    const __amdgpu_buffer_rsrc_t rb =
+        rsrc(eo.base + ((size_t)min(id, eo.vocab - 1) * eo.d + col0) * 4, valid < 1024u ? valid : 1024u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[j], 0, 0, 0);
+  }
+}
+
+// kOdd: the step is an odd one of its split, whose k-block is odd (splits
+// start at even k-blocks).  Past a split's last k-block the clamped block may
+// have the other parity; such stages are never read.  Waves 4-7 return at once.
+constexpr int kDma16 = 8;              // LDS DMA instructions per step of each of waves 0-3
+template <bool kOdd>
+__device__ __forceinline__ void gemm_dma16(uint8_t* stage, const uint8_t* __restrict__ pimg, const EOperand& eo,
+                                           int kb, int col0, const uint32_t (&voff)[2][4],
+                                           const uint32_t (&poff)[4], int wave) {
+  if (wave >= 4) return;
+  const __amdgpu_buffer_rsrc_t ra = rsrc(pimg + (size_t)kb * kPImg, kPImg);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(eo.base + ((size_t)(kb >> 1) * eo.n_tiles + col0 / kGN) * kEBlock, kEBlock);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint8_t* dst = stage + (64 * wave + 16 * j) * kImgRow;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)dst, 16, poff[j], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[kOdd ? 1 : 0][j], 0, 0, 0);
   }
 }
 
@@ -536,7 +546,6 @@ struct Frags {
   bf16x8 ah[4], al[4], bh[2], bl[2];
 };
 
-template <bool kF32E>
 __device__ __forceinline__ void gemm_frags(Frags& f, const uint8_t* stage, int wm, int wn, int lane) {
   const int h = lane >> 5;
 #pragma unroll
@@ -545,39 +554,29 @@ __device__ __forceinline__ void gemm_frags(Frags& f, const uint8_t* stage, int w
     f.ah[i] = *reinterpret_cast<const bf16x8*>(stage + swz_off(ra, h));
     f.al[i] = *reinterpret_cast<const bf16x8*>(stage + swz_off(ra, 2 + h));
   }
-  if constexpr (kF32E) {
-    // The lane's two column fragments are the adjacent columns 64 wn + 2 c and
-    // + 1 (c = lane % 32; the epilogue maps them back), so one 8-byte read per
-    // id row serves both.  Ids 8h .. 8h + 7 come from their float32 rows and
-    // are split into the bf16 hi / lo pairs exactly as dg_embedding_pack forms
-    // them.
-    const int cb = 64 * wn + 2 * (lane & 31);
-    float x0[8], x1[8];
+  // The lane's two column fragments are the adjacent columns 64 wn + 2 c and
+  // + 1 (c = lane % 32; the epilogue maps them back), so one 8-byte read per
+  // id row serves both.  Ids 8h .. 8h + 7 come from their float32 rows and are
+  // split into bf16 hi / lo pairs.
+  const int cb = 64 * wn + 2 * (lane & 31);
+  float x0[8], x1[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = 8 * h + e;
-      const f32x2 v = *reinterpret_cast<const f32x2*>(stage + kArr + row * 1024 + (e32_chunk(row, cb >> 2) << 4) +
-                                                      (cb & 3) * 4);
-      x0[e] = v[0];
-      x1[e] = v[1];
-    }
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) split2(x0[2 * e], x0[2 * e + 1], hi[e], lo[e]);
-    f.bh[0] = __builtin_bit_cast(bf16x8, (u32x4){hi[0], hi[1], hi[2], hi[3]});
-    f.bl[0] = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], lo[2], lo[3]});
-#pragma unroll
-    for (int e = 0; e < 4; ++e) split2(x1[2 * e], x1[2 * e + 1], hi[e], lo[e]);
-    f.bh[1] = __builtin_bit_cast(bf16x8, (u32x4){hi[0], hi[1], hi[2], hi[3]});
-    f.bl[1] = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], lo[2], lo[3]});
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int rb = 64 * wn + 32 * i + (lane & 31);
-      f.bh[i] = *reinterpret_cast<const bf16x8*>(stage + kArr + swz_off(rb, h));
-      f.bl[i] = *reinterpret_cast<const bf16x8*>(stage + kArr + swz_off(rb, 2 + h));
-    }
+  for (int e = 0; e < 8; ++e) {
+    const int row = 8 * h + e;
+    const f32x2 v = *reinterpret_cast<const f32x2*>(stage + kArr + row * 1024 + (e32_chunk(row, cb >> 2) << 4) +
+                                                    (cb & 3) * 4);
+    x0[e] = v[0];
+    x1[e] = v[1];
   }
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) split2(x0[2 * e], x0[2 * e + 1], hi[e], lo[e]);
+  f.bh[0] = __builtin_bit_cast(bf16x8, (u32x4){hi[0], hi[1], hi[2], hi[3]});
+  f.bl[0] = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], lo[2], lo[3]});
+#pragma unroll
+  for (int e = 0; e < 4; ++e) split2(x1[2 * e], x1[2 * e + 1], hi[e], lo[e]);
+  f.bh[1] = __builtin_bit_cast(bf16x8, (u32x4){hi[0], hi[1], hi[2], hi[3]});
+  f.bl[1] = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], lo[2], lo[3]});
 }
 
 // acc[mb][nb] += A(rows 128*wm + 32*mb ..) x B(cols 64*wn + 32*nb ..) for one 16-id k step.
@@ -661,10 +660,10 @@ template <bool kLone>
 __device__ __forceinline__ void gemm_convert8b(i32x8 (&b)[2], const Raw8& r, int lane) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    b[i][4] = (int)f16x4_to_fp8(r.q0[i][0], r.q0[i][1]);
-    b[i][5] = (int)f16x4_to_fp8(r.q0[i][2], r.q0[i][3]);
-    b[i][6] = (int)f16x4_to_fp8(r.q1[i][0], r.q1[i][1]);
-    b[i][7] = (int)f16x4_to_fp8(r.q1[i][2], r.q1[i][3]);
+    b[i][4] = (int)f16x4_to_fp8((uint32_t)b[i][4], r.q0[i][0], r.q0[i][1]);
+    b[i][5] = (int)f16x4_to_fp8((uint32_t)b[i][5], r.q0[i][2], r.q0[i][3]);
+    b[i][6] = (int)f16x4_to_fp8((uint32_t)b[i][6], r.q1[i][0], r.q1[i][1]);
+    b[i][7] = (int)f16x4_to_fp8((uint32_t)b[i][7], r.q1[i][2], r.q1[i][3]);
     if (kLone && lane >= 32) b[i] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
   }
 }
@@ -690,18 +689,26 @@ __device__ __forceinline__ void gemm_mma8(const i32x8 (&a)[2], const i32x8 (&b)[
 }
 
 // The packed-table pipeline keeps five LDS stages and synchronises once per
-// pair of steps.  The even step s waits until every step sent so far (up to
-// s + 2) has landed, passes the barrier and sends steps s + 3 and s + 4 (into
-// the stages of s - 2 and s - 1, last read before the barrier).  A step's
-// stage thus stays intact through the pair that reads it, and the fp8 work of
-// a pair (s, s + 1) spreads over both steps:
-//   even s:  fp8 MFMAs of the previous pair's row blocks 2-3 (zeros before
-//            the first pair); read this pair's B and the A bytes of row
-//            blocks 0-1; fp16 MFMAs of step s; then convert B's Q16 half.
+// pair of steps.  Waves 0-3 move every step (gemm_dma16), one step in each step
+// of a pair: at the even step s, after the barrier, step s + 3 (into the stage
+// of s - 2), and at the odd step s + 1 step s + 4 (into the stage of s - 1);
+// both stages were last read before that barrier.  The even step waits until
+// all but the newest step have landed (so s and s + 1 are in LDS) and then
+// passes the barrier; a step is read only during its own pair, so its stage
+// stays intact while the pair reads it.  The fp8 work of a pair (s, s + 1)
+// spreads over both steps:
+//   even s:  read the fp16 fragments of step s; fp8 MFMAs of the previous
+//            pair's row blocks 2-3 (zeros before the first pair); read this
+//            pair's B, the fp16 fragments of step s + 1 and the A bytes of
+//            row blocks 0-1; fp16 MFMAs of step s; convert B's Q16 half.
 //   odd s+1: read the A bytes of row blocks 2-3; fp16 MFMAs of step s + 1;
 //            fp8 MFMAs of row blocks 0-1.
-// Each step issues 12 MFMAs (8 fp16, 4 fp8) and 16 or 10 fragment reads; every
-// step is sent two steps before the pair that needs it.
+// Each step issues 12 MFMAs (8 fp16, 4 fp8).  Why waves 0-3 carry all the
+// DMA: the hardware gives the older of two waves on a SIMD the matrix core
+// first, so waves 0-3 (dispatched first) run ahead of waves 4-7 and used to
+// wait at the barrier; their DMA instructions, which can stall on the CU's
+// memory queue, now sit where there is slack, and waves 4-7 issue none.  The
+// two groups run the same loop (gemm_loop16) with and without the DMA.
 constexpr int kStages16 = 5;
 __device__ __forceinline__ uint8_t* stage16(uint8_t* smem, int k) { return smem + (k % kStages16) * kStage; }
 
@@ -709,22 +716,21 @@ struct Ops8 {
   i32x8 a01[2], a23[2], b[2];
 };
 
-template <bool kLone>
+template <bool kLone, bool kDma>
 __device__ __forceinline__ void gemm_even16(int s, uint8_t* smem, Frags16& cur, Frags16& nxt, Ops8& o,
                                             f32x16 (&acc)[4][2], const uint8_t* __restrict__ pimg,
-                                            const EOperand& eo, int kb0, int kb_last, int n_kb, int col_pad,
-                                            int col0, const uint32_t (&voff)[2][2], const uint32_t (&poff)[2],
-                                            int wave, int wm, int wn, int lane) {
+                                            const EOperand& eo, int kb0, int kb_last, int col0,
+                                            const uint32_t (&voff)[2][4], const uint32_t (&poff)[4], int wave,
+                                            int wm, int wn, int lane) {
   // the MFMAs touch no memory: keep the scheduler from moving them across the
   // workgroup barrier into another iteration
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt_lgkm0<0>();
+  wait_vmcnt_lgkm0<kDma16>();
   raw_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  gemm_dma<false, true>(stage16(smem, s + 3), pimg, eo, min(kb0 + s + 3, kb_last), n_kb, col_pad, col0, voff, poff,
-                        wave);
-  gemm_dma<false, false>(stage16(smem, s + 4), pimg, eo, min(kb0 + s + 4, kb_last), n_kb, col_pad, col0, voff,
-                         poff, wave);
+  gemm_frags16(cur, stage16(smem, s), wm, wn, lane);
+  if constexpr (kDma)
+    gemm_dma16<true>(stage16(smem, s + 3), pimg, eo, min(kb0 + s + 3, kb_last), col0, voff, poff, wave);
   gemm_mma8<2>(o.a23, o.b, acc);
   // the previous pair's B is consumed before this pair's is read over it
   __builtin_amdgcn_sched_barrier(0);
@@ -741,20 +747,47 @@ __device__ __forceinline__ void gemm_even16(int s, uint8_t* smem, Frags16& cur, 
   gemm_convert8b<kLone>(o.b, raw, lane);
 }
 
-__device__ __forceinline__ void gemm_odd16(int s1, uint8_t* smem, Frags16& cur, Frags16& nxt, Ops8& o,
-                                           f32x16 (&acc)[4][2], const uint8_t* __restrict__ pimg,
-                                           const EOperand& eo, int kb0, int kb_last, int n_kb, int col_pad,
-                                           int col0, const uint32_t (&voff)[2][2], const uint32_t (&poff)[2],
-                                           int wave, int wm, int wn, int lane) {
+template <bool kDma>
+__device__ __forceinline__ void gemm_odd16(int s1, uint8_t* smem, Frags16& cur, Ops8& o, f32x16 (&acc)[4][2],
+                                           const uint8_t* __restrict__ pimg, const EOperand& eo, int kb0,
+                                           int kb_last, int col0, const uint32_t (&voff)[2][4],
+                                           const uint32_t (&poff)[4], int wave, int wm, int lane) {
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kDma)
+    gemm_dma16<false>(stage16(smem, s1 + 3), pimg, eo, min(kb0 + s1 + 3, kb_last), col0, voff, poff, wave);
   __builtin_amdgcn_sched_barrier(0);
   // reads first (consumed after the next barrier), then the fp16 MFMAs on
-  // fragments read early in the even step, then the fp8 ones on the A bytes
-  // read last there
+  // fragments read in the even step, then the fp8 ones on the A bytes read
+  // last there
   gemm_reads8a<2>(o.a23, stage16(smem, s1 - 1 + (lane >> 5)), wm, lane);
-  gemm_frags16(nxt, stage16(smem, s1 + 1), wm, wn, lane);
   gemm_mma16(cur, acc);
   __builtin_amdgcn_sched_barrier(0);
   gemm_mma8<0>(o.a01, o.b, acc);
+}
+
+// The whole k loop of one wave.  kDma: waves 0-3, which send the steps.
+template <bool kDma>
+__device__ __forceinline__ void gemm_loop16(uint8_t* smem, f32x16 (&acc)[4][2], const uint8_t* __restrict__ pimg,
+                                            const EOperand& eo, int kb0, int kb_last, int nsteps, int col0,
+                                            const uint32_t (&voff)[2][4], const uint32_t (&poff)[4], int wave,
+                                            int wm, int wn, int lane) {
+  Frags16 ga, gb;
+  Ops8 o;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) o.a01[i] = o.a23[i] = o.b[i] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    gemm_even16<false, kDma>(s, smem, ga, gb, o, acc, pimg, eo, kb0, kb_last, col0, voff, poff, wave, wm, wn, lane);
+    gemm_odd16<kDma>(s + 1, smem, gb, o, acc, pimg, eo, kb0, kb_last, col0, voff, poff, wave, wm, lane);
+  }
+  if (s < nsteps) {
+    // the split's last k-block has no partner: its corrections go alone.  Its
+    // stage and the next (the clamped repeat) are in LDS by the barrier.
+    gemm_even16<true, kDma>(s, smem, ga, gb, o, acc, pimg, eo, kb0, kb_last, col0, voff, poff, wave, wm, wn, lane);
+    gemm_reads8a<2>(o.a23, stage16(smem, s + (lane >> 5)), wm, lane);
+    gemm_mma8<0>(o.a01, o.b, acc);
+  }
+  gemm_mma8<2>(o.a23, o.b, acc);
 }
 
 // Iteration s of the pipeline: step s+1 has landed in LDS (waited before the
@@ -763,12 +796,11 @@ __device__ __forceinline__ void gemm_odd16(int s1, uint8_t* smem, Frags16& cur, 
 // fragments of step s+1 are read (kFrags).  kAhead = number of DMA steps
 // issued beyond s+1 at the wait.  Every variant is straight-line code, so the
 // compiler's wait-count tracking stays exact across the unrolled iterations.
-template <int kAhead, bool kDma, bool kFrags, bool kF32E>
+template <int kAhead, bool kDma, bool kFrags>
 __device__ __forceinline__ void gemm_iter(int s, uint8_t* smem, Frags& cur, Frags& nxt,
                                           f32x16 (&acc)[4][2], const uint8_t* __restrict__ pimg,
-                                          const EOperand& eo, int kb0, int kb_last,
-                                          int n_kb, int col_pad, int col0,
-                                          const uint32_t (&voff)[2][2], const uint32_t (&poff)[2],
+                                          const EOperand& eo, int kb0, int kb_last, int col0,
+                                          const uint32_t (&voff)[2], const uint32_t (&poff)[2],
                                           int wave, int wm, int wn, int lane) {
   // the fragments of step s were read an iteration ago: drain them here, before
   // this iteration's reads are queued behind them
@@ -777,14 +809,14 @@ __device__ __forceinline__ void gemm_iter(int s, uint8_t* smem, Frags& cur, Frag
   // past the split's last k-block the DMA repeats that block into a stage that
   // is never read again, so every iteration runs the same code
   if (kDma)
-    gemm_dma<kF32E>(smem + ((s + kDist) % kStages) * kStage, pimg, eo, min(kb0 + s + kDist, kb_last), n_kb,
-                    col_pad, col0, voff, poff, wave);
-  if (kFrags) gemm_frags<kF32E>(nxt, smem + ((s + 1) % kStages) * kStage, wm, wn, lane);
+    gemm_dma(smem + ((s + kDist) % kStages) * kStage, pimg, eo, min(kb0 + s + kDist, kb_last), col0, voff, poff,
+             wave);
+  if (kFrags) gemm_frags(nxt, smem + ((s + 1) % kStages) * kStage, wm, wn, lane);
   gemm_mma(cur, acc);
   // issue order: the next step's fragment reads first, then the MFMAs with the
   // LDS DMA instructions spread between them, so a DMA that has to wait for
   // queue space never holds back more than a few MFMAs
-  if (kFrags) __builtin_amdgcn_sched_group_barrier(0x100, kF32E ? 16 : 12, 0);
+  if (kFrags) __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
@@ -796,7 +828,7 @@ template <bool kF32E>
 __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restrict__ pimg,
                                                           const uint8_t* __restrict__ eimg,
                                                           float* __restrict__ zp, int n_rows, int d,
-                                                          int col_pad, int n_tiles, int n_mt,
+                                                          int n_tiles, int n_mt,
                                                           int kb_per_split, int n_kb, int vocab) {
   const EOperand eo{eimg, d, vocab, n_tiles};
   __shared__ __attribute__((aligned(16))) uint8_t smem[(kF32E ? kStages : kStages16) * kStage];
@@ -823,26 +855,6 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 2, wn = wave & 3;
-  // lane offsets of the 16-byte chunk that belongs at this lane's swizzled LDS
-  // slot (p images and E tiles are both [row or column][64 B] per k-block in
-  // LDS); voff[parity of the k-block][instruction]
-  uint32_t voff[2][2], poff[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 32 * wave + 16 * j + (lane >> 2);
-    const int chunk = (lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
-    poff[j] = (uint32_t)(row * kImgRow + chunk * 16);
-    if (kF32E) {
-      // float32 E: id row 2 wave + j, lane's slot holds 16-byte chunk e32_chunk
-      voff[0][j] = voff[1][j] = (uint32_t)(e32_chunk(2 * wave + j, lane) * 16);
-    } else {
-      // packed table, column row: Q16 chunks of k-block 2j' or 2j' + 1, or the
-      // pair's residual chunks (even k-blocks only; odd ones load zeros)
-      const uint32_t q16 = (uint32_t)(row * 32 + (chunk & 1) * 16);
-      voff[0][j] = chunk < 2 ? q16 : (uint32_t)(kEResid + row * 32 + (chunk - 2) * 16);
-      voff[1][j] = chunk < 2 ? (uint32_t)kEHalf + q16 : (1u << 30);
-    }
-  }
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -852,24 +864,35 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
 
-  // prologue: steps 0..kDist-1 in flight (clamped to the last k-block), step 0
-  // landed, its fragments read
+  // Lane offsets of the 16-byte chunk that belongs at this lane's swizzled LDS
+  // slot (p images and packed E tiles are both [row or column][64 B] per
+  // k-block in LDS).  Past the split's last k-block the DMA repeats that block
+  // into stages that are never read, so every iteration runs the same code.
   const int kb_last = kb0 + nsteps - 1;
-  gemm_dma<kF32E, false>(smem, pimg, eo, min(kb0, kb_last), n_kb, col_pad, col0, voff, poff, wave);
-  gemm_dma<kF32E, true>(smem + kStage, pimg, eo, min(kb0 + 1, kb_last), n_kb, col_pad, col0, voff, poff, wave);
-  gemm_dma<kF32E, false>(smem + 2 * kStage, pimg, eo, min(kb0 + 2, kb_last), n_kb, col_pad, col0, voff, poff, wave);
-  static_assert(kDist == 3, "the prologue sends three steps");
-  wait_vmcnt<(kDist - 1) * kDmaPerStep>();
-  raw_barrier();
-
-  // every iteration sends a DMA step and reads the next step's fragments (the
-  // last ones read data that is never used)
   if constexpr (kF32E) {
+    uint32_t voff[2], poff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = 32 * wave + 16 * j + (lane >> 2);
+      const int chunk = (lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
+      poff[j] = (uint32_t)(row * kImgRow + chunk * 16);
+      // id row 2 wave + j, lane's slot holds 16-byte chunk e32_chunk
+      voff[j] = (uint32_t)(e32_chunk(2 * wave + j, lane) * 16);
+    }
+    // prologue: steps 0..kDist-1 in flight (clamped to the last k-block), step
+    // 0 landed, its fragments read
+    gemm_dma(smem, pimg, eo, min(kb0, kb_last), col0, voff, poff, wave);
+    gemm_dma(smem + kStage, pimg, eo, min(kb0 + 1, kb_last), col0, voff, poff, wave);
+    gemm_dma(smem + 2 * kStage, pimg, eo, min(kb0 + 2, kb_last), col0, voff, poff, wave);
+    static_assert(kDist == 3, "the prologue sends three steps");
+    wait_vmcnt<(kDist - 1) * kDmaPerStep>();
+    raw_barrier();
+    // every iteration sends a DMA step and reads the next step's fragments
+    // (the last ones read data that is never used)
     Frags fa, fb;
-    gemm_frags<kF32E>(fa, smem, wm, wn, lane);
+    gemm_frags(fa, smem, wm, wn, lane);
 #define DG_ITER(S, C, N) \
-  gemm_iter<1, true, true, kF32E>(S, smem, C, N, acc, pimg, eo, kb0, kb_last, n_kb, col_pad, col0, voff, poff, \
-                                  wave, wm, wn, lane)
+  gemm_iter<1, true, true>(S, smem, C, N, acc, pimg, eo, kb0, kb_last, col0, voff, poff, wave, wm, wn, lane)
     int s = 0;
     for (; s + 1 < nsteps; s += 2) {
       DG_ITER(s, fa, fb);
@@ -878,32 +901,30 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
     if (s < nsteps) DG_ITER(s, fa, fb);
 #undef DG_ITER
   } else {
-    Frags16 ga, gb;
-    Ops8 o;
+    // waves 0-3 move whole steps: rows / columns 64 (wave % 4) + 16 j + lane / 4;
+    // voff[parity of the k-block][instruction].  A column row takes the Q16
+    // chunks of k-block 2j' or 2j' + 1, or the pair's residual chunks (even
+    // k-blocks only; odd ones load zeros).
+    uint32_t voff[2][4], poff[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      o.a01[i] = o.a23[i] = o.b[i] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) {
+      const int row = 64 * (wave & 3) + 16 * j + (lane >> 2);
+      const int chunk = (lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
+      poff[j] = (uint32_t)(row * kImgRow + chunk * 16);
+      const uint32_t q16 = (uint32_t)(row * 32 + (chunk & 1) * 16);
+      voff[0][j] = chunk < 2 ? q16 : (uint32_t)(kEResid + row * 32 + (chunk - 2) * 16);
+      voff[1][j] = chunk < 2 ? (uint32_t)kEHalf + q16 : (1u << 30);
     }
-    gemm_frags16(ga, smem, wm, wn, lane);
-#define DG_EVEN(L, S) \
-  gemm_even16<L>(S, smem, ga, gb, o, acc, pimg, eo, kb0, kb_last, n_kb, col_pad, col0, voff, poff, wave, wm, wn, lane)
-#define DG_ODD(S) \
-  gemm_odd16(S, smem, gb, ga, o, acc, pimg, eo, kb0, kb_last, n_kb, col_pad, col0, voff, poff, wave, wm, wn, lane)
-    int s = 0;
-    for (; s + 1 < nsteps; s += 2) {
-      DG_EVEN(false, s);
-      DG_ODD(s + 1);
-    }
-    if (s < nsteps) {
-      // the split's last k-block has no partner: its corrections go alone.  Its
-      // stage and the next (the clamped repeat) stay intact, as no DMA follows.
-      DG_EVEN(true, s);
-      gemm_reads8a<2>(o.a23, stage16(smem, s + (lane >> 5)), wm, lane);
-      gemm_mma8<0>(o.a01, o.b, acc);
-    }
-    gemm_mma8<2>(o.a23, o.b, acc);
-#undef DG_EVEN
-#undef DG_ODD
+    // prologue: steps 0-2 in flight, 0 and 1 landed
+    gemm_dma16<false>(smem, pimg, eo, min(kb0, kb_last), col0, voff, poff, wave);
+    gemm_dma16<true>(smem + kStage, pimg, eo, min(kb0 + 1, kb_last), col0, voff, poff, wave);
+    gemm_dma16<false>(smem + 2 * kStage, pimg, eo, min(kb0 + 2, kb_last), col0, voff, poff, wave);
+    wait_vmcnt<kDma16>();
+    raw_barrier();
+    if (wave < 4)
+      gemm_loop16<true>(smem, acc, pimg, eo, kb0, kb_last, nsteps, col0, voff, poff, wave, wm, wn, lane);
+    else
+      gemm_loop16<false>(smem, acc, pimg, eo, kb0, kb_last, nsteps, col0, voff, poff, wave, wm, wn, lane);
   }
   wait_vmcnt<0>();
 
@@ -1824,11 +1845,11 @@ hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void*
   prof_begin("samp_gemm", s);
   if (eb.emb_f32)
     samp_gemm<true><<<p.n_mt * p.n_tiles * p.n_splits, kGThreads, 0, s>>>(
-        pimg, static_cast<const uint8_t*>(emb_packed), zp, p.n, p.d, p.col_pad, p.n_tiles, p.n_mt,
+        pimg, static_cast<const uint8_t*>(emb_packed), zp, p.n, p.d, p.n_tiles, p.n_mt,
         p.kb_per_split, p.n_kb, p.vocab);
   else
     samp_gemm<false><<<p.n_mt * p.n_tiles * p.n_splits, kGThreads, 0, s>>>(
-        pimg, static_cast<const uint8_t*>(emb_packed), zp, p.n, p.d, p.col_pad, p.n_tiles, p.n_mt,
+        pimg, static_cast<const uint8_t*>(emb_packed), zp, p.n, p.d, p.n_tiles, p.n_mt,
         p.kb_per_split, p.n_kb, p.vocab);
   prof_end(s);
   e = hipGetLastError();
