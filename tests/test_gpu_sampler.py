@@ -113,6 +113,29 @@ def test_ragged_shapes(n, vocab, d):
     check_z(gz, ref["z"])
 
 
+@pytest.mark.parametrize("n_kb", [2, 4, 5, 6, 7])
+def test_short_splits(n_kb):
+    """One vocabulary split of n_kb 16-id k-blocks (the last one ragged): the
+    contraction's prologue, whole pairs and a lone last k-block at the counts
+    where they meet."""
+    torch, dg = require_gpu()
+    n, vocab, d = 64, 16 * n_kb - 3, 40
+    log(f"sampler short split n_kb={n_kb} V={vocab}")
+    rng = np.random.default_rng(n_kb)
+    logits = (rng.standard_normal((n, vocab)) * 2).astype(np.float32)
+    logits[::4, vocab - 1] += 9.0
+    emb = (rng.standard_normal((vocab, d)) * 0.02).astype(np.float32)
+    emb[vocab - 1] += 1.0                      # the ragged block's row stands out in z
+    ids = rng.integers(0, vocab, n).astype(np.int32)
+    mask = (rng.random(n) < 0.2).astype(np.uint8)
+    ctrl = S.Ctrl(seed=5, gstep=2, tau=0.9, flags=S.AUTO_ADVANCE)
+    g = GpuSampler(torch, dg, emb, ids, mask, ctrl)
+    gids, gmask, gk, gz, gnu = g.step(logits)
+    ref = S.sampler_step(logits, emb, ids, mask, ctrl)
+    assert check_step(ids, mask, gids, gmask, gk, ref, 0.9) == 0
+    check_z(gz, ref["z"])
+
+
 @pytest.mark.parametrize("scale", [300.0, 1e-5, 0.02])
 def test_table_scales(scale):
     """The packed table's exponent shift at both ends: z of tables with entries
