@@ -705,10 +705,10 @@ __device__ __forceinline__ void gemm_mma8(const i32x8 (&a)[2], const i32x8 (&b)[
 //            fp8 MFMAs of row blocks 0-1.
 // Each step issues 12 MFMAs (8 fp16, 4 fp8).  Why waves 0-3 carry all the
 // DMA: the hardware gives the older of two waves on a SIMD the matrix core
-// first, so waves 0-3 (dispatched first) run ahead of waves 4-7 and used to
-// wait at the barrier; their DMA instructions, which can stall on the CU's
-// memory queue, now sit where there is slack, and waves 4-7 issue none.  The
-// two groups run the same loop (gemm_loop16) with and without the DMA.
+// first, so waves 0-3 (dispatched first) run ahead of waves 4-7 and reach the
+// barrier early; their DMA instructions, which can stall on the CU's memory
+// queue, sit where there is that slack, and waves 4-7 issue none.  The two
+// groups run the same loop (gemm_loop16) with and without the DMA.
 constexpr int kStages16 = 5;
 __device__ __forceinline__ uint8_t* stage16(uint8_t* smem, int k) { return smem + (k % kStages16) * kStage; }
 
