@@ -186,6 +186,10 @@ def main():
         # matrix-core peaks: the time they need at peak over the time taken
         "split_mfma_floor_us": round(split_floor_us, 1),
         "split_mfma_frac": round(split_floor_us / gemm_us, 4),
+        # from the committed rocprofv3 counter run of the same sources (None if
+        # stale): the clock the chip held and the matrix cores' busy fraction
+        "counters_clock_ghz": measured_counter("samp_gemm", "clock_ghz"),
+        "counters_mfma_busy": measured_counter("samp_gemm", "mfma_busy"),
         "timing": "HIP events around each launch on its stream, eager steps right after the timed region",
     }
     # the whole sampler (four kernels) against the same HBM floor, and against
@@ -738,8 +742,9 @@ def sources_sha256(kernel):
     return h.hexdigest()
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed counter summary, or None if the
+def measured_counter(kernel, field):
+    """One field of the committed counter summary for a kernel (HBM bytes per
+    launch, effective clock, matrix-core busy fraction), or None if the
     kernel's sources changed since its counters were taken."""
     try:
         with open(COUNTERS) as f:
@@ -749,7 +754,12 @@ def measured_traffic(kernel):
         return None
     if k.get("sources_sha256") != sources_sha256(kernel):
         return None
-    return k["hbm_bytes"]
+    return k.get(field)
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary (None if stale)."""
+    return measured_counter(kernel, "hbm_bytes")
 
 
 def workload_sweep(torch, dg, workloads):
