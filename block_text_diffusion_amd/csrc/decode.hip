@@ -24,10 +24,13 @@ __global__ __launch_bounds__(256) void canvas_init_kernel(int32_t* __restrict__ 
 }
 
 constexpr int kSynThreads = 256;
+constexpr int kSynGroups = 8;          // 4-id groups per thread (one Philox call each)
 constexpr float kSpike = 30.0f;
 constexpr uint32_t kChoosePerStep = 20u;
 
-// grid (ceil(V / 1024), n); each thread produces ids 4m..4m+3 from one Philox call.
+// grid (ceil(V / (4 kSynGroups kSynThreads)), n); each thread produces kSynGroups
+// groups of ids 4m..4m+3 (m strided by the workgroup size), one Philox call per
+// group.  The row's spike target is drawn once per workgroup.
 template <bool kAligned>
 __global__ __launch_bounds__(kSynThreads) void synth_logits_kernel(
     float* __restrict__ logits, const int32_t* __restrict__ ids,
@@ -58,20 +61,23 @@ __global__ __launch_bounds__(kSynThreads) void synth_logits_kernel(
   }
   __syncthreads();
   const int target = s_target;
-  const int j = 4 * (blockIdx.x * kSynThreads + t);
-  if (j >= vocab) return;
-  const Philox4 h = philox4x32_10((uint32_t)j >> 2, (uint32_t)row, gstep, kStreamSynNoise, k0, k1);
-  float v[4] = {table[h.w0 >> 16], table[h.w1 >> 16], table[h.w2 >> 16], table[h.w3 >> 16]};
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (j + e == target) v[e] = v[e] + kSpike;
-  float* dst = logits + (size_t)row * vocab + j;
-  if (kAligned && j + 3 < vocab) {
-    *reinterpret_cast<f32x4*>(dst) = (f32x4){v[0], v[1], v[2], v[3]};
-  } else {
+#pragma unroll 2
+  for (int g = 0; g < kSynGroups; ++g) {
+    const int j = 4 * ((blockIdx.x * kSynGroups + g) * kSynThreads + t);
+    if (j >= vocab) return;
+    const Philox4 h = philox4x32_10((uint32_t)j >> 2, (uint32_t)row, gstep, kStreamSynNoise, k0, k1);
+    float v[4] = {table[h.w0 >> 16], table[h.w1 >> 16], table[h.w2 >> 16], table[h.w3 >> 16]};
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (j + e < vocab) dst[e] = v[e];
+      if (j + e == target) v[e] = v[e] + kSpike;
+    float* dst = logits + (size_t)row * vocab + j;
+    if (kAligned && j + 3 < vocab) {
+      *reinterpret_cast<f32x4*>(dst) = (f32x4){v[0], v[1], v[2], v[3]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j + e < vocab) dst[e] = v[e];
+    }
   }
 }
 
@@ -176,7 +182,7 @@ hipError_t launch_synth_logits(float* logits, const int32_t* ids, const uint8_t*
                                const dg_ctrl* ctrl, const float* table, int table_size, int n,
                                int vocab, hipStream_t s) {
   (void)table_size;
-  const dim3 grid((vocab + 4 * kSynThreads - 1) / (4 * kSynThreads), n);
+  const dim3 grid((vocab + 4 * kSynGroups * kSynThreads - 1) / (4 * kSynGroups * kSynThreads), n);
   prof_begin("synth_logits", s);
   if (vocab % 4 == 0)
     synth_logits_kernel<true><<<grid, kSynThreads, 0, s>>>(logits, ids, committed, ctrl, table, n, vocab);
