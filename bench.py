@@ -40,6 +40,7 @@ KERNEL_SOURCES = {
 }
 BF16_PEAK_TFLOPS = 2516.6
 FP8_PEAK_TFLOPS = 5000.0
+FP6_PEAK_TFLOPS = 10100.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
 SAMPLER_KERNELS = ("samp_stats", "samp_gemm", "samp_combine", "samp_finalize")
 
@@ -159,14 +160,14 @@ def main():
 
     # Algorithmic work of the dominant kernel per launch (one step): the method
     # reads the logits and E once and writes z, and does 2 N V d flops.  The
-    # contraction runs one fp16 product and two fp8 correction products per
+    # contraction runs one fp16 product and two fp6 correction products per
     # fp32-accurate one; at 412.3 GFLOP over 3.493 GB (118 flop/B) it is below
     # the fp16 ridge (2516.6 / 8 = 315 flop/B), so the bound is HBM bandwidth.
     gemm_us = per_kernel_us["samp_gemm"]
     flops_method = 2.0 * n * vocab * dm                         # softmax(l)·E
-    flops_fp16, flops_fp8 = flops_method, 2.0 * flops_method    # the products the matrix cores execute
-    # matrix-core time at the datasheet peaks (fp16 = bf16 rate, fp8 twice it)
-    split_floor_us = (flops_fp16 / BF16_PEAK_TFLOPS + flops_fp8 / FP8_PEAK_TFLOPS) / 1e12 * 1e6
+    flops_fp16, flops_fp6 = flops_method, 2.0 * flops_method    # the products the matrix cores execute
+    # matrix-core time at the datasheet peaks (fp16 = bf16 rate, fp6 four times it)
+    split_floor_us = (flops_fp16 / BF16_PEAK_TFLOPS + flops_fp6 / FP6_PEAK_TFLOPS) / 1e12 * 1e6
     bytes_method = 4.0 * (n * vocab + vocab * dm + n * dm)      # logits + E + z, each once
     gbs = bytes_method / (gemm_us * 1e-6) / 1e9
     roofline = {
@@ -182,7 +183,7 @@ def main():
         "algorithmic_flops": flops_method,
         "arithmetic_intensity": round(flops_method / bytes_method, 1),
         "hbm_floor_us": round(bytes_method / (HBM_PEAK_GBS * 1e9) * 1e6, 1),
-        # the split-precision products (fp16 + two fp8) against the datasheet
+        # the split-precision products (fp16 + two fp6) against the datasheet
         # matrix-core peaks: the time they need at peak over the time taken
         "split_mfma_floor_us": round(split_floor_us, 1),
         "split_mfma_frac": round(split_floor_us / gemm_us, 4),
@@ -224,8 +225,8 @@ def main():
                                  # the contraction's bytes are almost all reads
                                  "measured_read_peak": probes["read_gbs"],
                                  "frac_of_read": round(gbs / probes["read_gbs"], 4),
-                                 # the probe measures bf16; fp16 runs at that rate, fp8 at twice it
-                                 "split_mfma_frac": round((flops_fp16 + flops_fp8 / 2) / (gemm_us * 1e-6) / 1e12
+                                 # the probe measures bf16; fp16 runs at that rate, fp6 at four times it
+                                 "split_mfma_frac": round((flops_fp16 + flops_fp6 / 4) / (gemm_us * 1e-6) / 1e12
                                                           / probes["mfma_tflops"], 4)}
         sampler["frac_measured_hbm"] = round(bytes_method / (probes["copy_gbs"] * 1e9) * 1e6 / samp_us, 4)
         attn["roofline"]["secondary"] = {"measured_peak": probes["mfma_tflops"], "unit": "TFLOP/s",
@@ -301,9 +302,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        # attention in bf16; the sampler's contraction in fp16 + fp8 products
+        # attention in bf16; the sampler's contraction in fp16 + fp6 products
         # with fp32 accumulation, its softmax statistics in fp32
-        "dtype": "bf16+fp16+fp8+f32",
+        "dtype": "bf16+fp16+fp6+f32",
         "data": "synthetic",
         "config": {"workload": "long_context_step: canvas 256, prefix 4096, 16q/8kv heads, head_dim 128 "
                                "bf16; vocab 262144, d_model 3072 fp32; one captured graph per step",

@@ -132,7 +132,7 @@ def dg_embedding_packed_bytes(vocab, d_model):
 
 
 def dg_embedding_pack(emb, packed=None, stream=None):
-    """E [V, d] float32 on the GPU -> the split-bf16 layout dg_sampler_step streams (uint8 tensor)."""
+    """E [V, d] float32 on the GPU -> the fp16 + fp6 layout dg_sampler_step streams (uint8 tensor)."""
     torch = _torch()
     _need(emb, "emb", (torch.float32,))
     vocab, d = emb.shape

@@ -17,7 +17,7 @@
 //   samp_gemm      z_s = sum_j p_j E_j over one split for a 256 x 256 tile, both
 //                  operands streamed through LDS, fp32 accumulation.  On the
 //                  packed table (dg_embedding_pack) each product is one fp16
-//                  term plus two fp8 corrections (below); on the plain float32
+//                  term plus two fp6 corrections (below); on the plain float32
 //                  table E is split into bf16 hi / lo while it streams and the
 //                  product is bf16x3 (p_hi E_hi + p_hi E_lo + p_lo E_hi).
 //   samp_combine   per row: merge the split statistics (log-sum-exp), the
@@ -25,20 +25,26 @@
 //                  z = sum_s 2^((m_s - m) log2 e) z_s / S.
 //   samp_finalize  count open positions; advance the step counters.
 //
-// fp16 + fp8 split precision.  With P = p 2^14 (p <= 1) and Q = E 2^c, where
-// c puts max|Q| in [2^7, 2^8), P16 = fp16(P), Pe = P - P16, Q16 = fp16(Q),
-// Qe = Q - Q16, the contraction sums
-//     P16 Q16  +  2^-5 [ fp8(P 2^-6) fp8(Qe 2^11)  +  fp8(Pe 2^5) fp8(Q16) ]
-// = PQ + Pe Qe + (the fp8 roundings of the two correction terms).
-// fp16 x fp16 products are exact in fp32; the corrections are 2^-11 of a term
-// and carry fp8 (e4m3) relative error <= 2^-4, so each term is within about
-// 2^-14 of P Q.  The exponents keep every fp8 operand at most 256 (e4m3 holds
-// 448).  The table stores Q16 and fp8(Qe 2^11), 3 bytes per element;
-// fp8(Q16) is formed in the contraction.  One v_mfma_f32_32x32x16_f16 per 16
-// ids and one v_mfma_scale_f32_32x32x64_f8f6f4 per 32 ids (corrections of two
-// k-blocks side by side in K, block scale 2^-5 on A): the work of two bf16
-// products instead of bf16x3's three.  The combine multiplies by 2^-(14 + c),
-// which dg_embedding_pack stores after the table.
+// fp16 + fp6 split precision.  The table holds each row at its own scale:
+// Q_k = E_k 2^(c + d_k), where c puts max|E| 2^c in [2^7, 2^8) and the row
+// shift d_k (0-40) brings row k's own maximum there as well; the weights carry
+// the inverse shift, P'_k = p_k 2^(14 - d_k), so P'_k Q_k = 2^(14 + c) p_k E_k.
+// With P'16 = fp16(P'), Q16 = fp16(Q), the contraction sums
+//     P'16 Q16  +  P'16 (Q - Q16)  +  (P' - P'16) Q16
+// = P'Q - (P' - P'16)(Q - Q16), the first term on fp16 matrix cores (exact
+// products, fp32 sums), the two corrections (2^-11 of a term) on fp6 ones:
+// e2m3 codes (three mantissa bits, 7.5 at most) under power-of-two block
+// scales, one per row and 16-id k-block on the p side (the codes of P'16 and of
+// fp16((P' - P'16) 2^11)) and one per 16-id k-block and 64-column group on
+// the table side (the codes of (Q - Q16) 2^11 and of Q16).  A code keeps
+// relative error <= 2^-4 unless it is far below its block's largest value;
+// the row shifts keep the table's rows level, so that a block's small values
+// belong to small terms.  The table stores Q16, the codes of (Q - Q16) 2^11 and
+// their scale (3 bytes per element) and one shift byte per id; the codes of
+// Q16 are formed in the contraction.  One v_mfma_f32_32x32x16_f16 per 16 ids
+// and one v_mfma_scale_f32_32x32x64_f8f6f4 (fp6 x fp6, per-lane scales) per
+// 32 ids (the corrections of two k-blocks side by side in K).  The combine
+// multiplies by 2^-(14 + c), which dg_embedding_pack stores after the table.
 #include "dg_common.hpp"
 #include "dg_internal.hpp"
 
@@ -78,62 +84,75 @@ constexpr int kStatsThreads = 256;
 // Record layouts of one 64-byte slot (16 ids of one row of p, or one column of E
 // in LDS):
 //   bf16x3:    bf16 hi of ids 0-15 | bf16 lo of ids 0-15
-//   fp16 + fp8 (p side):  fp16 P16 of ids 0-15 | fp8 P 2^-6 | fp8 Pe 2^5
-//   fp16 + fp8 (E side, in LDS):  fp16 Q16 of ids 0-15 | fp8 Qe 2^11 of this
-//              k-block and of the next (even k-blocks only)
-constexpr float kPScale = 16384.0f;    // P = p 2^14
+//   fp16 + fp6 (p side):  fp16 P'16 of ids 0-15 | 32 e2m3 codes (24 bytes) |
+//              scale byte | 7 zero bytes (p_record)
+//   fp16 + fp6 (E side, in LDS):  fp16 Q16 of ids 0-15 | the residual chunks
+//              of this k-block and of the next (even k-blocks only), each 12
+//              bytes of e2m3 codes, a scale byte and 3 zero bytes
+constexpr int kPExp = 14;              // P = p 2^14 (before the row shift)
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x32 __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
 
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, (f16x2){(_Float16)a, (_Float16)b});
 }
 
-// four fp32 values to four e4m3 bytes (round to nearest even), id order
-__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+// e2m3 code (sign in bit 5, two exponent bits of bias 1, three mantissa bits)
+// of v, |v| <= 7.5, rounded to the nearest value with ties to the even code.
+// Below 1 the values are spaced 1/8 apart, so the code is rint(8 |v|) (8 is the
+// code of 1.0); from 1 up the float's mantissa is rounded to three bits and
+// its exponent rebiased from 127 to 1.  NaN gives 31.
+__device__ __forceinline__ uint32_t e2m3_code(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t ab = b & 0x7fffffffu;
+  const float a = __uint_as_float(ab);
+  const uint32_t nrm = min(((ab + 0x7ffffu + ((ab >> 20) & 1u)) >> 20) - 1008u, 31u);
+  const uint32_t sub = (uint32_t)__builtin_rintf(a * 8.0f);
+  return (a < 1.0f ? sub : nrm) | ((b >> 26) & 32u);
 }
 
-// Four weights P = p 2^14 as fp16 P16 (two dwords), e4m3 of P 2^-6 and e4m3 of
-// (P - P16) 2^5 (one dword each, id order).
-__device__ __forceinline__ void split_p(const float (&x)[4], uint32_t (&h16)[2], uint32_t& p8, uint32_t& pe8) {
-  h16[0] = pack_f16x2(x[0], x[1]);
-  h16[1] = pack_f16x2(x[2], x[3]);
-  float r[4];
+// The smallest e >= lo with m <= 7.5 2^e (m >= 0): for m = 1.f 2^E that is
+// E - 2, plus one when 1.f > 1.875.
+__device__ __forceinline__ int e2m3_scale_exp(float m, int lo) {
+  const uint32_t b = __float_as_uint(m);
+  return max((int)(b >> 23) - 129 + (int)((b & 0x7fffffu) > 0x700000u), lo);
+}
+
+// The correction half of a p record from the 16 weights P' of one row and
+// k-block (P' = p 2^(14 - d), d the id's row shift in the table): fp16 P'16
+// (eight dwords, id order), then 32 e2m3 codes (six dwords): P'16 of ids
+// 0-15 and r = fp16((P' - P'16) 2^11) of ids 0-15, both divided by 2^es, the
+// smallest power of two (at least 2^-116) that brings the largest of the 32
+// fp16 values to 7.5 or below (the conversion rounds to nearest, ties to the
+// even code); then the E8M0 byte 116 + es (so the matrix core multiplies the
+// codes by 2^(es - 11)) and a zero dword.
+__device__ __forceinline__ void p_record(const float (&x)[16], u32x4 (&rec)[4]) {
+  // w: P'16 of ids 0-15 (dwords 0-7), then r of ids 0-15 (dwords 8-15)
+  u32x16 w;
+  float mx = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const f16x2 h = __builtin_bit_cast(f16x2, h16[e >> 1]);
-    r[e] = x[e] - (float)h[e & 1];
+  for (int k = 0; k < 8; ++k) {
+    w[k] = pack_f16x2(x[2 * k], x[2 * k + 1]);
+    const f16x2 hh = __builtin_bit_cast(f16x2, (uint32_t)w[k]);
+    // (P' - P'16) 2^11, exact: both products are exact and so is their sum
+    const float r0 = __builtin_fmaf((float)hh[0], -2048.0f, x[2 * k] * 2048.0f);
+    const float r1 = __builtin_fmaf((float)hh[1], -2048.0f, x[2 * k + 1] * 2048.0f);
+    w[8 + k] = pack_f16x2(r0, r1);
+    mx = fmaxf(mx, fmaxf(fmaxf(x[2 * k], x[2 * k + 1]), fmaxf(fabsf(r0), fabsf(r1))));
   }
-  p8 = pack_fp8x4(x[0] * 0.015625f, x[1] * 0.015625f, x[2] * 0.015625f, x[3] * 0.015625f);
-  pe8 = pack_fp8x4(r[0] * 32.0f, r[1] * 32.0f, r[2] * 32.0f, r[3] * 32.0f);
-}
-
-// Four table values Q as fp16 Q16 (two dwords) and e4m3 of (Q - Q16) 2^11.
-__device__ __forceinline__ void split_q(const float (&x)[4], uint32_t (&h16)[2], uint32_t& qe8) {
-  h16[0] = pack_f16x2(x[0], x[1]);
-  h16[1] = pack_f16x2(x[2], x[3]);
-  float r[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const f16x2 h = __builtin_bit_cast(f16x2, h16[e >> 1]);
-    r[e] = (x[e] - (float)h[e & 1]) * 2048.0f;
-  }
-  qe8 = pack_fp8x4(r[0], r[1], r[2], r[3]);
-}
-
-// Four fp16 values (two dwords) to four e4m3 bytes, round to nearest even, no
-// scale (v_cvt_scalef32_pk_fp8_f16 with scale 1).
-typedef short i16x2 __attribute__((ext_vector_type(2)));
-// Both words of old are replaced; passing the value the result overwrites lets
-// the conversions write that register in place.
-__device__ __forceinline__ uint32_t f16x4_to_fp8(uint32_t old, uint32_t lo, uint32_t hi) {
-  i16x2 r = __builtin_bit_cast(i16x2, old);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, __builtin_bit_cast(f16x2, lo), 1.0f, false);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, __builtin_bit_cast(f16x2, hi), 1.0f, true);
-  return __builtin_bit_cast(uint32_t, r);
+  // the largest of the 32 fp16 values: fp16 rounding is monotonic, so it is
+  // the fp16 rounding of the largest float
+  const int es = e2m3_scale_exp((float)(_Float16)mx, -116);
+  const u32x6 c = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(__builtin_bit_cast(f16x32, w),
+                                                              __uint_as_float((uint32_t)(127 + es) << 23));
+  rec[0] = (u32x4){w[0], w[1], w[2], w[3]};
+  rec[1] = (u32x4){w[4], w[5], w[6], w[7]};
+  rec[2] = (u32x4){c[0], c[1], c[2], c[3]};
+  rec[3] = (u32x4){c[4], c[5], (uint32_t)(116 + es), 0u};
 }
 
 __device__ __forceinline__ float rescale_factor(float m_old, float m_new, float c) {
@@ -197,8 +216,11 @@ constexpr int kStatsThreadsWG = 64 * kStatsRows * kStatsWavesPerRow;
 // consecutive logits, and lanes 4k .. 4k + 3 hold one k-block.  The logits
 // are read from HBM once and kept in registers: the split maximum is reduced
 // first, then the same registers give exp(l - m_s), the sums and the p
-// image records (kF16: fp16 + fp8, else bf16 hi / lo).  Each round's image
-// slots are staged in LDS as
+// image records (kF16: fp16 + fp6 from p_record, else bf16 hi / lo).  For the
+// fp6 records a lane needs a whole k-block: each quad passes its weights
+// through a per-wave LDS area so that lane 4k + q takes k-block 64 q + k' of
+// the round (k' = L / 4), all 16 ids.  Each round's image slots are staged in
+// LDS as
 // [k-block][2 rows][64 B] and leave as 1 KB per store instruction (8 k-blocks'
 // 128-byte lines; staging through LDS measured faster than storing from the
 // registers, and whole lines measured faster than one row's 64-byte halves).
@@ -206,10 +228,14 @@ template <bool kAligned, bool kF16>
 __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __restrict__ logits,
                                                               const dg_ctrl* __restrict__ ctrl,
                                                               StatsPartial* __restrict__ part,
-                                                              uint8_t* __restrict__ pimg, int n_rows,
+                                                              uint8_t* __restrict__ pimg,
+                                                              const uint8_t* __restrict__ shifts, int n_rows,
                                                               int n_canvas, int vocab, int kb_per_split,
                                                               int n_kb, bool want_h) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[kStatsLanes * kStatsRows * kImgRow];
+  // kF16: each wave's weights of one round, regrouped so that a lane holds one
+  // whole k-block (4 KB per wave)
+  __shared__ __attribute__((aligned(16))) uint8_t regroup[kF16 ? kStatsThreadsWG / 64 * 4096 : 16];
   __shared__ StatsPartial red[kStatsRows][kStatsWavesPerRow];
   const int split = blockIdx.x;
   const int t = threadIdx.x;
@@ -296,6 +322,12 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
   for (int i = 0; i < kStatsIters; ++i) {
     const int base = kb0 + kStatsLanes * i;
     if (base >= kb1) break;   // uniform over the workgroup
+    // kF16: this lane's k-block of the round (64 (L % 4) + L / 4) and its ids' row shifts
+    const int kbl = base + 64 * (L % 4) + L / 4;
+    u32x4 dsh = (u32x4){0u, 0u, 0u, 0u};
+    if constexpr (kF16)
+      if (kbl < kb1) dsh = *reinterpret_cast<const u32x4*>(shifts + (size_t)kbl * kKB);
+    uint8_t* rg = regroup + (kF16 ? (wave * 4096 + (lane >> 2) * 64) : 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int c = 4 * i + q;
@@ -312,21 +344,34 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
         }
       }
       // k-block 64 q + L / 4 of the round, ids 4 (L % 4) .. 4 (L % 4) + 3 of it
-      uint8_t* slot = stage + ((kStatsLanes / 4 * q + L / 4) * kStatsRows + r) * kImgRow;
       if constexpr (kF16) {
-        const float P[4] = {pp[0] * kPScale, pp[1] * kPScale, pp[2] * kPScale, pp[3] * kPScale};
-        uint32_t h16[2], c8, e8;
-        split_p(P, h16, c8, e8);
-        *reinterpret_cast<uint2*>(slot + (L % 4) * 8) = make_uint2(h16[0], h16[1]);
-        *reinterpret_cast<uint32_t*>(slot + 32 + (L % 4) * 4) = c8;
-        *reinterpret_cast<uint32_t*>(slot + 48 + (L % 4) * 4) = e8;
+        // to the lane of this quad that takes k-block 64 q + L / 4 (chunk
+        // position xor-swizzled by the lane's place in the quad)
+        *reinterpret_cast<f32x4*>(rg + q * 1024 + 16 * ((L % 4) ^ q)) = (f32x4){pp[0], pp[1], pp[2], pp[3]};
       } else {
+        uint8_t* slot = stage + ((kStatsLanes / 4 * q + L / 4) * kStatsRows + r) * kImgRow;
         uint32_t hi[2], lo[2];
         split2(pp[0], pp[1], hi[0], lo[0]);
         split2(pp[2], pp[3], hi[1], lo[1]);
         *reinterpret_cast<uint2*>(slot + (L % 4) * 8) = make_uint2(hi[0], hi[1]);
         *reinterpret_cast<uint2*>(slot + 32 + (L % 4) * 8) = make_uint2(lo[0], lo[1]);
       }
+    }
+    if constexpr (kF16) {
+      // the 16 weights of k-block kbl (the quad's lanes wrote them in this
+      // wave, so no barrier is needed), scaled by 2^(14 - d) per id
+      float x[16];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(rg + (L % 4) * 1024 + 16 * (k ^ (L % 4)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * k + e] = __builtin_ldexpf(w4[e], kPExp - (int)((dsh[k] >> (8 * e)) & 0xffu));
+      }
+      u32x4 rec[4];
+      p_record(x, rec);
+      u32x4* slot = reinterpret_cast<u32x4*>(stage + ((kStatsLanes / 4 * (L % 4) + L / 4) * kStatsRows + r) * kImgRow);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) slot[k] = rec[k];
     }
     __syncthreads();
     // write-out: the row slots of k-block kbl are contiguous; thread T moves
@@ -361,14 +406,17 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
 }
 
 // ---------------------------------------------------------------------------
-// E packing: Q = E 2^c as fp16 Q16 plus e4m3 of (Q - Q16) 2^11.  Columns are
-// padded to whole 256-column tiles and ids to whole pairs of 16-id k-blocks
-// (zeros).  For each k-block pair j and column tile t, one 24 KB block at
-// ((j n_tiles + t) 24 KB): the Q16 records of k-block 2j (256 columns x 32 B:
-// ids 0-7, ids 8-15), those of k-block 2j + 1, then 256 columns x 32 B of
-// residual bytes (16 for k-block 2j, 16 for 2j + 1).  After the blocks:
-// kAmaxParts partial maxima of |E| (working space of the pack) and the
-// PackTail record.
+// E packing: Q_k = E_k 2^(c + d_k) as fp16 Q16 plus the e2m3 codes of
+// (Q - Q16) 2^11.  Columns are padded to whole 256-column tiles and ids to
+// whole pairs of 16-id k-blocks (zeros).  For each k-block pair j and column
+// tile t, one 24 KB block at ((j n_tiles + t) 24 KB): the Q16 records of
+// k-block 2j (256 columns x 32 B: ids 0-7, ids 8-15), those of k-block 2j + 1,
+// then 256 columns x 32 B of residual chunks (16 B for k-block 2j, 16 for
+// 2j + 1: 12 bytes of codes, code i at bit 6i, under the scale 2^eB of the
+// k-block and 64-column group, then the byte 127 + eB and three zeros).  After
+// the blocks: the row shifts d_k (one byte per id of the padded vocabulary,
+// 256-byte aligned), kAmaxParts partial maxima of |E| (working space of the
+// pack) and the PackTail record.
 // ---------------------------------------------------------------------------
 constexpr int kEBlock = 24576;          // bytes per (k-block pair, column tile)
 constexpr int kEHalf = 8192;            // Q16 records of one k-block and tile
@@ -433,37 +481,80 @@ __global__ __launch_bounds__(256) void emb_scale_kernel(const float* __restrict_
 
 // grid (2 n_pairs, n_tiles): one thread per column and k-block (k-blocks on x,
 // which takes the large count).
+// Row shifts: d_k = min(max(8 - c - e_k, 0), 40) for max|E_k| in
+// [2^(e_k - 1), 2^e_k), so that max|E_k| 2^(c + d_k) lies in [2^7, 2^8) unless
+// capped.  Rows without a positive finite maximum (zero rows) and ids past
+// vocab take the largest shift, 40: their weights P' = P 2^-40 then never set
+// a k-block's correction scale.  One wave per id.
+__global__ __launch_bounds__(256) void emb_shift_kernel(const float* __restrict__ emb, int vocab, int d,
+                                                        int n_ids, const PackTail* __restrict__ tail,
+                                                        uint8_t* __restrict__ shifts) {
+  const int id = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (id >= n_ids) return;   // uniform over the wave
+  float m = 0.0f;
+  if (id < vocab)
+    for (int j = lane; j < d; j += 64) m = fmaxf(m, fabsf(emb[(size_t)id * d + j]));
+  m = wave_max(m);
+  if (lane == 0) {
+    int sh = 40;
+    if (m > 0.0f && m <= 3.4028234663852886e38f) {
+      int e;
+      (void)frexpf(m, &e);
+      sh = min(max(8 - tail->c - e, 0), 40);
+    }
+    shifts[id] = (uint8_t)sh;
+  }
+}
+
 __global__ __launch_bounds__(256) void emb_pack_kernel(const float* __restrict__ emb,
                                                        uint8_t* __restrict__ out, int vocab, int d,
-                                                       int n_tiles, const PackTail* __restrict__ tail) {
+                                                       int n_tiles, const PackTail* __restrict__ tail,
+                                                       const uint8_t* __restrict__ shifts) {
   const int cl = threadIdx.x;                 // column within the tile
   const int tile = blockIdx.y;
   const int col = tile * 256 + cl;
   const int kb = blockIdx.x;
-  const float sc = ldexpf(1.0f, tail->c);
-  uint32_t h16[8], qe8[4];
+  const int c = tail->c;
+  uint32_t h16[8];
+  float qe[16];
+  float mx = 0.0f;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    float x[4];
+  for (int g = 0; g < 8; ++g) {
+    float x[2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int k = kb * kKB + 4 * g + e;
-      x[e] = (k < vocab && col < d) ? emb[(size_t)k * d + col] * sc : 0.0f;
+    for (int e = 0; e < 2; ++e) {
+      const int k = kb * kKB + 2 * g + e;
+      x[e] = (k < vocab && col < d) ? ldexpf(emb[(size_t)k * d + col], c + (int)shifts[k]) : 0.0f;
     }
-    uint32_t h[2];
-    split_q(x, h, qe8[g]);
-    h16[2 * g] = h[0];
-    h16[2 * g + 1] = h[1];
+    h16[g] = pack_f16x2(x[0], x[1]);
+    const f16x2 h = __builtin_bit_cast(f16x2, h16[g]);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      qe[2 * g + e] = (x[e] - (float)h[e]) * 2048.0f;
+      mx = fmaxf(mx, fmaxf(fabsf(qe[2 * g + e]), fabsf((float)h[e])));
+    }
+  }
+  // one scale per k-block and 64-column group (the group one wave holds)
+  const int eb = e2m3_scale_exp(wave_max(mx), -126);
+  const float inv = __uint_as_float((uint32_t)(127 - eb) << 23);
+  uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t c = e2m3_code(qe[i] * inv);
+    const int bit = 6 * i;
+    w[bit / 32] |= c << (bit % 32);
+    if (bit % 32 > 26) w[bit / 32 + 1] |= c >> (32 - bit % 32);
   }
   uint8_t* blk = out + ((size_t)(kb >> 1) * n_tiles + tile) * kEBlock;
   uint8_t* q = blk + (kb & 1) * kEHalf + cl * 32;
   *reinterpret_cast<u32x4*>(q) = (u32x4){h16[0], h16[1], h16[2], h16[3]};
   *reinterpret_cast<u32x4*>(q + 16) = (u32x4){h16[4], h16[5], h16[6], h16[7]};
-  *reinterpret_cast<u32x4*>(blk + kEResid + cl * 32 + (kb & 1) * 16) = (u32x4){qe8[0], qe8[1], qe8[2], qe8[3]};
+  *reinterpret_cast<u32x4*>(blk + kEResid + cl * 32 + (kb & 1) * 16) = (u32x4){w[0], w[1], w[2], (uint32_t)(127 + eb)};
 }
 
 // ---------------------------------------------------------------------------
-// z_s = p · E over one split on MFMA (fp16 + fp8 on the packed table, bf16x3
+// z_s = p · E over one split on MFMA (fp16 + fp6 on the packed table, bf16x3
 // on the float32 table).  A four-stage LDS pipeline fed
 // by direct global-to-LDS loads: no staging registers and no LDS store
 // instructions; the fragments of the next step are read while the MFMAs of
@@ -591,14 +682,16 @@ __device__ __forceinline__ void gemm_mma(const Frags& f, f32x16 (&acc)[4][2]) {
     }
 }
 
-// fp16 + fp8 operands.  The fp16 fragments of one k step are the first two
+// fp16 + fp6 operands.  The fp16 fragments of one k step are the first two
 // chunks of the slots (ids 8h .. 8h + 7 for lane half h, as in the bf16 case).
-// The fp8 corrections of k-blocks s and s + 1 (s even) feed one 32 x 32 x 64
-// MFMA per output block: lane half h supplies the 32 correction bytes of
-// k-block s + h, and A and B pair byte for byte: A = [fp8(P 2^-6) | fp8(Pe 2^5)]
-// (chunks 2 and 3 of the p slot, in k-block s + h's stage), B = [fp8(Qe 2^11) |
-// fp8(Q16)] (the residual chunk 2 + h in stage s, and Q16 of k-block s + h
-// converted).
+// The fp6 corrections of k-blocks s and s + 1 (s even) feed one 32 x 32 x 64
+// MFMA per output block: lane half h supplies the 32 codes of k-block s + h
+// (six dwords) and their scale, which the MFMA applies to exactly those 32
+// products; A and B pair code for code: A = [codes of P'16 | codes of r]
+// (record dwords 8-13 of the p slot, scale dword 14, in k-block s + h's
+// stage), B = [codes of (Q - Q16) 2^11 | codes of Q16] (the residual chunk
+// 2 + h in stage s with its scale byte, and Q16 of k-block s + h converted
+// under that scale).
 struct Frags16 {
   f16x8 a[4], b[2];
 };
@@ -613,29 +706,28 @@ __device__ __forceinline__ void gemm_frags16(Frags16& f, const uint8_t* stage, i
     f.b[i] = *reinterpret_cast<const f16x8*>(stage + kArr + swz_off(64 * wn + 32 * i + (lane & 31), h));
 }
 
-__device__ __forceinline__ i32x8 join8(const u32x4& x, const u32x4& y) {
-  return (i32x8){(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
-}
-
-// A bytes of row blocks kMb0 and kMb0 + 1, from this lane's stage (k-block s + h)
+// A codes and scale byte of row blocks kMb0 and kMb0 + 1, from this lane's
+// stage (k-block s + h): the record's dwords 8-13 (e2m3 codes) and 14 (scale)
 template <int kMb0>
-__device__ __forceinline__ void gemm_reads8a(i32x8 (&a)[2], const uint8_t* stage_h, int wm, int lane) {
+__device__ __forceinline__ void gemm_reads6a(i32x8 (&a)[2], int (&sa)[2], const uint8_t* stage_h, int wm, int lane) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int ra = 128 * wm + 32 * (kMb0 + i) + (lane & 31);
-    a[i] = join8(*reinterpret_cast<const u32x4*>(stage_h + swz_off(ra, 2)),
-                 *reinterpret_cast<const u32x4*>(stage_h + swz_off(ra, 3)));
+    const u32x4 c2 = *reinterpret_cast<const u32x4*>(stage_h + swz_off(ra, 2));
+    const u32x4 c3 = *reinterpret_cast<const u32x4*>(stage_h + swz_off(ra, 3));
+    a[i] = (i32x8){(int)c2[0], (int)c2[1], (int)c2[2], (int)c2[3], (int)c3[0], (int)c3[1], 0, 0};
+    sa[i] = (int)c3[2];
   }
 }
 
-// B: the residual bytes (chunk 2 + h of stage s) now, and the 16 Q16 values of
-// k-block s + h (two chunks) raw, for gemm_convert8b.  The Q16 chunks are read
+// B: the residual codes and scale (chunk 2 + h of stage s) now, and the 16 Q16 values of
+// k-block s + h (two chunks) raw, for gemm_convert6b.  The Q16 chunks are read
 // first, so their conversion waits for the fewest reads.
-struct Raw8 {
+struct Raw6 {
   u32x4 q0[2], q1[2];
 };
 
-__device__ __forceinline__ void gemm_reads8b(i32x8 (&b)[2], Raw8& r, const uint8_t* stage_s,
+__device__ __forceinline__ void gemm_reads6b(i32x8 (&b)[2], int& sb, Raw6& r, const uint8_t* stage_s,
                                              const uint8_t* stage_h, int wn, int lane) {
   const int h = lane >> 5;
 #pragma unroll
@@ -648,22 +740,29 @@ __device__ __forceinline__ void gemm_reads8b(i32x8 (&b)[2], Raw8& r, const uint8
   for (int i = 0; i < 2; ++i) {
     const int rb = 64 * wn + 32 * i + (lane & 31);
     const u32x4 qe = *reinterpret_cast<const u32x4*>(stage_s + kArr + swz_off(rb, 2 + h));
-    // the upper half is written by gemm_convert8b
+    // dwords 3-5 are written by gemm_convert6b; both column blocks lie in one
+    // 64-column group and carry the same scale byte
 #pragma unroll
-    for (int e = 0; e < 4; ++e) b[i][e] = (int)qe[e];
+    for (int e = 0; e < 3; ++e) b[i][e] = (int)qe[e];
+    if (i == 0) sb = (int)qe[3];
   }
 }
 
-// B's second half, fp8(Q16).  kLone: k-block s is the split's last and has no
-// partner, so lane half 1 contributes zero.
+// B's second half, the codes of Q16 of both column blocks, in one conversion
+// under the group's scale (e2m3 of Q16 / 2^eB, nearest, ties to the even
+// code).  kLone: k-block s is the split's last and has no partner, so lane
+// half 1 contributes zero.
 template <bool kLone>
-__device__ __forceinline__ void gemm_convert8b(i32x8 (&b)[2], const Raw8& r, int lane) {
+__device__ __forceinline__ void gemm_convert6b(i32x8 (&b)[2], int sb, const Raw6& r, int lane) {
+  const u32x16 w = (u32x16){r.q0[0][0], r.q0[0][1], r.q0[0][2], r.q0[0][3], r.q1[0][0], r.q1[0][1],
+                            r.q1[0][2], r.q1[0][3], r.q0[1][0], r.q0[1][1], r.q0[1][2], r.q0[1][3],
+                            r.q1[1][0], r.q1[1][1], r.q1[1][2], r.q1[1][3]};
+  const u32x6 c = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(__builtin_bit_cast(f16x32, w),
+                                                              __uint_as_float((uint32_t)sb << 23));
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    b[i][4] = (int)f16x4_to_fp8((uint32_t)b[i][4], r.q0[i][0], r.q0[i][1]);
-    b[i][5] = (int)f16x4_to_fp8((uint32_t)b[i][5], r.q0[i][2], r.q0[i][3]);
-    b[i][6] = (int)f16x4_to_fp8((uint32_t)b[i][6], r.q1[i][0], r.q1[i][1]);
-    b[i][7] = (int)f16x4_to_fp8((uint32_t)b[i][7], r.q1[i][2], r.q1[i][3]);
+#pragma unroll
+    for (int e = 0; e < 3; ++e) b[i][3 + e] = (int)c[3 * i + e];
     if (kLone && lane >= 32) b[i] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
   }
 }
@@ -676,16 +775,17 @@ __device__ __forceinline__ void gemm_mma16(const Frags16& f, f32x16 (&acc)[4][2]
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[mb], f.b[nb], acc[mb][nb], 0, 0, 0);
 }
 
-// fp8 MFMAs of row blocks kMb0, kMb0 + 1: e4m3 x e4m3 (format selectors 0),
-// block scale 2^-5 on A (E8M0 122), 1 on B
+// fp6 MFMAs of row blocks kMb0, kMb0 + 1: e2m3 x e2m3 (format selectors 2;
+// six dwords of each operand are read), per-lane E8M0 scales from the records
 template <int kMb0>
-__device__ __forceinline__ void gemm_mma8(const i32x8 (&a)[2], const i32x8 (&b)[2], f32x16 (&acc)[4][2]) {
+__device__ __forceinline__ void gemm_mma6(const i32x8 (&a)[2], const int (&sa)[2], const i32x8 (&b)[2], int sb,
+                                          f32x16 (&acc)[4][2]) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
       acc[kMb0 + i][nb] =
-          __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[nb], acc[kMb0 + i][nb], 0, 0, 0, 122, 0, 127);
+          __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[nb], acc[kMb0 + i][nb], 2, 2, 0, sa[i], 0, sb);
 }
 
 // The packed-table pipeline keeps five LDS stages and synchronises once per
@@ -695,15 +795,15 @@ __device__ __forceinline__ void gemm_mma8(const i32x8 (&a)[2], const i32x8 (&b)[
 // both stages were last read before that barrier.  The even step waits until
 // all but the newest step have landed (so s and s + 1 are in LDS) and then
 // passes the barrier; a step is read only during its own pair, so its stage
-// stays intact while the pair reads it.  The fp8 work of a pair (s, s + 1)
+// stays intact while the pair reads it.  The fp6 work of a pair (s, s + 1)
 // spreads over both steps:
-//   even s:  read the fp16 fragments of step s; fp8 MFMAs of the previous
+//   even s:  read the fp16 fragments of step s; fp6 MFMAs of the previous
 //            pair's row blocks 2-3 (zeros before the first pair); read this
-//            pair's B, the fp16 fragments of step s + 1 and the A bytes of
+//            pair's B, the fp16 fragments of step s + 1 and the A codes of
 //            row blocks 0-1; fp16 MFMAs of step s; convert B's Q16 half.
-//   odd s+1: read the A bytes of row blocks 2-3; fp16 MFMAs of step s + 1;
-//            fp8 MFMAs of row blocks 0-1.
-// Each step issues 12 MFMAs (8 fp16, 4 fp8).  Why waves 0-3 carry all the
+//   odd s+1: read the A codes of row blocks 2-3; fp16 MFMAs of step s + 1;
+//            fp6 MFMAs of row blocks 0-1.
+// Each step issues 12 MFMAs (8 fp16, 4 fp6).  Why waves 0-3 carry all the
 // DMA: the hardware gives the older of two waves on a SIMD the matrix core
 // first, so waves 0-3 (dispatched first) run ahead of waves 4-7 and reach the
 // barrier early; their DMA instructions, which can stall on the CU's memory
@@ -712,12 +812,13 @@ __device__ __forceinline__ void gemm_mma8(const i32x8 (&a)[2], const i32x8 (&b)[
 constexpr int kStages16 = 5;
 __device__ __forceinline__ uint8_t* stage16(uint8_t* smem, int k) { return smem + (k % kStages16) * kStage; }
 
-struct Ops8 {
+struct Ops6 {
   i32x8 a01[2], a23[2], b[2];
+  int sa01[2], sa23[2], sb;
 };
 
 template <bool kLone, bool kDma>
-__device__ __forceinline__ void gemm_even16(int s, uint8_t* smem, Frags16& cur, Frags16& nxt, Ops8& o,
+__device__ __forceinline__ void gemm_even16(int s, uint8_t* smem, Frags16& cur, Frags16& nxt, Ops6& o,
                                             f32x16 (&acc)[4][2], const uint8_t* __restrict__ pimg,
                                             const EOperand& eo, int kb0, int kb_last, int col0,
                                             const uint32_t (&voff)[2][4], const uint32_t (&poff)[4], int wave,
@@ -731,24 +832,24 @@ __device__ __forceinline__ void gemm_even16(int s, uint8_t* smem, Frags16& cur, 
   gemm_frags16(cur, stage16(smem, s), wm, wn, lane);
   if constexpr (kDma)
     gemm_dma16<true>(stage16(smem, s + 3), pimg, eo, min(kb0 + s + 3, kb_last), col0, voff, poff, wave);
-  gemm_mma8<2>(o.a23, o.b, acc);
+  gemm_mma6<2>(o.a23, o.sa23, o.b, o.sb, acc);
   // the previous pair's B is consumed before this pair's is read over it
   __builtin_amdgcn_sched_barrier(0);
   // reads in the order they are needed: B (converted at the end of this
   // step), the next step's fp16 fragments (first MFMAs of the odd step), the A
-  // bytes of row blocks 0-1 (last MFMAs of the odd step)
+  // codes of row blocks 0-1 (last MFMAs of the odd step)
   const int h = lane >> 5;
-  Raw8 raw;
-  gemm_reads8b(o.b, raw, stage16(smem, s), stage16(smem, s + h), wn, lane);
+  Raw6 raw;
+  gemm_reads6b(o.b, o.sb, raw, stage16(smem, s), stage16(smem, s + h), wn, lane);
   gemm_frags16(nxt, stage16(smem, s + 1), wm, wn, lane);
-  gemm_reads8a<0>(o.a01, stage16(smem, s + h), wm, lane);
+  gemm_reads6a<0>(o.a01, o.sa01, stage16(smem, s + h), wm, lane);
   gemm_mma16(cur, acc);
   __builtin_amdgcn_sched_barrier(0);
-  gemm_convert8b<kLone>(o.b, raw, lane);
+  gemm_convert6b<kLone>(o.b, o.sb, raw, lane);
 }
 
 template <bool kDma>
-__device__ __forceinline__ void gemm_odd16(int s1, uint8_t* smem, Frags16& cur, Ops8& o, f32x16 (&acc)[4][2],
+__device__ __forceinline__ void gemm_odd16(int s1, uint8_t* smem, Frags16& cur, Ops6& o, f32x16 (&acc)[4][2],
                                            const uint8_t* __restrict__ pimg, const EOperand& eo, int kb0,
                                            int kb_last, int col0, const uint32_t (&voff)[2][4],
                                            const uint32_t (&poff)[4], int wave, int wm, int lane) {
@@ -757,12 +858,12 @@ __device__ __forceinline__ void gemm_odd16(int s1, uint8_t* smem, Frags16& cur, 
     gemm_dma16<false>(stage16(smem, s1 + 3), pimg, eo, min(kb0 + s1 + 3, kb_last), col0, voff, poff, wave);
   __builtin_amdgcn_sched_barrier(0);
   // reads first (consumed after the next barrier), then the fp16 MFMAs on
-  // fragments read in the even step, then the fp8 ones on the A bytes read
+  // fragments read in the even step, then the fp6 ones on the A codes read
   // last there
-  gemm_reads8a<2>(o.a23, stage16(smem, s1 - 1 + (lane >> 5)), wm, lane);
+  gemm_reads6a<2>(o.a23, o.sa23, stage16(smem, s1 - 1 + (lane >> 5)), wm, lane);
   gemm_mma16(cur, acc);
   __builtin_amdgcn_sched_barrier(0);
-  gemm_mma8<0>(o.a01, o.b, acc);
+  gemm_mma6<0>(o.a01, o.sa01, o.b, o.sb, acc);
 }
 
 // The whole k loop of one wave.  kDma: waves 0-3, which send the steps.
@@ -772,9 +873,13 @@ __device__ __forceinline__ void gemm_loop16(uint8_t* smem, f32x16 (&acc)[4][2], 
                                             const uint32_t (&voff)[2][4], const uint32_t (&poff)[4], int wave,
                                             int wm, int wn, int lane) {
   Frags16 ga, gb;
-  Ops8 o;
+  Ops6 o;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) o.a01[i] = o.a23[i] = o.b[i] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
+  for (int i = 0; i < 2; ++i) {
+    o.a01[i] = o.a23[i] = o.b[i] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
+    o.sa01[i] = o.sa23[i] = 127;
+  }
+  o.sb = 127;
   int s = 0;
   for (; s + 1 < nsteps; s += 2) {
     gemm_even16<false, kDma>(s, smem, ga, gb, o, acc, pimg, eo, kb0, kb_last, col0, voff, poff, wave, wm, wn, lane);
@@ -784,10 +889,10 @@ __device__ __forceinline__ void gemm_loop16(uint8_t* smem, f32x16 (&acc)[4][2], 
     // the split's last k-block has no partner: its corrections go alone.  Its
     // stage and the next (the clamped repeat) are in LDS by the barrier.
     gemm_even16<true, kDma>(s, smem, ga, gb, o, acc, pimg, eo, kb0, kb_last, col0, voff, poff, wave, wm, wn, lane);
-    gemm_reads8a<2>(o.a23, stage16(smem, s + (lane >> 5)), wm, lane);
-    gemm_mma8<0>(o.a01, o.b, acc);
+    gemm_reads6a<2>(o.a23, o.sa23, stage16(smem, s + (lane >> 5)), wm, lane);
+    gemm_mma6<0>(o.a01, o.sa01, o.b, o.sb, acc);
   }
-  gemm_mma8<2>(o.a23, o.b, acc);
+  gemm_mma6<2>(o.a23, o.sa23, o.b, o.sb, acc);
 }
 
 // Iteration s of the pipeline: step s+1 has landed in LDS (waited before the
@@ -979,7 +1084,7 @@ __global__ __launch_bounds__(256) void samp_combine(const float* __restrict__ lo
       merge_partial(r, q, c_t);
     }
     const bool bad = r.bad || !(r.m > -INFINITY);
-    // z_s of the fp16 + fp8 contraction is in units of 2^(14 + c)
+    // z_s of the fp16 + fp6 contraction is in units of 2^(14 + c)
     const float inv_s1 = (1.0f / r.s1) * (tail ? tail->zscale : 1.0f);
     for (int sp = threadIdx.x; sp < n_splits; sp += kWave)
       s_w[sp] = rescale_factor(pr[sp].m, r.m, kLog2e) * inv_s1;
@@ -1753,12 +1858,22 @@ static size_t embedding_image_bytes(int vocab, int d) {
   return n_pairs * n_tiles * kEBlock;
 }
 
+// one row-shift byte per id of the padded vocabulary (whole k-block pairs), 256-byte aligned
+static size_t shift_bytes(int vocab) {
+  const size_t n_pairs = ((size_t)(vocab + kKB - 1) / kKB + 1) / 2;
+  return align_up(n_pairs * 2 * kKB, 256);
+}
+
 size_t embedding_packed_bytes(int vocab, int d) {
-  return embedding_image_bytes(vocab, d) + kAmaxParts * sizeof(float) + kPackTailBytes;
+  return embedding_image_bytes(vocab, d) + shift_bytes(vocab) + kAmaxParts * sizeof(float) + kPackTailBytes;
+}
+
+static const uint8_t* pack_shifts(const void* packed, int vocab, int d) {
+  return static_cast<const uint8_t*>(packed) + embedding_image_bytes(vocab, d);
 }
 
 static const PackTail* pack_tail(const void* packed, int vocab, int d) {
-  return reinterpret_cast<const PackTail*>(static_cast<const uint8_t*>(packed) + embedding_image_bytes(vocab, d) +
+  return reinterpret_cast<const PackTail*>(pack_shifts(packed, vocab, d) + shift_bytes(vocab) +
                                            kAmaxParts * sizeof(float));
 }
 
@@ -1766,7 +1881,8 @@ hipError_t launch_embedding_pack(const float* emb, void* packed, int vocab, int 
   const int n_pairs = ((vocab + kKB - 1) / kKB + 1) / 2;
   const int n_tiles = (d + kGN - 1) / kGN;
   uint8_t* base = static_cast<uint8_t*>(packed);
-  float* part = reinterpret_cast<float*>(base + embedding_image_bytes(vocab, d));
+  uint8_t* shifts = base + embedding_image_bytes(vocab, d);
+  float* part = reinterpret_cast<float*>(shifts + shift_bytes(vocab));
   PackTail* tail = const_cast<PackTail*>(pack_tail(packed, vocab, d));
   prof_begin("emb_pack", s);
   emb_amax_kernel<<<kAmaxParts, 256, 0, s>>>(emb, (size_t)vocab * (size_t)d, part);
@@ -1776,7 +1892,12 @@ hipError_t launch_embedding_pack(const float* emb, void* packed, int vocab, int 
     e = hipGetLastError();
   }
   if (e == hipSuccess) {
-    emb_pack_kernel<<<dim3(2 * n_pairs, n_tiles), 256, 0, s>>>(emb, base, vocab, d, n_tiles, tail);
+    const int n_ids = (int)shift_bytes(vocab);
+    emb_shift_kernel<<<n_ids / 4, 256, 0, s>>>(emb, vocab, d, n_ids, tail, shifts);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    emb_pack_kernel<<<dim3(2 * n_pairs, n_tiles), 256, 0, s>>>(emb, base, vocab, d, n_tiles, tail, shifts);
     e = hipGetLastError();
   }
   prof_end(s);
@@ -1825,11 +1946,12 @@ hipError_t launch_sampler(const SamplerPlan& p, const float* logits, const void*
   float* zp = reinterpret_cast<float*>(base + p.off_zp);
   const bool aligned = (p.vocab % 4) == 0;
 
+  const uint8_t* shifts = eb.emb_f32 ? nullptr : pack_shifts(emb_packed, p.vocab, p.d);
   prof_begin("samp_stats", s);
   const dim3 sgrid(p.n_splits, (p.n + kStatsRows - 1) / kStatsRows);
 #define DG_STATS(A, F)                                                                                  \
-  samp_stats<A, F><<<sgrid, kStatsThreadsWG, 0, s>>>(logits, ctrl, part, pimg, p.n, p.n_canvas, p.vocab, \
-                                                     p.kb_per_split, p.n_kb, eb.on)
+  samp_stats<A, F><<<sgrid, kStatsThreadsWG, 0, s>>>(logits, ctrl, part, pimg, shifts, p.n, p.n_canvas, \
+                                                     p.vocab, p.kb_per_split, p.n_kb, eb.on)
   if (eb.emb_f32) {
     if (aligned) DG_STATS(true, false);
     else DG_STATS(false, false);

@@ -217,11 +217,14 @@ size_t dg_sampler_workspace_bytes(int n_canvas, int vocab, int d_model);
 
 /*
  * The embedding table E in the layout the sampler streams.  The contraction
- * z = softmax(logits)·E runs on fp16 and fp8 matrix cores in split precision:
- * with Q = E·2^c (c chosen so that max|Q| lies in [2^7, 2^8)), each element
- * is held as Q16 = fp16(Q) plus one e4m3 byte, fp8((Q - Q16)·2^11) (3 bytes;
- * the contraction forms fp8(Q16) itself), so E is converted once, when the
- * weights are loaded, rather than on every step:
+ * z = softmax(logits)·E runs on fp16 and fp6 matrix cores in split precision.
+ * Each row k is held at its own scale, Q_k = E_k·2^(c + d_k): c brings
+ * max|E|·2^c into [2^7, 2^8) and the row shift d_k (0-40) brings row k's own
+ * maximum there too (zero rows take 40).  Each element is held as
+ * Q16 = fp16(Q) plus an e2m3 (fp6) code of (Q - Q16)·2^11 under a power-of-two
+ * scale shared by 16 ids and 64 columns (3 bytes per element; the contraction
+ * forms the codes of Q16 itself), so E is converted once, when the weights are
+ * loaded, rather than on every step:
  *   emb        [vocab, d_model] float32 (input)
  *   packed     dg_embedding_packed_bytes(vocab, d_model) bytes (output).  Ids
  *              are grouped in blocks of 16 and the blocks in pairs (ids past
@@ -229,14 +232,20 @@ size_t dg_sampler_workspace_bytes(int n_canvas, int vocab, int d_model);
  *              zero padded).  For pair j and tile t, a 24576-byte block at
  *              (j·n_tiles + t)·24576: the 256 columns' fp16 Q16 of the pair's
  *              first 16 ids (32 bytes per column, id order), the same for the
- *              second 16 ids, then per column the 16 residual bytes of the
- *              first block and the 16 of the second.  After the blocks: 4096
- *              bytes the pack uses as working space, then a 256-byte record:
- *              float 2^-(14 + c), int32 c.
+ *              second 16 ids, then per column 16 bytes for the first block and
+ *              16 for the second: 12 bytes of e2m3 codes (code i at bits
+ *              6i..6i+5, little-endian), the scale byte 127 + eB (the codes are
+ *              of (Q - Q16)·2^11 / 2^eB, eB the smallest exponent, at least
+ *              -126, with the block's and 64-column group's largest |Q - Q16|·2^11
+ *              and |Q16| at most 7.5·2^eB; nearest, ties to the even code) and
+ *              three zero bytes.  After the blocks: the row shifts d_k, one
+ *              byte per id of the whole block pairs (ids past vocab: 40),
+ *              padded to a multiple of 256 bytes; 4096 bytes the pack uses as
+ *              working space; a 256-byte record: float 2^-(14 + c), int32 c.
  * E is expected finite: a non-finite entry makes z undefined (c = 0 then; a
  * zero table also gives c = 0).  c is at most 80 (tables with max|E| below
- * 2^-72 keep fewer bits).  The caller owns both buffers.
- * Asynchronous on `stream`.
+ * 2^-72 keep fewer bits), and so are rows 2^40 below the largest.  The caller
+ * owns both buffers.  Asynchronous on `stream`.
  */
 size_t dg_embedding_packed_bytes(int vocab, int d_model);
 int dg_embedding_pack(const float* emb, void* packed, int vocab, int d_model, hipStream_t stream);

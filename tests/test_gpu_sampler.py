@@ -5,6 +5,7 @@ from dataclasses import replace
 import numpy as np
 import pytest
 
+import e2m3
 import workloads
 from gpu_util import check_step, check_z, log, require_gpu, to_dev
 from oracle import sampler as S
@@ -134,6 +135,33 @@ def test_short_splits(n_kb):
     ref = S.sampler_step(logits, emb, ids, mask, ctrl)
     assert check_step(ids, mask, gids, gmask, gk, ref, 0.9) == 0
     check_z(gz, ref["z"])
+
+
+@pytest.mark.parametrize("spread", [6, 30])
+def test_rows_of_very_different_size(spread):
+    """Table rows scaled by 2^u, u uniform in [-spread, 0], some rows zero, and
+    one large row among small ones in every k-block: each row is held at its
+    own scale (the row shifts), so z meets the bound where one block-wide
+    scale would lose the small rows' corrections."""
+    torch, dg = require_gpu()
+    n, vocab, d = 96, 4099, 200
+    log(f"sampler row sizes spread={spread}")
+    rng = np.random.default_rng(spread)
+    emb = (rng.standard_normal((vocab, d)) * 0.02).astype(np.float32)
+    emb *= np.exp2(rng.uniform(-spread, 0, vocab))[:, None].astype(np.float32)
+    emb[::16] *= np.float32(2.0 ** spread)
+    emb[5::23] = 0.0
+    logits = (rng.standard_normal((n, vocab)) * 2).astype(np.float32)
+    logits[::5, 17] += 8.0
+    ids = rng.integers(0, vocab, n).astype(np.int32)
+    mask = (rng.random(n) < 0.2).astype(np.uint8)
+    ctrl = S.Ctrl(seed=3, gstep=1, tau=0.9, flags=S.AUTO_ADVANCE)
+    g = GpuSampler(torch, dg, emb, ids, mask, ctrl)
+    gids, gmask, gk, gz, gnu = g.step(logits)
+    ref = S.sampler_step(logits, emb, ids, mask, ctrl)
+    assert check_step(ids, mask, gids, gmask, gk, ref, 0.9) == 0
+    worst, total = check_z(gz, ref["z"])
+    log(f"row sizes spread={spread}: z relative L2 worst row {worst:.3e}")
 
 
 @pytest.mark.parametrize("scale", [300.0, 1e-5, 0.02])
@@ -290,44 +318,67 @@ def test_deterministic_and_resume():
         np.testing.assert_array_equal(x, y)
 
 
-def _fp8_bytes(torch, x):
-    """float32 -> e4m3 codes, round to nearest even (torch's float8_e4m3fn)."""
-    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn)
-    return t.view(torch.uint8).numpy()
+def _row_shifts(emb, c):
+    """d_k = min(max(8 - c - e_k, 0), 40) with max|E_k| in [2^(e_k - 1), 2^e_k); 40 for zero rows."""
+    m = np.abs(emb).max(axis=1).astype(np.float64)
+    e = np.frexp(m)[1]
+    return np.where(m > 0, np.clip(8 - c - e, 0, 40), 40).astype(np.int64)
 
 
-@pytest.mark.parametrize("vocab,d,scale", [(37, 260, 0.02), (4096, 512, 0.02), (16, 1, 0.02), (300, 64, 700.0),
-                                           (64, 8, 3e-6), (48, 300, 0.5)])
-def test_embedding_pack_layout(vocab, d, scale):
-    """The packed table: Q = E 2^c with max|Q| in [2^7, 2^8); for each pair of
-    16-id k-blocks and 256-column tile a 24 KB block holding the fp16 Q16 of
-    k-block 2j (256 columns x 16 ids), those of k-block 2j + 1, then per column
-    the e4m3 bytes of (Q - Q16) 2^11 for k-block 2j and for 2j + 1; after the
-    blocks, 1024 floats of pack workspace and the record (2^-(14+c), c).  Every
-    byte is compared with numpy's fp16 and torch's e4m3 rounding."""
+@pytest.mark.parametrize("vocab,d,scale,spread", [(37, 260, 0.02, 0), (4096, 512, 0.02, 0), (16, 1, 0.02, 0),
+                                                  (300, 64, 700.0, 0), (64, 8, 3e-6, 0), (48, 300, 0.5, 0),
+                                                  (1000, 96, 0.02, 12), (77, 130, 1e-3, 50)])
+def test_embedding_pack_layout(vocab, d, scale, spread):
+    """The packed table: c such that max|E| 2^c lies in [2^7, 2^8), and for
+    each id a shift d_k so that row k's Q = E_k 2^(c + d_k) reaches that range
+    too (at most 40); for each pair of 16-id k-blocks and 256-column tile a
+    24 KB block holding the fp16 Q16 of k-block 2j (256 columns x 16 ids),
+    those of k-block 2j + 1, then per column 16 bytes for k-block 2j and 16 for
+    2j + 1: the e2m3 codes of (Q - Q16) 2^11 (12 bytes, code i at bit 6i) under
+    the scale 2^eB of the k-block and 64-column group, the byte 127 + eB and
+    three zeros; after the blocks, the shift bytes (one per id of the whole
+    k-block pairs, 256-byte aligned), 1024 floats of pack workspace and the
+    record (2^-(14+c), c).  Every byte is compared with numpy's fp16 rounding
+    and the e2m3 model.  spread > 0 scales the rows by 2^u, u uniform in
+    [-spread, 0] (rows far apart in size, some zero)."""
     torch, dg = require_gpu()
     rng = np.random.default_rng(vocab + d)
     emb = (rng.standard_normal((vocab, d)) * scale).astype(np.float32)
+    if spread:
+        emb *= np.exp2(np.round(rng.uniform(-spread, 0, vocab)))[:, None].astype(np.float32)
+        emb[::7] = 0.0
     packed = dg.dg_embedding_pack(to_dev(emb)).cpu().numpy()
     n_pairs, n_tiles = -(-vocab // 32), -(-d // 256)
     image = n_pairs * n_tiles * 24576
-    assert packed.size == image + 4096 + 256 == dg.dg_embedding_packed_bytes(vocab, d)
-    zscale = packed[image + 4096:image + 4100].view(np.float32)[0]
-    c = int(packed[image + 4100:image + 4104].view(np.int32)[0])
+    n_sh = -(-n_pairs * 32 // 256) * 256
+    assert packed.size == image + n_sh + 4096 + 256 == dg.dg_embedding_packed_bytes(vocab, d)
+    tail = image + n_sh + 4096
+    zscale = packed[tail:tail + 4].view(np.float32)[0]
+    c = int(packed[tail + 4:tail + 8].view(np.int32)[0])
     top = float(np.abs(emb).max()) * 2.0 ** c
     assert 128.0 <= top < 256.0, (c, top)
     assert zscale == np.float32(2.0 ** -(14 + c))
     full = np.zeros((n_pairs * 32, n_tiles * 256), np.float32)
     full[:vocab, :d] = emb
-    q = full * np.float32(2.0 ** c)                                   # [id, column]
+    shifts = np.full(n_sh, 40, np.int64)
+    shifts[:vocab] = _row_shifts(emb, c)
+    np.testing.assert_array_equal(packed[image:image + n_sh], shifts)
+    q = full * np.exp2(c + shifts[:n_pairs * 32])[:, None].astype(np.float32)    # [id, column], exact
     q16 = q.astype(np.float16)
-    qe8 = _fp8_bytes(torch, (q - q16.astype(np.float32)) * np.float32(2048.0))
+    qe = ((q - q16.astype(np.float32)) * np.float32(2048.0)).astype(np.float64)
+    nb, ng = n_pairs * 2, n_tiles * 4
+    m = np.maximum(np.abs(qe), np.abs(q16.astype(np.float64))).reshape(nb, 16, ng, 64).max(axis=(1, 3))
+    eb = e2m3.scale_exp(m, -126)                                      # [kb, group]
+    codes = e2m3.encode(qe.reshape(nb, 16, ng, 64) / np.exp2(eb)[:, None, :, None])
+    chunk = np.zeros((nb, ng, 64, 16), np.uint8)                      # [kb, group, column, byte]
+    chunk[..., :12] = e2m3.pack16(codes.transpose(0, 2, 3, 1))
+    chunk[..., 12] = np.broadcast_to((127 + eb)[:, :, None], (nb, ng, 64))
     # reference blocks [pair, tile, 24576]
     q16_kb = q16.reshape(n_pairs, 2, 16, n_tiles, 256).transpose(0, 3, 1, 4, 2)     # [pair, tile, kb&1, col, id]
-    qe_kb = qe8.reshape(n_pairs, 2, 16, n_tiles, 256).transpose(0, 3, 4, 1, 2)      # [pair, tile, col, kb&1, id]
+    res_kb = chunk.reshape(n_pairs, 2, n_tiles, 256, 16).transpose(0, 2, 3, 1, 4)   # [pair, tile, col, kb&1, byte]
     blocks = packed[:image].reshape(n_pairs, n_tiles, 24576)
     np.testing.assert_array_equal(blocks[:, :, :16384].copy().view(np.float16).reshape(q16_kb.shape), q16_kb)
-    np.testing.assert_array_equal(blocks[:, :, 16384:].reshape(qe_kb.shape), qe_kb)
+    np.testing.assert_array_equal(blocks[:, :, 16384:].reshape(res_kb.shape), res_kb)
 
 
 @pytest.mark.parametrize("n,vocab,d", [(256, 262144, 3072), (256, 4097, 260), (17, 12345, 516), (1, 2, 4)])
