@@ -216,26 +216,36 @@ constexpr int kStatsThreadsWG = 64 * kStatsRows * kStatsWavesPerRow;
 // consecutive logits, and lanes 4k .. 4k + 3 hold one k-block.  The logits
 // are read from HBM once and kept in registers: the split maximum is reduced
 // first, then the same registers give exp(l - m_s), the sums and the p
-// image records (kF16: fp16 + fp6 from p_record, else bf16 hi / lo).  For the
-// fp6 records a lane needs a whole k-block: each quad passes its weights
-// through a per-wave LDS area so that lane 4k + q takes k-block 64 q + k' of
-// the round (k' = L / 4), all 16 ids.  Each round's image slots are staged in
-// LDS as
-// [k-block][2 rows][64 B] and leave as 1 KB per store instruction (8 k-blocks'
-// 128-byte lines; staging through LDS measured faster than storing from the
-// registers, and whole lines measured faster than one row's 64-byte halves).
+// image records (kF16: fp16 + fp6 from p_record, else bf16 hi / lo).  Each
+// round's image slots are staged in LDS and leave as 1 KB per store
+// instruction (8 k-blocks' 128-byte lines of the image; staging through LDS
+// measured faster than storing from the registers, and whole lines measured
+// faster than one row's 64-byte halves).  For the fp6 records a lane needs a
+// whole k-block: each lane writes its weights P' (already carrying the row
+// shifts, which the split holds in LDS) into the slot of their k-block, and
+// lane 4k + q then reads k-block 64 q + k' (k' = L / 4) back whole and
+// replaces it with its record.  The four writers of a slot are the lanes of
+// one quad, in the same wave, so no barrier separates the two.  Four waves
+// per SIMD are kept (128 registers: two values spill, stored at the start and
+// reloaded at the end).
+//
+// The staging holds one round's slots as [row][k-block][64 B], the 16-byte
+// chunk position xor-swizzled with bits 6-7 of the k-block (the quad place of
+// the lane that takes it), so that a wave's 16-byte accesses to the same chunk
+// of 64 k-blocks spread over all banks.
+__device__ __forceinline__ int stage_off(int r, int kb_local, int chunk) {
+  return (r * kStatsLanes + kb_local) * kImgRow + 16 * (chunk ^ ((kb_local >> 6) & 3));
+}
+
 template <bool kAligned, bool kF16>
-__global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __restrict__ logits,
-                                                              const dg_ctrl* __restrict__ ctrl,
-                                                              StatsPartial* __restrict__ part,
-                                                              uint8_t* __restrict__ pimg,
-                                                              const uint8_t* __restrict__ shifts, int n_rows,
-                                                              int n_canvas, int vocab, int kb_per_split,
-                                                              int n_kb, bool want_h) {
+__global__ __launch_bounds__(kStatsThreadsWG) __attribute__((amdgpu_waves_per_eu(4)))
+void samp_stats(const float* __restrict__ logits, const dg_ctrl* __restrict__ ctrl,
+                StatsPartial* __restrict__ part, uint8_t* __restrict__ pimg,
+                const uint8_t* __restrict__ shifts, int n_rows, int n_canvas, int vocab, int kb_per_split,
+                int n_kb, bool want_h) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[kStatsLanes * kStatsRows * kImgRow];
-  // kF16: each wave's weights of one round, regrouped so that a lane holds one
-  // whole k-block (4 KB per wave)
-  __shared__ __attribute__((aligned(16))) uint8_t regroup[kF16 ? kStatsThreadsWG / 64 * 4096 : 16];
+  // kF16: the row shifts of the split's k-blocks (16 bytes each)
+  __shared__ __attribute__((aligned(16))) uint8_t shl[kF16 ? kMaxKbPerSplit * kKB : 16];
   __shared__ StatsPartial red[kStatsRows][kStatsWavesPerRow];
   const int split = blockIdx.x;
   const int t = threadIdx.x;
@@ -261,6 +271,18 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
   const int kb1 = min(n_kb, kb0 + kb_per_split);
   const int id_end = min(vocab, kb1 * kKB);          // first id past this split
 
+  if constexpr (kF16) {
+    // the split's shift bytes into LDS by direct loads, 1 KB per instruction
+    // (bytes past the split read as zero); they land before the barrier that
+    // follows the logits' first pass
+    const __amdgpu_buffer_rsrc_t rs = rsrc(shifts + (size_t)kb0 * kKB, (uint32_t)(kb1 - kb0) * kKB);
+#pragma unroll
+    for (int k = 0; k < kMaxKbPerSplit * kKB / 1024 / (kStatsThreadsWG / 64); ++k) {
+      const int piece = wave + (kStatsThreadsWG / 64) * k;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(shl + 1024 * piece), 16, 1024 * piece + 16 * lane, 0,
+                                               0, 0);
+    }
+  }
   // group c: first id, and whether it lies in the split
   auto gid0 = [&](int c) { return kb0 * kKB + 4 * (kStatsLanes * c + L); };
   f32x4 v[kStatsChunks];
@@ -302,6 +324,7 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
   for (int o = 32; o > 0; o >>= 1) bad |= __shfl_xor(bad, o);
   const int qw = wave % kStatsWavesPerRow;
   if (lane == 0) red[r][qw] = StatsPartial{m, 0.f, 0.f, bid, gbest, gid, bad, 0.f};
+  if constexpr (kF16) wait_vmcnt<0>();   // this wave's shift loads have landed in LDS
   __syncthreads();
   {
     StatsPartial acc = red[r][0];
@@ -322,12 +345,6 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
   for (int i = 0; i < kStatsIters; ++i) {
     const int base = kb0 + kStatsLanes * i;
     if (base >= kb1) break;   // uniform over the workgroup
-    // kF16: this lane's k-block of the round (64 (L % 4) + L / 4) and its ids' row shifts
-    const int kbl = base + 64 * (L % 4) + L / 4;
-    u32x4 dsh = (u32x4){0u, 0u, 0u, 0u};
-    if constexpr (kF16)
-      if (kbl < kb1) dsh = *reinterpret_cast<const u32x4*>(shifts + (size_t)kbl * kKB);
-    uint8_t* rg = regroup + (kF16 ? (wave * 4096 + (lane >> 2) * 64) : 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int c = 4 * i + q;
@@ -344,34 +361,41 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
         }
       }
       // k-block 64 q + L / 4 of the round, ids 4 (L % 4) .. 4 (L % 4) + 3 of it
+      const int kbq = kStatsLanes / 4 * q + L / 4;
       if constexpr (kF16) {
-        // to the lane of this quad that takes k-block 64 q + L / 4 (chunk
-        // position xor-swizzled by the lane's place in the quad)
-        *reinterpret_cast<f32x4*>(rg + q * 1024 + 16 * ((L % 4) ^ q)) = (f32x4){pp[0], pp[1], pp[2], pp[3]};
+        // P' = p 2^(14 - d) per id, in the slot (chunk L % 4) of the lane that
+        // takes this k-block
+        const uint32_t d4 =
+            *reinterpret_cast<const uint32_t*>(shl + (size_t)(kStatsLanes * i + kbq) * kKB + 4 * (L % 4));
+        f32x4 w4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w4[e] = __builtin_ldexpf(pp[e], kPExp - (int)((d4 >> (8 * e)) & 0xffu));
+        *reinterpret_cast<f32x4*>(stage + stage_off(r, kbq, L % 4)) = w4;
       } else {
-        uint8_t* slot = stage + ((kStatsLanes / 4 * q + L / 4) * kStatsRows + r) * kImgRow;
         uint32_t hi[2], lo[2];
         split2(pp[0], pp[1], hi[0], lo[0]);
         split2(pp[2], pp[3], hi[1], lo[1]);
-        *reinterpret_cast<uint2*>(slot + (L % 4) * 8) = make_uint2(hi[0], hi[1]);
-        *reinterpret_cast<uint2*>(slot + 32 + (L % 4) * 8) = make_uint2(lo[0], lo[1]);
+        *reinterpret_cast<uint2*>(stage + stage_off(r, kbq, (L % 4) >> 1) + 8 * (L & 1)) = make_uint2(hi[0], hi[1]);
+        *reinterpret_cast<uint2*>(stage + stage_off(r, kbq, 2 + ((L % 4) >> 1)) + 8 * (L & 1)) =
+            make_uint2(lo[0], lo[1]);
       }
     }
     if constexpr (kF16) {
-      // the 16 weights of k-block kbl (the quad's lanes wrote them in this
-      // wave, so no barrier is needed), scaled by 2^(14 - d) per id
+      // this lane's k-block of the round, 64 (L % 4) + L / 4: its 16 weights
+      // P' (the quad's lanes wrote them into its slot in this wave, so no
+      // barrier is needed); the record then replaces them in the same slot
+      const int kbo = kStatsLanes / 4 * (L % 4) + L / 4;
       float x[16];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const f32x4 w4 = *reinterpret_cast<const f32x4*>(rg + (L % 4) * 1024 + 16 * (k ^ (L % 4)));
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(stage + stage_off(r, kbo, k));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * k + e] = __builtin_ldexpf(w4[e], kPExp - (int)((dsh[k] >> (8 * e)) & 0xffu));
+        for (int e = 0; e < 4; ++e) x[4 * k + e] = w4[e];
       }
       u32x4 rec[4];
       p_record(x, rec);
-      u32x4* slot = reinterpret_cast<u32x4*>(stage + ((kStatsLanes / 4 * (L % 4) + L / 4) * kStatsRows + r) * kImgRow);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) slot[k] = rec[k];
+      for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(stage + stage_off(r, kbo, k)) = rec[k];
     }
     __syncthreads();
     // write-out: the row slots of k-block kbl are contiguous; thread T moves
@@ -384,7 +408,8 @@ __global__ __launch_bounds__(kStatsThreadsWG) void samp_stats(const float* __res
       const int off = c % (kStatsRows * kImgRow / 16);          // 16-byte piece of the k-block's slots
       const int kb = base + kbl;
       if (kb < kb1 && row0 + off / (kImgRow / 16) < n_rows) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(stage + c * 16);
+        const u32x4 w =
+            *reinterpret_cast<const u32x4*>(stage + stage_off(off / (kImgRow / 16), kbl, off % (kImgRow / 16)));
         *reinterpret_cast<u32x4*>(pimg + ((size_t)mt * n_kb + kb) * kPImg + (size_t)(row0 % kGM) * kImgRow +
                                   off * 16) = w;
       }
