@@ -518,8 +518,18 @@ __global__ __launch_bounds__(256) void emb_shift_kernel(const float* __restrict_
   const int lane = threadIdx.x & 63;
   if (id >= n_ids) return;   // uniform over the wave
   float m = 0.0f;
-  if (id < vocab)
-    for (int j = lane; j < d; j += 64) m = fmaxf(m, fabsf(emb[(size_t)id * d + j]));
+  if (id < vocab) {
+    const float* row = emb + (size_t)id * d;
+    if ((d & 3) == 0 && (reinterpret_cast<uintptr_t>(emb) & 15) == 0) {
+      const f32x4* r4 = reinterpret_cast<const f32x4*>(row);
+      for (int j = lane; j < d / 4; j += 64) {
+        const f32x4 v = r4[j];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+      }
+    } else {
+      for (int j = lane; j < d; j += 64) m = fmaxf(m, fabsf(row[j]));
+    }
+  }
   m = wave_max(m);
   if (lane == 0) {
     int sh = 40;
