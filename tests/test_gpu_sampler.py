@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import e2m3
+import p_records as PR
 import workloads
 from gpu_util import check_step, check_z, log, require_gpu, to_dev
 from oracle import sampler as S
@@ -379,6 +380,65 @@ def test_embedding_pack_layout(vocab, d, scale, spread):
     blocks = packed[:image].reshape(n_pairs, n_tiles, 24576)
     np.testing.assert_array_equal(blocks[:, :, :16384].copy().view(np.float16).reshape(q16_kb.shape), q16_kb)
     np.testing.assert_array_equal(blocks[:, :, 16384:].reshape(res_kb.shape), res_kb)
+
+
+def _sampler_plan(n, vocab, d):
+    """The sampler's split plan (k-blocks of 16 ids; splits of an even number of
+    k-blocks, at least 16 and at most 1024 each, about 256 workgroups for the
+    contraction) and the byte offset of the p images in its workspace, after
+    the per-(row, split) statistics records of 32 bytes."""
+    n_mt, n_kb, n_tiles = -(-n // 256), -(-vocab // 16), -(-d // 256)
+    splits = max(256 // (n_tiles * n_mt), 1)
+    splits = min(splits, -(-n_kb // 16))
+    splits = max(splits, -(-n_kb // 1024), 1)
+    kbps = -(-n_kb // splits)
+    kbps += kbps & 1
+    n_splits = -(-n_kb // kbps)
+    return n_kb, kbps, n_splits, -(-(n * n_splits * 32) // 256) * 256
+
+
+@pytest.mark.parametrize("n,vocab,d", [(64, 4099, 200), (256, 20000, 64)])
+def test_p_image_records(n, vocab, d):
+    """The statistics pass's p records, read back from the workspace, against
+    their definition (tests/p_records.py): for row i and k-block k (split s),
+    P' = p 2^(14 - d_id) with p = exp2((l - m_s) log2 e) and d_id the table's
+    row shifts.  P'16 matches fp16 of the reference to one fp16 ulp (the
+    device's exp2 is not correctly rounded); the codes of P'16 match the e2m3
+    model exactly; es is the rule applied to the record's own values; the codes
+    of r are within half a code step of the reference residual
+    (tests/test_p_records_check.py shows the check rejecting planted mistakes)."""
+    torch, dg = require_gpu()
+    log(f"p records n={n} V={vocab} d={d}")
+    rng = np.random.default_rng(n + vocab)
+    emb = (rng.standard_normal((vocab, d)) * 0.02).astype(np.float32)
+    emb *= np.exp2(np.round(rng.uniform(-12, 0, vocab)))[:, None].astype(np.float32)
+    emb[3::29] = 0.0
+    logits = (rng.standard_normal((n, vocab)) * 2).astype(np.float32)
+    logits[::3, 11] += 9.0
+    packed = dg.dg_embedding_pack(to_dev(emb))
+    ws = torch.empty(dg.dg_sampler_workspace_bytes(n, vocab, d), dtype=torch.uint8, device="cuda")
+    ids = to_dev(rng.integers(0, vocab, n).astype(np.int32))
+    mask = to_dev(np.zeros(n, np.uint8))
+    z = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    kappa = torch.empty(n, dtype=torch.float32, device="cuda")
+    nu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ctrl = dg.make_ctrl(seed=1, tau=0.9, flags=0)
+    dg.dg_sampler_step(to_dev(logits), packed, ids, mask, z, kappa, nu, ctrl, workspace=ws)
+    torch.cuda.synchronize()
+    pk, wsb = packed.cpu().numpy(), ws.cpu().numpy()
+    n_kb, kbps, n_splits, off = _sampler_plan(n, vocab, d)
+    image = -(-vocab // 32) * -(-d // 256) * 24576
+    shifts = pk[image:image + n_kb * 16].astype(np.int64)
+    rec = wsb[off:off + n_kb * 256 * 64].reshape(n_kb, 256, 64)[:, :n]        # [kb, row, byte]; one row tile
+    # reference P' per (row, id): fp64 exp2, rounded to float32
+    lf = np.full((n, n_kb * 16), -np.inf, np.float32)
+    lf[:, :vocab] = logits
+    m_s = np.repeat(np.stack([lf[:, s * kbps * 16:(s + 1) * kbps * 16].max(axis=1) for s in range(n_splits)], 1),
+                    kbps * 16, axis=1)[:, :n_kb * 16]                                   # split maxima per id
+    log2e = np.float32(1.4426950408889634)
+    p = np.exp2(lf.astype(np.float64) * float(log2e) - m_s.astype(np.float64) * float(log2e))
+    pref = np.ldexp(p, (14 - shifts)[None, :]).astype(np.float32).reshape(n, n_kb, 16).transpose(1, 0, 2)
+    PR.check_records(rec, pref)
 
 
 @pytest.mark.parametrize("n,vocab,d", [(256, 262144, 3072), (256, 4097, 260), (17, 12345, 516), (1, 2, 4)])
