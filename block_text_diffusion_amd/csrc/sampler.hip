@@ -755,22 +755,9 @@ __device__ __forceinline__ void gemm_reads6a(i32x8 (&a)[2], int (&sa)[2], const 
   }
 }
 
-// B: the residual codes and scale (chunk 2 + h of stage s) now, and the 16 Q16 values of
-// k-block s + h (two chunks) raw, for gemm_convert6b.  The Q16 chunks are read
-// first, so their conversion waits for the fewest reads.
-struct Raw6 {
-  u32x4 q0[2], q1[2];
-};
-
-__device__ __forceinline__ void gemm_reads6b(i32x8 (&b)[2], int& sb, Raw6& r, const uint8_t* stage_s,
-                                             const uint8_t* stage_h, int wn, int lane) {
+// B: the residual codes and scale of k-block s + h (chunk 2 + h of stage s)
+__device__ __forceinline__ void gemm_reads6b(i32x8 (&b)[2], int& sb, const uint8_t* stage_s, int wn, int lane) {
   const int h = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rb = 64 * wn + 32 * i + (lane & 31);
-    r.q0[i] = *reinterpret_cast<const u32x4*>(stage_h + kArr + swz_off(rb, 0));
-    r.q1[i] = *reinterpret_cast<const u32x4*>(stage_h + kArr + swz_off(rb, 1));
-  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int rb = 64 * wn + 32 * i + (lane & 31);
@@ -780,6 +767,30 @@ __device__ __forceinline__ void gemm_reads6b(i32x8 (&b)[2], int& sb, Raw6& r, co
 #pragma unroll
     for (int e = 0; e < 3; ++e) b[i][e] = (int)qe[e];
     if (i == 0) sb = (int)qe[3];
+  }
+}
+
+// The 16 Q16 values of k-block s + h for both column blocks (ids 0-7 in q0,
+// 8-15 in q1), from the fp16 B fragments instead of LDS: lane half 0 holds
+// chunk 0 (ids 0-7) of steps s (cur) and s + 1 (nxt), half 1 chunk 1 (ids
+// 8-15); one swap between the halves (v_permlane32_swap: the upper half of
+// its first operand trades places with the lower half of its second) leaves
+// every lane both chunks of its own k-block.
+struct Raw6 {
+  u32x4 q0[2], q1[2];
+};
+
+__device__ __forceinline__ void gemm_q16_exchange(Raw6& r, const Frags16& cur, const Frags16& nxt) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const u32x4 c4 = __builtin_bit_cast(u32x4, cur.b[i]);
+    const u32x4 n4 = __builtin_bit_cast(u32x4, nxt.b[i]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(c4[e], n4[e], false, false);
+      r.q0[i][e] = sw[0];
+      r.q1[i][e] = sw[1];
+    }
   }
 }
 
@@ -870,14 +881,16 @@ __device__ __forceinline__ void gemm_even16(int s, uint8_t* smem, Frags16& cur, 
   gemm_mma6<2>(o.a23, o.sa23, o.b, o.sb, acc);
   // the previous pair's B is consumed before this pair's is read over it
   __builtin_amdgcn_sched_barrier(0);
-  // reads in the order they are needed: B (converted at the end of this
-  // step), the next step's fp16 fragments (first MFMAs of the odd step), the A
-  // codes of row blocks 0-1 (last MFMAs of the odd step)
+  // reads in the order they are needed: B's residual codes, the next step's
+  // fp16 fragments (first MFMAs of the odd step; with this step's they also
+  // give B's Q16 values), the A codes of row blocks 0-1 (last MFMAs of the odd
+  // step)
   const int h = lane >> 5;
-  Raw6 raw;
-  gemm_reads6b(o.b, o.sb, raw, stage16(smem, s), stage16(smem, s + h), wn, lane);
+  gemm_reads6b(o.b, o.sb, stage16(smem, s), wn, lane);
   gemm_frags16(nxt, stage16(smem, s + 1), wm, wn, lane);
   gemm_reads6a<0>(o.a01, o.sa01, stage16(smem, s + h), wm, lane);
+  Raw6 raw;
+  gemm_q16_exchange(raw, cur, nxt);
   gemm_mma16(cur, acc);
   __builtin_amdgcn_sched_barrier(0);
   gemm_convert6b<kLone>(o.b, o.sb, raw, lane);
