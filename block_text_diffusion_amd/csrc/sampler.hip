@@ -410,8 +410,11 @@ void samp_stats(const float* __restrict__ logits, const dg_ctrl* __restrict__ ct
       if (kb < kb1 && row0 + off / (kImgRow / 16) < n_rows) {
         const u32x4 w =
             *reinterpret_cast<const u32x4*>(stage + stage_off(off / (kImgRow / 16), kbl, off % (kImgRow / 16)));
-        *reinterpret_cast<u32x4*>(pimg + ((size_t)mt * n_kb + kb) * kPImg + (size_t)(row0 % kGM) * kImgRow +
-                                  off * 16) = w;
+        // non-temporal: the images stream out rather than stay dirty in this
+        // XCD's L2 (the contraction reads them from other XCDs); measured
+        // ~5 us onto this kernel and ~15 us off the contraction that follows
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(pimg + ((size_t)mt * n_kb + kb) * kPImg +
+                                                                  (size_t)(row0 % kGM) * kImgRow + off * 16));
       }
     }
     __syncthreads();
