@@ -243,9 +243,11 @@ size_t dg_sampler_workspace_bytes(int n_canvas, int vocab, int d_model);
  *              padded to a multiple of 256 bytes; 4096 bytes the pack uses as
  *              working space; a 256-byte record: float 2^-(14 + c), int32 c.
  * E is expected finite: a non-finite entry makes z undefined (c = 0 then; a
- * zero table also gives c = 0).  c is at most 80 (tables with max|E| below
- * 2^-72 keep fewer bits), and so are rows 2^40 below the largest.  The caller
- * owns both buffers.  Asynchronous on `stream`.
+ * zero table also gives c = 0).  c is at most 80; below max|E| = 2^-72 the
+ * row shifts carry the rest, which keeps full precision down to about 2^-90
+ * (further down the shifted weights leave fp16's normal range).  Rows more
+ * than 2^40 below the largest keep fewer bits.  The caller owns both buffers.
+ * Asynchronous on `stream`.
  */
 size_t dg_embedding_packed_bytes(int vocab, int d_model);
 int dg_embedding_pack(const float* emb, void* packed, int vocab, int d_model, hipStream_t stream);
