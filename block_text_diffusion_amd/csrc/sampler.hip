@@ -190,7 +190,9 @@ __device__ __forceinline__ void merge_partial(StatsPartial& r, const StatsPartia
 template <bool kAligned>
 __device__ __forceinline__ f32x4 load4(const float* __restrict__ x, int j, int vocab) {
   if (kAligned) {
-    if (j < vocab) return *reinterpret_cast<const f32x4*>(x + j);
+    // non-temporal: the logits are read once and should not displace
+    // lines that other workgroups will read again
+    if (j < vocab) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x + j));
     return (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   }
   f32x4 v;
@@ -667,7 +669,10 @@ __device__ __forceinline__ void gemm_dma16(uint8_t* stage, const uint8_t* __rest
   for (int j = 0; j < 4; ++j) {
     uint8_t* dst = stage + (64 * wave + 16 * j) * kImgRow;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)dst, 16, poff[j], 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[kOdd ? 1 : 0][j], 0, 0, 0);
+    // E with the non-temporal policy (the nt bit of the cache-policy
+    // argument): each line of the table is used once, while the p images
+    // stay in L2 for the split's other column tiles
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + kArr), 16, voff[kOdd ? 1 : 0][j], 0, 0, 2);
   }
 }
 
@@ -1095,7 +1100,9 @@ __global__ __launch_bounds__(kGThreads, 1) void samp_gemm(const uint8_t* __restr
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = kGM * mt + 128 * wm + 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < n_rows && col < d) out[(size_t)row * d + col] = acc[mb][nb][v];
+        // non-temporal: the partials leave as they are written instead of
+        // in one write-back at the kernel's end
+        if (row < n_rows && col < d) __builtin_nontemporal_store(acc[mb][nb][v], out + (size_t)row * d + col);
       }
     }
   }
